@@ -1,0 +1,18 @@
+"""fp64 CPU oracle for the TokenGate pruned-prefill layer (test infrastructure).
+
+Only tests/, __graft_entry__.smoke() and bench.py's CPU-baseline leg may
+import this package; the HIP library never does.
+"""
+
+from .tokengate import (  # noqa: F401
+    compact,
+    gate_scores,
+    gated_attention,
+    gated_prefill,
+    kept_rows,
+    logsigmoid,
+    prompt_of_rows,
+    select_topk,
+    sigmoid,
+    silu,
+)

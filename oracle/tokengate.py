@@ -1,0 +1,293 @@
+"""fp64 CPU oracle for the TokenGate pruned-prefill layer.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check in
+__graft_entry__ and the CPU-baseline leg of bench.py may import, call or
+execute anything in this package. The HIP library and its Python binding
+never import it, and it imports nothing from them: the two share no code,
+constants or helpers. It is written to be read against the pages, not to
+be fast.
+
+Sources (pages about "TokenGate: Adapting LLMs for Fast and
+Memory-Efficient Prefill with Learned Token Pruning"):
+
+  [DE-prune] spke.com article (German), section
+             "Wie hat TokenGate das Pruning von Tokens verstanden?":
+             three-phase forward; a small MLP scores every token from its
+             post-attention residual at the gate layer; a top-K selector
+             keeps the best-scored tokens; layers above the gate see only
+             the kept tokens and build no KV for the rest; only the
+             document part of the prompt can be pruned, never the question.
+  [DE-attn]  same article, section "Was ist token-gated Attention?":
+             each kept token's score becomes a bias on the attention logits
+             above the gate; a learnable per-head gain and a learnable
+             temperature (the latter for queries that now see fewer keys).
+  [DE-impl]  same article, section "Wie wird TokenGate implementiert?":
+             a placeholder marks the prunable document; generation takes a
+             kept-prefill-token budget; the attention kernel is a key-bias
+             attention.
+  [TH-how]   ai4bro.com post, section on how learned token pruning works
+             (same three phases; query tokens are never pruned).
+  [IT-keep]  ai.info news, section "TokenGate impara quali token mantenere":
+             the component ranks tokens at an intermediate layer and sends
+             only the kept tokens' representations upward.
+
+The pages fix the bias only qualitatively. The form used here, on both
+sides, is: logit_ij = q_i.k_j / (sqrt(D) * tau) + g_h * logsigmoid(s_j) for
+kept document keys, with bias 0 for keys outside the document span, and key
+j visible to query i iff pos_j <= pos_i (original positions).
+
+Readings taken where the pages are silent (each listed in the design notes):
+  * gate MLP: Linear(d->H) -> SiLU -> Linear(H->1); optional biases b1, b2
+    (default zero); the input is the raw residual;
+  * ties in the top-K go to the lower row id; -0 equals +0; NaN ranks
+    below every number;
+  * kept rows are emitted in ascending row order, prompt by prompt;
+  * one gain per query head, one scalar tau dividing only the q.k term;
+  * query head h reads KV head floor(h * Hkv / Hq) (contiguous groups).
+
+Parity pins: every function here is checked in tests/ against something
+other than itself (brute force on tiny inputs, closed forms, invariants, or
+a library routine it reduces to). None is unpinned.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Iterable, List, Optional, Sequence
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    """View any array-like (NumPy array, torch CPU tensor) as fp64 NumPy."""
+    if hasattr(a, "detach"):
+        a = a.detach().cpu()
+        if str(a.dtype) in ("torch.bfloat16", "torch.float16"):
+            a = a.float()
+        a = a.numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Step 1: gate score.  [DE-prune], [TH-how], [IT-keep]
+# ---------------------------------------------------------------------------
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    """Logistic function 1 / (1 + e^-z), evaluated without overflow."""
+    z = np.asarray(z, dtype=np.float64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = ez / (1.0 + ez)
+    return out
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z)."""
+    return z * sigmoid(z)
+
+
+def gate_scores(x, w1, w2, b1=None, b2: float = 0.0, block_rows: int = 8192) -> np.ndarray:
+    """Score every row r of the residual x[N, d]:
+
+        h_r = W1 x_r + b1        (W1 is [H, d], the nn.Linear layout)
+        s_r = w2 . SiLU(h_r) + b2
+
+    Returns s[N] in fp64. Rows are processed in blocks only to bound memory.
+    """
+    w1 = _f64(w1)
+    w2 = _f64(w2).reshape(-1)
+    b1v = None if b1 is None else _f64(b1).reshape(-1)
+    n = int(x.shape[0])
+    out = np.empty(n, dtype=np.float64)
+    for r0 in range(0, n, block_rows):
+        xb = _f64(x[r0:r0 + block_rows])
+        h = xb @ w1.T
+        if b1v is not None:
+            h = h + b1v
+        out[r0:r0 + xb.shape[0]] = silu(h) @ w2 + float(b2)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Step 2: top-K selection, document rows only.  [DE-prune], [TH-how], [DE-impl]
+# ---------------------------------------------------------------------------
+
+def _doc_rows(p) -> np.ndarray:
+    return np.arange(p.start + p.doc_begin, p.start + p.doc_end, dtype=np.int64)
+
+
+def select_topk(scores, prompts: Sequence) -> np.ndarray:
+    """Kept row ids for every prompt, concatenated in prompt order.
+
+    For each prompt: rank its document rows by score, highest first, ties
+    to the lower row id, NaN below every number (-0 and +0 compare equal);
+    keep the first k_doc of them; keep every row of the prompt outside the
+    document span; emit the kept rows in ascending row order.
+    """
+    s = np.asarray(_f64(scores) if hasattr(scores, "detach") else scores)
+    out: List[np.ndarray] = []
+    for p in prompts:
+        if not (0 <= p.doc_begin <= p.doc_end <= p.length):
+            raise ValueError("document span outside the prompt")
+        if not (0 <= p.k_doc <= p.doc_end - p.doc_begin):
+            raise ValueError("k_doc outside [0, n_doc]")
+        rows = np.arange(p.start, p.start + p.length, dtype=np.int64)
+        doc = _doc_rows(p)
+        sd = s[doc]
+        is_nan = np.isnan(sd)
+        neg = np.where(is_nan, 0.0, -sd.astype(np.float64))
+        # np.lexsort sorts by its last key first: NaN flag, then -score,
+        # then row id. It is a stable sort.
+        order = np.lexsort((doc, neg, is_nan))
+        keep_doc = doc[order[:p.k_doc]]
+        in_doc = np.zeros(p.length, dtype=bool)
+        in_doc[p.doc_begin:p.doc_end] = True
+        keep = np.concatenate([rows[~in_doc], keep_doc])
+        out.append(np.sort(keep))
+    return np.concatenate(out) if out else np.zeros(0, dtype=np.int64)
+
+
+def kept_rows(prompts: Iterable) -> int:
+    """M = sum over prompts of k_doc + (length - n_doc)."""
+    return int(sum(p.k_doc + p.length - (p.doc_end - p.doc_begin) for p in prompts))
+
+
+# ---------------------------------------------------------------------------
+# Step 3: compaction.  [DE-prune] (only kept tokens go up, no KV for the
+# pruned), [IT-keep]; bias per [DE-attn] in the form stated above.
+# ---------------------------------------------------------------------------
+
+def logsigmoid(s) -> np.ndarray:
+    """log(sigmoid(s)) = min(s, 0) - log1p(exp(-|s|)), in fp64."""
+    s = np.asarray(s, dtype=np.float64)
+    return np.minimum(s, 0.0) - np.log1p(np.exp(-np.abs(s)))
+
+
+def prompt_of_rows(rows: np.ndarray, prompts: Sequence) -> np.ndarray:
+    """Index of the prompt that holds each row."""
+    starts = np.array([p.start for p in prompts], dtype=np.int64)
+    return np.searchsorted(starts, rows, side="right") - 1
+
+
+def compact(kept: np.ndarray, prompts: Sequence, tensors: Sequence = (), scores=None,
+            pos=None):
+    """Gather the kept rows.
+
+    Returns (gathered, pos_kept, bias_kept):
+      gathered[t] = tensors[t][kept]           (row gather, bit-exact)
+      pos_kept[m] = pos[kept[m]], or kept[m] - start of its prompt when no
+                    position array is given
+      bias_kept[m]= logsigmoid(scores[kept[m]]) for document rows, else 0
+    """
+    kept = np.asarray(kept, dtype=np.int64)
+    gathered = [t[kept] for t in tensors]
+    pid = prompt_of_rows(kept, prompts)
+    starts = np.array([p.start for p in prompts], dtype=np.int64)
+    if pos is None:
+        pos_kept = kept - starts[pid]
+    else:
+        pos_kept = np.asarray(pos)[kept].astype(np.int64)
+    bias = np.zeros(len(kept), dtype=np.float64)
+    if scores is not None and len(kept):
+        db = np.array([p.start + p.doc_begin for p in prompts], dtype=np.int64)[pid]
+        de = np.array([p.start + p.doc_end for p in prompts], dtype=np.int64)[pid]
+        is_doc = (kept >= db) & (kept < de)
+        sk = _f64(scores)[kept] if hasattr(scores, "detach") else np.asarray(scores, np.float64)[kept]
+        bias[is_doc] = logsigmoid(sk[is_doc])
+    return gathered, pos_kept, bias
+
+
+# ---------------------------------------------------------------------------
+# Step 4: token-gated attention.  [DE-attn], [DE-prune], [DE-impl]
+# ---------------------------------------------------------------------------
+
+def gated_attention(q, k, v, bias, pos, seg_lens: Sequence[int], hq: int, hkv: int,
+                    gain, tau: float, rows: Optional[np.ndarray] = None,
+                    block_rows: int = 256):
+    """Token-gated causal attention over packed kept rows.
+
+    q[M, hq, D], k/v[M, hkv, D], bias[M], pos[M], gain[hq]; the packed rows
+    form consecutive segments (one per prompt) of lengths seg_lens. For
+    segment rows i (queries) and j (keys) and query head h with KV head
+    kv = floor(h * hkv / hq):
+
+        l_ij  = q_i . k_j / (sqrt(D) * tau) + gain[h] * bias[j]
+        J_i   = { j in the segment : pos[j] <= pos[i] }
+        o_i   = sum_{j in J_i} softmax_j(l_i.) v_j
+        lse_i = log sum_{j in J_i} exp(l_ij)
+
+    Returns (o[M, hq, D], lse[hq, M]) in fp64. `rows`, if given, restricts
+    the queries computed to those packed row ids (other outputs are NaN).
+    """
+    if hq % hkv:
+        raise ValueError("hq must be a multiple of hkv")
+    qd, kd, vd = _f64(q), _f64(k), _f64(v)
+    b = _f64(bias).reshape(-1)
+    ps = np.asarray(pos.detach().cpu().numpy() if hasattr(pos, "detach") else pos, dtype=np.int64)
+    g = _f64(gain).reshape(-1)
+    m_tot, _, dh = qd.shape
+    scale = 1.0 / (math.sqrt(dh) * float(tau))
+    o = np.full((m_tot, hq, dh), np.nan)
+    lse = np.full((hq, m_tot), np.nan)
+    want = None
+    if rows is not None:
+        want = np.zeros(m_tot, dtype=bool)
+        want[np.asarray(rows, dtype=np.int64)] = True
+    off = 0
+    for ln in seg_lens:
+        ln = int(ln)
+        seg = slice(off, off + ln)
+        q_rows = np.arange(off, off + ln)
+        if want is not None:
+            q_rows = q_rows[want[off:off + ln]]
+        for h in range(hq):
+            kvh = (h * hkv) // hq
+            kh, vh = kd[seg, kvh, :], vd[seg, kvh, :]
+            bh = g[h] * b[seg]
+            for i0 in range(0, len(q_rows), block_rows):
+                qi = q_rows[i0:i0 + block_rows]
+                logits = (qd[qi, h, :] @ kh.T) * scale + bh[None, :]
+                visible = ps[seg][None, :] <= ps[qi][:, None]
+                logits = np.where(visible, logits, -np.inf)
+                mx = logits.max(axis=1, keepdims=True)
+                e = np.exp(logits - mx)
+                den = e.sum(axis=1, keepdims=True)
+                o[qi, h, :] = (e @ vh) / den
+                lse[h, qi] = (mx + np.log(den))[:, 0]
+        off += ln
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# The whole layer, in the pages' order.
+# ---------------------------------------------------------------------------
+
+def gated_prefill(x, w1, w2, prompts: Sequence, layers: Sequence = (), b1=None, b2: float = 0.0,
+                  hq: int = 0, hkv: int = 0, head_dim: int = 0, pos=None,
+                  decision_dtype=None, scores=None, attn_rows=None) -> dict:
+    """Gate -> select -> compact -> token-gated attention for every layer.
+
+    layers: objects with .q [N, hq*D], .k/.v [N, hkv*D], .gain [hq], .tau.
+    decision_dtype: if set (np.float32), the top-K decision is taken on the
+    scores rounded to that type, the precision the GPU path decides in; the
+    bias still uses the fp64 scores.
+    scores: optional precomputed scores (skips the gate).
+    """
+    s = gate_scores(x, w1, w2, b1, b2) if scores is None else _f64(scores)
+    s_dec = s if decision_dtype is None else s.astype(decision_dtype)
+    kept = select_topk(s_dec, prompts)
+    m = len(kept)
+    seg_lens = [p.k_doc + p.length - (p.doc_end - p.doc_begin) for p in prompts]
+    _, pos_kept, bias = compact(kept, prompts, (), s, pos)
+    outs = []
+    for layer in layers:
+        (qk, kk, vk), _, _ = compact(kept, prompts, (layer.q, layer.k, layer.v))
+        qk = _f64(qk).reshape(m, hq, head_dim)
+        kk = _f64(kk).reshape(m, hkv, head_dim)
+        vk = _f64(vk).reshape(m, hkv, head_dim)
+        o, lse = gated_attention(qk, kk, vk, bias, pos_kept, seg_lens, hq, hkv, layer.gain,
+                                 layer.tau, rows=attn_rows)
+        outs.append((o, lse))
+    return dict(scores=s, kept=kept, pos_kept=pos_kept, bias=bias, attn=outs, seg_lens=seg_lens)

@@ -1,0 +1,376 @@
+"""Pins for the fp64 oracle, independent of the oracle itself (CPU only).
+
+Every oracle function is checked against at least one of: hand-derived
+closed forms (tests/golden/hand_cases.json), pure-Python brute force on
+tiny inputs (tests/brute.py), exhaustive enumeration, invariants the pages
+fix, and library routines the operation reduces to (torch CPU fp64
+nn.functional.linear/silu/logsigmoid/scaled_dot_product_attention).
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from synthetic import Prompt, make_attention_inputs, make_scores, make_workload
+from tests import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+_MATH = {k: getattr(math, k) for k in ("log", "exp", "sqrt", "pi")}
+
+
+def ev(x):
+    """Evaluate a closed-form expression string (math names only)."""
+    if x is None:
+        return None
+    if isinstance(x, (int, float)):
+        return float(x)
+    if isinstance(x, list):
+        return [ev(e) for e in x]
+    return float(eval(x, {"__builtins__": {}}, _MATH))
+
+
+@pytest.fixture(scope="module")
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- gate ----
+
+def test_gate_golden(golden):
+    for case in golden["gate"]:
+        x = np.array(ev(case["x"]))
+        w1 = np.array(ev(case["w1"]))
+        w2 = np.array(ev(case["w2"]))
+        b1 = None if case["b1"] is None else np.array(ev(case["b1"]))
+        got = oracle.gate_scores(x, w1, w2, b1, ev(case["b2"]))
+        np.testing.assert_allclose(got, ev(case["expected"]), rtol=1e-15, atol=1e-15,
+                                   err_msg=case["name"])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_gate_vs_bruteforce(seed):
+    rng = np.random.default_rng(seed)
+    n, d, h = 7, 13, 5
+    x = rng.normal(size=(n, d)) * 2
+    w1 = rng.normal(size=(h, d))
+    w2 = rng.normal(size=h)
+    b1 = rng.normal(size=h)
+    got = oracle.gate_scores(x, w1, w2, b1, 0.7)
+    ref = brute.gate(x.tolist(), w1.tolist(), w2.tolist(), b1.tolist(), 0.7)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_gate_vs_torch_library():
+    g = torch.Generator().manual_seed(5)
+    n, d, h = 300, 96, 40
+    x = torch.randn(n, d, generator=g, dtype=torch.float64)
+    w1 = torch.randn(h, d, generator=g, dtype=torch.float64) / math.sqrt(d)
+    b1 = torch.randn(h, generator=g, dtype=torch.float64)
+    w2 = torch.randn(1, h, generator=g, dtype=torch.float64)
+    ref = F.linear(F.silu(F.linear(x, w1, b1)), w2, torch.tensor([-0.3], dtype=torch.float64))[:, 0]
+    got = oracle.gate_scores(x.numpy(), w1.numpy(), w2.numpy()[0], b1.numpy(), -0.3, block_rows=64)
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_gate_one_hot_reduces_to_silu():
+    rng = np.random.default_rng(0)
+    n, d, h = 50, 8, 3
+    x = rng.normal(size=(n, d)) * 5
+    w1 = np.zeros((h, d))
+    w1[0, 6] = 1.0
+    w1[1, 2] = 1.0
+    w2 = np.array([1.0, 0.0, 0.0])
+    s = oracle.gate_scores(x, w1, w2)
+    z = x[:, 6]
+    np.testing.assert_allclose(s, z / (1 + np.exp(-z)), rtol=1e-14, atol=1e-14)
+
+
+def test_planted_rows_score_top():
+    """The synthetic 16k workload plants 16 rows along the gate's first
+    hidden direction; the oracle gate must rank them all in the top 16 and
+    the selector must keep them."""
+    w = make_workload("qwen16k", with_layers=False)
+    s = oracle.gate_scores(w.x, w.w1, w.w2)
+    top16 = np.argsort(-s, kind="stable")[:16]
+    assert set(top16.tolist()) == set(w.planted.tolist())
+    kept = oracle.select_topk(s.astype(np.float32), w.prompts)
+    assert set(w.planted.tolist()) <= set(kept.tolist())
+
+
+# -------------------------------------------------------------- select ----
+
+def test_select_golden(golden):
+    for case in golden["select"]:
+        prompts = [Prompt(*p) for p in case["prompts"]]
+        got = oracle.select_topk(np.array(case["scores"], dtype=np.float64), prompts)
+        assert got.tolist() == case["expected"], case["name"]
+
+
+def _spans(n):
+    yield 0, n
+    if n >= 3:
+        yield 1, n - 1
+        yield 0, n - 2
+        yield 2, n
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6])
+def test_select_exhaustive_small(n):
+    """Every score vector in {0,1,2}^n, several document spans, every k."""
+    for vals in itertools.product((0.0, 1.0, 2.0), repeat=n):
+        s = np.array(vals)
+        for db, de in _spans(n):
+            for k in range(de - db + 1):
+                prompts = [Prompt(0, n, db, de, k)]
+                assert oracle.select_topk(s, prompts).tolist() == brute.select(s.tolist(), prompts)
+
+
+def test_select_exhaustive_nan_and_signed_zero():
+    """NaN ranks below every number; -0 and +0 tie (lower row wins)."""
+    vals = (float("nan"), -0.0, 0.0, 1.0, -float("inf"))
+    n = 5
+    for tup in itertools.product(vals, repeat=n):
+        s = np.array(tup)
+        for k in range(n + 1):
+            prompts = [Prompt(0, n, 0, n, k)]
+            assert oracle.select_topk(s, prompts).tolist() == brute.select(s.tolist(), prompts)
+
+
+def test_select_multi_prompt_bruteforce():
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        prompts, start = [], 0
+        for _ in range(rng.integers(1, 5)):
+            ln = int(rng.integers(0, 9))
+            db = int(rng.integers(0, ln + 1))
+            de = int(rng.integers(db, ln + 1))
+            prompts.append(Prompt(start, ln, db, de, int(rng.integers(0, de - db + 1))))
+            start += ln
+        s = rng.integers(-2, 3, size=start).astype(np.float64)
+        assert oracle.select_topk(s, prompts).tolist() == brute.select(s.tolist(), prompts)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "few", "signed0", "wide"])
+def test_select_invariants(kind):
+    s = make_scores(5000, seed=11, kind=kind).numpy()
+    prompts = [Prompt(0, 3000, 100, 2900, 700), Prompt(3000, 2000, 0, 1744, 1000)]
+    kept = oracle.select_topk(s, prompts)
+    assert len(kept) == oracle.kept_rows(prompts)
+    assert np.all(np.diff(kept) > 0)
+    ks = set(kept.tolist())
+    for p in prompts:
+        rows = range(p.start, p.start + p.length)
+        doc = range(p.start + p.doc_begin, p.start + p.doc_end)
+        # the question (every non-document row) survives
+        assert all(r in ks for r in rows if r not in doc)
+        kd = [r for r in doc if r in ks]
+        dropped = [r for r in doc if r not in ks]
+        assert len(kd) == p.k_doc
+        if kd and dropped:
+            lo = min(s[r] for r in kd)
+            hi = max(s[r] for r in dropped)
+            assert lo >= hi
+            # ties at the threshold go to the lower row ids
+            if lo == hi:
+                assert max(r for r in kd if s[r] == lo) < min(r for r in dropped if s[r] == hi)
+
+
+def test_select_budget_extremes():
+    s = make_scores(1000, seed=1).numpy()
+    full = [Prompt(0, 1000, 0, 900, 900)]
+    assert oracle.select_topk(s, full).tolist() == list(range(1000))
+    none = [Prompt(0, 1000, 0, 900, 0)]
+    assert oracle.select_topk(s, none).tolist() == list(range(900, 1000))
+    with pytest.raises(ValueError):
+        oracle.select_topk(s, [Prompt(0, 1000, 0, 900, 901)])
+
+
+# ------------------------------------------------------------- compact ----
+
+def test_logsigmoid_golden(golden):
+    for case in golden["logsigmoid"]:
+        assert oracle.logsigmoid(ev(case["s"])) == pytest.approx(ev(case["expected"]), rel=1e-15, abs=1e-15)
+
+
+def test_logsigmoid_vs_library_and_asymptotes():
+    s = np.concatenate([np.linspace(-60, 60, 2001), [-745.0, 700.0]])
+    ref = F.logsigmoid(torch.tensor(s, dtype=torch.float64)).numpy()
+    np.testing.assert_allclose(oracle.logsigmoid(s), ref, rtol=1e-14, atol=1e-300)
+    # log sigmoid(s) -> -e^{-s} for large s, -> s for very negative s
+    assert oracle.logsigmoid(40.0) == pytest.approx(-math.exp(-40.0), rel=1e-12)
+    assert oracle.logsigmoid(-40.0) == pytest.approx(-40.0 - math.exp(-40.0), rel=1e-15)
+    # independent form -log(1 + e^{-s}) where it does not overflow
+    t = np.linspace(-30, 30, 601)
+    np.testing.assert_allclose(oracle.logsigmoid(t), -np.log(1 + np.exp(-t)), rtol=1e-13, atol=4e-16)
+
+
+def test_compact_gather_pos_bias():
+    rng = np.random.default_rng(2)
+    prompts = [Prompt(0, 10, 2, 8, 3), Prompt(10, 6, 0, 4, 1)]
+    s = rng.normal(size=16)
+    kept = oracle.select_topk(s, prompts)
+    t1 = rng.normal(size=(16, 5))
+    t2 = np.arange(16 * 3).reshape(16, 3)
+    (g1, g2), pk, bias = oracle.compact(kept, prompts, (t1, t2), s)
+    for m, r in enumerate(kept):
+        assert np.array_equal(g1[m], t1[r]) and np.array_equal(g2[m], t2[r])
+        p = prompts[0] if r < 10 else prompts[1]
+        assert pk[m] == r - p.start
+        in_doc = p.start + p.doc_begin <= r < p.start + p.doc_end
+        # query rows carry no bias; document rows carry log sigmoid(score)
+        expect = math.log(1.0 / (1.0 + math.exp(-s[r]))) if in_doc else 0.0
+        assert bias[m] == pytest.approx(expect, rel=1e-13, abs=0)
+    pos = rng.integers(0, 100000, size=16)
+    _, pk2, _ = oracle.compact(kept, prompts, (), s, pos)
+    assert pk2.tolist() == pos[kept].tolist()
+
+
+def test_compact_full_budget_is_identity():
+    s = make_scores(200, seed=4).numpy()
+    prompts = [Prompt(0, 200, 0, 180, 180)]
+    kept = oracle.select_topk(s, prompts)
+    x = np.random.default_rng(0).normal(size=(200, 4))
+    (g,), pk, _ = oracle.compact(kept, prompts, (x,), s)
+    assert np.array_equal(g, x) and pk.tolist() == list(range(200))
+
+
+# ----------------------------------------------------------- attention ----
+
+def test_attention_golden(golden):
+    for case in golden["attention"]:
+        q = np.array(ev(case["q"]))
+        k = np.array(ev(case["k"]))
+        v = np.array(ev(case["v"]))
+        sc = case["scores"]
+        prompts = [Prompt(0, len(sc), 0, sum(1 for e in sc if e is not None), 0)]
+        bias = np.array([0.0 if e is None else oracle.logsigmoid(ev(e)) for e in sc])
+        o, lse = oracle.gated_attention(q, k, v, bias, np.array(case["pos"]), [len(sc)],
+                                        case["hq"], case["hkv"], np.array(ev(case["gain"])),
+                                        ev(case["tau"]))
+        np.testing.assert_allclose(o, ev(case["expected_o"]), rtol=1e-14, atol=1e-14)
+        np.testing.assert_allclose(lse, ev(case["expected_lse"]), rtol=1e-14, atol=1e-14)
+        del prompts
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (3, 3), (8, 2)])
+def test_attention_reduces_to_sdpa(hq, hkv):
+    """Full budget and zero gain: plain causal GQA attention (torch SDPA,
+    fp64, K/V heads repeated for each query-head group)."""
+    d, m, tau = 16, 70, 1.2
+    a = make_attention_inputs([m], hq, hkv, d, seed=7, dtype=torch.float64)
+    pos = np.arange(m)
+    o, lse = oracle.gated_attention(a["q"], a["k"], a["v"], a["bias"], pos, [m], hq, hkv,
+                                    np.zeros(hq), tau)
+    q = a["q"].permute(1, 0, 2)[None]
+    k = a["k"].permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None]
+    v = a["v"].permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None]
+    ref = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=1.0 / (math.sqrt(d) * tau))
+    np.testing.assert_allclose(o, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_with_bias_vs_sdpa_float_mask():
+    """Nonzero gain: SDPA with an additive float mask gain[h]*bias[j] on
+    visible keys and -inf elsewhere (positions with repeats)."""
+    hq, hkv, d, m, tau = 4, 2, 8, 41, 0.7
+    a = make_attention_inputs([m], hq, hkv, d, seed=9, dtype=torch.float64, pos_ties=True,
+                              n_query_tail=5)
+    pos = a["pos"].numpy()
+    o, _ = oracle.gated_attention(a["q"], a["k"], a["v"], a["bias"], pos, [m], hq, hkv,
+                                  a["gain"], tau)
+    vis = torch.tensor(pos[None, :] <= pos[:, None])
+    mask = torch.where(vis[None], a["gain"].double()[:, None, None] * a["bias"][None, None, :],
+                       torch.tensor(-math.inf, dtype=torch.float64))
+    q = a["q"].permute(1, 0, 2)[None]
+    k = a["k"].permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None]
+    v = a["v"].permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None]
+    ref = F.scaled_dot_product_attention(q, k, v, attn_mask=mask[None], scale=1.0 / (math.sqrt(d) * tau))
+    np.testing.assert_allclose(o, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_vs_multiplicative_bruteforce():
+    """exp(l_ij) = exp(q.k/(sqrt(D) tau)) * sigmoid(s_j)^g: the additive
+    log-sigmoid bias is the multiplicative re-weighting of each key."""
+    seg = [9, 1, 6]
+    hq, hkv, d = 4, 2, 4
+    a = make_attention_inputs(seg, hq, hkv, d, seed=13, dtype=torch.float64, pos_ties=True)
+    m = sum(seg)
+    rng = np.random.default_rng(0)
+    s = rng.normal(size=m) * 3
+    is_doc = rng.random(m) < 0.7
+    bias = np.where(is_doc, oracle.logsigmoid(s), 0.0)
+    pos = a["pos"].numpy()
+    gain = a["gain"].numpy()
+    o, lse = oracle.gated_attention(a["q"], a["k"], a["v"], bias, pos, seg, hq, hkv, gain, 1.2)
+    ob, lb = brute.attention_multiplicative(a["q"].tolist(), a["k"].tolist(), a["v"].tolist(),
+                                            s.tolist(), is_doc.tolist(), pos.tolist(), seg, hq, hkv,
+                                            gain.tolist(), 1.2)
+    np.testing.assert_allclose(o, ob, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, lb, rtol=1e-11, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    hq, hkv, d = 4, 2, 8
+    seg = [30, 17]
+    a = make_attention_inputs(seg, hq, hkv, d, seed=21, dtype=torch.float64)
+    m = sum(seg)
+    pos = a["pos"].numpy()
+    # V = 1 => O = 1 (softmax rows sum to one)
+    ones = np.ones((m, hkv, d))
+    o1, _ = oracle.gated_attention(a["q"], a["k"], ones, a["bias"], pos, seg, hq, hkv, a["gain"], 1.2)
+    np.testing.assert_allclose(o1, 1.0, rtol=0, atol=1e-14)
+    # the first row of each segment sees only itself
+    o, lse = oracle.gated_attention(a["q"], a["k"], a["v"], a["bias"], pos, seg, hq, hkv, a["gain"], 1.2)
+    vv = a["v"].numpy()
+    for off in (0, seg[0]):
+        for h in range(hq):
+            np.testing.assert_allclose(o[off, h], vv[off, (h * hkv) // hq], rtol=1e-14)
+    # equal keys: weights are sigmoid(s)^g, independent of q and of tau
+    kk = np.repeat(a["k"].numpy()[:1], m, axis=0)
+    s = np.random.default_rng(1).normal(size=m)
+    bias = oracle.logsigmoid(s)
+    for tau in (0.5, 3.0):
+        o2, _ = oracle.gated_attention(a["q"], kk, vv, bias, pos, seg, hq, hkv, a["gain"], tau)
+        i = seg[0] - 1
+        for h in range(hq):
+            w = (1.0 / (1.0 + np.exp(-s[:seg[0]]))) ** float(a["gain"][h])
+            ref = (w[:, None] * vv[:seg[0], (h * hkv) // hq]).sum(0) / w.sum()
+            np.testing.assert_allclose(o2[i, h], ref, rtol=1e-12)
+
+
+def test_attention_sampled_rows_match_full():
+    hq, hkv, d = 2, 1, 8
+    a = make_attention_inputs([50], hq, hkv, d, seed=3, dtype=torch.float64)
+    pos = a["pos"].numpy()
+    full, lf = oracle.gated_attention(a["q"], a["k"], a["v"], a["bias"], pos, [50], hq, hkv, a["gain"], 1.2)
+    rows = np.array([0, 7, 49])
+    part, lp = oracle.gated_attention(a["q"], a["k"], a["v"], a["bias"], pos, [50], hq, hkv, a["gain"], 1.2,
+                                      rows=rows)
+    np.testing.assert_array_equal(part[rows], full[rows])
+    assert np.isnan(part[1]).all()
+
+
+# ---------------------------------------------------------- end to end ----
+
+def test_tiny_layer_end_to_end_invariants():
+    w = make_workload("tiny")
+    lay = w.layers[0]
+    res = oracle.gated_prefill(w.x, w.w1, w.w2, w.prompts, [lay], hq=w.hq, hkv=w.hkv,
+                               head_dim=w.head_dim, decision_dtype=np.float32)
+    kept = res["kept"]
+    p = w.prompts[0]
+    assert len(kept) == p.k_doc + (p.length - p.n_doc) == 176
+    assert set(range(448, 512)) <= set(kept.tolist())
+    o, lse = res["attn"][0]
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    # the kept set is the top-112 document rows by score
+    s = res["scores"]
+    kd = kept[kept < 448]
+    assert np.min(s[kd]) >= np.max(np.delete(s[:448], kd))
