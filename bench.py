@@ -1,0 +1,246 @@
+"""Benchmark of the TokenGate pruned-prefill layer on one MI355X.
+
+A step is one pass of the whole layer over one batch: gate score -> top-K
+select -> compaction -> token-gated attention, four C-ABI calls on one
+stream, inputs already resident in HBM. The workload is the 16k
+Qwen3-1.7B-shaped layer: N=16384 rows (16000 document + 384 question),
+d_model 2048, gate 2048->256->1, keep 2000 document rows (12.5%), 16 query /
+8 KV heads, head_dim 128, bf16, 16 planted rows.
+
+Prints ONE JSON line. `value` is the layer latency in ms (lower is better);
+attention TFLOP/s and its fraction of the bf16 MFMA peak ride along, with a
+per-kernel breakdown, a roofline entry for the dominant kernel and the fp64
+oracle timed on the host cores as a reported CPU baseline.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "gated-prefill layer ms + attn TFLOP/s (% MFMA peak) at 16k, keep 12.5%"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--cpu-budget-s", type=float, default=30.0)
+    return ap.parse_args()
+
+
+def algorithmic_work(w, m):
+    """Algorithmic bytes / flops of one launch of each kernel at this workload."""
+    n, d = w.x.shape
+    h = w.w1.shape[0]
+    hq, hkv, dh = w.hq, w.hkv, w.head_dim
+    p = w.prompts[0]
+    # gate: read X once, W1 once, write one fp32 score per row
+    gate_bytes = n * d * 2 + h * d * 2 + h * 2 + n * 4
+    gate_flops = n * (2 * d * h + 4 * h)
+    # select: read each document score once, write one int32 per kept row
+    sel_bytes = p.n_doc * 4 + m * 4
+    # compact: read + write every gathered row (hidden, Q, K, V), index read,
+    # score read, position and bias writes
+    row = (d + (hq + 2 * hkv) * dh) * 2
+    comp_bytes = m * (2 * row + 4 + 4 + 4 + 4)
+    # attention: 4*D*Hq flop per visible (query, key) pair, causal incl. diagonal
+    pairs = m * (m + 1) // 2
+    attn_flops = 4 * dh * hq * pairs
+    return dict(gate=dict(bytes=gate_bytes, flops=gate_flops), select=dict(bytes=sel_bytes),
+                compact=dict(bytes=comp_bytes), attention=dict(flops=attn_flops))
+
+
+def source_hash(rel):
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "gate": "learned_token_pruning_layer_amd/csrc/gate_score.hip",
+    "select": "learned_token_pruning_layer_amd/csrc/select_topk.hip",
+    "compact": "learned_token_pruning_layer_amd/csrc/compact.hip",
+    "attention": "learned_token_pruning_layer_amd/csrc/gated_attention.hip",
+}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_qwen16k.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec or rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s):
+    """The fp64 oracle, untuned, on the host cores: one whole layer if it
+    fits the budget, else the gate + select + compaction in full and the
+    attention on an evenly spaced sample of query rows, scaled by the
+    number of visible (query, key) pairs."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    lay = w.layers[0]
+    x, w1, w2 = w.x.cpu(), w.w1.cpu(), w.w2.cpu()
+    q, k, v, gain = lay.q.cpu(), lay.k.cpu(), lay.v.cpu(), lay.gain.cpu()
+    hq, hkv, dh = w.hq, w.hkv, w.head_dim
+    t0 = time.perf_counter()
+    s = oracle.gate_scores(x, w1, w2)
+    kept = oracle.select_topk(s.astype(np.float32), w.prompts)
+    (qk, kk, vk), pk, bk = oracle.compact(kept, w.prompts, (q, k, v), s)
+    t_front = time.perf_counter() - t0
+    m = len(kept)
+    qk, kk, vk = qk.view(m, hq, dh), kk.view(m, hkv, dh), vk.view(m, hkv, dh)
+    # probe the attention cost on a small sample to size the run
+    probe = np.linspace(0, m - 1, 64).astype(np.int64)
+    t1 = time.perf_counter()
+    oracle.gated_attention(qk, kk, vk, bk, pk, [m], hq, hkv, gain, lay.tau, rows=probe)
+    t_probe = time.perf_counter() - t1
+    pairs_probe = float(np.sum(probe + 1))
+    pairs_all = m * (m + 1) / 2
+    est_full = t_probe * pairs_all / pairs_probe
+    if t_front + est_full <= budget_s:
+        t1 = time.perf_counter()
+        oracle.gated_attention(qk, kk, vk, bk, pk, [m], hq, hkv, gain, lay.tau)
+        t_attn = time.perf_counter() - t1
+        sample = f"one whole layer: gate over {w.n_rows} rows, select, compaction, attention over all {m} kept rows"
+    else:
+        nrow = max(64, int(m * budget_s / max(est_full, 1e-9) * 0.5))
+        rows = np.linspace(0, m - 1, min(nrow, m)).astype(np.int64)
+        t1 = time.perf_counter()
+        oracle.gated_attention(qk, kk, vk, bk, pk, [m], hq, hkv, gain, lay.tau, rows=rows)
+        t_attn = (time.perf_counter() - t1) * pairs_all / float(np.sum(rows + 1))
+        sample = (f"gate over {w.n_rows} rows, select and compaction in full; attention on {len(rows)} "
+                  f"evenly spaced query rows of {m}, scaled by visible (query, key) pairs")
+    total_ms = (t_front + t_attn) * 1e3
+    return dict(value=round(total_ms, 3), unit="ms", cores=int(threads), kind="oracle", sample=sample,
+                split_ms=dict(gate_select_compact=round(t_front * 1e3, 3), attention=round(t_attn * 1e3, 3)))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "gpus_requested": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import learned_token_pruning_layer_amd as tg
+    from synthetic import make_workload
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    w = make_workload("qwen16k", device=dev)
+    layer = tg.GatedPrefillLayer(w.x, w.w1, w.w2, w.prompts, w.layers, w.hq, w.hkv, w.head_dim)
+    m = layer.m
+    work = algorithmic_work(w, m)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        layer.run()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` whole-layer steps.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        layer.run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # Per-kernel durations: events between the four launches of each step.
+    names = ["gate", "select", "compact", "attention"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for e in evs:
+        e[0].record(stream)
+        layer.gate()
+        e[1].record(stream)
+        layer.select()
+        e[2].record(stream)
+        layer.compact()
+        e[3].record(stream)
+        layer.attention(0)
+        e[4].record(stream)
+    torch.cuda.synchronize()
+    per = {nm: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps * 1e3 for i, nm in enumerate(names)}
+
+    # Dominant kernel alone, back to back: average launch duration.
+    dom = max(per, key=per.get)
+    call = {"gate": layer.gate, "select": layer.select, "compact": layer.compact,
+            "attention": lambda: layer.attention(0)}[dom]
+    for _ in range(10):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dom_us = e0.elapsed_time(e1) / args.steps * 1e3
+
+    def roofline(kernel, us):
+        wk = work[kernel]
+        if kernel == "attention":
+            ach = wk["flops"] / (us * 1e-6) / 1e12
+            return dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                        frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic(kernel))
+        ach = wk["bytes"] / (us * 1e-6) / 1e9
+        return dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=measured_traffic(kernel))
+
+    attn_tflops = work["attention"]["flops"] / (per["attention"] * 1e-6) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 5),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen16k: one pruned-prefill layer, N=16384 (16000 doc + 384 query), "
+                               "keep 2000 doc rows (12.5%), d_model 2048, gate 2048->256->1, "
+                               "16 Q / 8 KV heads, head_dim 128, 16 planted rows",
+                   "n_rows": w.n_rows, "kept_rows": m, "global_batch": 1, "seq_len": w.n_rows},
+        "attn_tflops": round(attn_tflops, 2),
+        "attn_frac_mfma_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "kernels_us": {k: round(v, 2) for k, v in per.items()},
+        "kernel_rooflines": {k: roofline(k, per[k]) for k in names if k != "select"},
+        "roofline": dict(kernel=dom, launch_us=round(dom_us, 2), **roofline(dom, dom_us)),
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * tokengate.h - C ABI of the TokenGate pruned-prefill layer for MI355X (gfx950).
+ *
+ * The layer runs in four steps:
+ *
+ *   1. tg_gate_score       a small MLP scores every token from its residual at
+ *                          the gate layer;
+ *   2. tg_select_topk      per prompt, keep the best-scored document rows and
+ *                          every row outside the document (the question);
+ *   3. tg_compact          gather the kept rows of any number of row-major
+ *                          tensors (hidden states, Q, K, V), their original
+ *                          positions and their attention bias;
+ *   4. tg_gated_attention  causal attention over the kept rows only, with the
+ *                          bias of every kept key added to its logits.
+ *
+ * Sources: the pages about "TokenGate: Adapting LLMs for Fast and
+ * Memory-Efficient Prefill with Learned Token Pruning". The spke.com article
+ * (German) defines the steps in its section "Wie hat TokenGate das Pruning von
+ * Tokens verstanden?" (gate MLP on the post-attention residual of gate layer
+ * L, top-K selector, only the kept tokens go up, no KV for the pruned ones,
+ * only the document is prunable) and the bias in "Was ist token-gated
+ * Attention?" (kept score -> logit bias, per-head gain, temperature); its
+ * section "Wie wird TokenGate implementiert?" describes the budget given per
+ * call and the placeholder that marks the document. The pages fix the bias
+ * only qualitatively; this library computes, for kept rows i, j of a prompt
+ * and query head h,
+ *
+ *     logit_ij = q_i . k_j / (sqrt(head_dim) * tau) + gain[h] * b_j,
+ *     b_j      = logsigmoid(s_j) for document keys, 0 for the rest,
+ *
+ * over the keys j with pos_j <= pos_i.
+ *
+ * Conventions shared by every call:
+ *  - Tensor pointers are DEVICE pointers owned by the caller. tg_seq and
+ *    tg_gather arrays are HOST memory, read during the call only.
+ *  - The library allocates nothing and keeps no state other than a
+ *    thread-local error string. Scratch memory, where a call needs any, is a
+ *    caller-provided device workspace whose size the matching
+ *    *_workspace_bytes function returns.
+ *  - Every call validates its arguments on the host first. A status other
+ *    than TG_OK means nothing was enqueued; tg_last_error() gives details.
+ *    A failed launch returns TG_ERR_HIP. Faults inside a kernel surface at the
+ *    caller's next synchronisation, as with any HIP library.
+ *  - Calls are asynchronous on `stream` and never synchronise. Every output
+ *    size is known on the host (tg_kept_rows), so no call reads device memory
+ *    back.
+ *  - Outputs are bitwise deterministic for identical inputs.
+ *  - Prompts are packed back to back ("varlen"): prompt b owns packed rows
+ *    [start_b, start_b + len_b); kept rows are packed in the same prompt
+ *    order, prompt b's kept rows at [off_b, off_b + M_b) with
+ *    M_b = k_doc_b + len_b - (doc_end_b - doc_begin_b) and off_b the sum of
+ *    the earlier M's.
+ *  - bf16 is stored as the upper 16 bits of an IEEE binary32 (torch.bfloat16).
+ */
+#ifndef TOKENGATE_H
+#define TOKENGATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TG_OK = 0,
+    TG_ERR_INVALID_ARGUMENT = 1, /* a pointer, size or descriptor is wrong      */
+    TG_ERR_UNSUPPORTED = 2,      /* valid, but a shape/alignment not built here */
+    TG_ERR_WORKSPACE = 3,        /* workspace missing or too small              */
+    TG_ERR_HIP = 4               /* the HIP runtime refused a launch            */
+} tg_status;
+
+typedef enum { TG_F32 = 0, TG_BF16 = 1 } tg_dtype;
+
+/* Largest number of prompts one call accepts (descriptors travel as kernel
+ * arguments). */
+#define TG_MAX_SEQS 64
+/* Largest number of tensors one tg_compact call gathers. */
+#define TG_MAX_GATHERS 16
+
+/* One packed prompt (host memory). The prunable document is rows
+ * [start + doc_begin, start + doc_end); every other row of the prompt (the
+ * question) is always kept. k_doc = document rows to keep, 0 <= k_doc <=
+ * doc_end - doc_begin. Prompts must be given in increasing, non-overlapping
+ * row order. */
+typedef struct {
+    int64_t start;
+    int32_t len;
+    int32_t doc_begin;
+    int32_t doc_end;
+    int32_t k_doc;
+} tg_seq;
+
+/* One tensor to gather (host memory describing device buffers): kept row m
+ * is copied from src + kept_idx[m] * src_stride to dst + m * dst_stride,
+ * row_bytes bytes. All three sizes and both pointers must be multiples of
+ * 16 bytes. */
+typedef struct {
+    const void* src;
+    void* dst;
+    int64_t row_bytes;
+    int64_t src_stride;
+    int64_t dst_stride;
+} tg_gather;
+
+/* Rows kept by the given prompts: sum of k_doc + len - (doc_end - doc_begin).
+ * Host only. Returns -1 (and sets the error text) if a descriptor is invalid. */
+int64_t tg_kept_rows(const tg_seq* seqs, int32_t n_seqs);
+
+/* Step 1 - gate score. For each of the n_rows rows x_r of x (row-major
+ * [n_rows, d_model], dtype dt):
+ *     h = W1 x_r + b1,   scores[r] = w2 . SiLU(h) + b2,
+ * with W1 row-major [d_hidden, d_model] (nn.Linear layout), b1 [d_hidden]
+ * (nullable: zero), w2 [d_hidden], all of dtype dt; scores is fp32 [n_rows].
+ * Accumulation is fp32. bf16 inputs with d_model % 64 == 0, d_hidden in
+ * {128, 256} and 16-byte-aligned x and w1 take the MFMA path; every other
+ * shape takes a plain fp32-FMA path. Source: section "Wie hat TokenGate das
+ * Pruning von Tokens verstanden?" (the MLP gate scores every token from its
+ * post-attention residual at gate layer L). */
+tg_status tg_gate_score(tg_dtype dt, const void* x, int64_t n_rows, int32_t d_model,
+                        const void* w1, const void* b1, int32_t d_hidden, const void* w2,
+                        float b2, float* scores, hipStream_t stream);
+
+/* Device workspace tg_select_topk needs, in bytes (0 means none; pass NULL). */
+size_t tg_select_workspace_bytes(const tg_seq* seqs, int32_t n_seqs);
+
+/* Step 2 - top-K select. For each prompt, ranks its document rows by
+ * scores (fp32 [total rows]), highest first, ties to the lower row id, NaN
+ * below every number, -0 equal to +0; keeps the first k_doc of them and every
+ * row outside the document; writes the kept packed row ids (int32) in
+ * ascending order to kept_idx[off_b .. off_b + M_b). kept_idx must hold
+ * tg_kept_rows(seqs) entries. Bit-exact and deterministic. Sources: section
+ * "Wie hat TokenGate das Pruning von Tokens verstanden?" (top-K keeps the
+ * best-scored tokens; the question is never removed). */
+tg_status tg_select_topk(const float* scores, const tg_seq* seqs, int32_t n_seqs,
+                         int32_t* kept_idx, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Step 3 - compaction of the m_rows = tg_kept_rows(seqs) kept rows.
+ *  - gathers[0 .. n_gathers): row gathers, bit-exact (see tg_gather);
+ *  - pos_kept (nullable) int32 [m_rows]: pos[kept_idx[m]], or, with pos NULL,
+ *    kept_idx[m] - start of its prompt (original position in the prompt);
+ *  - bias_kept (nullable, needs scores) fp32 [m_rows]:
+ *    logsigmoid(scores[kept_idx[m]]) for document rows, 0 for the others.
+ * kept_idx rows must belong to the prompts and be ordered by prompt.
+ * Sources: section "Wie hat TokenGate das Pruning von Tokens verstanden?"
+ * (layers above the gate process only the K kept tokens and create no KV for
+ * the pruned), section "Was ist token-gated Attention?" (the kept score
+ * becomes the bias). */
+tg_status tg_compact(const int32_t* kept_idx, int64_t m_rows, const tg_seq* seqs,
+                     int32_t n_seqs, const tg_gather* gathers, int32_t n_gathers,
+                     const int32_t* pos, int32_t* pos_kept, const float* scores,
+                     float* bias_kept, hipStream_t stream);
+
+/* Device workspace tg_gated_attention needs, in bytes (0 means none). */
+size_t tg_attention_workspace_bytes(const tg_seq* seqs, int32_t n_seqs, int32_t hq,
+                                    int32_t hkv, int32_t head_dim);
+
+/* Step 4 - token-gated attention over the kept rows. q [M, hq, head_dim],
+ * k and v [M, hkv, head_dim], out [M, hq, head_dim] (all contiguous, dtype
+ * dt, M = tg_kept_rows(seqs)); bias_kept fp32 [M]; pos_kept int32 [M],
+ * non-decreasing within each prompt (tg_compact produces this whenever
+ * the original positions grow with the row id); gain fp32 [hq] (device);
+ * tau > 0. Query head h reads KV head h / (hq / hkv). For kept rows i, j of
+ * the same prompt:
+ *     logit_ij = q_i . k_j / (sqrt(head_dim) * tau) + gain[h] * bias_kept[j]
+ * over the keys with pos_kept[j] <= pos_kept[i], softmax, times V.
+ * lse (nullable) fp32 [hq, M] receives log sum_j exp(logit_ij). bf16 runs on
+ * MFMA with fp32 softmax and accumulation; fp32 runs on plain FMA.
+ * head_dim in {64, 128}; hq % hkv == 0. Sources: section "Was ist
+ * token-gated Attention?" (kept-token score as a bias on the attention
+ * logits above the gate, per-head gain, temperature) and "Wie wird TokenGate
+ * implementiert?" (a key-bias attention kernel). */
+tg_status tg_gated_attention(tg_dtype dt, const void* q, const void* k, const void* v,
+                             const float* bias_kept, const int32_t* pos_kept,
+                             const tg_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv,
+                             int32_t head_dim, const float* gain, float tau, void* out,
+                             float* lse, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* Static text of a status code. */
+const char* tg_status_string(tg_status status);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* tg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKENGATE_H */

@@ -1,0 +1,24 @@
+"""TokenGate pruned-prefill layer for MI355X (gfx950).
+
+The four steps (gate score, top-K select, compaction, token-gated
+attention) are HIP kernels behind the C ABI in include/tokengate.h; this
+package is the thin ctypes binding over it (argument marshalling only).
+"""
+
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    TG_BF16,
+    TG_F32,
+    TG_MAX_GATHERS,
+    TG_MAX_SEQS,
+    TokenGateError,
+    load,
+    seq_array,
+    tg_compact,
+    tg_gate_score,
+    tg_gated_attention,
+    tg_kept_rows,
+    tg_select_topk,
+)
+from .layer import GatedPrefillLayer  # noqa: F401

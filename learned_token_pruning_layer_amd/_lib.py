@@ -1,0 +1,244 @@
+"""ctypes binding of libtokengate.so (the C ABI in include/tokengate.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI. torch supplies device memory and the stream. There is no
+fallback: if the library is missing, or a tensor is not on a GPU, the call
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtokengate.so")
+
+TG_OK, TG_ERR_INVALID_ARGUMENT, TG_ERR_UNSUPPORTED, TG_ERR_WORKSPACE, TG_ERR_HIP = range(5)
+TG_F32, TG_BF16 = 0, 1
+TG_MAX_SEQS = 64
+TG_MAX_GATHERS = 16
+
+EXPORTED = (
+    "tg_kept_rows", "tg_gate_score", "tg_select_workspace_bytes", "tg_select_topk", "tg_compact",
+    "tg_attention_workspace_bytes", "tg_gated_attention", "tg_status_string", "tg_last_error",
+)
+
+
+class TokenGateError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"tokengate status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class TgSeq(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_int64), ("len", ctypes.c_int32), ("doc_begin", ctypes.c_int32),
+                ("doc_end", ctypes.c_int32), ("k_doc", ctypes.c_int32)]
+
+
+class TgGather(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("dst", ctypes.c_void_p), ("row_bytes", ctypes.c_int64),
+                ("src_stride", ctypes.c_int64), ("dst_stride", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    c_int, i32, i64, vp, f32 = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    seqp = ctypes.POINTER(TgSeq)
+    lib.tg_kept_rows.argtypes = [seqp, i32]
+    lib.tg_kept_rows.restype = i64
+    lib.tg_gate_score.argtypes = [c_int, vp, i64, i32, vp, vp, i32, vp, f32, vp, vp]
+    lib.tg_gate_score.restype = c_int
+    lib.tg_select_workspace_bytes.argtypes = [seqp, i32]
+    lib.tg_select_workspace_bytes.restype = ctypes.c_size_t
+    lib.tg_select_topk.argtypes = [vp, seqp, i32, vp, vp, ctypes.c_size_t, vp]
+    lib.tg_select_topk.restype = c_int
+    lib.tg_compact.argtypes = [vp, i64, seqp, i32, ctypes.POINTER(TgGather), i32, vp, vp, vp, vp, vp]
+    lib.tg_compact.restype = c_int
+    lib.tg_attention_workspace_bytes.argtypes = [seqp, i32, i32, i32, i32]
+    lib.tg_attention_workspace_bytes.restype = ctypes.c_size_t
+    lib.tg_gated_attention.argtypes = [c_int, vp, vp, vp, vp, vp, seqp, i32, i32, i32, i32, vp, f32,
+                                       vp, vp, vp, ctypes.c_size_t, vp]
+    lib.tg_gated_attention.restype = c_int
+    lib.tg_status_string.argtypes = [c_int]
+    lib.tg_status_string.restype = ctypes.c_char_p
+    lib.tg_last_error.argtypes = []
+    lib.tg_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != TG_OK:
+        lib = load()
+        raise TokenGateError(status, f"{lib.tg_status_string(status).decode()}: {lib.tg_last_error().decode()}")
+
+
+def seq_array(seqs: Sequence) -> ctypes.Array:
+    """Prompts as a tg_seq array. Accepts objects with start, length (or
+    len), doc_begin, doc_end, k_doc attributes, or 5-tuples in that order."""
+    arr = (TgSeq * max(1, len(seqs)))()
+    for i, s in enumerate(seqs):
+        if isinstance(s, tuple) and not hasattr(s, "start"):
+            start, ln, db, de, k = s
+        else:
+            start = s.start
+            ln = getattr(s, "length", None)
+            ln = s.len if ln is None else ln
+            db, de, k = s.doc_begin, s.doc_end, s.k_doc
+        arr[i] = TgSeq(int(start), int(ln), int(db), int(de), int(k))
+    return arr
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TG_F32
+    if t.dtype == torch.bfloat16:
+        return TG_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def tg_kept_rows(seqs: Sequence) -> int:
+    lib = load()
+    m = lib.tg_kept_rows(seq_array(seqs), len(seqs))
+    if m < 0:
+        raise TokenGateError(TG_ERR_INVALID_ARGUMENT, lib.tg_last_error().decode())
+    return int(m)
+
+
+def tg_gate_score(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, b1: Optional[torch.Tensor] = None,
+                  b2: float = 0.0, scores: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """scores[r] = w2 . SiLU(W1 x_r + b1) + b2 (fp32 [N])."""
+    lib = load()
+    for t, nm in ((x, "x"), (w1, "w1"), (w2, "w2")):
+        _dev(t, nm)
+    n, d = x.shape
+    h = w1.shape[0]
+    if w1.shape != (h, d) or w2.numel() != h or w1.dtype != x.dtype or w2.dtype != x.dtype:
+        raise ValueError("w1 must be [H, d] and w2 [H], same dtype as x")
+    if b1 is not None:
+        _dev(b1, "b1")
+        if b1.numel() != h or b1.dtype != x.dtype:
+            raise ValueError("b1 must be [H], same dtype as x")
+    if scores is None:
+        scores = torch.empty(n, dtype=torch.float32, device=x.device)
+    _check(lib.tg_gate_score(_dtype_code(x), x.data_ptr(), n, d, w1.data_ptr(), _ptr(b1), h, w2.data_ptr(),
+                             float(b2), scores.data_ptr(), _stream(stream)))
+    return scores
+
+
+def tg_select_topk(scores: torch.Tensor, seqs: Sequence, kept_idx: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Kept packed row ids (int32 [M]), ascending within each prompt."""
+    lib = load()
+    _dev(scores, "scores")
+    if scores.dtype != torch.float32:
+        raise ValueError("scores must be fp32")
+    sa = seq_array(seqs)
+    m = tg_kept_rows(seqs)
+    if kept_idx is None:
+        kept_idx = torch.empty(m, dtype=torch.int32, device=scores.device)
+    ws_bytes = lib.tg_select_workspace_bytes(sa, len(seqs))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=scores.device)
+    _check(lib.tg_select_topk(scores.data_ptr(), sa, len(seqs), kept_idx.data_ptr(), _ptr(workspace),
+                              ws_bytes if workspace is not None else 0, _stream(stream)))
+    return kept_idx
+
+
+def tg_compact(kept_idx: torch.Tensor, seqs: Sequence, tensors: Sequence[torch.Tensor] = (),
+               pos: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
+               want_pos: bool = True, outs: Optional[Sequence[torch.Tensor]] = None,
+               pos_kept: Optional[torch.Tensor] = None, bias_kept: Optional[torch.Tensor] = None,
+               stream=None) -> Tuple[List[torch.Tensor], Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """Gather kept rows of `tensors` (row = first dim), positions and bias.
+
+    Returns (gathered, pos_kept, bias_kept); bias_kept is computed when
+    `scores` is given."""
+    lib = load()
+    _dev(kept_idx, "kept_idx")
+    m = tg_kept_rows(seqs)
+    dev = kept_idx.device
+    gathered = []
+    garr = (TgGather * max(1, len(tensors)))()
+    for i, t in enumerate(tensors):
+        _dev(t, f"tensors[{i}]")
+        dst = outs[i] if outs is not None else torch.empty((m,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev)
+        row_bytes = int(math.prod(t.shape[1:])) * t.element_size()
+        garr[i] = TgGather(t.data_ptr(), dst.data_ptr(), row_bytes, row_bytes, row_bytes)
+        gathered.append(dst)
+    if want_pos and pos_kept is None:
+        pos_kept = torch.empty(m, dtype=torch.int32, device=dev)
+    if scores is not None and bias_kept is None:
+        bias_kept = torch.empty(m, dtype=torch.float32, device=dev)
+    if pos is not None:
+        _dev(pos, "pos")
+    _check(lib.tg_compact(kept_idx.data_ptr(), m, seq_array(seqs), len(seqs), garr, len(tensors),
+                          _ptr(pos), _ptr(pos_kept if want_pos else None), _ptr(scores),
+                          _ptr(bias_kept if scores is not None else None), _stream(stream)))
+    return gathered, (pos_kept if want_pos else None), (bias_kept if scores is not None else None)
+
+
+def tg_gated_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias_kept: torch.Tensor,
+                       pos_kept: torch.Tensor, seqs: Sequence, gain: torch.Tensor, tau: float,
+                       out: Optional[torch.Tensor] = None, want_lse: bool = False,
+                       lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Token-gated causal attention over the kept rows.
+
+    q [M, hq, D], k/v [M, hkv, D]; returns (out [M, hq, D], lse [hq, M] or None)."""
+    lib = load()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (bias_kept, "bias_kept"), (pos_kept, "pos_kept"), (gain, "gain")):
+        _dev(t, nm)
+    m, hq, dh = q.shape
+    hkv = k.shape[1]
+    if k.shape != (m, hkv, dh) or v.shape != (m, hkv, dh):
+        raise ValueError("k and v must be [M, hkv, D] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    if bias_kept.dtype != torch.float32 or pos_kept.dtype != torch.int32 or gain.dtype != torch.float32:
+        raise ValueError("bias_kept fp32, pos_kept int32, gain fp32 expected")
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((hq, m), dtype=torch.float32, device=q.device)
+    sa = seq_array(seqs)
+    ws_bytes = lib.tg_attention_workspace_bytes(sa, len(seqs), hq, hkv, dh)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _check(lib.tg_gated_attention(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), bias_kept.data_ptr(),
+                                  pos_kept.data_ptr(), sa, len(seqs), hq, hkv, dh, gain.data_ptr(), float(tau),
+                                  out.data_ptr(), _ptr(lse if want_lse else None), _ptr(workspace),
+                                  ws_bytes if workspace is not None else 0, _stream(stream)))
+    return out, (lse if want_lse else None)

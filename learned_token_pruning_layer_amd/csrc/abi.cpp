@@ -1,0 +1,244 @@
+// C-ABI entry points: argument validation on the host, descriptor tables,
+// kernel launches. Validation runs before anything touches the HIP runtime,
+// so every invalid call returns its status without enqueueing work.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "tg_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+tg_status fail(tg_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+tg_status hip_fail(hipError_t e, const char* what) {
+    return fail(TG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validates the prompt descriptors and fills the kernel-side table.
+// Returns TG_OK and the total kept rows through *m_total.
+tg_status build_seq_table(const tg_seq* seqs, int32_t n_seqs, tg::SeqTable* t, int64_t* m_total) {
+    if (n_seqs < 0 || n_seqs > TG_MAX_SEQS)
+        return fail(TG_ERR_INVALID_ARGUMENT, "n_seqs=%d outside [0, %d]", n_seqs, TG_MAX_SEQS);
+    if (n_seqs > 0 && !seqs) return fail(TG_ERR_INVALID_ARGUMENT, "seqs is NULL");
+    memset(t, 0, sizeof *t);
+    t->n = n_seqs;
+    int64_t next = 0, kept = 0;
+    for (int32_t b = 0; b < n_seqs; ++b) {
+        const tg_seq& s = seqs[b];
+        if (s.start < next)
+            return fail(TG_ERR_INVALID_ARGUMENT,
+                        "prompt %d: start=%lld overlaps or precedes the previous prompt", b,
+                        (long long)s.start);
+        if (s.len < 0) return fail(TG_ERR_INVALID_ARGUMENT, "prompt %d: len=%d < 0", b, s.len);
+        if (s.doc_begin < 0 || s.doc_begin > s.doc_end || s.doc_end > s.len)
+            return fail(TG_ERR_INVALID_ARGUMENT,
+                        "prompt %d: document span [%d, %d) outside the prompt (len %d)", b,
+                        s.doc_begin, s.doc_end, s.len);
+        const int32_t n_doc = s.doc_end - s.doc_begin;
+        if (s.k_doc < 0 || s.k_doc > n_doc)
+            return fail(TG_ERR_INVALID_ARGUMENT, "prompt %d: k_doc=%d outside [0, %d]", b, s.k_doc,
+                        n_doc);
+        if (s.start + s.len > (int64_t)INT32_MAX)
+            return fail(TG_ERR_UNSUPPORTED, "prompt %d: rows beyond 2^31-1 (int32 row ids)", b);
+        tg::SeqDesc& d = t->s[b];
+        d.start = s.start;
+        d.kept_off = kept;
+        d.len = s.len;
+        d.doc_begin = s.doc_begin;
+        d.doc_end = s.doc_end;
+        d.k_doc = s.k_doc;
+        d.n_kept = s.k_doc + (s.len - n_doc);
+        kept += d.n_kept;
+        next = s.start + s.len;
+    }
+    *m_total = kept;
+    return TG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tg_status_string(tg_status st) {
+    switch (st) {
+        case TG_OK: return "ok";
+        case TG_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case TG_ERR_UNSUPPORTED: return "unsupported shape or alignment";
+        case TG_ERR_WORKSPACE: return "workspace missing or too small";
+        case TG_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* tg_last_error(void) { return g_err.c_str(); }
+
+int64_t tg_kept_rows(const tg_seq* seqs, int32_t n_seqs) {
+    tg::SeqTable t;
+    int64_t m = 0;
+    if (build_seq_table(seqs, n_seqs, &t, &m) != TG_OK) return -1;
+    return m;
+}
+
+tg_status tg_gate_score(tg_dtype dt, const void* x, int64_t n_rows, int32_t d_model, const void* w1,
+                        const void* b1, int32_t d_hidden, const void* w2, float b2, float* scores,
+                        hipStream_t stream) {
+    g_err.clear();
+    if (dt != TG_F32 && dt != TG_BF16) return fail(TG_ERR_INVALID_ARGUMENT, "dtype %d unknown", (int)dt);
+    if (n_rows < 0) return fail(TG_ERR_INVALID_ARGUMENT, "n_rows=%lld < 0", (long long)n_rows);
+    if (d_model <= 0 || d_hidden <= 0)
+        return fail(TG_ERR_INVALID_ARGUMENT, "d_model=%d and d_hidden=%d must be > 0", d_model, d_hidden);
+    if (n_rows == 0) return TG_OK;
+    if (!x || !w1 || !w2 || !scores) return fail(TG_ERR_INVALID_ARGUMENT, "x, w1, w2, scores must be non-NULL");
+    if ((n_rows + 3) / 4 > (int64_t)INT32_MAX)
+        return fail(TG_ERR_UNSUPPORTED, "n_rows=%lld too large for one launch", (long long)n_rows);
+    const bool mfma = dt == TG_BF16 && d_model % 64 == 0 && (d_hidden == 128 || d_hidden == 256) &&
+                      aligned16(x) && aligned16(w1);
+    hipError_t e = mfma ? tg::launch_gate_mfma_bf16(x, n_rows, d_model, w1, b1, d_hidden, w2, b2, scores, stream)
+                        : tg::launch_gate_simple(dt, x, n_rows, d_model, w1, b1, d_hidden, w2, b2, scores, stream);
+    if (e != hipSuccess) return hip_fail(e, "tg_gate_score launch");
+    return TG_OK;
+}
+
+size_t tg_select_workspace_bytes(const tg_seq* seqs, int32_t n_seqs) {
+    (void)seqs;
+    (void)n_seqs;
+    return 0;
+}
+
+tg_status tg_select_topk(const float* scores, const tg_seq* seqs, int32_t n_seqs, int32_t* kept_idx,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_err.clear();
+    (void)workspace;
+    (void)workspace_bytes;
+    tg::SeqTable t;
+    int64_t m = 0;
+    tg_status st = build_seq_table(seqs, n_seqs, &t, &m);
+    if (st != TG_OK) return st;
+    if (n_seqs == 0) return TG_OK;
+    bool any_rows = false;
+    for (int b = 0; b < n_seqs; ++b) any_rows |= seqs[b].len > 0;
+    if (!any_rows) return TG_OK;
+    if (!scores) return fail(TG_ERR_INVALID_ARGUMENT, "scores is NULL");
+    if (m > 0 && !kept_idx) return fail(TG_ERR_INVALID_ARGUMENT, "kept_idx is NULL");
+    hipError_t e = tg::launch_select(scores, t, kept_idx, stream);
+    if (e != hipSuccess) return hip_fail(e, "tg_select_topk launch");
+    return TG_OK;
+}
+
+tg_status tg_compact(const int32_t* kept_idx, int64_t m_rows, const tg_seq* seqs, int32_t n_seqs,
+                     const tg_gather* gathers, int32_t n_gathers, const int32_t* pos,
+                     int32_t* pos_kept, const float* scores, float* bias_kept, hipStream_t stream) {
+    g_err.clear();
+    tg::SeqTable t;
+    int64_t m = 0;
+    tg_status st = build_seq_table(seqs, n_seqs, &t, &m);
+    if (st != TG_OK) return st;
+    if (m_rows != m)
+        return fail(TG_ERR_INVALID_ARGUMENT, "m_rows=%lld but the prompts keep %lld rows",
+                    (long long)m_rows, (long long)m);
+    if (n_gathers < 0 || n_gathers > TG_MAX_GATHERS)
+        return fail(TG_ERR_INVALID_ARGUMENT, "n_gathers=%d outside [0, %d]", n_gathers, TG_MAX_GATHERS);
+    if (n_gathers > 0 && !gathers) return fail(TG_ERR_INVALID_ARGUMENT, "gathers is NULL");
+    if (bias_kept && !scores) return fail(TG_ERR_INVALID_ARGUMENT, "bias_kept needs scores");
+    tg::GatherTable g;
+    memset(&g, 0, sizeof g);
+    g.n = n_gathers;
+    for (int i = 0; i < n_gathers; ++i) {
+        const tg_gather& d = gathers[i];
+        if (!d.src || !d.dst) return fail(TG_ERR_INVALID_ARGUMENT, "gather %d: NULL pointer", i);
+        if (d.row_bytes <= 0 || d.row_bytes > (int64_t)1 << 30)
+            return fail(TG_ERR_INVALID_ARGUMENT, "gather %d: row_bytes=%lld outside (0, 2^30]", i,
+                        (long long)d.row_bytes);
+        if (d.src_stride < d.row_bytes || d.dst_stride < d.row_bytes)
+            return fail(TG_ERR_INVALID_ARGUMENT, "gather %d: strides smaller than row_bytes", i);
+        if (d.row_bytes % 16 || d.src_stride % 16 || d.dst_stride % 16 || !aligned16(d.src) ||
+            !aligned16(d.dst))
+            return fail(TG_ERR_UNSUPPORTED, "gather %d: sizes and pointers must be multiples of 16 bytes", i);
+        g.g[i].src = (const char*)d.src;
+        g.g[i].dst = (char*)d.dst;
+        g.g[i].units = d.row_bytes / 16;
+        g.g[i].src_stride = d.src_stride;
+        g.g[i].dst_stride = d.dst_stride;
+    }
+    if (m == 0) return TG_OK;
+    if (!kept_idx) return fail(TG_ERR_INVALID_ARGUMENT, "kept_idx is NULL");
+    if (n_gathers == 0 && !pos_kept && !bias_kept) return TG_OK;
+    hipError_t e = tg::launch_compact(kept_idx, m, t, g, pos, pos_kept, scores, bias_kept, stream);
+    if (e != hipSuccess) return hip_fail(e, "tg_compact launch");
+    return TG_OK;
+}
+
+size_t tg_attention_workspace_bytes(const tg_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv,
+                                    int32_t head_dim) {
+    (void)seqs;
+    (void)n_seqs;
+    (void)hq;
+    (void)hkv;
+    (void)head_dim;
+    return 0;
+}
+
+tg_status tg_gated_attention(tg_dtype dt, const void* q, const void* k, const void* v,
+                             const float* bias_kept, const int32_t* pos_kept, const tg_seq* seqs,
+                             int32_t n_seqs, int32_t hq, int32_t hkv, int32_t head_dim,
+                             const float* gain, float tau, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    g_err.clear();
+    (void)workspace;
+    (void)workspace_bytes;
+    if (dt != TG_F32 && dt != TG_BF16) return fail(TG_ERR_INVALID_ARGUMENT, "dtype %d unknown", (int)dt);
+    if (hq <= 0 || hkv <= 0 || hq % hkv)
+        return fail(TG_ERR_INVALID_ARGUMENT, "hq=%d must be a positive multiple of hkv=%d", hq, hkv);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(TG_ERR_UNSUPPORTED, "head_dim=%d (built: 64, 128)", head_dim);
+    if (!(tau > 0.0f) || tau != tau || tau > 3.0e38f)
+        return fail(TG_ERR_INVALID_ARGUMENT, "tau must be finite and > 0");
+    tg::SeqTable st_;
+    int64_t m = 0;
+    tg_status st = build_seq_table(seqs, n_seqs, &st_, &m);
+    if (st != TG_OK) return st;
+    if (m == 0) return TG_OK;
+    if (!q || !k || !v || !bias_kept || !pos_kept || !gain || !out)
+        return fail(TG_ERR_INVALID_ARGUMENT, "q, k, v, bias_kept, pos_kept, gain, out must be non-NULL");
+    if (dt == TG_BF16 && !(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out)))
+        return fail(TG_ERR_UNSUPPORTED, "bf16 q, k, v, out must be 16-byte aligned");
+    const int bm = tg::attention_block_rows(dt, hq, hkv);
+    const int hw = tg::attention_heads_per_item(dt, hq, hkv);
+    const int64_t items_per_blk = hq / hw;
+    tg::AttnTable t;
+    memset(&t, 0, sizeof t);
+    t.n_seg = n_seqs;
+    t.m_total = m;
+    int64_t items = 0;
+    for (int b = 0; b < n_seqs; ++b) {
+        const tg::SeqDesc& d = st_.s[b];
+        t.s[b].kept_off = d.kept_off;
+        t.s[b].n = d.n_kept;
+        t.s[b].n_qblk = (d.n_kept + bm - 1) / bm;
+        t.s[b].item_base = (int32_t)items;
+        items += (int64_t)t.s[b].n_qblk * items_per_blk;
+        if (items > (int64_t)INT32_MAX) return fail(TG_ERR_UNSUPPORTED, "too many work items for one launch");
+    }
+    t.n_items = (int32_t)items;
+    hipError_t e = tg::launch_attention(dt, q, k, v, bias_kept, pos_kept, t, hq, hkv, head_dim, gain,
+                                        tau, out, lse, stream);
+    if (e != hipSuccess) return hip_fail(e, "tg_gated_attention launch");
+    return TG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Internal declarations shared by the HIP kernels and the C-ABI host layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tokengate.h"
+
+namespace tg {
+
+// Per-prompt descriptor as the kernels see it (passed by value as a kernel
+// argument, so no device allocation is needed for it).
+struct SeqDesc {
+    int64_t start;     // first packed input row
+    int64_t kept_off;  // first packed kept row
+    int32_t len;       // rows in the prompt
+    int32_t doc_begin; // document span, relative to start
+    int32_t doc_end;
+    int32_t k_doc;     // document rows kept
+    int32_t n_kept;    // k_doc + len - (doc_end - doc_begin)
+    int32_t pad;
+};
+
+struct SeqTable {
+    int32_t n;
+    int32_t pad;
+    SeqDesc s[TG_MAX_SEQS];
+};
+
+struct GatherDesc {
+    const char* src;
+    char* dst;
+    int64_t units;       // 16-byte units per row
+    int64_t src_stride;  // bytes
+    int64_t dst_stride;  // bytes
+};
+
+struct GatherTable {
+    int32_t n;
+    int32_t pad;
+    GatherDesc g[TG_MAX_GATHERS];
+};
+
+// Attention work decomposition: one entry per prompt.
+struct AttnSeg {
+    int64_t kept_off;   // first packed kept row of the prompt
+    int32_t n;          // kept rows of the prompt
+    int32_t n_qblk;     // query blocks of the prompt
+    int32_t item_base;  // first work item of the prompt
+    int32_t pad;
+};
+
+struct AttnTable {
+    int32_t n_seg;
+    int32_t n_items;
+    int64_t m_total;
+    AttnSeg s[TG_MAX_SEQS];
+};
+
+// Launchers (each returns hipGetLastError() after its launch).
+hipError_t launch_gate_mfma_bf16(const void* x, int64_t n, int d, const void* w1, const void* b1,
+                                 int h, const void* w2, float b2, float* scores, hipStream_t st);
+hipError_t launch_gate_simple(tg_dtype dt, const void* x, int64_t n, int d, const void* w1,
+                              const void* b1, int h, const void* w2, float b2, float* scores,
+                              hipStream_t st);
+hipError_t launch_select(const float* scores, const SeqTable& t, int32_t* kept, hipStream_t st);
+hipError_t launch_compact(const int32_t* kept, int64_t m, const SeqTable& t, const GatherTable& g,
+                          const int32_t* pos, int32_t* pos_kept, const float* scores,
+                          float* bias_kept, hipStream_t st);
+hipError_t launch_attention(tg_dtype dt, const void* q, const void* k, const void* v,
+                            const float* bias, const int32_t* pos, const AttnTable& t, int hq,
+                            int hkv, int head_dim, const float* gain, float tau, void* out,
+                            float* lse, hipStream_t st);
+
+// Query-row block per attention work item for a given dtype/head ratio.
+int attention_block_rows(tg_dtype dt, int hq, int hkv);
+int attention_heads_per_item(tg_dtype dt, int hq, int hkv);
+
+}  // namespace tg

@@ -1,0 +1,132 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/tokengate.h declares, and rejects invalid arguments on the host
+before any HIP call (NULL device pointers are fine: nothing is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import learned_token_pruning_layer_amd as tg
+from learned_token_pruning_layer_amd._lib import TgGather, seq_array
+from synthetic import Prompt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tokengate.h")
+
+INVALID, UNSUPPORTED = 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tg_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tg.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) == 9, names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(tg.EXPORTED)
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.tg_status_string(code)
+
+
+def test_kept_rows_and_validation(lib):
+    ps = [Prompt(0, 16384, 0, 16000, 2000)]
+    assert tg.tg_kept_rows(ps) == 2384
+    ragged = [Prompt(0, 100, 10, 90, 5), Prompt(100, 50, 0, 50, 50), Prompt(150, 0, 0, 0, 0)]
+    assert tg.tg_kept_rows(ragged) == (5 + 20) + 50 + 0
+    bad = [
+        [Prompt(0, 10, 0, 8, 9)],                          # k_doc > n_doc
+        [Prompt(0, 10, 0, 8, -1)],                         # k_doc < 0
+        [Prompt(0, 10, 3, 2, 0)],                          # doc_begin > doc_end
+        [Prompt(0, 10, 0, 11, 0)],                         # doc_end > len
+        [Prompt(0, -1, 0, 0, 0)],                          # negative length
+        [Prompt(5, 10, 0, 5, 1), Prompt(8, 10, 0, 5, 1)],  # overlapping prompts
+    ]
+    for b in bad:
+        assert lib.tg_kept_rows(seq_array(b), len(b)) == -1
+        assert lib.tg_last_error()
+    many = [Prompt(i, 1, 0, 1, 1) for i in range(tg.TG_MAX_SEQS + 1)]
+    assert lib.tg_kept_rows(seq_array(many), len(many)) == -1
+
+
+def test_select_rejects_before_launch(lib):
+    bad = [Prompt(0, 10, 0, 8, 9)]
+    st = lib.tg_select_topk(None, seq_array(bad), 1, None, None, 0, None)
+    assert st == INVALID and b"k_doc" in lib.tg_last_error()
+    ok = [Prompt(0, 10, 0, 8, 3)]
+    assert lib.tg_select_topk(None, seq_array(ok), 1, None, None, 0, None) == INVALID  # NULL scores
+    assert lib.tg_select_workspace_bytes(seq_array(ok), 1) == 0
+
+
+def test_gate_rejects_before_launch(lib):
+    assert lib.tg_gate_score(7, None, 10, 64, None, None, 64, None, 0.0, None, None) == INVALID
+    assert lib.tg_gate_score(0, None, -1, 64, None, None, 64, None, 0.0, None, None) == INVALID
+    assert lib.tg_gate_score(0, None, 10, 0, None, None, 64, None, 0.0, None, None) == INVALID
+    assert lib.tg_gate_score(1, None, 10, 64, None, None, 64, None, 0.0, None, None) == INVALID  # NULLs
+    assert lib.tg_gate_score(1, None, 0, 64, None, None, 64, None, 0.0, None, None) == 0  # empty: no-op
+
+
+def test_compact_rejects_before_launch(lib):
+    ps = [Prompt(0, 10, 0, 8, 3)]
+    sa = seq_array(ps)
+    assert lib.tg_compact(None, 4, sa, 1, None, 0, None, None, None, None, None) == INVALID  # m mismatch
+    g = (TgGather * 1)()
+    g[0] = TgGather(16, 32, 24, 32, 32)  # row_bytes not a multiple of 16
+    assert lib.tg_compact(None, 5, sa, 1, g, 1, None, None, None, None, None) == UNSUPPORTED
+    g[0] = TgGather(16, 32, 32, 16, 32)  # stride below row_bytes
+    assert lib.tg_compact(None, 5, sa, 1, g, 1, None, None, None, None, None) == INVALID
+    g[0] = TgGather(None, 32, 32, 32, 32)
+    assert lib.tg_compact(None, 5, sa, 1, g, 1, None, None, None, None, None) == INVALID
+    # bias requested without scores
+    assert lib.tg_compact(None, 5, sa, 1, None, 0, None, None, None, ctypes.c_void_p(64), None) == INVALID
+    # too many gathers
+    assert lib.tg_compact(None, 5, sa, 1, g, tg.TG_MAX_GATHERS + 1, None, None, None, None, None) == INVALID
+
+
+def test_attention_rejects_before_launch(lib):
+    ps = [Prompt(0, 10, 0, 8, 3)]
+    sa = seq_array(ps)
+
+    def call(dt=1, hq=16, hkv=8, d=128, tau=1.2, q=None):
+        return lib.tg_gated_attention(dt, q, None, None, None, None, sa, 1, hq, hkv, d, None, tau,
+                                      None, None, None, 0, None)
+
+    assert call(hq=12, hkv=8) == INVALID
+    assert call(hkv=0) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(tau=0.0) == INVALID
+    assert call(tau=float("nan")) == INVALID
+    assert call(tau=float("inf")) == INVALID
+    assert call(dt=5) == INVALID
+    assert call() == INVALID  # NULL tensors
+    assert lib.tg_attention_workspace_bytes(sa, 1, 16, 8, 128) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 64)
+    with pytest.raises(ValueError):
+        tg.tg_gate_score(x, torch.zeros(128, 64), torch.zeros(128))
+
+
+def test_product_never_touches_oracle():
+    pkg = os.path.join(ROOT, "learned_token_pruning_layer_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", src, re.M), f
+                assert "oracle" not in src or f.endswith(".py") is False or "import oracle" not in src, f

@@ -1,0 +1,385 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Each stage gets identical seeded synthetic inputs on both sides (the
+oracle never sees a GPU output). Bars:
+  select, compaction gathers, positions: bit-exact;
+  fp32 scores and outputs: |diff| <= 1e-4;
+  bf16 attention outputs: per (row, head) max|diff| <= 2e-2 * max|O_ref|;
+  bf16 gate scores: |diff| <= 2e-2 * max|s_ref| over the prompt;
+  bias: |diff| <= 1e-6 * max(1, |b|).
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import learned_token_pruning_layer_amd as tg
+from synthetic import (Prompt, doc_budget, make_attention_inputs, make_ragged, make_scores,
+                       make_workload, ragged_prompts)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def note(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def f64(t):
+    return t.detach().float().cpu().double().numpy() if t.dtype == torch.bfloat16 else t.detach().cpu().double().numpy()
+
+
+def assert_rowmax_close(got, ref, rel=2e-2):
+    """bf16 bar: per (row, head), max |got-ref| <= rel * max |ref|."""
+    err = np.abs(got - ref).max(axis=-1)
+    scale = np.abs(ref).max(axis=-1)
+    bad = err > rel * scale
+    assert not bad.any(), f"{bad.sum()} (row, head) pairs over the bar; worst ratio {np.max(err / np.maximum(scale, 1e-30)):.3e}"
+    return float(np.max(err / np.maximum(scale, 1e-30)))
+
+
+# ------------------------------------------------------------------ gate ----
+
+def test_gate_fp32_tiny():
+    note("gate fp32 tiny (N=512, d=256, H=64)")
+    w = make_workload("tiny", device=DEV, with_layers=False)
+    s = tg.tg_gate_score(w.x, w.w1, w.w2)
+    ref = oracle.gate_scores(w.x.cpu(), w.w1.cpu(), w.w2.cpu())
+    assert np.abs(f64(s) - ref).max() <= 1e-4
+
+
+@pytest.mark.parametrize("n,d,h,with_b1", [(1000, 2048, 256, False), (65, 512, 128, True),
+                                           (1, 2048, 256, True), (200, 192, 64, False), (130, 100, 24, True)])
+def test_gate_bf16(n, d, h, with_b1):
+    note(f"gate bf16 n={n} d={d} h={h} b1={with_b1}")
+    g = torch.Generator(device=DEV).manual_seed(n + d + h)
+    x = torch.randn(n, d, generator=g, device=DEV).to(torch.bfloat16)
+    w1 = (torch.randn(h, d, generator=g, device=DEV) / math.sqrt(d)).to(torch.bfloat16)
+    w2 = (torch.randn(h, generator=g, device=DEV) / math.sqrt(h)).to(torch.bfloat16)
+    b1 = (torch.randn(h, generator=g, device=DEV) * 0.5).to(torch.bfloat16) if with_b1 else None
+    s = tg.tg_gate_score(x, w1, w2, b1, b2=0.375)
+    ref = oracle.gate_scores(x.cpu(), w1.cpu(), w2.cpu(), None if b1 is None else b1.cpu(), 0.375)
+    err = np.abs(f64(s) - ref)
+    assert err.max() <= 2e-2 * np.abs(ref).max()
+    # fp32 accumulation of exact bf16 products: far inside the bar
+    assert err.max() <= 1e-3 * max(1.0, np.abs(ref).max())
+
+
+def test_gate_bf16_qwen16k_sampled():
+    note("gate bf16 qwen16k full size, 1024 sampled rows + planted rows")
+    w = make_workload("qwen16k", device=DEV, with_layers=False)
+    s = f64(tg.tg_gate_score(w.x, w.w1, w.w2))
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([rng.choice(w.n_rows, 1024, replace=False), w.planted, [w.n_rows - 1]]))
+    ref = oracle.gate_scores(w.x[torch.as_tensor(rows, device=DEV)].cpu(), w.w1.cpu(), w.w2.cpu())
+    assert np.abs(s[rows] - ref).max() <= 2e-2 * np.abs(ref).max()
+    # planted rows rank first
+    assert set(np.argsort(-s, kind="stable")[:16].tolist()) == set(w.planted.tolist())
+
+
+# ---------------------------------------------------------------- select ----
+
+def check_select(scores, prompts):
+    got = tg.tg_select_topk(scores.to(DEV), prompts).cpu().numpy()
+    ref = oracle.select_topk(scores.cpu().numpy(), prompts)
+    assert got.dtype == np.int32
+    assert np.array_equal(got.astype(np.int64), ref), "kept index set or order differs"
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "few", "signed0", "wide"])
+def test_select_single_prompt(kind):
+    note(f"select 16384 rows kind={kind}")
+    s = make_scores(16384, seed=3, kind=kind)
+    for k in (0, 1, 2, 1000, 2000, 15999, 16000):
+        check_select(s, [Prompt(0, 16384, 0, 16000, k)])
+
+
+def test_select_nan_inf_and_spans():
+    note("select NaN/inf, inner document span")
+    s = make_scores(5000, seed=5)
+    s[::7] = float("nan")
+    s[3::11] = float("inf")
+    s[5::13] = -float("inf")
+    s[10:20] = -0.0
+    s[20:30] = 0.0
+    for k in (0, 17, 1000, 2500, 4000):
+        check_select(s, [Prompt(0, 5000, 300, 4300, k)])
+
+
+def test_select_multi_prompt_edges():
+    note("select multi-prompt: empty prompt, all-question prompt, tiny prompts")
+    s = make_scores(7000, seed=8, kind="ties")
+    prompts = [Prompt(0, 1, 0, 1, 1), Prompt(1, 0, 0, 0, 0), Prompt(1, 300, 0, 0, 0),
+               Prompt(301, 2500, 100, 2400, 123), Prompt(2801, 3, 1, 2, 0), Prompt(2804, 4196, 0, 4000, 4000),
+               Prompt(7000, 0, 0, 0, 0)]
+    check_select(s, prompts)
+
+
+def test_select_exhaustive_tiny_on_gpu():
+    note("select exhaustive {0,1,2}^5 with every budget (batched as prompts)")
+    import itertools
+    vals = [np.array(v, dtype=np.float32) for v in itertools.product((0.0, 1.0, 2.0), repeat=5)]
+    for k in range(6):
+        batch = vals[:60]
+        for i0 in range(0, len(vals), 60):
+            batch = vals[i0:i0 + 60]
+            s = torch.from_numpy(np.concatenate(batch))
+            prompts = [Prompt(5 * i, 5, 0, 5, k) for i in range(len(batch))]
+            check_select(s, prompts)
+
+
+def test_select_long128k_and_ragged():
+    note("select 131072 rows (keep 8128) and 8 ragged prompts")
+    s = make_scores(131072, seed=12)
+    check_select(s, [Prompt(0, 131072, 0, 130048, 8128)])
+    prompts = ragged_prompts()
+    n = prompts[-1].start + prompts[-1].length
+    check_select(make_scores(n, seed=13, kind="ties"), prompts)
+
+
+# --------------------------------------------------------------- compact ----
+
+def test_compact_bit_exact_and_bias():
+    note("compact: 5 tensors, positions, bias")
+    prompts = [Prompt(0, 3000, 50, 2900, 400), Prompt(3000, 1000, 0, 744, 100), Prompt(4000, 64, 0, 0, 0)]
+    n = 4064
+    s = make_scores(n, seed=21) * 4
+    kept = torch.from_numpy(oracle.select_topk(s.numpy(), prompts).astype(np.int32))
+    g = torch.Generator(device=DEV).manual_seed(1)
+    ts = [torch.randn(n, 2048, generator=g, device=DEV).to(torch.bfloat16),
+          torch.randn(n, 16, 128, generator=g, device=DEV).to(torch.bfloat16),
+          torch.randn(n, 8, 128, generator=g, device=DEV).to(torch.bfloat16),
+          torch.randn(n, 4, generator=g, device=DEV),
+          torch.randint(-2**31, 2**31 - 1, (n, 12), generator=g, device=DEV, dtype=torch.int32)]
+    pos = torch.randint(0, 10**6, (n,), generator=g, device=DEV, dtype=torch.int32)
+    kd = kept.to(DEV)
+    for use_pos in (False, True):
+        outs, pk, bias = tg.tg_compact(kd, prompts, ts, pos=pos if use_pos else None, scores=s.to(DEV))
+        (r_ts), r_pos, r_bias = oracle.compact(kept.numpy().astype(np.int64), prompts,
+                                               [t.cpu() for t in ts], s.numpy(),
+                                               pos.cpu().numpy() if use_pos else None)
+        for o, r in zip(outs, r_ts):
+            assert torch.equal(o.cpu(), r)
+        assert np.array_equal(pk.cpu().numpy().astype(np.int64), r_pos)
+        b = bias.cpu().double().numpy()
+        assert np.all(np.abs(b - r_bias) <= 1e-6 * np.maximum(1.0, np.abs(r_bias)))
+        assert np.all(b[np.asarray(r_bias) == 0.0] == 0.0)
+
+
+def test_compact_full_budget_identity():
+    note("compact at 100% budget is the identity")
+    n = 1000
+    prompts = [Prompt(0, n, 0, 900, 900)]
+    kept = tg.tg_select_topk(make_scores(n, seed=2).to(DEV), prompts)
+    x = torch.randn(n, 256, device=DEV)
+    (xk,), pk, _ = tg.tg_compact(kept, prompts, [x])
+    assert torch.equal(xk, x) and torch.equal(pk.cpu(), torch.arange(n, dtype=torch.int32))
+
+
+# ------------------------------------------------------------- attention ----
+
+def run_attention(a, hq, hkv, tau=1.2, want_lse=True):
+    segs = a["seg_lens"]
+    prompts, st = [], 0
+    for ln in segs:
+        prompts.append(Prompt(st, ln, 0, 0, 0))
+        st += ln
+    return tg.tg_gated_attention(a["q"].to(DEV), a["k"].to(DEV), a["v"].to(DEV), a["bias"].to(DEV),
+                                 a["pos"].to(DEV), prompts, a["gain"].to(DEV), tau, want_lse=want_lse)
+
+
+def ref_attention(a, hq, hkv, tau=1.2, rows=None):
+    return oracle.gated_attention(a["q"], a["k"], a["v"], a["bias"], a["pos"].numpy(), a["seg_lens"],
+                                  hq, hkv, a["gain"], tau, rows=rows)
+
+
+@pytest.mark.parametrize("segs,hq,hkv,d", [([176], 4, 2, 64), ([1, 40, 100, 33], 4, 2, 64),
+                                           ([130], 3, 1, 128), ([97], 8, 2, 64)])
+def test_attention_fp32(segs, hq, hkv, d):
+    note(f"attention fp32 segs={segs} hq={hq} hkv={hkv} d={d}")
+    a = make_attention_inputs(segs, hq, hkv, d, seed=sum(segs), dtype=torch.float32, n_query_tail=7)
+    o, lse = run_attention(a, hq, hkv)
+    ro, rl = ref_attention(a, hq, hkv)
+    assert np.abs(f64(o) - ro).max() <= 1e-4
+    assert np.abs(f64(lse) - rl).max() <= 1e-4
+
+
+BF16_CASES = [
+    ([2384], 16, 8, 128, False),          # the 16k layer's kept set
+    ([1, 31, 64, 65, 200], 16, 8, 128, False),
+    ([300, 129], 16, 8, 128, True),       # repeated positions
+    ([257], 8, 8, 128, False),            # no GQA (G = 1)
+    ([190], 16, 4, 128, False),           # G = 4
+    ([150, 77], 12, 4, 64, False),        # G = 3, head_dim 64
+    ([500], 4, 2, 64, True),
+]
+
+
+@pytest.mark.parametrize("segs,hq,hkv,d,ties", BF16_CASES)
+def test_attention_bf16(segs, hq, hkv, d, ties):
+    note(f"attention bf16 segs={segs} hq={hq} hkv={hkv} d={d} ties={ties}")
+    a = make_attention_inputs(segs, hq, hkv, d, seed=len(segs) * 7 + hq, dtype=torch.bfloat16,
+                              n_query_tail=16, pos_ties=ties)
+    o, lse = run_attention(a, hq, hkv)
+    ro, rl = ref_attention(a, hq, hkv)
+    worst = assert_rowmax_close(f64(o), ro)
+    note(f"  worst rel-to-row-max error {worst:.2e}")
+    assert np.abs(f64(lse) - rl).max() <= 2e-2 * max(1.0, np.abs(rl).max())
+
+
+def test_attention_bf16_sharp_logits():
+    note("attention bf16 with large logits (online softmax rescaling)")
+    a = make_attention_inputs([700], 16, 8, 128, seed=99, dtype=torch.bfloat16, qk_std=3.0)
+    o, _ = run_attention(a, 16, 8, tau=0.5)
+    ro, _ = ref_attention(a, 16, 8, tau=0.5)
+    assert_rowmax_close(f64(o), ro)
+
+
+def test_attention_ones_and_first_row():
+    note("attention closed forms: V=1 gives 1; a prompt's first row returns its own V")
+    a = make_attention_inputs([333, 64], 16, 8, 128, seed=5, dtype=torch.bfloat16)
+    a1 = dict(a)
+    a1["v"] = torch.ones_like(a["v"])
+    o, _ = run_attention(a1, 16, 8)
+    assert np.abs(f64(o) - 1.0).max() <= 1e-2
+    o, _ = run_attention(a, 16, 8)
+    for off in (0, 333):
+        for h in range(16):
+            assert torch.equal(o[off, h].cpu(), a["v"][off, h // 2])
+
+
+def test_attention_reduces_to_sdpa_full_budget_zero_gain():
+    note("attention at full budget with zero gain equals causal SDPA (fp32 CPU)")
+    m, hq, hkv, d = 600, 16, 8, 128
+    a = make_attention_inputs([m], hq, hkv, d, seed=17, dtype=torch.bfloat16)
+    a["pos"] = torch.arange(m, dtype=torch.int32)
+    a["gain"] = torch.zeros(hq)
+    o, _ = run_attention(a, hq, hkv, tau=1.0)
+    q = a["q"].float().permute(1, 0, 2)[None]
+    k = a["k"].float().permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None].contiguous()
+    v = a["v"].float().permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None].contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=1 / math.sqrt(d))
+    assert_rowmax_close(f64(o), ref[0].permute(1, 0, 2).double().numpy())
+
+
+def test_attention_bf16_long_sampled():
+    note("attention bf16 long kept set (M=9152), 128 sampled query rows")
+    m = 9152
+    a = make_attention_inputs([m], 16, 8, 128, seed=31, dtype=torch.bfloat16, n_query_tail=1024)
+    o, lse = run_attention(a, 16, 8)
+    rows = np.unique(np.concatenate([np.random.default_rng(1).choice(m, 120, replace=False),
+                                     [0, 1, 63, 64, m - 1]]))
+    ro, rl = ref_attention(a, 16, 8, rows=rows)
+    assert_rowmax_close(f64(o)[rows], ro[rows])
+
+
+def test_attention_deterministic_and_fully_written():
+    note("attention determinism and poisoned-output check")
+    a = make_attention_inputs([1000, 23], 16, 8, 128, seed=3, dtype=torch.bfloat16)
+    prompts = [Prompt(0, 1000, 0, 0, 0), Prompt(1000, 23, 0, 0, 0)]
+    args = [a[n].to(DEV) for n in ("q", "k", "v", "bias", "pos")]
+    out1 = torch.full_like(args[0], float("nan"))
+    lse1 = torch.full((16, 1023), float("nan"), device=DEV)
+    tg.tg_gated_attention(*args, prompts, a["gain"].to(DEV), 1.2, out=out1, want_lse=True, lse=lse1)
+    out2, lse2 = tg.tg_gated_attention(*args, prompts, a["gain"].to(DEV), 1.2, want_lse=True)
+    assert not torch.isnan(out1).any() and not torch.isnan(lse1).any()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+# ------------------------------------------------------------ end to end ----
+
+def run_layer(w, layers=None):
+    lay = tg.GatedPrefillLayer(w.x, w.w1, w.w2, w.prompts, w.layers if layers is None else layers,
+                               w.hq, w.hkv, w.head_dim, want_lse=True)
+    lay.run()
+    torch.cuda.synchronize()
+    return lay
+
+
+def test_end_to_end_tiny_fp32():
+    note("end to end: tiny fp32 layer (N=512, keep 112 + 64 query)")
+    w = make_workload("tiny", device=DEV)
+    lay = run_layer(w)
+    wl = w.layers[0]
+    ref = oracle.gated_prefill(w.x.cpu(), w.w1.cpu(), w.w2.cpu(), w.prompts,
+                               [type("L", (), dict(q=wl.q.cpu(), k=wl.k.cpu(), v=wl.v.cpu(), gain=wl.gain.cpu(), tau=wl.tau))],
+                               hq=w.hq, hkv=w.hkv, head_dim=w.head_dim, decision_dtype=np.float32)
+    assert np.abs(f64(lay.scores) - ref["scores"]).max() <= 1e-4
+    # the decision is taken on fp32 scores on both sides
+    ref_kept_gpu_scores = oracle.select_topk(lay.scores.cpu().numpy(), w.prompts)
+    assert np.array_equal(lay.kept.cpu().numpy().astype(np.int64), ref_kept_gpu_scores)
+    assert np.array_equal(lay.kept.cpu().numpy().astype(np.int64), ref["kept"])
+    assert np.array_equal(lay.pos_kept.cpu().numpy(), ref["pos_kept"])
+    assert np.abs(f64(lay.bias_kept) - ref["bias"]).max() <= 1e-4
+    o, lse = ref["attn"][0]
+    assert np.abs(f64(lay.outs[0]) - o).max() <= 1e-4
+    assert torch.equal(lay.hidden_kept.cpu(), w.x.cpu()[torch.as_tensor(ref["kept"])])
+
+
+def test_end_to_end_qwen16k():
+    note("end to end: qwen16k bf16 layer (N=16384, keep 2000 + 384 query)")
+    w = make_workload("qwen16k", device=DEV)
+    lay = run_layer(w)
+    wl = w.layers[0]
+    s_ref = oracle.gate_scores(w.x.cpu(), w.w1.cpu(), w.w2.cpu())
+    s_gpu = f64(lay.scores)
+    assert np.abs(s_gpu - s_ref).max() <= 2e-2 * np.abs(s_ref).max()
+    kept = lay.kept.cpu().numpy().astype(np.int64)
+    ref_kept = oracle.select_topk(s_ref.astype(np.float32), w.prompts)
+    flips = len(set(kept.tolist()) ^ set(ref_kept.tolist()))
+    note(f"  threshold flips vs fp64-gate selection: {flips}")
+    # identical scores give identical selection
+    assert np.array_equal(kept, oracle.select_topk(lay.scores.cpu().numpy(), w.prompts))
+    assert set(w.planted.tolist()) <= set(kept.tolist())
+    assert set(range(16000, 16384)) <= set(kept.tolist())
+    # attention against the oracle on the GPU's kept set (same compaction)
+    (qk, kk, vk), pk, bk = oracle.compact(kept, w.prompts, (wl.q.cpu(), wl.k.cpu(), wl.v.cpu()),
+                                          s_ref, None)
+    assert torch.equal(lay.qkv_kept[0][0].cpu(), qk) and torch.equal(lay.qkv_kept[0][2].cpu(), vk)
+    assert np.array_equal(lay.pos_kept.cpu().numpy(), pk)
+    m = len(kept)
+    o, _ = oracle.gated_attention(qk.view(m, 16, 128), kk.view(m, 8, 128), vk.view(m, 8, 128), bk, pk,
+                                  [m], 16, 8, wl.gain.cpu(), wl.tau)
+    assert_rowmax_close(f64(lay.outs[0]), o)
+
+
+def test_end_to_end_sweep32k_full_budget_is_unpruned():
+    note("sweep32k at 100% budget and zero gain: equals unpruned causal attention")
+    w = make_workload("sweep32k", device=DEV, k_doc=doc_budget(1.0, 32256))
+    wl = w.layers[0]
+    wl.gain = torch.zeros_like(wl.gain)
+    lay = run_layer(w)
+    assert torch.equal(lay.kept.cpu(), torch.arange(32768, dtype=torch.int32))
+    n = 32768
+    rows = np.array([0, 1, 5000, 20000, 32767])
+    o, _ = oracle.gated_attention(wl.q.cpu().view(n, 16, 128), wl.k.cpu().view(n, 8, 128),
+                                  wl.v.cpu().view(n, 8, 128), np.zeros(n), np.arange(n), [n], 16, 8,
+                                  np.zeros(16), wl.tau, rows=rows)
+    assert_rowmax_close(f64(lay.outs[0])[rows], o[rows])
+
+
+def test_end_to_end_ragged_four_layers():
+    note("end to end: ragged 8 prompts, 4 above-gate layers (sampled rows)")
+    prompts = [Prompt(p.start, p.length, p.doc_begin, p.doc_end, p.k_doc) for p in ragged_prompts()]
+    w = make_ragged(device=DEV)
+    lay = run_layer(w)
+    kept = lay.kept.cpu().numpy().astype(np.int64)
+    assert np.array_equal(kept, oracle.select_topk(lay.scores.cpu().numpy(), prompts))
+    s_ref_rows = np.random.default_rng(0).choice(w.n_rows, 512, replace=False)
+    s_ref = oracle.gate_scores(w.x[torch.as_tensor(s_ref_rows, device=DEV)].cpu(), w.w1.cpu(), w.w2.cpu())
+    assert np.abs(f64(lay.scores)[s_ref_rows] - s_ref).max() <= 2e-2 * np.abs(s_ref).max()
+    seg = [p.n_kept for p in prompts]
+    bias = f64(lay.bias_kept)
+    pk = lay.pos_kept.cpu().numpy()
+    m = len(kept)
+    rows = np.random.default_rng(2).choice(m, 64, replace=False)
+    for i, wl in enumerate(w.layers):
+        qk, kk, vk = (t.cpu() for t in lay.qkv_kept[i])
+        o, _ = oracle.gated_attention(qk.view(m, 16, 128), kk.view(m, 8, 128), vk.view(m, 8, 128), bias, pk,
+                                      seg, 16, 8, wl.gain.cpu(), wl.tau, rows=rows)
+        assert_rowmax_close(f64(lay.outs[i])[rows], o[rows])
