@@ -42,6 +42,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -88,22 +92,98 @@ __device__ __forceinline__ Item decode_item(const AttnTable& t, int item, int hk
     return it;
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(
+#define LDS_AS __attribute__((address_space(3)))
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Direct global->LDS loads (global_load_lds_dwordx4 / _dword): lane l's 16
+// (or 4) bytes land at LDS address m0 + 16*l (or 4*l); nothing is written to
+// VGPRs. Issued from inline asm so that the compiler's conservative LDS-DMA
+// tracking (which would make every LDS read wait for all DMA in flight,
+// including the next stage's prefetch) stays out of the ring; the ring
+// orders itself with explicit vmcnt waits. The compiler's own waits can only
+// get stronger from this, since it undercounts the loads in flight.
+// The compiler reserves m0 and warns that the clobber is not honoured; no
+// other code in these kernels reads or writes m0, so nothing depends on it.
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, const LDS_AS void* l) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, const LDS_AS void* l) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
+}
+
+// Workgroup barrier for the LDS ring. __syncthreads() would also wait for
+// every outstanding global->LDS load (including the next stage's prefetch);
+// here each wave waits for exactly the loads it needs (wait_vmcnt) and for
+// its own LDS reads, and the compiler is kept from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// LDS transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// i receives element i%4 of the 4-element rows addressed by lanes i/4,
+// 4+i/4, 8+i/4 and 12+i/4 of its group.
+__device__ __forceinline__ v4i16 lds_read_tr16(const LDS_AS char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)p);
+}
+
+// LDS swizzles of the K and V tiles (row = key within the tile, CH = 16-byte
+// chunks per row; 16 for head_dim 128, 8 for 64). The LDS has 64 banks of 4
+// bytes. K is read with ds_read_b128, 16 lanes (16 consecutive keys, one
+// chunk) per cycle: XOR with the key spreads them over 16 distinct chunk
+// positions. V is read with ds_read_b64_tr_b16, 32 lanes (4 keys x 4
+// chunks x 2 halves of a chunk) per cycle: XOR the chunk's upper bits with
+// the key's low bits so the 16 (key, chunk) pairs again cover all 64 banks.
+template <int CH>
+__device__ __forceinline__ int swz_k(int row) { return CH == 16 ? (row & 15) : ((row >> 1) & 7); }
+template <int CH>
+__device__ __forceinline__ int swz_v(int row) { return CH == 16 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
+
+// Workgroup = HW query heads of one KV head x 2 key splits, 32 query rows.
+// Wave w: head slot w % HW, split w / HW; split p owns key tiles kt = 2i + p.
+// K and V tiles (64 keys x D) stream straight from global memory into LDS
+// (global_load_lds, 16 bytes per lane, no staging registers) through a
+// two-stage ring; 16-byte chunk c of key row r is stored at position
+// c ^ swz(r), which keeps both the K operand reads (ds_read_b128) and the
+// V^T operand reads (ds_read_b64_tr_b16) free of bank conflicts. The
+// two splits' (max, sum, O) are merged through LDS at the end.
+template <int D, int HW>
+__global__ __launch_bounds__(128 * HW) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ bias, const int32_t* __restrict__ pos, AttnTable t, int hq, int hkv,
-    int hw, const float* __restrict__ gain, float qk_scale, uint16_t* __restrict__ out,
+    const float* __restrict__ gain, float qk_scale, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
-    constexpr int KST = D + 8;    // K tile row stride (bf16)
-    constexpr int VST = BN + 8;   // V^T tile row stride (bf16)
-    constexpr int KS = D / 16;    // k-steps of the QK^T contraction
-    constexpr int DB = D / 32;    // 32-wide d blocks of the output
-    constexpr int KU = (BN * D / 8) / 256;        // K 16-byte units per thread
-    constexpr int VU = (BN / 2) * (D / 8) / 256;  // V key-pair units per thread
-    __shared__ __attribute__((aligned(16))) uint16_t ks_[BN * KST];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_[D * VST];
-    __shared__ float bs_[BN];
-    __shared__ int32_t ps_[BN];
+    constexpr int NW = 2 * HW;                    // waves
+    constexpr int ROWB = D * 2;                   // bytes per K/V row
+    constexpr int CH = ROWB / 16;                 // 16-byte chunks per row
+    constexpr int TILEB = BN * ROWB;              // bytes per K or V tile
+    constexpr int RPI = 1024 / ROWB;              // rows per 1 KB load instruction
+    constexpr int IPT = TILEB / 1024;             // load instructions per tile
+    constexpr int TPW = IPT / NW;                 // instructions per tile per wave
+    constexpr int SPW = 4 / NW;                   // small (bias/pos) loads per wave
+    constexpr int LPW = 4 * TPW + SPW;            // load instructions per wave per stage
+    static_assert(IPT % NW == 0 && 4 % NW == 0, "loads must split evenly over waves");
+    constexpr int KS = D / 16;                    // k-steps of q.k
+    constexpr int DB = D / 32;                    // 32-wide d blocks of O
+
+    __shared__ __attribute__((aligned(1024))) char tile0[2][2][TILEB];  // stage 0: [split][K,V]
+    __shared__ __attribute__((aligned(1024))) char tile1[2][2][TILEB];  // stage 1
+    // [split][bias bits, position][key] per stage
+    __shared__ __attribute__((aligned(16))) uint32_t small0[2][2][BN], small1[2][2][BN];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -111,24 +191,34 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const int G = hq / hkv;
-    const int ngroups = G / hw;
-    const int rw = 4 / hw;  // 32-row slabs per workgroup
-    const int bm = 32 * rw;
+    const int ngroups = G / HW;
+    const int hl = wave % HW;
+    const int split = wave / HW;
 
-    const Item it = decode_item(t, blockIdx.x, hkv, ngroups);
-    const int64_t off = t.s[it.seg].kept_off;
-    const int n = t.s[it.seg].n;
-    const int slab = wave / hw;
-    const int h = it.kvh * G + it.hg * hw + (wave % hw);
-    const int i0 = it.qb * bm + slab * 32;  // first query row of this wave (segment-relative)
-    const int q_last_blk = min(n, it.qb * bm + bm) - 1;
-    const int kt_end = key_tile_end(pos, off, n, q_last_blk);
+    // Work item: consecutive items differ in KV head first, so with 8 KV
+    // heads each XCD (items are dealt round-robin to the 8 XCDs) serves one
+    // KV head and keeps its K/V in its own L2; query blocks run longest first.
+    int sg = 0;
+    for (int i = 1; i < t.n_seg; ++i)
+        if (t.s[i].item_base <= (int)blockIdx.x) sg = i;
+    const int local = blockIdx.x - t.s[sg].item_base;
+    const int per_qb = hkv * ngroups;
+    const int qb = t.s[sg].n_qblk - 1 - local / per_qb;
+    const int rest = local % per_qb;
+    const int kvh = rest % hkv;
+    const int hg = rest / hkv;
+    const int64_t off = t.s[sg].kept_off;
+    const int n = t.s[sg].n;
+    const int h = kvh * G + hg * HW + hl;
+    const int i0 = qb * 32;
+    const int q_last = min(n, i0 + 32) - 1;
+    const int n_tiles = key_tile_end(pos, off, n, q_last);
+    const int n_it = (n_tiles + 1) / 2;
 
-    // This lane's query row (clamped for the ragged tail; never stored).
     const int qi = min(i0 + l32, n - 1);
     const int32_t my_pos = pos[off + qi];
-    const int32_t wave_pos_lo = pos[off + min(i0, n - 1)];
-    const int32_t wave_pos_hi = pos[off + min(i0 + 31, n - 1)];
+    const int32_t wave_pos_lo = pos[off + i0];
+    const int32_t wave_pos_hi = pos[off + q_last];
     const float c = qk_scale * LOG2E;
     const float gl2 = gain[h] * LOG2E;
 
@@ -138,64 +228,40 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
 #pragma unroll
         for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(qrow + s * 16);
     }
+    // The ring's vmcnt bookkeeping counts only its own loads: finish every
+    // other vector-memory load first and keep the compiler from moving any
+    // past this point.
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
 
-    // Cooperative tile loader (registers -> LDS).
     const int64_t kv_row_stride = (int64_t)hkv * D;
-    const uint16_t* kbase = k + (off * hkv + it.kvh) * D;
-    const uint16_t* vbase = v + (off * hkv + it.kvh) * D;
-    uint4 kr[KU], vr[VU][2];
-    float br = 0.0f;
-    int32_t pr = 0;
-    auto load_tile = [&](int kt) {
-        const int j0 = kt * BN;
+    const uint16_t* kbase = k + (off * hkv + kvh) * D;
+    const uint16_t* vbase = v + (off * hkv + kvh) * D;
+
+    // Issue every load of iteration `it` into the given stage buffers. The
+    // array each instruction writes is fixed at compile time; the wave index
+    // only picks rows, so every wave issues exactly LPW loads per stage.
+    auto issue = [&](int it, char (*tl)[2][TILEB], uint32_t (*sm)[2][BN]) {
 #pragma unroll
-        for (int i = 0; i < KU; ++i) {
-            const int u = tid + 256 * i;
-            const int key = u / (D / 8), dc = u % (D / 8);
-            const int j = min(j0 + key, n - 1);
-            kr[i] = *(const uint4*)(kbase + (int64_t)j * kv_row_stride + dc * 8);
-        }
+        for (int tile_id = 0; tile_id < 4; ++tile_id) {
+            const int sp_ = tile_id >> 1, kind = tile_id & 1;
+            const uint16_t* base = kind ? vbase : kbase;
 #pragma unroll
-        for (int i = 0; i < VU; ++i) {
-            const int u = tid + 256 * i;
-            const int p = u % (BN / 2), dc = u / (BN / 2);
-            const int ja = min(j0 + 2 * p, n - 1), jb = min(j0 + 2 * p + 1, n - 1);
-            vr[i][0] = *(const uint4*)(vbase + (int64_t)ja * kv_row_stride + dc * 8);
-            vr[i][1] = *(const uint4*)(vbase + (int64_t)jb * kv_row_stride + dc * 8);
-        }
-        if (tid < BN) {
-            const int j = j0 + tid;
-            br = bias[off + min(j, n - 1)];
-            pr = (j < n) ? pos[off + j] : INT_MAX;
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < KU; ++i) {
-            const int u = tid + 256 * i;
-            const int key = u / (D / 8), dc = u % (D / 8);
-            *(uint4*)&ks_[key * KST + dc * 8] = kr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VU; ++i) {
-            const int u = tid + 256 * i;
-            const int p = u % (BN / 2), dc = u / (BN / 2);
-            const int key = 2 * p;
-            const int slot = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-            const uint32_t a[4] = {vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w};
-            const uint32_t b[4] = {vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // d = dc*8 + 2e and dc*8 + 2e + 1: pair (key, key+1) per row
-                const uint32_t lo = (a[e] & 0xffffu) | (b[e] << 16);
-                const uint32_t hi = (a[e] >> 16) | (b[e] & 0xffff0000u);
-                *(uint32_t*)&vt_[(dc * 8 + 2 * e) * VST + slot] = lo;
-                *(uint32_t*)&vt_[(dc * 8 + 2 * e + 1) * VST + slot] = hi;
+            for (int i = 0; i < TPW; ++i) {
+                const int rg = i * NW + wave;  // 1 KB row group of the tile
+                const int row = rg * RPI + lane / CH;
+                const int chunk = (lane % CH) ^ (kind ? swz_v<CH>(row) : swz_k<CH>(row));
+                const int j = min((2 * it + sp_) * BN + row, n - 1);
+                dma16(base + (int64_t)j * kv_row_stride + chunk * 8, (LDS_AS void*)&tl[sp_][kind][rg * 1024]);
             }
         }
-        if (tid < BN) {
-            bs_[tid] = br;
-            ps_[tid] = pr;
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int sid = wave * SPW + i;  // 0..3: split sid/2, bias (even) or position (odd)
+            const int sp_ = sid >> 1;
+            const int j = min((2 * it + sp_) * BN + lane, n - 1);
+            const void* src = (sid & 1) ? (const void*)(pos + off + j) : (const void*)(bias + off + j);
+            dma4(src, (LDS_AS void*)&sm[sp_][sid & 1][0]);
         }
     };
 
@@ -206,109 +272,178 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
         for (int j = 0; j < 16; ++j) acc_o[b][j] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
 
-    load_tile(0);
-    store_tile();
-    __syncthreads();
-
-    for (int kt = 0; kt < kt_end; ++kt) {
-        const bool more = kt + 1 < kt_end;
-        // Prefetch the next tile into registers (unconditional: the last
-        // iteration re-reads its own tile, keeping the registers in place).
-        load_tile(more ? kt + 1 : kt);
-
-        // A wave whose every query precedes the whole tile skips it.
-        if (ps_[0] <= wave_pos_hi) {
-            f32x16 acc_s[2];
+    // One key tile for this wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+    auto compute = [&](int kt, const char* kt_lds, const char* vt_lds, const uint32_t (*smv)[BN]) {
+        const LDS_AS char* kl = (const LDS_AS char*)kt_lds;
+        const LDS_AS char* vl = (const LDS_AS char*)vt_lds;
+        const LDS_AS float* bsv = (const LDS_AS float*)smv[0];
+        const LDS_AS int32_t* psv = (const LDS_AS int32_t*)smv[1];
+        if (kt >= n_tiles || psv[0] > wave_pos_hi) return;  // no visible key in this tile
+        // Element-wise masking only where some key may be invisible to some
+        // query of this wave: the ragged end, or keys past the first query.
+        const bool need_mask = (kt + 1) * BN > n || psv[BN - 1] > wave_pos_lo;
+        f32x16 acc_s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc_s[kb][j] = 0.0f;
+            const int row = kb * 32 + l32;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int chunk = (2 * s + hh) ^ swz_k<CH>(row);
+                const bf16x8 a = *(const LDS_AS bf16x8*)(kl + row * ROWB + chunk * 16);
+                acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc_s[kb], 0, 0, 0);
+            }
+        }
+        // Logits in the exp2 domain. Register j of block kb holds key
+        // kb*32 + 8(j/4) + 4hh + j%4 of this lane's query.
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int key0 = kb * 32 + 8 * g4 + 4 * hh;
+                const f32x4 bb = *(const LDS_AS f32x4*)&bsv[key0];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc_s[kb][4 * g4 + e] = fmaf(acc_s[kb][4 * g4 + e], c, gl2 * bb[e]);
+            }
+        }
+        if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) acc_s[kb][j] = 0.0f;
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int key0 = kb * 32 + 8 * g4 + 4 * hh;
+                    const i32x4 pp = *(const LDS_AS i32x4*)&psv[key0];
 #pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    const bf16x8 a = *(const bf16x8*)&ks_[(kb * 32 + l32) * KST + s * 16 + 8 * hh];
-                    acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc_s[kb], 0, 0, 0);
+                    for (int e = 0; e < 4; ++e) {
+                        const bool vis = (kt * BN + key0 + e < n) & (pp[e] <= my_pos);
+                        acc_s[kb][4 * g4 + e] = vis ? acc_s[kb][4 * g4 + e] : -INFINITY;
+                    }
                 }
             }
-            const bool need_mask = ps_[BN - 1] > wave_pos_lo;
-            float mx = -INFINITY;
+        }
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int key = kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-                    float x = fmaf(acc_s[kb][j], c, gl2 * bs_[key]);
-                    if (need_mask && ps_[key] > my_pos) x = -INFINITY;
-                    acc_s[kb][j] = x;
-                    mx = fmaxf(mx, x);
-                }
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, acc_s[kb][j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // The reference max only moves when some row's tile max exceeds it by
+        // more than 8 (a factor 256): softmax does not depend on the
+        // reference, and p <= 256 stays exact enough in fp32 and bf16. This
+        // skips almost every rescale of O after the first tiles.
+        if (__any(mx > m_run + 8.0f)) {
             const float m_new = fmaxf(m_run, mx);
             const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float corr = exp2f(m_run - m_use);
-            float lsum = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const float p = exp2f(acc_s[kb][j] - m_use);
-                    acc_s[kb][j] = p;
-                    lsum += p;
-                }
-            l_run = l_run * corr + lsum;
-            m_run = m_new;
-            // Rescale O only when some row's running max moved (corr == 1
-            // exactly otherwise, so skipping the multiply changes nothing).
-            if (__any(corr != 1.0f)) {
-#pragma unroll
-                for (int b = 0; b < DB; ++b)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) acc_o[b][j] *= corr;
-            }
-
-            // P^T as B operands: k-step s uses S^T registers 8*(s%2) .. +8 of block s/2.
-            bf16x8 pf[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                u32x4 w;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = pack_bf2(acc_s[s >> 1][8 * (s & 1) + 2 * e], acc_s[s >> 1][8 * (s & 1) + 2 * e + 1]);
-                pf[s] = __builtin_bit_cast(bf16x8, w);
-            }
+            const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
+            l_run *= corr;
 #pragma unroll
             for (int b = 0; b < DB; ++b)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const bf16x8 a = *(const bf16x8*)&vt_[(b * 32 + l32) * VST + s * 16 + 8 * hh];
-                    acc_o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s], acc_o[b], 0, 0, 0);
-                }
+                for (int j = 0; j < 16; ++j) acc_o[b][j] *= corr;
+            m_run = m_new;
         }
-        __syncthreads();
-        if (more) {
-            store_tile();
-            __syncthreads();
+        const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+        float lsum = 0.0f;
+        // P^T as B operands: k-step s uses S^T registers 8*(s%2) .. +8 of block s/2,
+        // i.e. keys 16s + 8(e/4) + 4hh + e%4 for slot e.
+        bf16x8 pf[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = __builtin_amdgcn_exp2f(acc_s[s >> 1][8 * (s & 1) + 2 * e] - m_use);
+                const float p1 = __builtin_amdgcn_exp2f(acc_s[s >> 1][8 * (s & 1) + 2 * e + 1] - m_use);
+                lsum += p0 + p1;
+                const f32x2 pp = {p0, p1};
+                w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, bf16x2));
+            }
+            pf[s] = __builtin_bit_cast(bf16x8, w);
         }
-    }
+        l_run += lsum;
+        // V^T operands by transpose reads: lane L of group g = L/16 addresses key
+        // 16s + 4(g/2) + (L%16)/4 (+8 for the upper four slots) at d = 32b + 16(g%2) + 4(L%4).
+        const int g = lane >> 4, r16 = lane & 15;
+        const int dsub = 16 * (g & 1) + 4 * (r16 & 3);
+        const int keyo = 4 * (g >> 1) + (r16 >> 2);
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+            const int dd = 32 * b + dsub;              // element offset in the row
+            const int ch = dd >> 3, sub = (dd & 7) * 2;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int ka = 16 * s + keyo, kb2 = ka + 8;
+                const v4i16 lo = lds_read_tr16(vl + ka * ROWB + ((ch ^ swz_v<CH>(ka)) * 16) + sub);
+                const v4i16 hi = lds_read_tr16(vl + kb2 * ROWB + ((ch ^ swz_v<CH>(kb2)) * 16) + sub);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc_o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s], acc_o[b], 0, 0, 0);
+            }
+        }
+    };
 
-    // Epilogue: normalise, round, store. Register j of d-block b holds
-    // d = 32b + 8(j/4) + 4hh + j%4 of query row i0 + l32.
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.0f / l_tot;
-    const int row = i0 + l32;
-    if (row < n) {
-        uint16_t* orow = out + ((off + row) * hq + h) * D;
+    // Two-stage ring: stage it%2 holds iteration it. Loads for it+2 are issued
+    // once every wave has finished reading stage it.
+    issue(0, tile0, small0);
+    if (n_it > 1) issue(1, tile1, small1);
+    for (int it = 0; it < n_it; it += 2) {
+        // ---- stage 0 ----
+        if (it + 1 < n_it) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
+        ring_barrier();
+        compute(2 * it + split, tile0[split][0], tile0[split][1], small0[split]);
+        ring_barrier();
+        if (it + 2 < n_it) issue(it + 2, tile0, small0);
+        if (it + 1 >= n_it) break;
+        // ---- stage 1 ----
+        if (it + 2 < n_it) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
+        ring_barrier();
+        compute(2 * (it + 1) + split, tile1[split][0], tile1[split][1], small1[split]);
+        ring_barrier();
+        if (it + 3 < n_it) issue(it + 3, tile1, small1);
+    }
+    wait_vmcnt<0>();
+
+    // Merge the two key splits: split 1 hands (m, l, O) to split 0 through LDS.
+    float* xo = (float*)&tile0[0][0][0];  // [HW][DB*16][64] floats, free after the loop
+    float* xm = (float*)&tile1[0][0][0];  // [HW][64] max, then [HW][64] sum
+    if (split == 1) {
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int d = 32 * b + 8 * g4 + 4 * hh;
-                uint2 w;
-                w.x = pack_bf2(acc_o[b][4 * g4 + 0] * inv, acc_o[b][4 * g4 + 1] * inv);
-                w.y = pack_bf2(acc_o[b][4 * g4 + 2] * inv, acc_o[b][4 * g4 + 3] * inv);
-                *(uint2*)(orow + d) = w;
-            }
-        if (lse && hh == 0) lse[(int64_t)h * t.m_total + off + row] = (m_run + log2f(l_tot)) * LN2;
+            for (int j = 0; j < 16; ++j) xo[(hl * DB * 16 + b * 16 + j) * 64 + lane] = acc_o[b][j];
+        xm[hl * 64 + lane] = m_run;
+        xm[HW * 64 + hl * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (split == 0) {
+        const float m1 = xm[hl * 64 + lane];
+        const float l1 = xm[HW * 64 + hl * 64 + lane];
+        const float m = fmaxf(m_run, m1);
+        const float mu = (m == -INFINITY) ? 0.0f : m;
+        const float a0 = __builtin_amdgcn_exp2f(m_run - mu), a1 = __builtin_amdgcn_exp2f(m1 - mu);
+        float lt = l_run * a0 + l1 * a1;
+        lt += __shfl_xor(lt, 32);
+        const float inv = 1.0f / lt;
+        const int row = i0 + l32;
+        if (row < n) {
+            uint16_t* orow = out + ((off + row) * hq + h) * D;
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    float o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = 4 * g4 + e;
+                        o[e] = (acc_o[b][j] * a0 + xo[(hl * DB * 16 + b * 16 + j) * 64 + lane] * a1) * inv;
+                    }
+                    uint2 w;
+                    w.x = pack_bf2(o[0], o[1]);
+                    w.y = pack_bf2(o[2], o[3]);
+                    *(uint2*)(orow + 32 * b + 8 * g4 + 4 * hh) = w;
+                }
+            if (lse && hh == 0) lse[(int64_t)h * t.m_total + off + row] = (mu + log2f(lt)) * LN2;
+        }
     }
 }
 
@@ -402,16 +537,18 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
     }
 }
 
-int gcd4(int g) { return (g % 4 == 0) ? 4 : ((g % 2 == 0) ? 2 : 1); }
+int heads_per_wg(int g) { return (g % 2 == 0) ? 2 : 1; }
 
 }  // namespace
 
 int attention_heads_per_item(tg_dtype dt, int hq, int hkv) {
-    return dt == TG_F32 ? 1 : gcd4(hq / hkv);
+    return dt == TG_F32 ? 1 : heads_per_wg(hq / hkv);
 }
 
 int attention_block_rows(tg_dtype dt, int hq, int hkv) {
-    return dt == TG_F32 ? 64 : 32 * (4 / gcd4(hq / hkv));
+    (void)hq;
+    (void)hkv;
+    return dt == TG_F32 ? 64 : 32;
 }
 
 hipError_t launch_attention(tg_dtype dt, const void* q, const void* k, const void* v,
@@ -422,15 +559,17 @@ hipError_t launch_attention(tg_dtype dt, const void* q, const void* k, const voi
     const float qk_scale = 1.0f / (sqrtf((float)head_dim) * tau);
     const dim3 grid((unsigned)t.n_items);
     if (dt == TG_BF16) {
-        const int hw = gcd4(hq / hkv);
-        if (head_dim == 128)
-            hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, st, (const uint16_t*)q,
-                               (const uint16_t*)k, (const uint16_t*)v, bias, pos, t, hq, hkv, hw,
-                               gain, qk_scale, (uint16_t*)out, lse);
+        const int hw = heads_per_wg(hq / hkv);
+        const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)k, *vv = (const uint16_t*)v;
+        uint16_t* oo = (uint16_t*)out;
+        if (head_dim == 128 && hw == 2)
+            hipLaunchKernelGGL((attn_bf16_kernel<128, 2>), grid, dim3(256), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
+        else if (head_dim == 128)
+            hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), grid, dim3(128), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
+        else if (hw == 2)
+            hipLaunchKernelGGL((attn_bf16_kernel<64, 2>), grid, dim3(256), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
         else
-            hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, st, (const uint16_t*)q,
-                               (const uint16_t*)k, (const uint16_t*)v, bias, pos, t, hq, hkv, hw,
-                               gain, qk_scale, (uint16_t*)out, lse);
+            hipLaunchKernelGGL((attn_bf16_kernel<64, 1>), grid, dim3(128), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
     } else {
         if (head_dim == 128)
             hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, st, (const float*)q,
