@@ -9,16 +9,24 @@
 // token's score per section "Was ist token-gated Attention?" of the spke.com
 // article, in the form logsigmoid(s) for document rows and 0 for the rest.
 //
-// HBM-bound row copy. Each workgroup owns a few consecutive kept rows and
-// copies every tensor's rows in 16-byte units, four loads in flight per
-// thread before the stores, so consecutive lanes touch consecutive bytes of
-// a row (coalesced) on both sides.
+// HBM-bound row copy. A workgroup owns a few consecutive kept rows and
+// flattens (tensor, row, 16-byte unit) of every gathered tensor into one
+// index space; each thread issues all of its loads (up to CU units) before
+// any store, so a workgroup keeps its whole share of bytes in flight at
+// once, and consecutive lanes touch consecutive bytes of a row (coalesced)
+// on both sides.
 #include "tg_internal.hpp"
+#include "tg_device.hpp"
 
 namespace tg {
 namespace {
 
+#define GLOBAL_AS __attribute__((address_space(1)))
+typedef const GLOBAL_AS u32x4* gsrc_t;
+typedef GLOBAL_AS u32x4* gdst_t;
+
 constexpr int CT = 256;
+constexpr int CU = 12;       // 16-byte units per thread (in flight at once)
 constexpr int MAX_RPB = 16;
 
 __device__ __forceinline__ int find_seq(const SeqTable& t, int64_t row) {
@@ -39,6 +47,8 @@ __global__ __launch_bounds__(CT) void compact_kernel(const int32_t* __restrict__
                                                      const float* __restrict__ scores,
                                                      float* __restrict__ bias_kept) {
     __shared__ int64_t src_row[MAX_RPB];
+    __shared__ int32_t unit_base[TG_MAX_GATHERS + 1];  // prefix of units per row over tensors
+    __shared__ GatherDesc gds[TG_MAX_GATHERS];         // descriptors, indexable per thread
     const int tid = threadIdx.x;
     const int64_t m0 = (int64_t)blockIdx.x * rpb;
     const int nr = (int)((m - m0) < rpb ? (m - m0) : rpb);
@@ -58,29 +68,47 @@ __global__ __launch_bounds__(CT) void compact_kernel(const int32_t* __restrict__
             }
         }
     }
-    __syncthreads();
-    for (int gi = 0; gi < g.n; ++gi) {
-        const GatherDesc gd = g.g[gi];
-        const int units = (int)gd.units;
-        const int total = nr * units;
-        for (int u0 = 0; u0 < total; u0 += 4 * CT) {
-            uint4 val[4];
-            int rr[4], cc[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int u = u0 + q * CT + tid;
-                rr[q] = u / units;
-                cc[q] = u - rr[q] * units;
-                if (u < total && src_row[rr[q]] >= 0)
-                    val[q] = *(const uint4*)(gd.src + src_row[rr[q]] * gd.src_stride + (int64_t)cc[q] * 16);
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int u = u0 + q * CT + tid;
-                if (u < total && src_row[rr[q]] >= 0)
-                    *(uint4*)(gd.dst + (m0 + rr[q]) * gd.dst_stride + (int64_t)cc[q] * 16) = val[q];
-            }
+    if (tid == 0) {
+        int acc = 0;
+        for (int i = 0; i < g.n; ++i) {  // uniform index into the kernel argument
+            gds[i] = g.g[i];
+            unit_base[i] = acc;
+            acc += (int)g.g[i].units;
         }
+        unit_base[g.n] = acc;
+    }
+    __syncthreads();
+    const int per_row = unit_base[g.n];
+    const int total = nr * per_row;
+    for (int u0 = 0; u0 < total; u0 += CU * CT) {
+        u32x4 val[CU];
+        gdst_t dst[CU];
+#pragma unroll
+        for (int q = 0; q < CU; ++q) {
+            const int u = u0 + q * CT + tid;
+            // Loads are unconditional (a lane with nothing to copy re-reads the
+            // first unit of the first tensor) so they all issue together.
+            gsrc_t src = (gsrc_t)gds[0].src;
+            dst[q] = nullptr;
+            if (u < total) {
+                const int rr = u / per_row;
+                int w = u - rr * per_row;
+                int gi = 0;
+#pragma unroll
+                for (int i = 1; i < TG_MAX_GATHERS; ++i) gi += (i < g.n && unit_base[i] <= w) ? 1 : 0;
+                w -= unit_base[gi];
+                const int64_t sr = src_row[rr];
+                if (sr >= 0) {
+                    const GatherDesc& gd = gds[gi];
+                    src = (gsrc_t)(gd.src + sr * gd.src_stride + (int64_t)w * 16);
+                    dst[q] = (gdst_t)(gd.dst + (m0 + rr) * gd.dst_stride + (int64_t)w * 16);
+                }
+            }
+            val[q] = *src;
+        }
+#pragma unroll
+        for (int q = 0; q < CU; ++q)
+            if (dst[q]) *dst[q] = val[q];
     }
 }
 
@@ -89,8 +117,11 @@ __global__ __launch_bounds__(CT) void compact_kernel(const int32_t* __restrict__
 hipError_t launch_compact(const int32_t* kept, int64_t m, const SeqTable& t, const GatherTable& g,
                           const int32_t* pos, int32_t* pos_kept, const float* scores,
                           float* bias_kept, hipStream_t st) {
-    // Aim for >= ~1024 workgroups so all 256 CUs stay busy; at most 16 rows each.
-    int64_t rpb = (m + 1023) / 1024;
+    // Rows per workgroup: as many as fit CU units per thread, so every
+    // thread's loads are issued together; at most 16 rows.
+    int64_t per_row = 0;
+    for (int i = 0; i < g.n; ++i) per_row += g.g[i].units;
+    int64_t rpb = per_row > 0 ? (int64_t)(CU * CT) / per_row : MAX_RPB;
     if (rpb < 1) rpb = 1;
     if (rpb > MAX_RPB) rpb = MAX_RPB;
     const int64_t blocks = (m + rpb - 1) / rpb;

@@ -8,24 +8,31 @@
 // bf16 path: a skinny GEMM H^T = W1 . X^T on v_mfma_f32_32x32x16_bf16 with
 // the SiLU, the w2 dot product and the cross-wave reduction fused into the
 // epilogue, so the [N, H] hidden activations never leave registers. One
-// workgroup (4 waves) owns 64 rows and all H hidden units (each wave H/4 of
-// them). The 64-row X tile is shared by the 4 waves through LDS; each wave
-// streams its own slice of W1 (L2-resident: 1 MiB at H=256, d=2048) straight
-// into MFMA operand registers.
+// workgroup owns 64 rows and all H hidden units, one wave per 32 hidden
+// units (8 waves at H = 256).
 //
+// The kernel streams X from HBM once; it is sized so that enough bytes are
+// in flight per CU to cover HBM latency:
+//  * the 64-row X tile moves global -> LDS with direct loads
+//    (global_load_lds_dwordx4, no staging registers) through an 8-stage
+//    ring of 64-wide k chunks, 7 chunks ahead of the MFMAs;
+//  * each wave's 32 rows of W1 (L2-resident: 1 MiB at H=256, d=2048) move
+//    into registers through a matching 8-deep register ring;
+//  * the chunk loop is unrolled by the ring depth, so every ring index is a
+//    compile-time constant.
 // Both operands are k-contiguous (W1 rows and X rows), so the MFMA lane
 // layouts load 16-byte vectors directly. Inside a 64-wide k chunk the
 // k-step / lane-half order is permuted (lane half hh, step ks covers k
 // hh*32 + ks*8 .. +8): the same permutation on both operands leaves the
 // contraction unchanged and lets every lane read 64 contiguous bytes of its
-// W1 row per chunk.
+// W1 row per chunk. X rows are 128-byte LDS rows whose 16-byte chunk c sits
+// at position c ^ ((row / 2) mod 8): 16 consecutive rows read one chunk
+// without bank conflicts (the LDS has 64 four-byte banks).
 #include "tg_internal.hpp"
+#include "tg_device.hpp"
 
 namespace tg {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
 
@@ -38,19 +45,21 @@ __device__ __forceinline__ float load_f<uint16_t>(const uint16_t* p, int64_t i) 
 
 __device__ __forceinline__ float silu(float h) { return h / (1.0f + __expf(-h)); }
 
-constexpr int GBM = 64;            // rows per workgroup
-constexpr int GBK = 64;            // k per chunk
-constexpr int GLDS = GBK + 8;      // LDS row stride in bf16 (144 bytes: conflict-free b128 reads)
+constexpr int GBM = 64;  // rows per workgroup
+constexpr int GBK = 64;  // k per chunk
+constexpr int GNS = 8;   // ring depth (chunks); 7 chunks in flight ahead of the MFMAs
 
-template <int HW>  // hidden units per wave (32 or 64); H = 4 * HW
-__global__ __launch_bounds__(256) void gate_mfma_kernel(const uint16_t* __restrict__ x, int64_t n,
-                                                        int d, const uint16_t* __restrict__ w1,
-                                                        const uint16_t* __restrict__ b1,
-                                                        const uint16_t* __restrict__ w2, float b2,
-                                                        float* __restrict__ scores) {
-    constexpr int HB = HW / 32;  // 32-row hidden blocks per wave
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][GBM * GLDS];
-    __shared__ float part[4][GBM];
+template <int NWV>  // waves per workgroup = H / 32
+__global__ __launch_bounds__(64 * NWV) void gate_mfma_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                             int d, const uint16_t* __restrict__ w1,
+                                                             const uint16_t* __restrict__ b1,
+                                                             const uint16_t* __restrict__ w2, float b2,
+                                                             float* __restrict__ scores) {
+    constexpr int L = GNS - 1;       // chunks in flight ahead
+    constexpr int XI = 8 / NWV;      // 1 KB X load instructions per wave per chunk
+    constexpr int OPS = 4 + XI;      // vector-memory ops per wave per chunk
+    __shared__ __attribute__((aligned(1024))) char xs[GNS][GBM * GBK * 2];
+    __shared__ float part[NWV][GBM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -59,93 +68,75 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(const uint16_t* __restri
     const int hh = lane >> 5;
     const int64_t row0 = (int64_t)blockIdx.x * GBM;
     const int nchunk = d / GBK;
+    const uint16_t* wrow = w1 + (int64_t)(wave * 32 + l32) * d + hh * 32;
 
-    // X tile loader: 64 rows x 8 sixteen-byte units = 512 units, 2 per thread.
-    int64_t xrow[2];
-    int xcol[2], xlds[2];
+    bf16x8 wr[GNS][4];
+    // Chunk c -> ring slot `slot`: this lane's 4 W1 vectors, then this
+    // wave's share of the X tile. Past the end the last chunk is re-read,
+    // so every wave issues exactly OPS loads per chunk.
+    auto issue = [&](int c, int slot) {
+        const int k0 = (c < nchunk ? c : nchunk - 1) * GBK;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = tid + 256 * i;
-        const int r = u >> 3;
-        const int c = (u & 7) * 8;
-        int64_t gr = row0 + r;
-        if (gr > n - 1) gr = n - 1;  // ragged tail: re-read the last row, never stored
-        xrow[i] = gr * (int64_t)d;
-        xcol[i] = c;
-        xlds[i] = r * GLDS + c;
-    }
-    // W1 rows of this lane (one per hidden block).
-    const uint16_t* wrow[HB];
+        for (int ks = 0; ks < 4; ++ks) wr[slot][ks] = *(const bf16x8*)(wrow + k0 + ks * 8);
+        asm volatile("" ::: "memory");
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-        wrow[hb] = w1 + (int64_t)(wave * HW + hb * 32 + l32) * d + hh * 32;
-
-    uint4 xr[2];
-    bf16x8 wr[HB][4], wn[HB][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) xr[i] = *(const uint4*)(x + xrow[i] + xcol[i]);
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) wr[hb][ks] = *(const bf16x8*)(wrow[hb] + ks * 8);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *(uint4*)&xs[0][xlds[i]] = xr[i];
-    __syncthreads();
-
-    f32x16 acc[HB][2];
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) acc[hb][tb][j] = 0.0f;
-
-    for (int c = 0; c < nchunk; ++c) {
-        const int buf = c & 1;
-        // Prefetch the next chunk (the last iteration re-reads its own chunk,
-        // which keeps the loads unconditional and the registers in place).
-        const int k1 = (c + 1 < nchunk ? c + 1 : c) * GBK;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) xr[i] = *(const uint4*)(x + xrow[i] + k1 + xcol[i]);
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) wn[hb][ks] = *(const bf16x8*)(wrow[hb] + k1 + ks * 8);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 xb[2];
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-                xb[tb] = *(const bf16x8*)&xs[buf][(tb * 32 + l32) * GLDS + hh * 32 + ks * 8];
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb)
-                    acc[hb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[hb][ks], xb[tb],
-                                                                          acc[hb][tb], 0, 0, 0);
+        for (int i = 0; i < XI; ++i) {
+            const int inst = wave * XI + i;  // rows 8*inst .. +8 of the tile
+            const int row = inst * 8 + (lane >> 3);
+            const int ch = (lane & 7) ^ ((row >> 1) & 7);
+            int64_t gr = row0 + row;
+            if (gr > n - 1) gr = n - 1;  // ragged tail: re-read the last row, never stored
+            dma16(x + gr * d + k0 + ch * 8, (const LDS_AS void*)&xs[slot][inst * 1024]);
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) *(uint4*)&xs[buf ^ 1][xlds[i]] = xr[i];
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) wr[hb][ks] = wn[hb][ks];
-        __syncthreads();
-    }
+    };
 
-    // Epilogue. acc[hb][tb] register j holds hidden unit
-    // wave*HW + hb*32 + 8*(j/4) + 4*hh + j%4 of token tb*32 + l32.
+    f32x16 acc[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[tb][j] = 0.0f;
+
+#pragma unroll
+    for (int p = 0; p < L; ++p) issue(p, p);
+
+    for (int cb = 0; cb < nchunk; cb += GNS) {
+#pragma unroll
+        for (int u = 0; u < GNS; ++u) {
+            const int c = cb + u;
+            ring_barrier();                  // every wave is done with slot (u - 1) mod GNS
+            issue(c + L, (u + L) % GNS);     // refill that slot, L chunks ahead
+            wait_vmcnt<OPS * L>();           // this wave's loads of chunk c are complete
+            ring_barrier();                  // ... and every other wave's
+            if (c < nchunk) {
+                const LDS_AS char* xt = (const LDS_AS char*)xs[u];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    bf16x8 xb[2];
+#pragma unroll
+                    for (int tb = 0; tb < 2; ++tb) {
+                        const int row = tb * 32 + l32;
+                        const int ch = (hh * 4 + ks) ^ ((row >> 1) & 7);
+                        xb[tb] = *(const LDS_AS bf16x8*)(xt + row * 128 + ch * 16);
+                    }
+#pragma unroll
+                    for (int tb = 0; tb < 2; ++tb)
+                        acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][ks], xb[tb], acc[tb], 0, 0, 0);
+                }
+            }
+        }
+    }
+    wait_vmcnt<0>();
+
+    // Epilogue. acc[tb] register j holds hidden unit wave*32 + 8*(j/4) +
+    // 4*hh + j%4 of token tb*32 + l32.
     float ps[2] = {0.0f, 0.0f};
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
+    for (int j = 0; j < 16; ++j) {
+        const int hid = wave * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+        const float bias = b1 ? bf2f(b1[hid]) : 0.0f;
+        const float wo = bf2f(w2[hid]);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int hid = wave * HW + hb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-            const float bias = b1 ? bf2f(b1[hid]) : 0.0f;
-            const float wo = bf2f(w2[hid]);
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) ps[tb] += wo * silu(acc[hb][tb][j] + bias);
-        }
+        for (int tb = 0; tb < 2; ++tb) ps[tb] += wo * silu(acc[tb][j] + bias);
     }
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -153,8 +144,12 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(const uint16_t* __restri
         if (hh == 0) part[wave][tb * 32 + l32] = ps[tb];
     }
     __syncthreads();
-    if (tid < GBM && row0 + tid < n)
-        scores[row0 + tid] = ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) + b2;
+    if (tid < GBM && row0 + tid < n) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) sum += part[w][tid];
+        scores[row0 + tid] = sum + b2;
+    }
 }
 
 // Plain path (fp32, or bf16 shapes the MFMA kernel does not take): one wave
@@ -186,12 +181,12 @@ __global__ __launch_bounds__(256) void gate_simple_kernel(const T* __restrict__ 
 
 hipError_t launch_gate_mfma_bf16(const void* x, int64_t n, int d, const void* w1, const void* b1,
                                  int h, const void* w2, float b2, float* scores, hipStream_t st) {
-    const dim3 grid((unsigned)((n + GBM - 1) / GBM)), block(256);
+    const dim3 grid((unsigned)((n + GBM - 1) / GBM));
     if (h == 256)
-        hipLaunchKernelGGL(gate_mfma_kernel<64>, grid, block, 0, st, (const uint16_t*)x, n, d,
+        hipLaunchKernelGGL(gate_mfma_kernel<8>, grid, dim3(512), 0, st, (const uint16_t*)x, n, d,
                            (const uint16_t*)w1, (const uint16_t*)b1, (const uint16_t*)w2, b2, scores);
     else
-        hipLaunchKernelGGL(gate_mfma_kernel<32>, grid, block, 0, st, (const uint16_t*)x, n, d,
+        hipLaunchKernelGGL(gate_mfma_kernel<4>, grid, dim3(256), 0, st, (const uint16_t*)x, n, d,
                            (const uint16_t*)w1, (const uint16_t*)b1, (const uint16_t*)w2, b2, scores);
     return hipGetLastError();
 }

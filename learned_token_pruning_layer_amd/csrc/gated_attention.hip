@@ -33,34 +33,17 @@
 //
 // fp32 path: one thread per query row, K/V tiles in LDS, plain fp32 FMA.
 #include "tg_internal.hpp"
+#include "tg_device.hpp"
 
 #include <limits.h>
 
 namespace tg {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr int BN = 64;  // keys per tile
-
-__device__ __forceinline__ uint16_t f2bf(float f) {
-    // round to nearest even (inputs are finite)
-    uint32_t u = __float_as_uint(f);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
-}
 
 // Index of the key tile one past the last tile a query block can see:
 // tiles up to the block's last row, extended while the next tile starts at
@@ -90,48 +73,6 @@ __device__ __forceinline__ Item decode_item(const AttnTable& t, int item, int hk
     it.kvh = rest / ngroups;
     it.hg = rest % ngroups;
     return it;
-}
-
-#define LDS_AS __attribute__((address_space(3)))
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
-// Direct global->LDS loads (global_load_lds_dwordx4 / _dword): lane l's 16
-// (or 4) bytes land at LDS address m0 + 16*l (or 4*l); nothing is written to
-// VGPRs. Issued from inline asm so that the compiler's conservative LDS-DMA
-// tracking (which would make every LDS read wait for all DMA in flight,
-// including the next stage's prefetch) stays out of the ring; the ring
-// orders itself with explicit vmcnt waits. The compiler's own waits can only
-// get stronger from this, since it undercounts the loads in flight.
-// The compiler reserves m0 and warns that the clobber is not honoured; no
-// other code in these kernels reads or writes m0, so nothing depends on it.
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* g, const LDS_AS void* l) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* g, const LDS_AS void* l) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
-}
-
-// Workgroup barrier for the LDS ring. __syncthreads() would also wait for
-// every outstanding global->LDS load (including the next stage's prefetch);
-// here each wave waits for exactly the loads it needs (wait_vmcnt) and for
-// its own LDS reads, and the compiler is kept from moving memory accesses
-// across the barrier.
-__device__ __forceinline__ void ring_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
 }
 
 // LDS transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane
@@ -356,8 +297,7 @@ __global__ __launch_bounds__(128 * HW) void attn_bf16_kernel(
                 const float p0 = __builtin_amdgcn_exp2f(acc_s[s >> 1][8 * (s & 1) + 2 * e] - m_use);
                 const float p1 = __builtin_amdgcn_exp2f(acc_s[s >> 1][8 * (s & 1) + 2 * e + 1] - m_use);
                 lsum += p0 + p1;
-                const f32x2 pp = {p0, p1};
-                w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, bf16x2));
+                w[e] = pack_bf16x2(p0, p1);
             }
             pf[s] = __builtin_bit_cast(bf16x8, w);
         }
@@ -438,8 +378,8 @@ __global__ __launch_bounds__(128 * HW) void attn_bf16_kernel(
                         o[e] = (acc_o[b][j] * a0 + xo[(hl * DB * 16 + b * 16 + j) * 64 + lane] * a1) * inv;
                     }
                     uint2 w;
-                    w.x = pack_bf2(o[0], o[1]);
-                    w.y = pack_bf2(o[2], o[3]);
+                    w.x = pack_bf16x2(o[0], o[1]);
+                    w.y = pack_bf16x2(o[2], o[3]);
                     *(uint2*)(orow + 32 * b + 8 * g4 + 4 * hh) = w;
                 }
             if (lse && hh == 0) lse[(int64_t)h * t.m_total + off + row] = (mu + log2f(lt)) * LN2;

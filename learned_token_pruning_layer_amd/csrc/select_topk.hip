@@ -9,25 +9,29 @@
 //
 // One 1024-thread workgroup per prompt:
 //  1. Scores map to order-preserving u32 keys (larger key = better rank).
-//  2. A 4-pass MSB radix select (8-bit digits, LDS histograms with integer
-//     atomics, a block scan over the 256 bins from the top) finds the k-th
-//     largest key T and rem = how many keys equal to T are kept.
-//  3. Emission walks the prompt in row order, 1024 rows per step. Each row
-//     is "above" (outside the document, or key > T) or "tied" (document key
-//     == T); wavefront ballots plus mbcnt give the rank of each row within
-//     its wave, a 16-entry LDS table of wave totals gives the block prefix.
-//     Kept rows are the above rows and the first rem tied rows; a kept row's
-//     output slot is (#above before it) + min(#tied before it, rem), so rows
-//     land in ascending order without a sort.
+//     Prompts whose document fits (up to 36864 rows) keep their keys in LDS
+//     for the whole kernel, so HBM is read once.
+//  2. A 3-pass MSB radix select (11, 11 and 10-bit digits; LDS histograms
+//     with integer atomics; a block scan over the bins from the top) finds
+//     the k-th largest key T and rem = how many keys equal to T are kept.
+//  3. Emission: each thread owns 16 consecutive rows and counts its rows
+//     that are "above" (outside the document, or key > T) and "tied"
+//     (document key == T); one block-wide exclusive scan (wavefront shuffle
+//     scans, then a scan of the 16 wave totals) gives every thread its
+//     rank. Kept rows are the above rows and the first rem tied rows; a kept
+//     row's output slot is (#above before it) + min(#tied before it, rem),
+//     so rows land in ascending order without a sort.
 // Integer work only: the result is bit-exact and deterministic.
 #include "tg_internal.hpp"
 
 namespace tg {
 namespace {
 
-constexpr int ST = 1024;   // threads per workgroup (16 waves)
+constexpr int ST = 1024;    // threads per workgroup (16 waves)
 constexpr int NW = ST / 64;
-constexpr int UNR = 8;     // rows loaded per thread before use (memory-level parallelism)
+constexpr int ITEMS = 16;   // consecutive rows per thread in the emission
+constexpr int CAP = 36864;  // document keys kept in LDS (144 KB)
+constexpr int NB = 2048;    // histogram bins (11-bit digits)
 
 __device__ __forceinline__ uint32_t score_key(float f) {
     uint32_t b = __float_as_uint(f);
@@ -36,13 +40,20 @@ __device__ __forceinline__ uint32_t score_key(float f) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+// Inclusive scan of v over the wave (shuffle-up ladder).
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(v, off);
+        if (lane >= off) v += o;
+    }
+    return v;
 }
 
 __global__ __launch_bounds__(ST) void select_kernel(const float* __restrict__ scores, SeqTable t,
                                                     int32_t* __restrict__ kept) {
-    __shared__ uint32_t hist[256];
+    __shared__ uint32_t keys[CAP];
+    __shared__ uint32_t hist[NB];
     __shared__ uint32_t wtot[NW][2];
     __shared__ uint32_t pick[2];
 
@@ -53,114 +64,128 @@ __global__ __launch_bounds__(ST) void select_kernel(const float* __restrict__ sc
     const int64_t dbeg = sd.start + sd.doc_begin;
     const int32_t n_doc = sd.doc_end - sd.doc_begin;
     const int32_t k = sd.k_doc;
+    const bool resident = n_doc <= CAP;
 
     // mode 0: keep no document row; 1: keep all; 2: threshold T with rem ties.
     const int mode = (k == 0) ? 0 : (k == n_doc ? 1 : 2);
     uint32_t thr = 0, rem = 0;
     if (mode == 2) {
-        uint32_t prefix = 0, mask = 0;
-        rem = (uint32_t)k;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            if (tid < 256) hist[tid] = 0;
-            __syncthreads();
-            for (int32_t i0 = 0; i0 < n_doc; i0 += ST * UNR) {
-                float v[UNR];
+        if (resident) {
+            for (int32_t i0 = 0; i0 < n_doc; i0 += ST * 8) {
+                float v[8];
 #pragma unroll
-                for (int u = 0; u < UNR; ++u) {
+                for (int u = 0; u < 8; ++u) {
                     const int32_t i = i0 + u * ST + tid;
                     v[u] = (i < n_doc) ? scores[dbeg + i] : 0.0f;
                 }
 #pragma unroll
-                for (int u = 0; u < UNR; ++u) {
+                for (int u = 0; u < 8; ++u) {
                     const int32_t i = i0 + u * ST + tid;
-                    const uint32_t key = score_key(v[u]);
-                    if (i < n_doc && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+                    if (i < n_doc) keys[i] = score_key(v[u]);
                 }
             }
-            __syncthreads();
-            // Bins from the top: thread b < 256 owns bin 255 - b. Inclusive scan
-            // within each wave, then add the totals of the waves before.
-            uint32_t c = 0, inc = 0;
-            if (tid < 256) {
-                c = hist[255 - tid];
-                inc = c;
+        }
+        uint32_t prefix = 0, mask = 0;
+        rem = (uint32_t)k;
 #pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t o = __shfl_up(inc, off);
-                    if (lane >= off) inc += o;
+        for (int pass = 0; pass < 3; ++pass) {
+            const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+            const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+            const int nbins = (int)dmask + 1;
+            hist[tid] = 0;
+            hist[tid + ST] = 0;
+            __syncthreads();
+            for (int32_t i0 = 0; i0 < n_doc; i0 += ST * 4) {
+                uint32_t kv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int32_t i = i0 + u * ST + tid;
+                    kv[u] = (i < n_doc) ? (resident ? keys[i] : score_key(scores[dbeg + i])) : 0u;
                 }
-                if (lane == 63) wtot[wave][0] = inc;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int32_t i = i0 + u * ST + tid;
+                    if (i < n_doc && (kv[u] & mask) == prefix) atomicAdd(&hist[(kv[u] >> shift) & dmask], 1u);
+                }
             }
             __syncthreads();
-            if (tid < 256) {
-                for (int w = 0; w < wave; ++w) inc += wtot[w][0];
-                const uint32_t exc = inc - c;
-                if (exc < rem && rem <= inc) {
-                    pick[0] = 255u - (uint32_t)tid;
-                    pick[1] = rem - exc;
-                }
+            // Bins from the top, two per thread: bins nbins-1-2t and nbins-2-2t.
+            const int b0 = nbins - 1 - 2 * tid, b1 = b0 - 1;
+            const uint32_t c0 = b0 >= 0 ? hist[b0] : 0u, c1 = b1 >= 0 ? hist[b1] : 0u;
+            const uint32_t inc = wave_scan(c0 + c1, lane);
+            if (lane == 63) wtot[wave][0] = inc;
+            __syncthreads();
+            uint32_t before = inc - (c0 + c1);
+            for (int w = 0; w < wave; ++w) before += wtot[w][0];
+            if (before < rem && rem <= before + c0) {
+                pick[0] = (uint32_t)b0;
+                pick[1] = rem - before;
+            } else if (before + c0 < rem && rem <= before + c0 + c1) {
+                pick[0] = (uint32_t)b1;
+                pick[1] = rem - before - c0;
             }
             __syncthreads();
             prefix |= pick[0] << shift;
-            mask |= 255u << shift;
+            mask |= dmask << shift;
             rem = pick[1];
             __syncthreads();
         }
         thr = prefix;
     }
 
-    // Emission in row order.
+    // Emission in row order, ST*ITEMS rows per step.
     uint32_t carry_above = 0, carry_tied = 0;
     const int32_t len = sd.len;
-    for (int32_t r0 = 0; r0 < len; r0 += ST * UNR) {
-        float v[UNR];
+    for (int32_t r0 = 0; r0 < len; r0 += ST * ITEMS) {
+        const int32_t base = r0 + tid * ITEMS;
+        uint32_t cls[ITEMS];  // 0: dropped, 1: above, 2: tied
+        uint32_t na = 0, nt = 0;
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int32_t r = r0 + u * ST + tid;
-            const bool in_doc = r < len && r >= sd.doc_begin && r < sd.doc_end;
-            v[u] = (mode == 2 && in_doc) ? scores[sd.start + r] : 0.0f;
+        for (int u = 0; u < ITEMS; ++u) {
+            const int32_t r = base + u;
+            uint32_t c = 0;
+            if (r < len) {
+                const bool in_doc = r >= sd.doc_begin && r < sd.doc_end;
+                if (!in_doc || mode == 1) {
+                    c = 1;
+                } else if (mode == 2) {
+                    const int32_t i = r - sd.doc_begin;
+                    const uint32_t key = resident ? keys[i] : score_key(scores[dbeg + i]);
+                    c = key > thr ? 1u : (key == thr ? 2u : 0u);
+                }
+            }
+            cls[u] = c;
+            na += c == 1;
+            nt += c == 2;
+        }
+        const uint32_t ia = wave_scan(na, lane), it = wave_scan(nt, lane);
+        if (lane == 63) {
+            wtot[wave][0] = ia;
+            wtot[wave][1] = it;
+        }
+        __syncthreads();
+        uint32_t pa = carry_above + ia - na, pt = carry_tied + it - nt, ta = 0, tt = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const uint32_t a = wtot[w][0], b = wtot[w][1];
+            if (w < wave) { pa += a; pt += b; }
+            ta += a;
+            tt += b;
         }
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int32_t r = r0 + u * ST + tid;
-            const bool valid = r < len;
-            const bool in_doc = valid && r >= sd.doc_begin && r < sd.doc_end;
-            bool above, tied = false;
-            if (mode == 0) {
-                above = valid && !in_doc;
-            } else if (mode == 1) {
-                above = valid;
-            } else {
-                const uint32_t key = score_key(v[u]);
-                above = valid && (!in_doc || key > thr);
-                tied = in_doc && key == thr;
-            }
-            const uint64_t ba = __ballot(above);
-            const uint64_t bt = __ballot(tied);
-            if (lane == 0) {
-                wtot[wave][0] = (uint32_t)__popcll(ba);
-                wtot[wave][1] = (uint32_t)__popcll(bt);
-            }
-            __syncthreads();
-            uint32_t pa = 0, pt = 0, ta = 0, tt = 0;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const uint32_t a = wtot[w][0], b = wtot[w][1];
-                if (w < wave) { pa += a; pt += b; }
-                ta += a;
-                tt += b;
-            }
-            const uint32_t above_before = carry_above + pa + lanes_below(ba);
-            const uint32_t tied_before = carry_tied + pt + lanes_below(bt);
-            if (above || (tied && tied_before < rem)) {
-                const uint32_t slot = above_before + (tied_before < rem ? tied_before : rem);
+        for (int u = 0; u < ITEMS; ++u) {
+            const uint32_t c = cls[u];
+            if (c == 1 || (c == 2 && pt < rem)) {
+                const uint32_t slot = pa + (pt < rem ? pt : rem);
                 if (slot < (uint32_t)sd.n_kept)  // always true when the counts are right
-                    kept[sd.kept_off + slot] = (int32_t)(sd.start + r);
+                    kept[sd.kept_off + slot] = (int32_t)(sd.start + base + u);
             }
-            carry_above += ta;
-            carry_tied += tt;
-            __syncthreads();
+            pa += c == 1;
+            pt += c == 2;
         }
+        carry_above += ta;
+        carry_tied += tt;
+        __syncthreads();
     }
 }
 

@@ -54,7 +54,8 @@ def test_gate_fp32_tiny():
 
 
 @pytest.mark.parametrize("n,d,h,with_b1", [(1000, 2048, 256, False), (65, 512, 128, True),
-                                           (1, 2048, 256, True), (200, 192, 64, False), (130, 100, 24, True)])
+                                           (1, 2048, 256, True), (77, 320, 256, True), (300, 1088, 128, False),
+                                           (200, 192, 64, False), (130, 100, 24, True)])
 def test_gate_bf16(n, d, h, with_b1):
     note(f"gate bf16 n={n} d={d} h={h} b1={with_b1}")
     g = torch.Generator(device=DEV).manual_seed(n + d + h)
