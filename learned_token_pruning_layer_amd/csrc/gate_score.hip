@@ -11,23 +11,23 @@
 // workgroup owns 64 rows and all H hidden units, one wave per 32 hidden
 // units (8 waves at H = 256).
 //
-// The kernel streams X from HBM once; it is sized so that enough bytes are
-// in flight per CU to cover HBM latency:
-//  * the 64-row X tile moves global -> LDS with direct loads
-//    (global_load_lds_dwordx4, no staging registers) through an 8-stage
-//    ring of 64-wide k chunks, 7 chunks ahead of the MFMAs;
-//  * each wave's 32 rows of W1 (L2-resident: 1 MiB at H=256, d=2048) move
-//    into registers through a matching 8-deep register ring;
-//  * the chunk loop is unrolled by the ring depth, so every ring index is a
-//    compile-time constant.
+// The kernel streams X from HBM once and W1 (L2-resident: 1 MiB at H=256,
+// d=2048) once per 64 rows; it keeps enough of both in flight per CU:
+//  * both move global -> LDS with direct loads (global_load_lds_dwordx4,
+//    no staging registers): X through a 6-stage ring of 64-wide k chunks
+//    (5 chunks ahead of the MFMAs), W1 through a 3-stage ring (2 ahead; it
+//    comes from L2). Every W1 load instruction covers 8 whole 128-byte row
+//    segments, so each fetched cache line is used in full;
+//  * the chunk loop is unrolled by 6, so every ring slot is a compile-time
+//    constant, and all loads are counted explicitly (wait_vmcnt).
 // Both operands are k-contiguous (W1 rows and X rows), so the MFMA lane
 // layouts load 16-byte vectors directly. Inside a 64-wide k chunk the
 // k-step / lane-half order is permuted (lane half hh, step ks covers k
 // hh*32 + ks*8 .. +8): the same permutation on both operands leaves the
 // contraction unchanged and lets every lane read 64 contiguous bytes of its
-// W1 row per chunk. X rows are 128-byte LDS rows whose 16-byte chunk c sits
-// at position c ^ ((row / 2) mod 8): 16 consecutive rows read one chunk
-// without bank conflicts (the LDS has 64 four-byte banks).
+// W1 row per chunk. X and W1 rows are 128-byte LDS rows whose 16-byte chunk
+// c sits at position c ^ ((row / 2) mod 8): 16 consecutive rows read one
+// chunk without bank conflicts (the LDS has 64 four-byte banks).
 #include "tg_internal.hpp"
 #include "tg_device.hpp"
 
@@ -47,7 +47,8 @@ __device__ __forceinline__ float silu(float h) { return h / (1.0f + __expf(-h));
 
 constexpr int GBM = 64;  // rows per workgroup
 constexpr int GBK = 64;  // k per chunk
-constexpr int GNS = 8;   // ring depth (chunks); 7 chunks in flight ahead of the MFMAs
+constexpr int GNX = 6;   // X ring depth (chunks)
+constexpr int GNW = 3;   // W1 ring depth (chunks)
 
 template <int NWV>  // waves per workgroup = H / 32
 __global__ __launch_bounds__(64 * NWV) void gate_mfma_kernel(const uint16_t* __restrict__ x, int64_t n,
@@ -55,10 +56,12 @@ __global__ __launch_bounds__(64 * NWV) void gate_mfma_kernel(const uint16_t* __r
                                                              const uint16_t* __restrict__ b1,
                                                              const uint16_t* __restrict__ w2, float b2,
                                                              float* __restrict__ scores) {
-    constexpr int L = GNS - 1;       // chunks in flight ahead
-    constexpr int XI = 8 / NWV;      // 1 KB X load instructions per wave per chunk
-    constexpr int OPS = 4 + XI;      // vector-memory ops per wave per chunk
-    __shared__ __attribute__((aligned(1024))) char xs[GNS][GBM * GBK * 2];
+    constexpr int XI = 8 / NWV;       // 1 KB X load instructions per wave per chunk
+    constexpr int WI = 4;             // 1 KB W1 load instructions per wave per chunk (32 rows)
+    constexpr int OPS = XI + WI;      // loads per wave per chunk
+    constexpr int WTILE = NWV * 32 * GBK * 2;
+    __shared__ __attribute__((aligned(1024))) char xs[GNX][GBM * GBK * 2];
+    __shared__ __attribute__((aligned(1024))) char ws[GNW][WTILE];
     __shared__ float part[NWV][GBM];
 
     const int tid = threadIdx.x;
@@ -68,25 +71,33 @@ __global__ __launch_bounds__(64 * NWV) void gate_mfma_kernel(const uint16_t* __r
     const int hh = lane >> 5;
     const int64_t row0 = (int64_t)blockIdx.x * GBM;
     const int nchunk = d / GBK;
-    const uint16_t* wrow = w1 + (int64_t)(wave * 32 + l32) * d + hh * 32;
 
-    bf16x8 wr[GNS][4];
-    // Chunk c -> ring slot `slot`: this lane's 4 W1 vectors, then this
-    // wave's share of the X tile. Past the end the last chunk is re-read,
-    // so every wave issues exactly OPS loads per chunk.
-    auto issue = [&](int c, int slot) {
-        const int k0 = (c < nchunk ? c : nchunk - 1) * GBK;
+    // Iteration it loads X for chunk it + GNX - 1 and W1 for chunk it + GNW - 1
+    // (past the end the last chunk is re-read, so every wave issues exactly
+    // OPS loads per iteration; iterations below 0 only prime the X ring).
+    auto issue = [&](int it, int xslot, int wslot) {
+        {
+            const int c = it + GNX - 1;
+            const int k0 = (c < nchunk ? c : nchunk - 1) * GBK;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) wr[slot][ks] = *(const bf16x8*)(wrow + k0 + ks * 8);
-        asm volatile("" ::: "memory");
+            for (int i = 0; i < XI; ++i) {
+                const int inst = wave * XI + i;  // rows 8*inst .. +8 of the X tile
+                const int row = inst * 8 + (lane >> 3);
+                const int ch = (lane & 7) ^ ((row >> 1) & 7);
+                int64_t gr = row0 + row;
+                if (gr > n - 1) gr = n - 1;  // ragged tail: re-read the last row, never stored
+                dma16(x + gr * d + k0 + ch * 8, (const LDS_AS void*)&xs[xslot][inst * 1024]);
+            }
+        }
+        const int c = it + GNW - 1;
+        if (c >= 0) {
+            const int k0 = (c < nchunk ? c : nchunk - 1) * GBK;
 #pragma unroll
-        for (int i = 0; i < XI; ++i) {
-            const int inst = wave * XI + i;  // rows 8*inst .. +8 of the tile
-            const int row = inst * 8 + (lane >> 3);
-            const int ch = (lane & 7) ^ ((row >> 1) & 7);
-            int64_t gr = row0 + row;
-            if (gr > n - 1) gr = n - 1;  // ragged tail: re-read the last row, never stored
-            dma16(x + gr * d + k0 + ch * 8, (const LDS_AS void*)&xs[slot][inst * 1024]);
+            for (int i = 0; i < WI; ++i) {
+                const int row = wave * 32 + i * 8 + (lane >> 3);  // this wave's own W1 rows
+                const int ch = (lane & 7) ^ ((row >> 1) & 7);
+                dma16(w1 + (int64_t)row * d + k0 + ch * 8, (const LDS_AS void*)&ws[wslot][row * 128 - (lane >> 3) * 128]);
+            }
         }
     };
 
@@ -96,21 +107,28 @@ __global__ __launch_bounds__(64 * NWV) void gate_mfma_kernel(const uint16_t* __r
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[tb][j] = 0.0f;
 
+    // Prime: iterations -(GNX-1) .. -1.
 #pragma unroll
-    for (int p = 0; p < L; ++p) issue(p, p);
+    for (int p = -(GNX - 1); p < 0; ++p) issue(p, (p + GNX - 1) % GNX, ((p + GNW - 1) % GNW + GNW) % GNW);
 
-    for (int cb = 0; cb < nchunk; cb += GNS) {
+    for (int cb = 0; cb < nchunk; cb += GNX) {
 #pragma unroll
-        for (int u = 0; u < GNS; ++u) {
+        for (int u = 0; u < GNX; ++u) {
             const int c = cb + u;
-            ring_barrier();                  // every wave is done with slot (u - 1) mod GNS
-            issue(c + L, (u + L) % GNS);     // refill that slot, L chunks ahead
-            wait_vmcnt<OPS * L>();           // this wave's loads of chunk c are complete
-            ring_barrier();                  // ... and every other wave's
+            ring_barrier();  // every wave is done with chunk c-1's slots
+            issue(c, (u + GNX - 1) % GNX, (u + GNW - 1) % GNW);
+            // W1(c) is this wave's youngest needed load; 2 iterations of OPS
+            // loads were issued after it (and X(c) is older still).
+            wait_vmcnt<OPS * (GNW - 1)>();
+            ring_barrier();  // ... and every other wave's loads of chunk c landed
             if (c < nchunk) {
                 const LDS_AS char* xt = (const LDS_AS char*)xs[u];
+                const LDS_AS char* wt = (const LDS_AS char*)ws[u % GNW];
+                const int wr = wave * 32 + l32;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
+                    const int cw = (hh * 4 + ks) ^ ((wr >> 1) & 7);
+                    const bf16x8 a = *(const LDS_AS bf16x8*)(wt + wr * 128 + cw * 16);
                     bf16x8 xb[2];
 #pragma unroll
                     for (int tb = 0; tb < 2; ++tb) {
@@ -120,7 +138,7 @@ __global__ __launch_bounds__(64 * NWV) void gate_mfma_kernel(const uint16_t* __r
                     }
 #pragma unroll
                     for (int tb = 0; tb < 2; ++tb)
-                        acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][ks], xb[tb], acc[tb], 0, 0, 0);
+                        acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb[tb], acc[tb], 0, 0, 0);
                 }
             }
         }

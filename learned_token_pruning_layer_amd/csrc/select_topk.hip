@@ -14,13 +14,15 @@
 //  2. A 3-pass MSB radix select (11, 11 and 10-bit digits; LDS histograms
 //     with integer atomics; a block scan over the bins from the top) finds
 //     the k-th largest key T and rem = how many keys equal to T are kept.
-//  3. Emission: each thread owns 16 consecutive rows and counts its rows
-//     that are "above" (outside the document, or key > T) and "tied"
-//     (document key == T); one block-wide exclusive scan (wavefront shuffle
-//     scans, then a scan of the 16 wave totals) gives every thread its
-//     rank. Kept rows are the above rows and the first rem tied rows; a kept
-//     row's output slot is (#above before it) + min(#tied before it, rem),
-//     so rows land in ascending order without a sort.
+//  3. Emission: each wave owns 1024 consecutive rows, walked 64 at a time
+//     (lane-consecutive, conflict-free LDS reads). A row is "above"
+//     (outside the document, or key > T) or "tied" (document key == T);
+//     wavefront ballots + popcounts give each wave its totals, one scan of
+//     the 16 wave totals gives each wave its starting rank, and a second walk
+//     ranks every row with ballot + mbcnt. Kept rows are the above rows and
+//     the first rem tied rows; a kept row's output slot is
+//     (#above before it) + min(#tied before it, rem), so rows land in
+//     ascending order without a sort.
 // Integer work only: the result is bit-exact and deterministic.
 #include "tg_internal.hpp"
 
@@ -29,7 +31,7 @@ namespace {
 
 constexpr int ST = 1024;    // threads per workgroup (16 waves)
 constexpr int NW = ST / 64;
-constexpr int ITEMS = 16;   // consecutive rows per thread in the emission
+constexpr int WROWS = 1024; // consecutive rows per wave in the emission
 constexpr int CAP = 36864;  // document keys kept in LDS (144 KB)
 constexpr int NB = 2048;    // histogram bins (11-bit digits)
 
@@ -38,6 +40,10 @@ __device__ __forceinline__ uint32_t score_key(float f) {
     if ((b & 0x7fffffffu) > 0x7f800000u) return 0u;  // NaN: below every number
     if ((b & 0x7fffffffu) == 0u) b = 0u;             // -0 ranks as +0
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Inclusive scan of v over the wave (shuffle-up ladder).
@@ -71,15 +77,15 @@ __global__ __launch_bounds__(ST) void select_kernel(const float* __restrict__ sc
     uint32_t thr = 0, rem = 0;
     if (mode == 2) {
         if (resident) {
-            for (int32_t i0 = 0; i0 < n_doc; i0 += ST * 8) {
-                float v[8];
+            for (int32_t i0 = 0; i0 < n_doc; i0 += ST * 16) {
+                float v[16];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
+                for (int u = 0; u < 16; ++u) {
                     const int32_t i = i0 + u * ST + tid;
                     v[u] = (i < n_doc) ? scores[dbeg + i] : 0.0f;
                 }
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
+                for (int u = 0; u < 16; ++u) {
                     const int32_t i = i0 + u * ST + tid;
                     if (i < n_doc) keys[i] = score_key(v[u]);
                 }
@@ -133,38 +139,33 @@ __global__ __launch_bounds__(ST) void select_kernel(const float* __restrict__ sc
         thr = prefix;
     }
 
-    // Emission in row order, ST*ITEMS rows per step.
-    uint32_t carry_above = 0, carry_tied = 0;
+    // Emission in row order, NW*WROWS rows per step.
+    // Row class: 0 dropped, 1 above, 2 tied.
     const int32_t len = sd.len;
-    for (int32_t r0 = 0; r0 < len; r0 += ST * ITEMS) {
-        const int32_t base = r0 + tid * ITEMS;
-        uint32_t cls[ITEMS];  // 0: dropped, 1: above, 2: tied
+    auto classify = [&](int32_t r) -> uint32_t {
+        if (r >= len) return 0u;
+        const bool in_doc = r >= sd.doc_begin && r < sd.doc_end;
+        if (!in_doc || mode == 1) return 1u;
+        if (mode == 0) return 0u;
+        const int32_t i = r - sd.doc_begin;
+        const uint32_t key = resident ? keys[i] : score_key(scores[dbeg + i]);
+        return key > thr ? 1u : (key == thr ? 2u : 0u);
+    };
+    uint32_t carry_above = 0, carry_tied = 0;
+    for (int32_t r0 = 0; r0 < len; r0 += NW * WROWS) {
+        const int32_t wbase = r0 + wave * WROWS;
         uint32_t na = 0, nt = 0;
-#pragma unroll
-        for (int u = 0; u < ITEMS; ++u) {
-            const int32_t r = base + u;
-            uint32_t c = 0;
-            if (r < len) {
-                const bool in_doc = r >= sd.doc_begin && r < sd.doc_end;
-                if (!in_doc || mode == 1) {
-                    c = 1;
-                } else if (mode == 2) {
-                    const int32_t i = r - sd.doc_begin;
-                    const uint32_t key = resident ? keys[i] : score_key(scores[dbeg + i]);
-                    c = key > thr ? 1u : (key == thr ? 2u : 0u);
-                }
-            }
-            cls[u] = c;
-            na += c == 1;
-            nt += c == 2;
+        for (int u = 0; u < WROWS / 64; ++u) {
+            const uint32_t c = classify(wbase + u * 64 + lane);
+            na += (uint32_t)__popcll(__ballot(c == 1u));
+            nt += (uint32_t)__popcll(__ballot(c == 2u));
         }
-        const uint32_t ia = wave_scan(na, lane), it = wave_scan(nt, lane);
-        if (lane == 63) {
-            wtot[wave][0] = ia;
-            wtot[wave][1] = it;
+        if (lane == 0) {
+            wtot[wave][0] = na;
+            wtot[wave][1] = nt;
         }
         __syncthreads();
-        uint32_t pa = carry_above + ia - na, pt = carry_tied + it - nt, ta = 0, tt = 0;
+        uint32_t pa = carry_above, pt = carry_tied, ta = 0, tt = 0;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             const uint32_t a = wtot[w][0], b = wtot[w][1];
@@ -172,16 +173,20 @@ __global__ __launch_bounds__(ST) void select_kernel(const float* __restrict__ sc
             ta += a;
             tt += b;
         }
-#pragma unroll
-        for (int u = 0; u < ITEMS; ++u) {
-            const uint32_t c = cls[u];
-            if (c == 1 || (c == 2 && pt < rem)) {
-                const uint32_t slot = pa + (pt < rem ? pt : rem);
-                if (slot < (uint32_t)sd.n_kept)  // always true when the counts are right
-                    kept[sd.kept_off + slot] = (int32_t)(sd.start + base + u);
+        if (pa < (uint32_t)sd.n_kept) {  // this wave has kept rows to place
+            for (int u = 0; u < WROWS / 64; ++u) {
+                const int32_t r = wbase + u * 64 + lane;
+                const uint32_t c = classify(r);
+                const uint64_t ba = __ballot(c == 1u), bt = __ballot(c == 2u);
+                const uint32_t ma = pa + lanes_below(ba), mt = pt + lanes_below(bt);
+                if (c == 1u || (c == 2u && mt < rem)) {
+                    const uint32_t slot = ma + (mt < rem ? mt : rem);
+                    if (slot < (uint32_t)sd.n_kept)  // always true when the counts are right
+                        kept[sd.kept_off + slot] = (int32_t)(sd.start + r);
+                }
+                pa += (uint32_t)__popcll(ba);
+                pt += (uint32_t)__popcll(bt);
             }
-            pa += c == 1;
-            pt += c == 2;
         }
         carry_above += ta;
         carry_tied += tt;

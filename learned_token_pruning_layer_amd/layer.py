@@ -12,7 +12,10 @@ from typing import List, Optional, Sequence
 
 import torch
 
-from ._lib import tg_compact, tg_gate_score, tg_gated_attention, tg_kept_rows, tg_select_topk
+import ctypes
+import math
+
+from ._lib import TG_BF16, TG_F32, TgGather, _check, load, seq_array, tg_kept_rows
 
 
 class GatedPrefillLayer:
@@ -60,30 +63,62 @@ class GatedPrefillLayer:
             self.lses.append(torch.empty((hq, m), dtype=torch.float32, device=dev) if want_lse else None)
         self.srcs = srcs
         self.dsts = ([self.hidden_kept] if gather_hidden else []) + [t for trip in self.qkv_kept for t in trip]
+        self._prepare()
+
+    def _prepare(self):
+        """Marshal every C-ABI argument once, so a step is four plain calls."""
+        lib = self._lib = load()
+        dt = TG_F32 if self.x.dtype == torch.float32 else TG_BF16
+        n, d = self.x.shape
+        h = self.w1.shape[0]
+        self._seqs = seq_array(self.prompts)
+        ns = len(self.prompts)
+        self._gate_args = (dt, self.x.data_ptr(), n, d, self.w1.data_ptr(),
+                           None if self.b1 is None else self.b1.data_ptr(), h, self.w2.data_ptr(),
+                           ctypes.c_float(self.b2), self.scores.data_ptr())
+        self._sel_args = (self.scores.data_ptr(), self._seqs, ns, self.kept.data_ptr(), None, 0)
+        garr = (TgGather * max(1, len(self.srcs)))()
+        for i, (src, dst) in enumerate(zip(self.srcs, self.dsts)):
+            rb = int(math.prod(src.shape[1:])) * src.element_size()
+            garr[i] = TgGather(src.data_ptr(), dst.data_ptr(), rb, rb, rb)
+        self._garr = garr
+        self._comp_args = (self.kept.data_ptr(), self.m, self._seqs, ns, garr, len(self.srcs),
+                           None if self.pos is None else self.pos.data_ptr(), self.pos_kept.data_ptr(),
+                           self.scores.data_ptr(), self.bias_kept.data_ptr())
+        self._attn_args = []
+        for i, lay in enumerate(self.layers):
+            qk, kk, vk = self.qkv_kept[i]
+            lse = self.lses[i]
+            self._attn_args.append((dt, qk.data_ptr(), kk.data_ptr(), vk.data_ptr(), self.bias_kept.data_ptr(),
+                                    self.pos_kept.data_ptr(), self._seqs, ns, self.hq, self.hkv, self.head_dim,
+                                    lay.gain.data_ptr(), ctypes.c_float(lay.tau), self.outs[i].data_ptr(),
+                                    None if lse is None else lse.data_ptr(), None, 0))
+
+    @staticmethod
+    def _stream(stream):
+        if stream is None:
+            return torch.cuda.current_stream().cuda_stream
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
     # The four steps, individually callable (the bench times each).
     def gate(self, stream=None):
-        tg_gate_score(self.x, self.w1, self.w2, self.b1, self.b2, scores=self.scores, stream=stream)
+        _check(self._lib.tg_gate_score(*self._gate_args, self._stream(stream)))
 
     def select(self, stream=None):
-        tg_select_topk(self.scores, self.prompts, kept_idx=self.kept, stream=stream)
+        _check(self._lib.tg_select_topk(*self._sel_args, self._stream(stream)))
 
     def compact(self, stream=None):
-        tg_compact(self.kept, self.prompts, self.srcs, pos=self.pos, scores=self.scores, outs=self.dsts,
-                   pos_kept=self.pos_kept, bias_kept=self.bias_kept, stream=stream)
+        _check(self._lib.tg_compact(*self._comp_args, self._stream(stream)))
 
     def attention(self, i: int = 0, stream=None):
-        lay = self.layers[i]
-        qk, kk, vk = self.qkv_kept[i]
-        m, hq, hkv, dh = self.m, self.hq, self.hkv, self.head_dim
-        tg_gated_attention(qk.view(m, hq, dh), kk.view(m, hkv, dh), vk.view(m, hkv, dh), self.bias_kept,
-                           self.pos_kept, self.prompts, lay.gain, lay.tau, out=self.outs[i],
-                           want_lse=self.want_lse, lse=self.lses[i], stream=stream)
+        _check(self._lib.tg_gated_attention(*self._attn_args[i], self._stream(stream)))
 
     def run(self, stream=None):
         """One whole step: all four steps, every layer's attention."""
-        self.gate(stream)
-        self.select(stream)
-        self.compact(stream)
-        for i in range(len(self.layers)):
-            self.attention(i, stream)
+        st = self._stream(stream)
+        lib = self._lib
+        _check(lib.tg_gate_score(*self._gate_args, st))
+        _check(lib.tg_select_topk(*self._sel_args, st))
+        _check(lib.tg_compact(*self._comp_args, st))
+        for args in self._attn_args:
+            _check(lib.tg_gated_attention(*args, st))
