@@ -43,16 +43,16 @@ namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-constexpr int BN = 64;  // keys per tile
 
 // Index of the key tile one past the last tile a query block can see:
 // tiles up to the block's last row, extended while the next tile starts at
 // a position not after the block's last position (repeated positions).
+template <int TB>
 __device__ __forceinline__ int key_tile_end(const int32_t* __restrict__ pos, int64_t off, int n,
                                             int q_last) {
-    int kt_end = q_last / BN + 1;
+    int kt_end = q_last / TB + 1;
     const int32_t pl = pos[off + q_last];
-    while (kt_end * BN < n && pos[off + kt_end * BN] <= pl) ++kt_end;
+    while (kt_end * TB < n && pos[off + kt_end * TB] <= pl) ++kt_end;
     return kt_end;
 }
 
@@ -102,8 +102,8 @@ __device__ __forceinline__ int swz_v(int row) { return CH == 16 ? ((row & 3) << 
 // c ^ swz(r), which keeps both the K operand reads (ds_read_b128) and the
 // V^T operand reads (ds_read_b64_tr_b16) free of bank conflicts. The
 // two splits' (max, sum, O) are merged through LDS at the end.
-template <int D, int HW>
-__global__ __launch_bounds__(128 * HW) void attn_bf16_kernel(
+template <int D, int HW, int BN>
+__global__ __launch_bounds__(128 * HW, BN == 32 ? 2 : 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ bias, const int32_t* __restrict__ pos, AttnTable t, int hq, int hkv,
     const float* __restrict__ gain, float qk_scale, uint16_t* __restrict__ out,
@@ -120,11 +120,14 @@ __global__ __launch_bounds__(128 * HW) void attn_bf16_kernel(
     static_assert(IPT % NW == 0 && 4 % NW == 0, "loads must split evenly over waves");
     constexpr int KS = D / 16;                    // k-steps of q.k
     constexpr int DB = D / 32;                    // 32-wide d blocks of O
+    constexpr int KBN = BN / 32;                  // 32-key blocks per tile
+    constexpr int PS = BN / 16;                   // 16-key k-steps of P.V per tile
+    constexpr int SM = 64;                        // bias/pos entries per tile (one dword load)
 
     __shared__ __attribute__((aligned(1024))) char tile0[2][2][TILEB];  // stage 0: [split][K,V]
     __shared__ __attribute__((aligned(1024))) char tile1[2][2][TILEB];  // stage 1
     // [split][bias bits, position][key] per stage
-    __shared__ __attribute__((aligned(16))) uint32_t small0[2][2][BN], small1[2][2][BN];
+    __shared__ __attribute__((aligned(16))) uint32_t small0[2][2][SM], small1[2][2][SM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(128 * HW) void attn_bf16_kernel(
     const int h = kvh * G + hg * HW + hl;
     const int i0 = qb * 32;
     const int q_last = min(n, i0 + 32) - 1;
-    const int n_tiles = key_tile_end(pos, off, n, q_last);
+    const int n_tiles = key_tile_end<BN>(pos, off, n, q_last);
     const int n_it = (n_tiles + 1) / 2;
 
     const int qi = min(i0 + l32, n - 1);
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(128 * HW) void attn_bf16_kernel(
     // Issue every load of iteration `it` into the given stage buffers. The
     // array each instruction writes is fixed at compile time; the wave index
     // only picks rows, so every wave issues exactly LPW loads per stage.
-    auto issue = [&](int it, char (*tl)[2][TILEB], uint32_t (*sm)[2][BN]) {
+    auto issue = [&](int it, char (*tl)[2][TILEB], uint32_t (*sm)[2][SM]) {
 #pragma unroll
         for (int tile_id = 0; tile_id < 4; ++tile_id) {
             const int sp_ = tile_id >> 1, kind = tile_id & 1;
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(128 * HW) void attn_bf16_kernel(
     float m_run = -INFINITY, l_run = 0.0f;
 
     // One key tile for this wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
-    auto compute = [&](int kt, const char* kt_lds, const char* vt_lds, const uint32_t (*smv)[BN]) {
+    auto compute = [&](int kt, const char* kt_lds, const char* vt_lds, const uint32_t (*smv)[SM]) {
         const LDS_AS char* kl = (const LDS_AS char*)kt_lds;
         const LDS_AS char* vl = (const LDS_AS char*)vt_lds;
         const LDS_AS float* bsv = (const LDS_AS float*)smv[0];
@@ -223,9 +226,9 @@ __global__ __launch_bounds__(128 * HW) void attn_bf16_kernel(
         // Element-wise masking only where some key may be invisible to some
         // query of this wave: the ragged end, or keys past the first query.
         const bool need_mask = (kt + 1) * BN > n || psv[BN - 1] > wave_pos_lo;
-        f32x16 acc_s[2];
+        f32x16 acc_s[KBN];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KBN; ++kb) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc_s[kb][j] = 0.0f;
             const int row = kb * 32 + l32;
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(128 * HW) void attn_bf16_kernel(
         // kb*32 + 8(j/4) + 4hh + j%4 of this lane's query.
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KBN; ++kb) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int key0 = kb * 32 + 8 * g4 + 4 * hh;
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(128 * HW) void attn_bf16_kernel(
         }
         if (need_mask) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < KBN; ++kb) {
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int key0 = kb * 32 + 8 * g4 + 4 * hh;
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(128 * HW) void attn_bf16_kernel(
             }
         }
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KBN; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) mx = fmaxf(mx, acc_s[kb][j]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -288,9 +291,9 @@ __global__ __launch_bounds__(128 * HW) void attn_bf16_kernel(
         float lsum = 0.0f;
         // P^T as B operands: k-step s uses S^T registers 8*(s%2) .. +8 of block s/2,
         // i.e. keys 16s + 8(e/4) + 4hh + e%4 for slot e.
-        bf16x8 pf[4];
+        bf16x8 pf[PS];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < PS; ++s) {
             u32x4 w;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -312,7 +315,7 @@ __global__ __launch_bounds__(128 * HW) void attn_bf16_kernel(
             const int dd = 32 * b + dsub;              // element offset in the row
             const int ch = dd >> 3, sub = (dd & 7) * 2;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            for (int s = 0; s < PS; ++s) {
                 const int ka = 16 * s + keyo, kb2 = ka + 8;
                 const v4i16 lo = lds_read_tr16(vl + ka * ROWB + ((ch ^ swz_v<CH>(ka)) * 16) + sub);
                 const v4i16 hi = lds_read_tr16(vl + kb2 * ROWB + ((ch ^ swz_v<CH>(kb2)) * 16) + sub);
@@ -479,6 +482,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 
 int heads_per_wg(int g) { return (g % 2 == 0) ? 2 : 1; }
 
+// Keys per K/V tile of the bf16 kernel.
+#ifndef ATTN_BN
+#define ATTN_BN 32
+#endif
+
 }  // namespace
 
 int attention_heads_per_item(tg_dtype dt, int hq, int hkv) {
@@ -503,13 +511,13 @@ hipError_t launch_attention(tg_dtype dt, const void* q, const void* k, const voi
         const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)k, *vv = (const uint16_t*)v;
         uint16_t* oo = (uint16_t*)out;
         if (head_dim == 128 && hw == 2)
-            hipLaunchKernelGGL((attn_bf16_kernel<128, 2>), grid, dim3(256), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
+            hipLaunchKernelGGL((attn_bf16_kernel<128, 2, ATTN_BN>), grid, dim3(256), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
         else if (head_dim == 128)
-            hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), grid, dim3(128), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
+            hipLaunchKernelGGL((attn_bf16_kernel<128, 1, ATTN_BN>), grid, dim3(128), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
         else if (hw == 2)
-            hipLaunchKernelGGL((attn_bf16_kernel<64, 2>), grid, dim3(256), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
+            hipLaunchKernelGGL((attn_bf16_kernel<64, 2, ATTN_BN>), grid, dim3(256), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
         else
-            hipLaunchKernelGGL((attn_bf16_kernel<64, 1>), grid, dim3(128), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
+            hipLaunchKernelGGL((attn_bf16_kernel<64, 1, ATTN_BN>), grid, dim3(128), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
     } else {
         if (head_dim == 128)
             hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, st, (const float*)q,
