@@ -35,6 +35,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (the scale reference for --pmc byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="CPU only: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--calibrate-copy run into profiles/traffic_qwen16k.json and exit")
     return ap.parse_args()
 
 
@@ -84,6 +89,47 @@ def measured_traffic(kernel):
     if not rec or rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+COPY_BYTES = 256 << 20
+KERNEL_NAMES = {"gate": "gate_mfma_kernel", "select": "select_kernel", "compact": "compact_kernel",
+                "attention": "attn_bf16_kernel"}
+
+
+def traffic_summary(fetch_csv, write_csv):
+    """Per-launch HBM-side bytes of each kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for a plain copy of
+    COPY_BYTES (which reads and writes exactly that many bytes)."""
+    import csv
+
+    def load(path, counter):
+        per = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return per
+
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        per = load(path, counter)
+        copies = [v for k, vals in per.items() if "copy" in k.lower() for v in vals if v > COPY_BYTES / 2]
+        if not copies:
+            raise SystemExit(f"no copy kernel of ~{COPY_BYTES} bytes found in {path}")
+        scale = COPY_BYTES / (sum(copies) / len(copies))
+        for key, pat in KERNEL_NAMES.items():
+            vals = [v for k, vs in per.items() if pat in k for v in vs]
+            if vals:
+                rec = out.setdefault(key, {})
+                rec[counter.lower() + "_bytes"] = sum(vals) / len(vals) * scale
+                rec[counter.lower() + "_scale"] = scale
+    for key, rec in out.items():
+        rec["hbm_bytes_per_launch"] = rec.get("fetch_size_bytes", 0.0) + rec.get("write_size_bytes", 0.0)
+        rec["source_sha256_16"] = source_hash(KERNEL_SOURCES[key])
+    dst = os.path.join(ROOT, "profiles", "traffic_qwen16k.json")
+    with open(dst, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(json.dumps(out, indent=1, sort_keys=True))
 
 
 def cpu_baseline(w, budget_s):
@@ -138,6 +184,9 @@ def cpu_baseline(w, budget_s):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_summary(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "gpus_requested": args.gpus}))
@@ -237,6 +286,12 @@ def main():
         "roofline": dict(kernel=dom, launch_us=round(dom_us, 2), **roofline(dom, dom_us)),
         "wall_s_timed": round(wall, 4),
     }
+    if args.calibrate_copy:
+        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
     print(json.dumps(rec), flush=True)
