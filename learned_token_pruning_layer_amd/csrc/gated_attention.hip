@@ -94,40 +94,41 @@ __device__ __forceinline__ int swz_k(int row) { return CH == 16 ? (row & 15) : (
 template <int CH>
 __device__ __forceinline__ int swz_v(int row) { return CH == 16 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
 
-// Workgroup = HW query heads of one KV head x 2 key splits, 32 query rows.
-// Wave w: head slot w % HW, split w / HW; split p owns key tiles kt = 2i + p.
+// Workgroup = HW query heads of one KV head x SPL key splits, 32 query rows.
+// Wave w: head slot w % HW, split w / HW; split p owns key tiles kt = SPL*i + p.
 // K and V tiles (64 keys x D) stream straight from global memory into LDS
 // (global_load_lds, 16 bytes per lane, no staging registers) through a
 // two-stage ring; 16-byte chunk c of key row r is stored at position
 // c ^ swz(r), which keeps both the K operand reads (ds_read_b128) and the
 // V^T operand reads (ds_read_b64_tr_b16) free of bank conflicts. The
-// two splits' (max, sum, O) are merged through LDS at the end.
-template <int D, int HW, int BN>
-__global__ __launch_bounds__(128 * HW, BN == 32 ? 2 : 1) void attn_bf16_kernel(
+// splits' (max, sum, O) are merged through LDS at the end, in split order.
+template <int D, int HW, int BN, int SPL>
+__global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ bias, const int32_t* __restrict__ pos, AttnTable t, int hq, int hkv,
     const float* __restrict__ gain, float qk_scale, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
-    constexpr int NW = 2 * HW;                    // waves
+    constexpr int NW = HW * SPL;                  // waves
     constexpr int ROWB = D * 2;                   // bytes per K/V row
     constexpr int CH = ROWB / 16;                 // 16-byte chunks per row
     constexpr int TILEB = BN * ROWB;              // bytes per K or V tile
     constexpr int RPI = 1024 / ROWB;              // rows per 1 KB load instruction
     constexpr int IPT = TILEB / 1024;             // load instructions per tile
-    constexpr int TPW = IPT / NW;                 // instructions per tile per wave
-    constexpr int SPW = 4 / NW;                   // small (bias/pos) loads per wave
-    constexpr int LPW = 4 * TPW + SPW;            // load instructions per wave per stage
-    static_assert(IPT % NW == 0 && 4 % NW == 0, "loads must split evenly over waves");
+    constexpr int NTL = 2 * SPL;                  // K and V tiles per stage
+    constexpr int TPW = NTL * IPT / NW;           // tile load instructions per wave per stage
+    constexpr int SPW = NTL / NW;                 // small (bias/pos) loads per wave per stage
+    constexpr int LPW = TPW + SPW;                // load instructions per wave per stage
+    static_assert((NTL * IPT) % NW == 0 && NTL % NW == 0, "loads must split evenly over waves");
     constexpr int KS = D / 16;                    // k-steps of q.k
     constexpr int DB = D / 32;                    // 32-wide d blocks of O
     constexpr int KBN = BN / 32;                  // 32-key blocks per tile
     constexpr int PS = BN / 16;                   // 16-key k-steps of P.V per tile
     constexpr int SM = 64;                        // bias/pos entries per tile (one dword load)
 
-    __shared__ __attribute__((aligned(1024))) char tile0[2][2][TILEB];  // stage 0: [split][K,V]
-    __shared__ __attribute__((aligned(1024))) char tile1[2][2][TILEB];  // stage 1
+    __shared__ __attribute__((aligned(1024))) char tile0[SPL][2][TILEB];  // stage 0: [split][K,V]
+    __shared__ __attribute__((aligned(1024))) char tile1[SPL][2][TILEB];  // stage 1
     // [split][bias bits, position][key] per stage
-    __shared__ __attribute__((aligned(16))) uint32_t small0[2][2][SM], small1[2][2][SM];
+    __shared__ __attribute__((aligned(16))) uint32_t small0[SPL][2][SM], small1[SPL][2][SM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(128 * HW, BN == 32 ? 2 : 1) void attn_bf16_kernel(
     const int i0 = qb * 32;
     const int q_last = min(n, i0 + 32) - 1;
     const int n_tiles = key_tile_end<BN>(pos, off, n, q_last);
-    const int n_it = (n_tiles + 1) / 2;
+    const int n_it = (n_tiles + SPL - 1) / SPL;
 
     const int qi = min(i0 + l32, n - 1);
     const int32_t my_pos = pos[off + qi];
@@ -187,23 +188,22 @@ __global__ __launch_bounds__(128 * HW, BN == 32 ? 2 : 1) void attn_bf16_kernel(
     // only picks rows, so every wave issues exactly LPW loads per stage.
     auto issue = [&](int it, char (*tl)[2][TILEB], uint32_t (*sm)[2][SM]) {
 #pragma unroll
-        for (int tile_id = 0; tile_id < 4; ++tile_id) {
+        for (int i = 0; i < TPW; ++i) {
+            const int inst = i * NW + wave;   // this wave's i-th 1 KB load of the stage
+            const int tile_id = inst / IPT;   // split tile_id/2, K (even) or V (odd)
+            const int rg = inst % IPT;        // 1 KB row group of the tile
             const int sp_ = tile_id >> 1, kind = tile_id & 1;
             const uint16_t* base = kind ? vbase : kbase;
-#pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                const int rg = i * NW + wave;  // 1 KB row group of the tile
-                const int row = rg * RPI + lane / CH;
-                const int chunk = (lane % CH) ^ (kind ? swz_v<CH>(row) : swz_k<CH>(row));
-                const int j = min((2 * it + sp_) * BN + row, n - 1);
-                dma16(base + (int64_t)j * kv_row_stride + chunk * 8, (LDS_AS void*)&tl[sp_][kind][rg * 1024]);
-            }
+            const int row = rg * RPI + lane / CH;
+            const int chunk = (lane % CH) ^ (kind ? swz_v<CH>(row) : swz_k<CH>(row));
+            const int j = min((SPL * it + sp_) * BN + row, n - 1);
+            dma16(base + (int64_t)j * kv_row_stride + chunk * 8, (LDS_AS void*)&tl[sp_][kind][rg * 1024]);
         }
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            const int sid = wave * SPW + i;  // 0..3: split sid/2, bias (even) or position (odd)
+            const int sid = wave * SPW + i;  // split sid/2, bias (even) or position (odd)
             const int sp_ = sid >> 1;
-            const int j = min((2 * it + sp_) * BN + lane, n - 1);
+            const int j = min((SPL * it + sp_) * BN + lane, n - 1);
             const void* src = (sid & 1) ? (const void*)(pos + off + j) : (const void*)(bias + off + j);
             dma4(src, (LDS_AS void*)&sm[sp_][sid & 1][0]);
         }
@@ -333,38 +333,60 @@ __global__ __launch_bounds__(128 * HW, BN == 32 ? 2 : 1) void attn_bf16_kernel(
         // ---- stage 0 ----
         if (it + 1 < n_it) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
         ring_barrier();
-        compute(2 * it + split, tile0[split][0], tile0[split][1], small0[split]);
+        compute(SPL * it + split, tile0[split][0], tile0[split][1], small0[split]);
         ring_barrier();
         if (it + 2 < n_it) issue(it + 2, tile0, small0);
         if (it + 1 >= n_it) break;
         // ---- stage 1 ----
         if (it + 2 < n_it) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
         ring_barrier();
-        compute(2 * (it + 1) + split, tile1[split][0], tile1[split][1], small1[split]);
+        compute(SPL * (it + 1) + split, tile1[split][0], tile1[split][1], small1[split]);
         ring_barrier();
         if (it + 3 < n_it) issue(it + 3, tile1, small1);
     }
     wait_vmcnt<0>();
 
-    // Merge the two key splits: split 1 hands (m, l, O) to split 0 through LDS.
-    float* xo = (float*)&tile0[0][0][0];  // [HW][DB*16][64] floats, free after the loop
-    float* xm = (float*)&tile1[0][0][0];  // [HW][64] max, then [HW][64] sum
-    if (split == 1) {
+    // Merge the key splits: splits 1.. hand (m, l, O) to split 0 through LDS
+    // (the ring buffers are free now); split 0 combines them in split order.
+    constexpr int PER = HW * DB * 16 * 64;            // floats of O per handing split
+    constexpr int CAP0 = SPL * 2 * TILEB / 4;         // floats in tile0
+    static_assert(PER <= CAP0, "merge buffer");
+    float* const f0 = (float*)&tile0[0][0][0];
+    float* const f1 = (float*)&tile1[0][0][0];
+    auto xo_of = [&](int q) -> float* {              // q = split - 1
+        return (q + 1) * PER <= CAP0 ? f0 + q * PER : f1 + (q - CAP0 / PER) * PER;
+    };
+    float* const xm = f1 + ((SPL - 1) - CAP0 / PER > 0 ? ((SPL - 1) - CAP0 / PER) * PER : 0);
+    // xm: [SPL-1][HW][64] max, then [SPL-1][HW][64] sum
+    if (split > 0) {
+        float* xo = xo_of(split - 1);
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
             for (int j = 0; j < 16; ++j) xo[(hl * DB * 16 + b * 16 + j) * 64 + lane] = acc_o[b][j];
-        xm[hl * 64 + lane] = m_run;
-        xm[HW * 64 + hl * 64 + lane] = l_run;
+        xm[((split - 1) * HW + hl) * 64 + lane] = m_run;
+        xm[((SPL - 1 + split - 1) * HW + hl) * 64 + lane] = l_run;
     }
     __syncthreads();
     if (split == 0) {
-        const float m1 = xm[hl * 64 + lane];
-        const float l1 = xm[HW * 64 + hl * 64 + lane];
-        const float m = fmaxf(m_run, m1);
+        float ms[SPL], ls[SPL];
+        ms[0] = m_run;
+        ls[0] = l_run;
+        float m = m_run;
+#pragma unroll
+        for (int q = 1; q < SPL; ++q) {
+            ms[q] = xm[((q - 1) * HW + hl) * 64 + lane];
+            ls[q] = xm[((SPL - 1 + q - 1) * HW + hl) * 64 + lane];
+            m = fmaxf(m, ms[q]);
+        }
         const float mu = (m == -INFINITY) ? 0.0f : m;
-        const float a0 = __builtin_amdgcn_exp2f(m_run - mu), a1 = __builtin_amdgcn_exp2f(m1 - mu);
-        float lt = l_run * a0 + l1 * a1;
+        float a[SPL];
+        float lt = 0.0f;
+#pragma unroll
+        for (int q = 0; q < SPL; ++q) {
+            a[q] = __builtin_amdgcn_exp2f(ms[q] - mu);
+            lt += ls[q] * a[q];
+        }
         lt += __shfl_xor(lt, 32);
         const float inv = 1.0f / lt;
         const int row = i0 + l32;
@@ -378,7 +400,11 @@ __global__ __launch_bounds__(128 * HW, BN == 32 ? 2 : 1) void attn_bf16_kernel(
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int j = 4 * g4 + e;
-                        o[e] = (acc_o[b][j] * a0 + xo[(hl * DB * 16 + b * 16 + j) * 64 + lane] * a1) * inv;
+                        float acc = acc_o[b][j] * a[0];
+#pragma unroll
+                        for (int q = 1; q < SPL; ++q)
+                            acc += xo_of(q - 1)[(hl * DB * 16 + b * 16 + j) * 64 + lane] * a[q];
+                        o[e] = acc * inv;
                     }
                     uint2 w;
                     w.x = pack_bf16x2(o[0], o[1]);
@@ -486,6 +512,10 @@ int heads_per_wg(int g) { return (g % 2 == 0) ? 2 : 1; }
 #ifndef ATTN_BN
 #define ATTN_BN 32
 #endif
+// Key splits per workgroup (waves = heads per workgroup x splits).
+#ifndef ATTN_SPL
+#define ATTN_SPL 2
+#endif
 
 }  // namespace
 
@@ -511,13 +541,13 @@ hipError_t launch_attention(tg_dtype dt, const void* q, const void* k, const voi
         const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)k, *vv = (const uint16_t*)v;
         uint16_t* oo = (uint16_t*)out;
         if (head_dim == 128 && hw == 2)
-            hipLaunchKernelGGL((attn_bf16_kernel<128, 2, ATTN_BN>), grid, dim3(256), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
+            hipLaunchKernelGGL((attn_bf16_kernel<128, 2, ATTN_BN, ATTN_SPL>), grid, dim3(128 * ATTN_SPL), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
         else if (head_dim == 128)
-            hipLaunchKernelGGL((attn_bf16_kernel<128, 1, ATTN_BN>), grid, dim3(128), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
+            hipLaunchKernelGGL((attn_bf16_kernel<128, 1, ATTN_BN, ATTN_SPL>), grid, dim3(64 * ATTN_SPL), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
         else if (hw == 2)
-            hipLaunchKernelGGL((attn_bf16_kernel<64, 2, ATTN_BN>), grid, dim3(256), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
+            hipLaunchKernelGGL((attn_bf16_kernel<64, 2, ATTN_BN, ATTN_SPL>), grid, dim3(128 * ATTN_SPL), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
         else
-            hipLaunchKernelGGL((attn_bf16_kernel<64, 1, ATTN_BN>), grid, dim3(128), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
+            hipLaunchKernelGGL((attn_bf16_kernel<64, 1, ATTN_BN, ATTN_SPL>), grid, dim3(64 * ATTN_SPL), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
     } else {
         if (head_dim == 128)
             hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, st, (const float*)q,
