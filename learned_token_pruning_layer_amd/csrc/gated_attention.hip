@@ -117,7 +117,6 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
     constexpr int NTL = 2 * SPL;                  // K and V tiles per stage
     constexpr int TPW = NTL * IPT / NW;           // tile load instructions per wave per stage
     constexpr int SPW = NTL / NW;                 // small (bias/pos) loads per wave per stage
-    constexpr int LPW = TPW + SPW;                // load instructions per wave per stage
     static_assert((NTL * IPT) % NW == 0 && NTL % NW == 0, "loads must split evenly over waves");
     constexpr int KS = D / 16;                    // k-steps of q.k
     constexpr int DB = D / 32;                    // 32-wide d blocks of O
@@ -132,7 +131,7 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: load set-up stays scalar
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const int G = hq / hkv;
@@ -179,33 +178,58 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
     wait_vmcnt<0>();
     asm volatile("" ::: "memory");
 
-    const int64_t kv_row_stride = (int64_t)hkv * D;
-    const uint16_t* kbase = k + (off * hkv + kvh) * D;
-    const uint16_t* vbase = v + (off * hkv + kvh) * D;
+    const int64_t rowb = (int64_t)hkv * ROWB;  // bytes between consecutive keys of one KV head
+    const char* kbase = (const char*)(k + (off * hkv + kvh) * D);
+    const char* vbase = (const char*)(v + (off * hkv + kvh) * D);
 
-    // Issue every load of iteration `it` into the given stage buffers. The
-    // array each instruction writes is fixed at compile time; the wave index
-    // only picks rows, so every wave issues exactly LPW loads per stage.
-    auto issue = [&](int it, char (*tl)[2][TILEB], uint32_t (*sm)[2][SM]) {
+    // Per-lane byte offsets of this wave's tile loads inside a tile (key row
+    // and swizzled chunk); the tile's first key moves the scalar base only.
+    uint32_t loff[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int inst = i * NW + wave;
+        const int rg = inst % IPT, kind = (inst / IPT) & 1;
+        const int row = rg * RPI + lane / CH;
+        const int chunk = (lane % CH) ^ (kind ? swz_v<CH>(row) : swz_k<CH>(row));
+        loff[i] = (uint32_t)(row * rowb + chunk * 16);
+    }
+
+    // Issue every load of iteration `it` into stage buffers at LDS byte
+    // addresses tl (tiles) and sm (bias/positions). The array each
+    // instruction writes follows from (i, wave); every wave issues exactly
+    // TPW + SPW loads per stage. Keys past the segment's end re-read its last
+    // key (only the last iteration has them, in a ragged tile or in a tile
+    // wholly past the end; they are masked or skipped, never used): there the
+    // scalar base moves to key min(r0, n-1), so every lane offset is >= 0.
+    auto issue = [&](int it, uint32_t tl, uint32_t sm) {
+        const bool full = (SPL * it + SPL) * BN <= n;
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int inst = i * NW + wave;   // this wave's i-th 1 KB load of the stage
             const int tile_id = inst / IPT;   // split tile_id/2, K (even) or V (odd)
             const int rg = inst % IPT;        // 1 KB row group of the tile
             const int sp_ = tile_id >> 1, kind = tile_id & 1;
-            const uint16_t* base = kind ? vbase : kbase;
-            const int row = rg * RPI + lane / CH;
-            const int chunk = (lane % CH) ^ (kind ? swz_v<CH>(row) : swz_k<CH>(row));
-            const int j = min((SPL * it + sp_) * BN + row, n - 1);
-            dma16(base + (int64_t)j * kv_row_stride + chunk * 8, (LDS_AS void*)&tl[sp_][kind][rg * 1024]);
+            const int key0 = (SPL * it + sp_) * BN;   // first key of the tile
+            const int r0 = min(key0, n - 1);
+            const char* base = (kind ? vbase : kbase) + r0 * rowb;
+            uint32_t vo = loff[i];
+            if (!full) {
+                const int row = rg * RPI + lane / CH;
+                const int chunk = (lane % CH) ^ (kind ? swz_v<CH>(row) : swz_k<CH>(row));
+                vo = (uint32_t)((min(key0 + row, n - 1) - r0) * rowb + chunk * 16);
+            }
+            dma16_so(base, vo, tl + (uint32_t)((sp_ * 2 + kind) * TILEB + rg * 1024));
         }
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             const int sid = wave * SPW + i;  // split sid/2, bias (even) or position (odd)
             const int sp_ = sid >> 1;
-            const int j = min((SPL * it + sp_) * BN + lane, n - 1);
-            const void* src = (sid & 1) ? (const void*)(pos + off + j) : (const void*)(bias + off + j);
-            dma4(src, (LDS_AS void*)&sm[sp_][sid & 1][0]);
+            const int key0 = (SPL * it + sp_) * BN;
+            const int r0 = min(key0, n - 1);
+            const char* base = (sid & 1) ? (const char*)(pos + off + r0) : (const char*)(bias + off + r0);
+            // one dword per lane covers SM >= BN keys: always clamp
+            const uint32_t vo = (uint32_t)(min(key0 + lane, n - 1) - r0) * 4u;
+            dma4_so(base, vo, sm + (uint32_t)((sp_ * 2 + (sid & 1)) * SM * 4));
         }
     };
 
@@ -325,26 +349,28 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
         }
     };
 
-    // Two-stage ring: stage it%2 holds iteration it. Loads for it+2 are issued
-    // once every wave has finished reading stage it.
-    issue(0, tile0, small0);
-    if (n_it > 1) issue(1, tile1, small1);
+    // Two-stage ring, one barrier per iteration: stage it%2 holds iteration
+    // it. After the barrier of iteration it, every wave's loads of stage it
+    // have landed and every wave has finished iteration it-1, so the loads of
+    // it+1 go into the other stage before this iteration's compute.
+    const uint32_t tl0 = LDS_ADDR(&tile0[0][0][0]), tl1 = LDS_ADDR(&tile1[0][0][0]);
+    const uint32_t sm0 = LDS_ADDR(&small0[0][0][0]), sm1 = LDS_ADDR(&small1[0][0][0]);
+    issue(0, tl0, sm0);
     for (int it = 0; it < n_it; it += 2) {
         // ---- stage 0 ----
-        if (it + 1 < n_it) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
+        wait_vmcnt<0>();
         ring_barrier();
+        if (it + 1 < n_it) issue(it + 1, tl1, sm1);
         compute(SPL * it + split, tile0[split][0], tile0[split][1], small0[split]);
-        ring_barrier();
-        if (it + 2 < n_it) issue(it + 2, tile0, small0);
         if (it + 1 >= n_it) break;
         // ---- stage 1 ----
-        if (it + 2 < n_it) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
+        wait_vmcnt<0>();
         ring_barrier();
+        if (it + 2 < n_it) issue(it + 2, tl0, sm0);
         compute(SPL * (it + 1) + split, tile1[split][0], tile1[split][1], small1[split]);
-        ring_barrier();
-        if (it + 3 < n_it) issue(it + 3, tile1, small1);
     }
     wait_vmcnt<0>();
+    ring_barrier();  // the merge below reuses the ring buffers
 
     // Merge the key splits: splits 1.. hand (m, l, O) to split 0 through LDS
     // (the ring buffers are free now); split 0 combines them in split order.

@@ -46,7 +46,21 @@ __device__ __forceinline__ void dma4(const void* g, const LDS_AS void* l) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
 }
+// The same with a wave-uniform 64-bit base (SGPR pair), a per-lane 32-bit
+// byte offset and the LDS destination as a plain LDS byte address.
+__device__ __forceinline__ void dma16_so(const void* sbase, uint32_t voff, uint32_t lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_so(const void* sbase, uint32_t voff, uint32_t lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// LDS byte address of a __shared__ object (the cast of a variable's address
+// needs no null check, unlike a cast of an arbitrary generic pointer).
+#define LDS_ADDR(obj) ((uint32_t)(uintptr_t)(LDS_AS const char*)(obj))
 
 // Workgroup barrier for LDS rings. __syncthreads() would also wait for every
 // outstanding global->LDS load (including prefetches of later stages); here
