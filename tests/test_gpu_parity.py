@@ -108,8 +108,24 @@ def test_select_nan_inf_and_spans():
     s[5::13] = -float("inf")
     s[10:20] = -0.0
     s[20:30] = 0.0
-    for k in (0, 17, 1000, 2500, 4000):
+    # 480 of the 4000 document rows stay NaN (they rank last): budgets above
+    # 3520 put the threshold among the NaN rows (key 0).
+    for k in (0, 17, 1000, 2500, 3519, 3520, 3521, 3700, 3999, 4000):
         check_select(s, [Prompt(0, 5000, 300, 4300, k)])
+
+
+@pytest.mark.parametrize("n", [16384, 16385, 32768, 32769])
+def test_select_path_boundaries(n):
+    # Prompt lengths at the edges of the 16-row and 32-row register paths
+    # and the streaming path; a NaN-heavy document puts some thresholds at
+    # key 0, where rows outside the document share the digit.
+    note(f"select boundary prompt of {n} rows")
+    s = make_scores(n, seed=40 + n % 7, kind="ties")
+    s[1::9] = float("nan")
+    n_doc = n - 150
+    nan_doc = int(torch.isnan(s[100:n - 50]).sum())
+    for k in (1, n_doc // 3, n_doc - nan_doc - 1, n_doc - nan_doc, n_doc - nan_doc // 2, n_doc - 1):
+        check_select(s, [Prompt(0, n, 100, n - 50, k)])
 
 
 def test_select_multi_prompt_edges():
