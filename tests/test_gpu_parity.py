@@ -380,6 +380,51 @@ def test_end_to_end_sweep32k_full_budget_is_unpruned():
     assert_rowmax_close(f64(lay.outs[0])[rows], o[rows])
 
 
+def check_layer_sampled(w, n_attn_rows=64, seed=0):
+    """Whole layer on the GPU against the oracle: the selection exactly (the
+    decision taken on the GPU's fp32 scores on both sides), the gate on every
+    kept row, the compaction bit-exactly, attention on sampled kept rows."""
+    lay = run_layer(w)
+    kept = lay.kept.cpu().numpy().astype(np.int64)
+    assert np.array_equal(kept, oracle.select_topk(lay.scores.cpu().numpy(), w.prompts))
+    ks = set(kept.tolist())
+    assert set(w.planted.tolist()) <= ks
+    for p in w.prompts:  # the question is never pruned
+        assert set(range(p.start + p.doc_end, p.start + p.length)) <= ks
+    s_kept = oracle.gate_scores(w.x[torch.as_tensor(kept, device=DEV)].cpu(), w.w1.cpu(), w.w2.cpu())
+    smax = np.abs(s_kept).max()
+    assert np.abs(f64(lay.scores)[kept] - s_kept).max() <= 2e-2 * smax
+    scores = np.full(w.n_rows, np.nan)
+    scores[kept] = s_kept
+    wl = w.layers[0]
+    (qk, kk, vk), pk, bk = oracle.compact(kept, w.prompts, (wl.q.cpu(), wl.k.cpu(), wl.v.cpu()), scores)
+    for got, ref in zip(lay.qkv_kept[0], (qk, kk, vk)):
+        assert torch.equal(got.cpu(), ref)
+    assert torch.equal(lay.hidden_kept.cpu(), w.x.cpu()[torch.as_tensor(kept)])
+    assert np.array_equal(lay.pos_kept.cpu().numpy(), pk)
+    # log-sigmoid is 1-Lipschitz: the bias can differ by at most the score difference
+    assert np.abs(f64(lay.bias_kept) - bk).max() <= 2e-2 * smax
+    m = len(kept)
+    rows = np.unique(np.concatenate([np.random.default_rng(seed).choice(m, n_attn_rows, replace=False), [0, m - 1]]))
+    hq, hkv, dh = w.hq, w.hkv, w.head_dim
+    o, _ = oracle.gated_attention(qk.view(m, hq, dh), kk.view(m, hkv, dh), vk.view(m, hkv, dh), bk, pk,
+                                  [p.n_kept for p in w.prompts], hq, hkv, wl.gain.cpu(), wl.tau, rows=rows)
+    assert_rowmax_close(f64(lay.outs[0])[rows], o[rows])
+
+
+@pytest.mark.parametrize("frac", [0.05, 0.10, 0.25, 0.50])
+def test_end_to_end_sweep32k_budgets(frac):
+    note(f"end to end: sweep32k at a {frac:.0%} document budget (sampled attention rows)")
+    w = make_workload("sweep32k", device=DEV, k_doc=doc_budget(frac, 32256))
+    check_layer_sampled(w)
+
+
+def test_end_to_end_long128k_sampled():
+    note("end to end: long128k (N=131072, keep 8128 + 1024 query), sampled attention rows")
+    w = make_workload("long128k", device=DEV)
+    check_layer_sampled(w)
+
+
 def test_end_to_end_ragged_four_layers():
     note("end to end: ragged 8 prompts, 4 above-gate layers (sampled rows)")
     prompts = [Prompt(p.start, p.length, p.doc_begin, p.doc_end, p.k_doc) for p in ragged_prompts()]

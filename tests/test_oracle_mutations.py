@@ -1,0 +1,53 @@
+"""The oracle's pins must catch plausible mistakes in the oracle itself.
+
+Each case plants one mistake (a dropped term, a wrong sign, index or operand, a
+wrong tie order) into a scratch copy of `oracle/tokengate.py`, on the CPU, and
+runs the pin tests against that copy in a subprocess; at least one pin has to
+fail. A case whose text no longer occurs in the oracle fails too, so the list
+follows edits of the oracle.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (what the mistake is, text in the oracle, planted replacement)
+MUTATIONS = [
+    ("bias scaled by 1/tau as well", "* scale + bh[None, :]", "* scale + bh[None, :] / float(tau)"),
+    ("gain of the KV head instead of the query head", "bh = g[h] * b[seg]", "bh = g[kvh] * b[seg]"),
+    ("strict causal mask (a query does not see itself)", "<= ps[qi][:, None]", "< ps[qi][:, None]"),
+    ("first gate bias dropped", "h = h + b1v", "h = h"),
+    ("SiLU with the wrong sign", "return z * sigmoid(z)", "return z * sigmoid(-z)"),
+    ("ties broken towards the higher row", "order = np.lexsort((doc, neg, is_nan))",
+     "order = np.lexsort((-doc, neg, is_nan))"),
+    ("query head mapped to the wrong KV head", "kvh = (h * hkv) // hq", "kvh = h % hkv"),
+    ("scale 1/(D tau) instead of 1/(sqrt(D) tau)", "scale = 1.0 / (math.sqrt(dh) * float(tau))",
+     "scale = 1.0 / (dh * float(tau))"),
+    ("log-sigmoid with the wrong sign of the log term", "np.minimum(s, 0.0) - np.log1p",
+     "np.minimum(s, 0.0) + np.log1p"),
+    ("bias also on question keys", "bias[is_doc] = logsigmoid(sk[is_doc])", "bias[:] = logsigmoid(sk)"),
+    ("keeps the lowest-scored rows", "keep_doc = doc[order[:p.k_doc]]",
+     "keep_doc = doc[order[-p.k_doc:]] if p.k_doc else doc[:0]"),
+    ("second gate bias dropped", "out[r0:r0 + xb.shape[0]] = silu(h) @ w2 + float(b2)",
+     "out[r0:r0 + xb.shape[0]] = silu(h) @ w2"),
+]
+
+
+@pytest.mark.parametrize("what,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(tmp_path, what, old, new):
+    src = open(os.path.join(ROOT, "oracle", "tokengate.py")).read()
+    assert src.count(old) == 1, f"mutation text not found once in the oracle: {old!r}"
+    for d in ("oracle", "synthetic", "tests"):
+        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+                        ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutations.py"))
+    (tmp_path / "oracle" / "tokengate.py").write_text(src.replace(old, new))
+    env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle_pins.py", "-x", "-q",
+                        "-p", "no:cacheprovider", "-m", "not gpu"],
+                       cwd=tmp_path, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"planted mistake survived every pin: {what}\n{r.stdout[-2000:]}"
+    assert "failed" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]
