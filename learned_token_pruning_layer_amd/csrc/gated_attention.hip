@@ -128,6 +128,8 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
     __shared__ __attribute__((aligned(1024))) char tile1[SPL][2][TILEB];  // stage 1
     // [split][bias bits, position][key] per stage
     __shared__ __attribute__((aligned(16))) uint32_t small0[SPL][2][SM], small1[SPL][2][SM];
+    // per wave: this head's bias term of the current tile, in units of q.k
+    __shared__ __attribute__((aligned(16))) float sbias[NW][BN];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -164,7 +166,9 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
     const int32_t wave_pos_lo = pos[off + i0];
     const int32_t wave_pos_hi = pos[off + q_last];
     const float c = qk_scale * LOG2E;
-    const float gl2 = gain[h] * LOG2E;
+    // The logit in the exp2 domain is c * (q.k + gb * bias): the bias term
+    // seeds the S^T accumulators, the scale c is applied inside exp2.
+    const float gb = gain[h] / qk_scale;
 
     bf16x8 qf[KS];
     {
@@ -250,11 +254,20 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
         // Element-wise masking only where some key may be invisible to some
         // query of this wave: the ragged end, or keys past the first query.
         const bool need_mask = (kt + 1) * BN > n || psv[BN - 1] > wave_pos_lo;
+        // This head's bias term for the tile's keys, computed once per wave
+        // (the wave reads it back below; its LDS accesses stay in order).
+        static_assert(BN <= 64, "one lane per key");
+        if (lane < BN) sbias[wave][lane] = bsv[lane] * gb;
         f32x16 acc_s[KBN];
 #pragma unroll
         for (int kb = 0; kb < KBN; ++kb) {
+            // Register j of block kb holds key kb*32 + 8(j/4) + 4hh + j%4 of this lane's query.
 #pragma unroll
-            for (int j = 0; j < 16; ++j) acc_s[kb][j] = 0.0f;
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 bb = *(const LDS_AS f32x4*)&sbias[wave][kb * 32 + 8 * g4 + 4 * hh];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc_s[kb][4 * g4 + e] = bb[e];
+            }
             const int row = kb * 32 + l32;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
@@ -263,19 +276,8 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
                 acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc_s[kb], 0, 0, 0);
             }
         }
-        // Logits in the exp2 domain. Register j of block kb holds key
-        // kb*32 + 8(j/4) + 4hh + j%4 of this lane's query.
+        // acc_s now holds q.k + gb * bias; the exp2-domain logit is c times it.
         float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < KBN; ++kb) {
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int key0 = kb * 32 + 8 * g4 + 4 * hh;
-                const f32x4 bb = *(const LDS_AS f32x4*)&bsv[key0];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc_s[kb][4 * g4 + e] = fmaf(acc_s[kb][4 * g4 + e], c, gl2 * bb[e]);
-            }
-        }
         if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < KBN; ++kb) {
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
         for (int kb = 0; kb < KBN; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) mx = fmaxf(mx, acc_s[kb][j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;  // c > 0: the max of the exp2-domain logits
         // The reference max only moves when some row's tile max exceeds it by
         // more than 8 (a factor 256): softmax does not depend on the
         // reference, and p <= 256 stays exact enough in fp32 and bf16. This
@@ -321,8 +323,8 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
             u32x4 w;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float p0 = __builtin_amdgcn_exp2f(acc_s[s >> 1][8 * (s & 1) + 2 * e] - m_use);
-                const float p1 = __builtin_amdgcn_exp2f(acc_s[s >> 1][8 * (s & 1) + 2 * e + 1] - m_use);
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(acc_s[s >> 1][8 * (s & 1) + 2 * e], c, -m_use));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(acc_s[s >> 1][8 * (s & 1) + 2 * e + 1], c, -m_use));
                 lsum += p0 + p1;
                 w[e] = pack_bf16x2(p0, p1);
             }
