@@ -123,7 +123,12 @@ tg_status tg_gate_score(tg_dtype dt, const void* x, int64_t n_rows, int32_t d_mo
                         const void* w1, const void* b1, int32_t d_hidden, const void* w2,
                         float b2, float* scores, hipStream_t stream);
 
-/* Device workspace tg_select_topk needs, in bytes (0 means none; pass NULL). */
+/* Device workspace tg_select_topk needs, in bytes: 0 (pass NULL) when every
+ * prompt has at most 32768 rows, else about 24.6 KB per longer prompt plus
+ * 16 bytes per 16384 of its rows (histograms and per-chunk counts of the
+ * multi-workgroup select). Also 0 for an invalid table (tg_select_topk then
+ * reports the error). The caller owns the buffer; its contents need no
+ * initialisation and are scratch after the call. */
 size_t tg_select_workspace_bytes(const tg_seq* seqs, int32_t n_seqs);
 
 /* Step 2 - top-K select. For each prompt, ranks its document rows by
@@ -131,7 +136,10 @@ size_t tg_select_workspace_bytes(const tg_seq* seqs, int32_t n_seqs);
  * below every number, -0 equal to +0; keeps the first k_doc of them and every
  * row outside the document; writes the kept packed row ids (int32) in
  * ascending order to kept_idx[off_b .. off_b + M_b). kept_idx must hold
- * tg_kept_rows(seqs) entries. Bit-exact and deterministic. Sources: section
+ * tg_kept_rows(seqs) entries. workspace: device memory, 4-byte aligned, of at
+ * least tg_select_workspace_bytes(seqs) bytes (TG_ERR_WORKSPACE otherwise);
+ * two calls in flight at once need two workspaces. Bit-exact and
+ * deterministic. Sources: section
  * "Wie hat TokenGate das Pruning von Tokens verstanden?" (top-K keeps the
  * best-scored tokens; the question is never removed). */
 tg_status tg_select_topk(const float* scores, const tg_seq* seqs, int32_t n_seqs,

@@ -172,8 +172,9 @@ def tg_select_topk(scores: torch.Tensor, seqs: Sequence, kept_idx: Optional[torc
     ws_bytes = lib.tg_select_workspace_bytes(sa, len(seqs))
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=scores.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.tg_select_topk(scores.data_ptr(), sa, len(seqs), kept_idx.data_ptr(), _ptr(workspace),
-                              ws_bytes if workspace is not None else 0, _stream(stream)))
+                              ws_have, _stream(stream)))
     return kept_idx
 
 

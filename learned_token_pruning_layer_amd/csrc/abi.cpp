@@ -115,16 +115,17 @@ tg_status tg_gate_score(tg_dtype dt, const void* x, int64_t n_rows, int32_t d_mo
 }
 
 size_t tg_select_workspace_bytes(const tg_seq* seqs, int32_t n_seqs) {
-    (void)seqs;
-    (void)n_seqs;
-    return 0;
+    tg::SeqTable t;
+    int64_t m = 0;
+    if (build_seq_table(seqs, n_seqs, &t, &m) != TG_OK) return 0;
+    g_err.clear();
+    tg::LongTable lt;
+    return tg::select_plan(t, &lt);
 }
 
 tg_status tg_select_topk(const float* scores, const tg_seq* seqs, int32_t n_seqs, int32_t* kept_idx,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
     g_err.clear();
-    (void)workspace;
-    (void)workspace_bytes;
     tg::SeqTable t;
     int64_t m = 0;
     tg_status st = build_seq_table(seqs, n_seqs, &t, &m);
@@ -135,7 +136,15 @@ tg_status tg_select_topk(const float* scores, const tg_seq* seqs, int32_t n_seqs
     if (!any_rows) return TG_OK;
     if (!scores) return fail(TG_ERR_INVALID_ARGUMENT, "scores is NULL");
     if (m > 0 && !kept_idx) return fail(TG_ERR_INVALID_ARGUMENT, "kept_idx is NULL");
-    hipError_t e = tg::launch_select(scores, t, kept_idx, stream);
+    tg::LongTable lt;
+    const size_t need = tg::select_plan(t, &lt);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(TG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                        need);
+        if ((uintptr_t)workspace % 4 != 0) return fail(TG_ERR_INVALID_ARGUMENT, "workspace not 4-byte aligned");
+    }
+    hipError_t e = tg::launch_select(scores, t, lt, workspace, kept_idx, stream);
     if (e != hipSuccess) return hip_fail(e, "tg_select_topk launch");
     return TG_OK;
 }

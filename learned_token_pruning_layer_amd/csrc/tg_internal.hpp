@@ -63,7 +63,30 @@ hipError_t launch_gate_mfma_bf16(const void* x, int64_t n, int d, const void* w1
 hipError_t launch_gate_simple(tg_dtype dt, const void* x, int64_t n, int d, const void* w1,
                               const void* b1, int h, const void* w2, float b2, float* scores,
                               hipStream_t st);
-hipError_t launch_select(const float* scores, const SeqTable& t, int32_t* kept, hipStream_t st);
+// Select: prompts of up to SEL_REG_MAX rows are handled by one workgroup
+// each; longer prompts by a multi-workgroup radix select over chunks of
+// SEL_CHUNK rows, which keeps its histograms and chunk counts in a workspace.
+constexpr int SEL_REG_MAX = 32768;
+constexpr int SEL_CHUNK = 16384;
+struct LongSeq {
+    int32_t seq;        // index in SeqTable
+    int32_t hist_base;  // first histogram workgroup (chunks of the document)
+    int32_t n_hist;
+    int32_t emit_base;  // first emission workgroup (chunks of the whole prompt)
+    int32_t n_emit;
+    int32_t pad;
+};
+struct LongTable {
+    int32_t n;
+    int32_t n_hist;     // histogram workgroups over all long prompts
+    int32_t n_emit;     // emission workgroups over all long prompts
+    int32_t pad;
+    LongSeq s[TG_MAX_SEQS];
+};
+// Fills the long-prompt table; returns the workspace bytes it needs.
+size_t select_plan(const SeqTable& t, LongTable* lt);
+hipError_t launch_select(const float* scores, const SeqTable& t, const LongTable& lt, void* workspace,
+                         int32_t* kept, hipStream_t st);
 hipError_t launch_compact(const int32_t* kept, int64_t m, const SeqTable& t, const GatherTable& g,
                           const int32_t* pos, int32_t* pos_kept, const float* scores,
                           float* bias_kept, hipStream_t st);

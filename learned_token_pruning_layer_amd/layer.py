@@ -76,7 +76,10 @@ class GatedPrefillLayer:
         self._gate_args = (dt, self.x.data_ptr(), n, d, self.w1.data_ptr(),
                            None if self.b1 is None else self.b1.data_ptr(), h, self.w2.data_ptr(),
                            ctypes.c_float(self.b2), self.scores.data_ptr())
-        self._sel_args = (self.scores.data_ptr(), self._seqs, ns, self.kept.data_ptr(), None, 0)
+        sel_ws = lib.tg_select_workspace_bytes(self._seqs, ns)
+        self.sel_ws = (torch.empty(sel_ws, dtype=torch.uint8, device=self.x.device) if sel_ws else None)
+        self._sel_args = (self.scores.data_ptr(), self._seqs, ns, self.kept.data_ptr(),
+                          None if self.sel_ws is None else self.sel_ws.data_ptr(), sel_ws)
         garr = (TgGather * max(1, len(self.srcs)))()
         for i, (src, dst) in enumerate(zip(self.srcs, self.dsts)):
             rb = int(math.prod(src.shape[1:])) * src.element_size()

@@ -15,7 +15,7 @@ from synthetic import Prompt
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tokengate.h")
 
-INVALID, UNSUPPORTED = 1, 2
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
 
 
 def declared_functions():
@@ -69,6 +69,18 @@ def test_select_rejects_before_launch(lib):
     ok = [Prompt(0, 10, 0, 8, 3)]
     assert lib.tg_select_topk(None, seq_array(ok), 1, None, None, 0, None) == INVALID  # NULL scores
     assert lib.tg_select_workspace_bytes(seq_array(ok), 1) == 0
+    # Prompts above 32768 rows take the multi-workgroup select, which needs a
+    # workspace: per long prompt 3 histograms of 2048 words and 4 state words,
+    # plus 4 words per 16384-row chunk of the prompt.
+    long = [Prompt(0, 100, 0, 90, 5), Prompt(100, 40000, 0, 39000, 7), Prompt(40100, 131072, 0, 130048, 8128)]
+    need = lib.tg_select_workspace_bytes(seq_array(long), 3)
+    assert need == 4 * (2 * (3 * 2048 + 4) + 4 * (3 + 8))
+    # Missing or short workspace is refused before anything is enqueued (the
+    # pointers below are never dereferenced).
+    fake = ctypes.c_void_p(4096)
+    assert lib.tg_select_topk(fake, seq_array(long), 3, fake, None, 0, None) == WORKSPACE
+    assert b"needed" in lib.tg_last_error()
+    assert lib.tg_select_topk(fake, seq_array(long), 3, fake, fake, need - 1, None) == WORKSPACE
 
 
 def test_gate_rejects_before_launch(lib):

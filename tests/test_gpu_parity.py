@@ -18,6 +18,7 @@ import torch
 
 import oracle
 import learned_token_pruning_layer_amd as tg
+from learned_token_pruning_layer_amd._lib import seq_array
 from synthetic import (Prompt, doc_budget, make_attention_inputs, make_ragged, make_scores,
                        make_workload, ragged_prompts)
 
@@ -117,7 +118,7 @@ def test_select_nan_inf_and_spans():
 @pytest.mark.parametrize("n", [16384, 16385, 32768, 32769])
 def test_select_path_boundaries(n):
     # Prompt lengths at the edges of the 16-row and 32-row register paths
-    # and the streaming path; a NaN-heavy document puts some thresholds at
+    # and the multi-workgroup path; a NaN-heavy document puts some thresholds at
     # key 0, where rows outside the document share the digit.
     note(f"select boundary prompt of {n} rows")
     s = make_scores(n, seed=40 + n % 7, kind="ties")
@@ -157,6 +158,45 @@ def test_select_long128k_and_ragged():
     prompts = ragged_prompts()
     n = prompts[-1].start + prompts[-1].length
     check_select(make_scores(n, seed=13, kind="ties"), prompts)
+
+
+def test_select_multi_workgroup_path():
+    # Prompts above 32768 rows: chunks of 16384 rows meet in a workspace.
+    # Ties, NaN thresholds (key 0), chunk-boundary lengths, a small document
+    # inside a long prompt, keep-none / keep-all, and long prompts mixed with
+    # short ones in one call.
+    note("select multi-workgroup: ties, NaN thresholds, chunk edges, mixed batch")
+    s = make_scores(49153, seed=60, kind="ties")
+    s[2::5] = float("nan")
+    n_doc = 49153 - 200
+    nan_doc = int(torch.isnan(s[150:49103]).sum())
+    for k in (0, 1, 7777, n_doc - nan_doc - 1, n_doc - nan_doc, n_doc - nan_doc + 1, n_doc - 1, n_doc):
+        check_select(s, [Prompt(0, 49153, 150, 49103, k)])
+    for n in (32770, 49152, 65536, 65537):
+        check_select(make_scores(n, seed=n, kind="few"), [Prompt(0, n, 0, n - 1, n // 3)])
+    s = make_scores(200000, seed=61, kind="signed0")
+    check_select(s, [Prompt(3, 70000, 30000, 30100, 50)])
+    prompts = [Prompt(0, 100, 0, 50, 10), Prompt(100, 40000, 0, 38000, 3000), Prompt(40100, 16384, 0, 16000, 10),
+               Prompt(56500, 98304, 1000, 98000, 70000), Prompt(154804, 32768, 0, 32000, 5),
+               Prompt(187572, 0, 0, 0, 0), Prompt(187572, 12000, 0, 0, 0)]
+    check_select(make_scores(199572, seed=62, kind="ties"), prompts)
+
+
+def test_select_workspace_reuse_and_2p24():
+    # A caller-provided workspace holding garbage, reused across calls with
+    # different tables; then one prompt of 2^24 rows (1024 chunks).
+    note("select workspace reuse; one prompt of 2^24 rows")
+    lib = tg.load()
+    p1 = [Prompt(0, 90000, 0, 89000, 4444)]
+    p2 = [Prompt(0, 40000, 10, 39990, 39000), Prompt(40000, 50000, 0, 50000, 1)]
+    need = max(lib.tg_select_workspace_bytes(seq_array(p), len(p)) for p in (p1, p2))
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)
+    s = make_scores(90000, seed=63, kind="ties")
+    for p in (p1, p2, p1):
+        got = tg.tg_select_topk(s.to(DEV), p, workspace=ws).cpu().numpy()
+        assert np.array_equal(got.astype(np.int64), oracle.select_topk(s.numpy(), p))
+    n = 1 << 24
+    check_select(make_scores(n, seed=64), [Prompt(0, n, 0, n - 4096, 1 << 20)])
 
 
 # --------------------------------------------------------------- compact ----
