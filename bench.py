@@ -260,6 +260,58 @@ def measure_extras(torch, tg, layer, w, steps, dev):
                                "note": "one prompt of 2^24 document rows, keep 1/8; chunks of 16384 rows, "
                                        "one workgroup each, reading the scores in 3 histogram passes, "
                                        "a count pass and a placement pass"}
+    del sc, kept, ws
+    out["configs"] = measure_configs(torch, tg, dev, timed, pct)
+    return out
+
+
+def measure_configs(torch, tg, dev, timed, pct):
+    """The other workloads, timed the same way (whole layer and attention
+    alone, p50 of event-timed reps): the 32k budget sweep, 128k at 6.25%
+    with the unpruned attention over all 131072 rows beside it, and the
+    ragged 8-prompt batch feeding 4 above-gate layers."""
+    from synthetic import SWEEP_FRACTIONS, Prompt, doc_budget, make_workload
+
+    def causal_flops(prompts, hq, dh):
+        return sum(4 * dh * hq * p.n_kept * (p.n_kept + 1) // 2 for p in prompts)
+
+    def run_one(w, prompts, reps, attn_reps=None):
+        lay = tg.GatedPrefillLayer(w.x, w.w1, w.w2, prompts, w.layers, w.hq, w.hkv, w.head_dim)
+        lay.run()
+        t_layer = pct(timed(lay.run, reps), 0.5)
+        t_attn = sum(pct(timed(lambda i=i: lay.attention(i), attn_reps or reps), 0.5) for i in range(len(w.layers)))
+        fl = causal_flops(prompts, w.hq, w.head_dim) * len(w.layers)
+        rec = {"kept_rows": lay.m, "layer_us": round(t_layer, 1), "attention_us": round(t_attn, 1),
+               "attention_tflops": round(fl / (t_attn * 1e-6) / 1e12, 1)}
+        del lay
+        return rec
+
+    out = {}
+    w = make_workload("sweep32k", device=dev)
+    p0 = w.prompts[0]
+    sweep = []
+    for frac in SWEEP_FRACTIONS:
+        k = doc_budget(frac, p0.n_doc)
+        sweep.append({"keep": frac, "k_doc": k, **run_one(w, [p0._replace(k_doc=k)], 30)})
+    out["sweep32k"] = {"n_rows": w.n_rows, "budgets": sweep}
+    del w
+    torch.cuda.empty_cache()
+    w = make_workload("long128k", device=dev)
+    p0 = w.prompts[0]
+    pruned = run_one(w, w.prompts, 20)
+    full = run_one(w, [p0._replace(k_doc=p0.n_doc)], 3, attn_reps=3)
+    out["long128k"] = {"n_rows": w.n_rows, "k_doc": p0.k_doc, **pruned,
+                       "unpruned": {k: full[k] for k in ("kept_rows", "attention_us", "attention_tflops")},
+                       "unpruned_attention_over_pruned_layer": round(full["attention_us"] / pruned["layer_us"], 1)}
+    del w
+    torch.cuda.empty_cache()
+    w = make_workload("ragged", device=dev)
+    out["ragged"] = {"n_rows": w.n_rows, "prompts": len(w.prompts), "layers": len(w.layers),
+                     **run_one(w, w.prompts, 20),
+                     "note": "layer_us: one gate, one select and one compaction for all prompts, then one "
+                             "attention call per layer; attention_us sums the 4 layers"}
+    del w
+    torch.cuda.empty_cache()
     return out
 
 
