@@ -36,6 +36,7 @@
 #include "tg_device.hpp"
 
 #include <limits.h>
+#include <utility>
 
 namespace tg {
 namespace {
@@ -59,6 +60,15 @@ __device__ __forceinline__ int key_tile_end(const int32_t* __restrict__ pos, int
 struct Item {
     int seg, qb, kvh, hg;
 };
+
+// f(integral_constant<int, I>) for I = B .. E-1, each index a compile-time constant.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 __device__ __forceinline__ Item decode_item(const AttnTable& t, int item, int hkv, int ngroups) {
     int s = 0;
@@ -186,43 +196,63 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
     const char* kbase = (const char*)(k + (off * hkv + kvh) * D);
     const char* vbase = (const char*)(v + (off * hkv + kvh) * D);
 
-    // Per-lane byte offsets of this wave's tile loads inside a tile (key row
-    // and swizzled chunk); the tile's first key moves the scalar base only.
-    uint32_t loff[TPW];
+    // Loads of one stage: wave w issues instructions w*TPW .. w*TPW+TPW-1 of
+    // the stage's NTL*IPT 1 KB instructions; instruction `inst` fills row
+    // group inst%IPT of tile inst/IPT (split tile/2; K for even, V for odd),
+    // at LDS offset inst*1 KB of the stage (tiles are laid out in that
+    // order). Inside row group rg a lane loads key row rg*RPI + lane/CH,
+    // chunk (lane%CH) ^ swz(row), which is the rg = 0 chunk with bits flipped
+    // by the constant swz(rg*RPI).
+    //
+    // Full stages (every key exists) use loop-invariant per-load lane offsets
+    // and one running scalar pointer per tile the wave loads, so a load costs
+    // one scalar add (its LDS destination) besides the instruction itself.
+    // A stage reaching past the segment's end (only the last one) re-reads
+    // the segment's last key for the missing rows (they are masked or
+    // skipped, never used) through the general per-lane computation.
+    constexpr int NTW = TPW >= IPT ? TPW / IPT : 1;  // tiles one wave loads per stage
+    static_assert(TPW % IPT == 0 || IPT % TPW == 0, "a wave's loads cover whole tiles or part of one");
+    const int first_tile = __builtin_amdgcn_readfirstlane((wave * TPW) / IPT);
+    const int64_t step_b = (int64_t)SPL * BN * rowb;  // bytes between a tile and the same tile one stage later
+    const char* tile_ptr0[NTW];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+        const int tile = first_tile + j;
+        tile_ptr0[j] = ((tile & 1) ? vbase : kbase) + (int64_t)(tile >> 1) * BN * rowb;
+    }
+    uint32_t voff[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-        const int inst = i * NW + wave;
+        const int inst = wave * TPW + i;
         const int rg = inst % IPT, kind = (inst / IPT) & 1;
-        const int row = rg * RPI + lane / CH;
-        const int chunk = (lane % CH) ^ (kind ? swz_v<CH>(row) : swz_k<CH>(row));
-        loff[i] = (uint32_t)(row * rowb + chunk * 16);
+        const uint32_t lo = (uint32_t)((lane / CH) * rowb + (((lane % CH) ^ (kind ? swz_v<CH>(lane / CH) : swz_k<CH>(lane / CH))) * 16));
+        const uint32_t flip = (uint32_t)((kind ? swz_v<CH>(rg * RPI) : swz_k<CH>(rg * RPI)) * 16);
+        voff[i] = (lo ^ flip) + (uint32_t)(rg * RPI * rowb);
     }
-
-    // Issue every load of iteration `it` into stage buffers at LDS byte
-    // addresses tl (tiles) and sm (bias/positions). The array each
-    // instruction writes follows from (i, wave); every wave issues exactly
-    // TPW + SPW loads per stage. Keys past the segment's end re-read its last
-    // key (only the last iteration has them, in a ragged tile or in a tile
-    // wholly past the end; they are masked or skipped, never used): there the
-    // scalar base moves to key min(r0, n-1), so every lane offset is >= 0.
-    auto issue = [&](int it, uint32_t tl, uint32_t sm) {
-        const bool full = (SPL * it + SPL) * BN <= n;
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int inst = i * NW + wave;   // this wave's i-th 1 KB load of the stage
-            const int tile_id = inst / IPT;   // split tile_id/2, K (even) or V (odd)
-            const int rg = inst % IPT;        // 1 KB row group of the tile
-            const int sp_ = tile_id >> 1, kind = tile_id & 1;
-            const int key0 = (SPL * it + sp_) * BN;   // first key of the tile
-            const int r0 = min(key0, n - 1);
-            const char* base = (kind ? vbase : kbase) + r0 * rowb;
-            uint32_t vo = loff[i];
-            if (!full) {
+    // bias/position loads: SPW per wave, small load id wave*SPW + i
+    const uint32_t wave_lds = (uint32_t)(wave * TPW * 1024);
+    auto issue = [&](int it, uint32_t tl, uint32_t sm) __attribute__((always_inline)) {
+        if ((SPL * it + SPL) * BN <= n) {
+            const int64_t adv = (int64_t)it * step_b;
+            const uint32_t ldsw = tl + wave_lds;
+            static_for<0, TPW>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int i = decltype(ic)::value;
+                dma16_so_at<i * 1024>(tile_ptr0[i * NTW / TPW] + adv, voff[i], ldsw);
+            });
+        } else {
+#pragma nounroll
+            for (int i = 0; i < TPW; ++i) {
+                const int inst = wave * TPW + i;
+                const int tile = inst / IPT, rg = inst % IPT;
+                const int sp_ = tile >> 1, kind = tile & 1;
+                const int key0 = (SPL * it + sp_) * BN;
+                const int r0 = min(key0, n - 1);
                 const int row = rg * RPI + lane / CH;
                 const int chunk = (lane % CH) ^ (kind ? swz_v<CH>(row) : swz_k<CH>(row));
-                vo = (uint32_t)((min(key0 + row, n - 1) - r0) * rowb + chunk * 16);
+                dma16_so((kind ? vbase : kbase) + (int64_t)r0 * rowb,
+                         (uint32_t)((min(key0 + row, n - 1) - r0) * rowb + chunk * 16),
+                         tl + (uint32_t)(inst * 1024));
             }
-            dma16_so(base, vo, tl + (uint32_t)((sp_ * 2 + kind) * TILEB + rg * 1024));
         }
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
@@ -237,6 +267,21 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
         }
     };
 
+    // Per-lane parts of the LDS operand addresses (stage base added per tile).
+    // K: key row l32 (+32 per 32-key block), chunk (2s + hh) ^ swz_k(row),
+    // which is the s = 0 chunk with bits flipped by 2s. V^T (transpose
+    // reads): lane L of group g = L/16 addresses key 16s + 4(g/2) + (L%16)/4
+    // (+8 for the upper four slots) at d = 32b + 16(g%2) + 4(L%4); the
+    // swizzled chunk of d-block b is the b = 0 chunk with bits flipped by 4b.
+    const uint32_t k_lane = (uint32_t)(l32 * ROWB + ((hh ^ swz_k<CH>(l32)) * 16));
+    uint32_t v_lane;
+    {
+        const int g = lane >> 4, r16 = lane & 15;
+        const int dsub = 16 * (g & 1) + 4 * (r16 & 3);
+        const int keyo = 4 * (g >> 1) + (r16 >> 2);
+        v_lane = (uint32_t)(keyo * ROWB + (((dsub >> 3) ^ swz_v<CH>(keyo)) * 16) + (dsub & 7) * 2);
+    }
+
     f32x16 acc_o[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b)
@@ -245,20 +290,32 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
     float m_run = -INFINITY, l_run = 0.0f;
 
     // One key tile for this wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
-    auto compute = [&](int kt, const char* kt_lds, const char* vt_lds, const uint32_t (*smv)[SM]) {
-        const LDS_AS char* kl = (const LDS_AS char*)kt_lds;
-        const LDS_AS char* vl = (const LDS_AS char*)vt_lds;
+    // Every LDS operand is read ahead of its use so that the read latency
+    // overlaps other work: the accumulator seeds and all K operands before the
+    // first q.k MFMA, the V^T operands right after the q.k MFMAs (the softmax
+    // runs while they arrive). sched_barrier keeps the compiler from sinking
+    // the reads back next to their uses.
+    auto compute = [&](int kt, const char* kt_lds, const char* vt_lds, const uint32_t (*smv)[SM])
+                       __attribute__((always_inline)) {
         const LDS_AS float* bsv = (const LDS_AS float*)smv[0];
         const LDS_AS int32_t* psv = (const LDS_AS int32_t*)smv[1];
-        if (kt >= n_tiles || psv[0] > wave_pos_hi) return;  // no visible key in this tile
-        // Element-wise masking only where some key may be invisible to some
-        // query of this wave: the ragged end, or keys past the first query.
-        const bool need_mask = (kt + 1) * BN > n || psv[BN - 1] > wave_pos_lo;
+        if (kt >= n_tiles) return;  // past the block's last visible key
+        // Positions never decrease along the kept rows, so keys before the
+        // block's first query row are visible to all of its queries: only tiles
+        // reaching row i0 (the ragged end among them) are masked element-wise.
+        const bool need_mask = (kt + 1) * BN > i0;
         // This head's bias term for the tile's keys, computed once per wave
         // (the wave reads it back below; its LDS accesses stay in order).
         static_assert(BN <= 64, "one lane per key");
         if (lane < BN) sbias[wave][lane] = bsv[lane] * gb;
+        // Operand addresses: XOR-swizzled chunks are one XOR away from the
+        // per-lane base. The empty asm makes the bases opaque per tile, so the
+        // compiler keeps one address register per kind instead of hoisting one
+        // per read and ring stage out of the loop.
+        uint32_t ka = LDS_ADDR(kt_lds) + k_lane, va = LDS_ADDR(vt_lds) + v_lane;
+        asm volatile("" : "+v"(ka), "+v"(va));
         f32x16 acc_s[KBN];
+        bf16x8 kf[KBN][KS];
 #pragma unroll
         for (int kb = 0; kb < KBN; ++kb) {
             // Register j of block kb holds key kb*32 + 8(j/4) + 4hh + j%4 of this lane's query.
@@ -268,16 +325,30 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc_s[kb][4 * g4 + e] = bb[e];
             }
-            const int row = kb * 32 + l32;
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int chunk = (2 * s + hh) ^ swz_k<CH>(row);
-                const bf16x8 a = *(const LDS_AS bf16x8*)(kl + row * ROWB + chunk * 16);
-                acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc_s[kb], 0, 0, 0);
+            for (int s = 0; s < KS; ++s)
+                kf[kb][s] = *(const LDS_AS bf16x8*)(uintptr_t)((ka ^ (uint32_t)(s << 5)) + kb * 32 * ROWB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < KBN; ++kb)
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][s], qf[s], acc_s[kb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 vf[DB][PS];
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+            const uint32_t vb = va ^ (uint32_t)(b << 6);
+#pragma unroll
+            for (int s = 0; s < PS; ++s) {
+                const v4i16 lo = lds_read_tr16((const LDS_AS char*)(uintptr_t)(vb + 16 * s * ROWB));
+                const v4i16 hi = lds_read_tr16((const LDS_AS char*)(uintptr_t)(vb + (16 * s + 8) * ROWB));
+                vf[b][s] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
         // acc_s now holds q.k + gb * bias; the exp2-domain logit is c times it.
-        float mx = -INFINITY;
         if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < KBN; ++kb) {
@@ -293,11 +364,15 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
                 }
             }
         }
+        float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < KBN; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) mx = fmaxf(mx, acc_s[kb][j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;  // c > 0: the max of the exp2-domain logits
+        {   // lanes l and l^32 hold the two halves of one query's keys
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;  // c > 0: max of the exp2-domain logits
+        }
         // The reference max only moves when some row's tile max exceeds it by
         // more than 8 (a factor 256): softmax does not depend on the
         // reference, and p <= 256 stays exact enough in fp32 and bf16. This
@@ -331,24 +406,10 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
             pf[s] = __builtin_bit_cast(bf16x8, w);
         }
         l_run += lsum;
-        // V^T operands by transpose reads: lane L of group g = L/16 addresses key
-        // 16s + 4(g/2) + (L%16)/4 (+8 for the upper four slots) at d = 32b + 16(g%2) + 4(L%4).
-        const int g = lane >> 4, r16 = lane & 15;
-        const int dsub = 16 * (g & 1) + 4 * (r16 & 3);
-        const int keyo = 4 * (g >> 1) + (r16 >> 2);
 #pragma unroll
-        for (int b = 0; b < DB; ++b) {
-            const int dd = 32 * b + dsub;              // element offset in the row
-            const int ch = dd >> 3, sub = (dd & 7) * 2;
+        for (int b = 0; b < DB; ++b)
 #pragma unroll
-            for (int s = 0; s < PS; ++s) {
-                const int ka = 16 * s + keyo, kb2 = ka + 8;
-                const v4i16 lo = lds_read_tr16(vl + ka * ROWB + ((ch ^ swz_v<CH>(ka)) * 16) + sub);
-                const v4i16 hi = lds_read_tr16(vl + kb2 * ROWB + ((ch ^ swz_v<CH>(kb2)) * 16) + sub);
-                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                acc_o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s], acc_o[b], 0, 0, 0);
-            }
-        }
+            for (int s = 0; s < PS; ++s) acc_o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[b][s], pf[s], acc_o[b], 0, 0, 0);
     };
 
     // Two-stage ring, one barrier per iteration: stage it%2 holds iteration

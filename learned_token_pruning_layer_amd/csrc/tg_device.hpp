@@ -56,6 +56,17 @@ __device__ __forceinline__ void dma4_so(const void* sbase, uint32_t voff, uint32
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
 }
+// The same with m0 = lds_base + IMM (one scalar add, no separate move).
+template <int IMM>
+__device__ __forceinline__ void dma16_so_at(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_add_u32 m0, %0, %3\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase), "n"(IMM)
+                 : "memory", "m0");
+}
+template <int IMM>
+__device__ __forceinline__ void dma4_so_at(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_add_u32 m0, %0, %3\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase), "n"(IMM)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // LDS byte address of a __shared__ object (the cast of a variable's address
