@@ -261,6 +261,64 @@ def gated_attention(q, k, v, bias, pos, seg_lens: Sequence[int], hq: int, hkv: i
 
 
 # ---------------------------------------------------------------------------
+# Next step after prefill: decode over the pruned KV cache.  [DE-prune] (the
+# layers above the gate build no KV for pruned tokens, so their cache holds
+# only the kept rows), [DE-attn] (each kept token's bias sits on the
+# attention logits of those layers), [DE-impl] (generation after a pruned
+# prefill). Readings: the bias stays on the cached keys' logits while
+# generating; newly generated tokens are not document tokens, so their bias
+# is 0; causality by original position as in prefill.
+# ---------------------------------------------------------------------------
+
+def decode_attention(q_new, k, v, bias, pos, segs: Sequence, hq: int, hkv: int, gain, tau: float):
+    """Attention of newly generated tokens over the pruned KV cache.
+
+    segs: (start, length, n_new) per sequence: cache rows
+    [start, start + length), whose last n_new rows are the new tokens
+    (appended before the call, with their own bias and position).
+    q_new[R, hq, D]: the new tokens' queries, sequence by sequence
+    (R = sum n_new). For new token t of a sequence (cache row
+    i = start + length - n_new + t) and query head h, kv = floor(h*hkv/hq):
+
+        l_j = q . k_j / (sqrt(D) * tau) + gain[h] * bias[j],
+              over cache rows j of the sequence with pos[j] <= pos[i]
+        o   = sum_j softmax(l)_j v_j,   lse = log sum_j exp(l_j)
+
+    Returns (o[R, hq, D], lse[hq, R]) in fp64, one query at a time.
+    """
+    if hq % hkv:
+        raise ValueError("hq must be a multiple of hkv")
+    qd, kd, vd = _f64(q_new), _f64(k), _f64(v)
+    b = _f64(bias).reshape(-1)
+    ps = np.asarray(pos.detach().cpu().numpy() if hasattr(pos, "detach") else pos, dtype=np.int64)
+    g = _f64(gain).reshape(-1)
+    n_out, _, dh = qd.shape
+    scale = 1.0 / (math.sqrt(dh) * float(tau))
+    o = np.zeros((n_out, hq, dh))
+    lse = np.zeros((hq, n_out))
+    r = 0
+    for start, length, n_new in segs:
+        start, length, n_new = int(start), int(length), int(n_new)
+        if not (0 <= n_new <= length):
+            raise ValueError("n_new outside [0, length]")
+        keys = np.arange(start, start + length)
+        for t in range(n_new):
+            i = start + length - n_new + t
+            vis = keys[ps[keys] <= ps[i]]
+            for h in range(hq):
+                kvh = (h * hkv) // hq
+                logits = (kd[vis, kvh, :] @ qd[r, h, :]) * scale + g[h] * b[vis]
+                mx = logits.max()
+                e = np.exp(logits - mx)
+                o[r, h, :] = (e @ vd[vis, kvh, :]) / e.sum()
+                lse[h, r] = mx + math.log(e.sum())
+            r += 1
+    if r != n_out:
+        raise ValueError("q_new rows do not match the segments' n_new")
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
 # The whole layer, in the pages' order.
 # ---------------------------------------------------------------------------
 

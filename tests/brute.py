@@ -88,3 +88,33 @@ def attention_multiplicative(q, k, v, s, is_doc, pos, seg_lens, hq, hkv, gain, t
                 lse[h][i] = math.log(den)
         off += ln
     return o, lse
+
+
+def decode_attention(q_new, k, v, bias, pos, segs, hq, hkv, gain, tau):
+    """Pure-Python decode over a cache: for each new token (the last n_new
+    rows of each segment) and head, o = sum_j w_j v_j / sum_j w_j with
+    w_j = exp(q.k_j / (sqrt(D) tau) + gain[h] bias[j]) over cache rows
+    j with pos[j] <= pos[new row]."""
+    d = len(k[0][0])
+    out, lse = [], [[] for _ in range(hq)]
+    r = 0
+    for start, length, n_new in segs:
+        for t in range(n_new):
+            i = start + length - n_new + t
+            row = []
+            for h in range(hq):
+                kv = (h * hkv) // hq
+                den, num = 0.0, [0.0] * d
+                for j in range(start, start + length):
+                    if pos[j] > pos[i]:
+                        continue
+                    dot = sum(q_new[r][h][c] * k[j][kv][c] for c in range(d))
+                    w = math.exp(dot / (math.sqrt(d) * tau) + gain[h] * bias[j])
+                    den += w
+                    for c in range(d):
+                        num[c] += w * v[j][kv][c]
+                row.append([x / den for x in num])
+                lse[h].append(math.log(den))
+            out.append(row)
+            r += 1
+    return out, lse

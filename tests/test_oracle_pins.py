@@ -357,6 +357,98 @@ def test_attention_sampled_rows_match_full():
     assert np.isnan(part[1]).all()
 
 
+# ---------------------------------------------------------------- decode ----
+
+def _decode_case(seed, segs, hq, hkv, d, n_new_max=3, pos_ties=False):
+    """Cache rows for `segs` (start, length, n_new) plus the new tokens' queries."""
+    m = max(st + ln for st, ln, _ in segs)
+    a = make_attention_inputs([m], hq, hkv, d, seed=seed, dtype=torch.float64, pos_ties=pos_ties)
+    pos = np.zeros(m, dtype=np.int64)
+    for st, ln, nn in segs:  # positions restart per sequence; new rows get bias 0
+        pos[st:st + ln] = a["pos"].numpy()[:ln]
+    bias = a["bias"].numpy().astype(np.float64)
+    for st, ln, nn in segs:
+        bias[st + ln - nn:st + ln] = 0.0
+    r = sum(nn for _, _, nn in segs)
+    q_new = torch.randn((r, hq, d), generator=torch.Generator().manual_seed(seed + 1), dtype=torch.float64)
+    return q_new.numpy(), a["k"].numpy(), a["v"].numpy(), bias, pos, a["gain"].numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (3, 1), (2, 2)])
+def test_decode_vs_bruteforce(hq, hkv):
+    segs = [(0, 9, 1), (9, 5, 2), (14, 1, 1), (15, 7, 3)]
+    q, k, v, b, pos, g = _decode_case(5, segs, hq, hkv, 4, pos_ties=True)
+    o, lse = oracle.decode_attention(q, k, v, b, pos, segs, hq, hkv, g, 0.9)
+    ob, lb = brute.decode_attention(q.tolist(), k.tolist(), v.tolist(), b.tolist(), pos.tolist(), segs,
+                                    hq, hkv, g.tolist(), 0.9)
+    np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lb, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_vs_sdpa_library():
+    """Each new token against its visible cache rows: torch SDPA (fp64) with
+    the additive float mask gain[h]*bias[j] and -inf on invisible rows."""
+    hq, hkv, d, tau = 4, 2, 16, 1.3
+    segs = [(0, 40, 2), (40, 25, 1)]
+    q, k, v, b, pos, g = _decode_case(11, segs, hq, hkv, d)
+    o, _ = oracle.decode_attention(q, k, v, b, pos, segs, hq, hkv, g, tau)
+    r = 0
+    for st, ln, nn in segs:
+        kk = torch.from_numpy(k[st:st + ln]).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None]
+        vv = torch.from_numpy(v[st:st + ln]).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None]
+        for t in range(nn):
+            i = st + ln - nn + t
+            vis = torch.from_numpy(pos[st:st + ln] <= pos[i])
+            mask = torch.where(vis[None, None, :], torch.from_numpy(g)[:, None, None] * torch.from_numpy(b[st:st + ln])[None, None, :],
+                               torch.tensor(-math.inf, dtype=torch.float64))
+            qq = torch.from_numpy(q[r]).reshape(hq, 1, d)[None]
+            ref = F.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask[None], scale=1.0 / (math.sqrt(d) * tau))
+            np.testing.assert_allclose(o[r], ref[0, :, 0, :].numpy(), rtol=1e-12, atol=1e-12)
+            r += 1
+
+
+def test_decode_closed_forms():
+    hq, hkv, d = 4, 2, 8
+    segs = [(0, 30, 1), (30, 1, 1), (31, 12, 2)]
+    q, k, v, b, pos, g = _decode_case(17, segs, hq, hkv, d)
+    # V = 1 => O = 1
+    o1, _ = oracle.decode_attention(q, k, np.ones_like(v), b, pos, segs, hq, hkv, g, 1.2)
+    np.testing.assert_allclose(o1, 1.0, rtol=0, atol=1e-14)
+    # a one-row cache: the new token sees only itself
+    o, lse = oracle.decode_attention(q, k, v, b, pos, segs, hq, hkv, g, 1.2)
+    for h in range(hq):
+        np.testing.assert_allclose(o[1, h], v[30, (h * hkv) // hq], rtol=1e-14)
+    # equal keys: weights exp(gain[h] * bias[j]), independent of q and tau
+    kk = np.repeat(k[:1], k.shape[0], axis=0)
+    for tau in (0.4, 5.0):
+        o2, _ = oracle.decode_attention(q, kk, v, b, pos, segs, hq, hkv, g, tau)
+        for h in range(hq):
+            w = np.exp(g[h] * b[0:30])
+            ref = (w[:, None] * v[0:30, (h * hkv) // hq]).sum(0) / w.sum()
+            np.testing.assert_allclose(o2[0, h], ref, rtol=1e-12)
+
+
+def test_decode_equals_prefill_last_rows():
+    """Two independent routes to the same numbers: the new tokens' rows of a
+    prefill over the cache (its queries filled in) equal the decode."""
+    hq, hkv, d = 4, 2, 8
+    segs = [(0, 21, 3), (21, 13, 1)]
+    q, k, v, b, pos, g = _decode_case(23, segs, hq, hkv, d, pos_ties=True)
+    m = 34
+    qfull = np.zeros((m, hq, d))
+    rows = []
+    r = 0
+    for st, ln, nn in segs:
+        for t in range(nn):
+            qfull[st + ln - nn + t] = q[r]
+            rows.append(st + ln - nn + t)
+            r += 1
+    o, lse = oracle.decode_attention(q, k, v, b, pos, segs, hq, hkv, g, 1.1)
+    of, lf = oracle.gated_attention(qfull, k, v, b, pos, [21, 13], hq, hkv, g, 1.1, rows=np.array(rows))
+    np.testing.assert_allclose(o, of[rows], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lf[:, rows], rtol=1e-12, atol=1e-13)
+
+
 # ---------------------------------------------------------- end to end ----
 
 def test_tiny_layer_end_to_end_invariants():
