@@ -188,6 +188,45 @@ tg_status tg_gated_attention(tg_dtype dt, const void* q, const void* k, const vo
                              float* lse, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* One cached sequence for decode (host memory): rows [start, start + len)
+ * of the KV cache of an above-gate layer (the kept rows of its pruned
+ * prefill, then the tokens generated since), whose last n_new rows are the
+ * tokens being decoded now. The caller appends their K, V, bias (0: they are
+ * not document tokens) and position before the call; their queries are the
+ * next n_new rows of q_new, sequence after sequence. */
+typedef struct {
+    int64_t start;
+    int32_t len;
+    int32_t n_new;
+} tg_kv_seq;
+
+/* Device workspace tg_decode_attention needs, in bytes (0 if no sequence
+ * has new tokens; also 0 for an invalid table, which the call reports). */
+size_t tg_decode_workspace_bytes(const tg_kv_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv,
+                                 int32_t head_dim);
+
+/* Decode over the pruned KV cache. For new token t of sequence b (cache row
+ * i = start + len - n_new + t) and query head h (KV head h / (hq / hkv)):
+ *     logit_j = q . k_j / (sqrt(head_dim) * tau) + gain[h] * bias[j]
+ * over the sequence's cache rows j with pos[j] <= pos[i], softmax, times V.
+ * q_new [R, hq, head_dim] (R = sum of n_new); k, v [rows, hkv, head_dim];
+ * out [R, hq, head_dim] (all contiguous, dtype dt; q_new, k, v 16-byte
+ * aligned); bias fp32 and pos int32 per cache row; gain fp32 [hq] (device);
+ * tau > 0; lse (nullable) fp32 [hq, R]. (hq / hkv) * n_new <= 8 per
+ * sequence; head_dim in {64, 128}. Workspace: device memory of at least
+ * tg_decode_workspace_bytes bytes, 4-byte aligned, owned by the caller
+ * (scratch; two calls in flight need two). Deterministic: the key splits
+ * are fixed by the table and merged in key order. Sources: section "Wie hat
+ * TokenGate das Pruning von Tokens verstanden?" (no KV for pruned tokens:
+ * the cache holds the kept rows), section "Was ist token-gated Attention?"
+ * (the kept tokens' bias on the logits above the gate) and "Wie wird
+ * TokenGate implementiert?" (generation after the pruned prefill). */
+tg_status tg_decode_attention(tg_dtype dt, const void* q_new, const void* k, const void* v,
+                              const float* bias, const int32_t* pos, const tg_kv_seq* seqs,
+                              int32_t n_seqs, int32_t hq, int32_t hkv, int32_t head_dim,
+                              const float* gain, float tau, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* Static text of a status code. */
 const char* tg_status_string(tg_status status);
 /* Detail of the last failure on the calling thread ("" if none). */

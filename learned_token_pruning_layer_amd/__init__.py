@@ -1,8 +1,9 @@
 """TokenGate pruned-prefill layer for MI355X (gfx950).
 
 The four steps (gate score, top-K select, compaction, token-gated
-attention) are HIP kernels behind the C ABI in include/tokengate.h; this
-package is the thin ctypes binding over it (argument marshalling only).
+attention) and decode over the pruned KV cache are HIP kernels behind the
+C ABI in include/tokengate.h; this package is the thin ctypes binding over
+it (argument marshalling only).
 """
 
 from ._lib import (  # noqa: F401
@@ -15,7 +16,9 @@ from ._lib import (  # noqa: F401
     TokenGateError,
     load,
     seq_array,
+    kv_seq_array,
     tg_compact,
+    tg_decode_attention,
     tg_gate_score,
     tg_gated_attention,
     tg_kept_rows,

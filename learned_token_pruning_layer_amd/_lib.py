@@ -25,7 +25,8 @@ TG_MAX_GATHERS = 16
 
 EXPORTED = (
     "tg_kept_rows", "tg_gate_score", "tg_select_workspace_bytes", "tg_select_topk", "tg_compact",
-    "tg_attention_workspace_bytes", "tg_gated_attention", "tg_status_string", "tg_last_error",
+    "tg_attention_workspace_bytes", "tg_gated_attention", "tg_decode_workspace_bytes", "tg_decode_attention",
+    "tg_status_string", "tg_last_error",
 )
 
 
@@ -39,6 +40,10 @@ class TokenGateError(RuntimeError):
 class TgSeq(ctypes.Structure):
     _fields_ = [("start", ctypes.c_int64), ("len", ctypes.c_int32), ("doc_begin", ctypes.c_int32),
                 ("doc_end", ctypes.c_int32), ("k_doc", ctypes.c_int32)]
+
+
+class TgKvSeq(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_int64), ("len", ctypes.c_int32), ("n_new", ctypes.c_int32)]
 
 
 class TgGather(ctypes.Structure):
@@ -74,6 +79,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tg_gated_attention.argtypes = [c_int, vp, vp, vp, vp, vp, seqp, i32, i32, i32, i32, vp, f32,
                                        vp, vp, vp, ctypes.c_size_t, vp]
     lib.tg_gated_attention.restype = c_int
+    kvp = ctypes.POINTER(TgKvSeq)
+    lib.tg_decode_workspace_bytes.argtypes = [kvp, i32, i32, i32, i32]
+    lib.tg_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.tg_decode_attention.argtypes = [c_int, vp, vp, vp, vp, vp, kvp, i32, i32, i32, i32, vp, f32,
+                                        vp, vp, vp, ctypes.c_size_t, vp]
+    lib.tg_decode_attention.restype = c_int
     lib.tg_status_string.argtypes = [c_int]
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_last_error.argtypes = []
@@ -242,4 +253,50 @@ def tg_gated_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias_k
                                   pos_kept.data_ptr(), sa, len(seqs), hq, hkv, dh, gain.data_ptr(), float(tau),
                                   out.data_ptr(), _ptr(lse if want_lse else None), _ptr(workspace),
                                   ws_bytes if workspace is not None else 0, _stream(stream)))
+    return out, (lse if want_lse else None)
+
+
+def kv_seq_array(seqs: Sequence) -> ctypes.Array:
+    """Decode sequences as a tg_kv_seq array: (start, len, n_new) tuples."""
+    arr = (TgKvSeq * max(1, len(seqs)))()
+    for i, (start, ln, n_new) in enumerate(seqs):
+        arr[i] = TgKvSeq(int(start), int(ln), int(n_new))
+    return arr
+
+
+def tg_decode_attention(q_new: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias: torch.Tensor,
+                        pos: torch.Tensor, seqs: Sequence, gain: torch.Tensor, tau: float,
+                        out: Optional[torch.Tensor] = None, want_lse: bool = False,
+                        lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Decode over the pruned KV cache.
+
+    q_new [R, hq, D] (the new tokens' queries, sequence by sequence);
+    k/v [rows, hkv, D], bias fp32 [rows], pos int32 [rows] (the cache, the
+    new tokens appended); seqs: (start, len, n_new) per sequence. Returns
+    (out [R, hq, D], lse [hq, R] or None)."""
+    lib = load()
+    for t, nm in ((q_new, "q_new"), (k, "k"), (v, "v"), (bias, "bias"), (pos, "pos"), (gain, "gain")):
+        _dev(t, nm)
+    r, hq, dh = q_new.shape
+    hkv = k.shape[1]
+    if k.dim() != 3 or k.shape[2] != dh or v.shape != k.shape:
+        raise ValueError("k and v must be [rows, hkv, D] matching q_new")
+    if k.dtype != q_new.dtype or v.dtype != q_new.dtype:
+        raise ValueError("q_new, k, v must share a dtype")
+    if bias.dtype != torch.float32 or pos.dtype != torch.int32 or gain.dtype != torch.float32:
+        raise ValueError("bias fp32, pos int32, gain fp32 expected")
+    if out is None:
+        out = torch.empty_like(q_new)
+    if want_lse and lse is None:
+        lse = torch.empty((hq, r), dtype=torch.float32, device=q_new.device)
+    sa = kv_seq_array(seqs)
+    ws_bytes = lib.tg_decode_workspace_bytes(sa, len(seqs), hq, hkv, dh)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q_new.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.tg_decode_attention(_dtype_code(q_new), q_new.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                   bias.data_ptr(), pos.data_ptr(), sa, len(seqs), hq, hkv, dh, gain.data_ptr(),
+                                   float(tau), out.data_ptr(), _ptr(lse if want_lse else None), _ptr(workspace),
+                                   ws_have, _stream(stream)))
     return out, (lse if want_lse else None)

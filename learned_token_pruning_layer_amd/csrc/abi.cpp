@@ -251,3 +251,111 @@ tg_status tg_gated_attention(tg_dtype dt, const void* q, const void* k, const vo
 }
 
 }  // extern "C"
+
+namespace {
+
+// Decode table: sequences with new tokens, their splits and output rows.
+tg_status build_decode_table(tg_dtype dt, const tg_kv_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv,
+                             int32_t head_dim, tg::DecTable* t, int64_t* r_total, size_t* ws_bytes) {
+    if (dt != TG_F32 && dt != TG_BF16) return fail(TG_ERR_INVALID_ARGUMENT, "dtype %d unknown", (int)dt);
+    if (hq <= 0 || hkv <= 0 || hq % hkv)
+        return fail(TG_ERR_INVALID_ARGUMENT, "hq=%d must be a positive multiple of hkv=%d", hq, hkv);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(TG_ERR_UNSUPPORTED, "head_dim=%d (built: 64, 128)", head_dim);
+    if (n_seqs < 0 || n_seqs > TG_MAX_SEQS)
+        return fail(TG_ERR_INVALID_ARGUMENT, "n_seqs=%d outside [0, %d]", n_seqs, TG_MAX_SEQS);
+    if (n_seqs > 0 && !seqs) return fail(TG_ERR_INVALID_ARGUMENT, "seqs is NULL");
+    memset(t, 0, sizeof *t);
+    const int g = hq / hkv;
+    int64_t rows = 0, keys = 0;
+    int nq_max = 0;
+    for (int b = 0; b < n_seqs; ++b) {
+        const tg_kv_seq& s = seqs[b];
+        if (s.start < 0 || s.len < 0 || s.n_new < 0 || s.n_new > s.len)
+            return fail(TG_ERR_INVALID_ARGUMENT, "sequence %d: start=%lld len=%d n_new=%d", b, (long long)s.start,
+                        s.len, s.n_new);
+        if (s.n_new == 0) continue;
+        if (tg::decode_query_slots(g * s.n_new) == 0)
+            return fail(TG_ERR_UNSUPPORTED, "sequence %d: (hq/hkv) * n_new = %d > 8", b, g * s.n_new);
+        nq_max = nq_max > g * s.n_new ? nq_max : g * s.n_new;
+        keys += s.len;
+        tg::DecSeq& d = t->s[t->n++];
+        d.start = s.start;
+        d.len = s.len;
+        d.n_new = s.n_new;
+        d.q_row0 = (int32_t)rows;
+        rows += s.n_new;
+    }
+    if (rows > (int64_t)INT32_MAX / hq) return fail(TG_ERR_UNSUPPORTED, "too many new tokens for one launch");
+    *r_total = rows;
+    t->nq_max = nq_max;
+    if (t->n == 0) {
+        *ws_bytes = 0;
+        return TG_OK;
+    }
+    // Keys per split: a power of two, a multiple of the keys one wave's lane
+    // groups take per block, sized for about 4096 waves in all and for at
+    // most 256 splits per sequence (the merge walks a query's splits).
+    const int esize = dt == TG_BF16 ? 2 : 4;
+    const int lpk = head_dim * esize / 16;
+    const int granule = (64 / lpk) * 8;
+    int64_t max_len = 0;
+    for (int b = 0; b < t->n; ++b) max_len = max_len > t->s[b].len ? max_len : t->s[b].len;
+    int64_t kpw = granule;
+    while (kpw < (1 << 20) && (kpw * 4096 < keys * hkv || kpw * 256 < max_len)) kpw *= 2;
+    t->kpw = (int32_t)kpw;
+    int64_t splits = 0;
+    for (int b = 0; b < t->n; ++b) {
+        t->s[b].split_base = (int32_t)splits;
+        splits += (t->s[b].len + kpw - 1) / kpw;
+    }
+    if (splits * hkv > (int64_t)INT32_MAX / 2) return fail(TG_ERR_UNSUPPORTED, "too many splits for one launch");
+    t->n_waves = (int32_t)(splits * hkv);
+    const int nq = tg::decode_query_slots(nq_max);
+    *ws_bytes = (size_t)t->n_waves * nq * (head_dim + 2) * sizeof(float);
+    return TG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tg_decode_workspace_bytes(const tg_kv_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv, int32_t head_dim) {
+    tg::DecTable t;
+    int64_t r = 0;
+    size_t ws = 0;
+    if (build_decode_table(TG_BF16, seqs, n_seqs, hq, hkv, head_dim, &t, &r, &ws) != TG_OK) return 0;
+    size_t ws32 = 0;
+    build_decode_table(TG_F32, seqs, n_seqs, hq, hkv, head_dim, &t, &r, &ws32);
+    g_err.clear();
+    return ws > ws32 ? ws : ws32;  // enough for either dtype
+}
+
+tg_status tg_decode_attention(tg_dtype dt, const void* q_new, const void* k, const void* v, const float* bias,
+                              const int32_t* pos, const tg_kv_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv,
+                              int32_t head_dim, const float* gain, float tau, void* out, float* lse,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_err.clear();
+    if (!(tau > 0.0f) || tau != tau || tau > 3.0e38f)
+        return fail(TG_ERR_INVALID_ARGUMENT, "tau must be finite and > 0");
+    tg::DecTable t;
+    int64_t r_total = 0;
+    size_t need = 0;
+    tg_status st = build_decode_table(dt, seqs, n_seqs, hq, hkv, head_dim, &t, &r_total, &need);
+    if (st != TG_OK) return st;
+    if (t.n == 0) return TG_OK;
+    if (!q_new || !k || !v || !bias || !pos || !gain || !out)
+        return fail(TG_ERR_INVALID_ARGUMENT, "q_new, k, v, bias, pos, gain, out must be non-NULL");
+    if (!(aligned16(q_new) && aligned16(k) && aligned16(v)))
+        return fail(TG_ERR_UNSUPPORTED, "q_new, k, v must be 16-byte aligned");
+    if (!workspace || workspace_bytes < need)
+        return fail(TG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                    need);
+    if ((uintptr_t)workspace % 4 != 0) return fail(TG_ERR_INVALID_ARGUMENT, "workspace not 4-byte aligned");
+    hipError_t e = tg::launch_decode(dt, q_new, k, v, bias, pos, t, hq, hkv, head_dim, gain, tau, out, lse, r_total,
+                                     workspace, stream);
+    if (e != hipSuccess) return hip_fail(e, "tg_decode_attention launch");
+    return TG_OK;
+}
+
+}  // extern "C"

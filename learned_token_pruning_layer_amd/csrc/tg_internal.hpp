@@ -95,6 +95,27 @@ hipError_t launch_attention(tg_dtype dt, const void* q, const void* k, const voi
                             int hkv, int head_dim, const float* gain, float tau, void* out,
                             float* lse, hipStream_t st);
 
+// Decode over the pruned KV cache: one entry per sequence with new tokens.
+struct DecSeq {
+    int64_t start;       // first cache row
+    int32_t len;         // cache rows (the new tokens are the last n_new)
+    int32_t n_new;
+    int32_t q_row0;      // first row of q_new / out for this sequence
+    int32_t split_base;  // first global split id (splits of kpw keys)
+};
+struct DecTable {
+    int32_t n;
+    int32_t kpw;      // keys per split (one wave per split and KV head)
+    int32_t n_waves;  // splits x KV heads
+    int32_t nq_max;   // largest (hq/hkv) * n_new over the sequences
+    DecSeq s[TG_MAX_SEQS];
+};
+// Query slots per wave for nq queries (0: more than supported).
+int decode_query_slots(int nq);
+hipError_t launch_decode(tg_dtype dt, const void* q, const void* k, const void* v, const float* bias,
+                         const int32_t* pos, const DecTable& t, int hq, int hkv, int head_dim, const float* gain,
+                         float tau, void* out, float* lse, int64_t r_total, void* ws, hipStream_t st);
+
 // Query-row block per attention work item for a given dtype/head ratio.
 int attention_block_rows(tg_dtype dt, int hq, int hkv);
 int attention_heads_per_item(tg_dtype dt, int hq, int hkv);

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(tg.EXPORTED)
@@ -81,6 +81,36 @@ def test_select_rejects_before_launch(lib):
     assert lib.tg_select_topk(fake, seq_array(long), 3, fake, None, 0, None) == WORKSPACE
     assert b"needed" in lib.tg_last_error()
     assert lib.tg_select_topk(fake, seq_array(long), 3, fake, fake, need - 1, None) == WORKSPACE
+
+
+def test_decode_table_and_rejects_before_launch(lib):
+    from learned_token_pruning_layer_amd._lib import kv_seq_array
+    # Workspace: one partial (max, sum, O[D]) per query slot for each wave;
+    # a wave covers kpw keys of one (sequence, KV head). 16 heads over 8 KV
+    # heads with one new token: 2 query slots. kpw is the smallest power of
+    # two >= 32 (bf16, head_dim 128: 4 lane groups x 8 keys) giving at most
+    # ~4096 waves and at most 256 splits per sequence: 9152 rows -> 64, so
+    # 143 + 47 splits for 9152 + 3000 rows.
+    segs = [(0, 9152, 1), (9152, 3000, 1), (12152, 10, 0)]
+    need = lib.tg_decode_workspace_bytes(kv_seq_array(segs), 3, 16, 8, 128)
+    assert need == (143 + 47) * 8 * 2 * (128 + 2) * 4
+    assert lib.tg_decode_workspace_bytes(kv_seq_array([(0, 5, 0)]), 1, 16, 8, 128) == 0
+    fake = ctypes.c_void_p(4096)
+    args = (fake, fake, fake, fake, fake, kv_seq_array(segs), 3, 16, 8, 128, fake, 1.0, fake, None)
+    assert lib.tg_decode_attention(1, *args, None, 0, None) == WORKSPACE
+    assert lib.tg_decode_attention(1, *args, fake, need - 4, None) == WORKSPACE
+    # (hq/hkv) * n_new above 8, n_new beyond the cache, bad head_dim, bad tau
+    assert lib.tg_decode_attention(1, fake, fake, fake, fake, fake, kv_seq_array([(0, 9, 5)]), 1, 16, 8, 128,
+                                   fake, 1.0, fake, None, fake, 1 << 20, None) == UNSUPPORTED
+    assert lib.tg_decode_attention(1, fake, fake, fake, fake, fake, kv_seq_array([(0, 3, 4)]), 1, 16, 8, 128,
+                                   fake, 1.0, fake, None, fake, 1 << 20, None) == INVALID
+    assert lib.tg_decode_attention(1, fake, fake, fake, fake, fake, kv_seq_array([(0, 3, 1)]), 1, 16, 8, 96,
+                                   fake, 1.0, fake, None, fake, 1 << 20, None) == UNSUPPORTED
+    assert lib.tg_decode_attention(1, fake, fake, fake, fake, fake, kv_seq_array([(0, 3, 1)]), 1, 16, 8, 128,
+                                   fake, 0.0, fake, None, fake, 1 << 20, None) == INVALID
+    # nothing to decode: OK without any pointer
+    assert lib.tg_decode_attention(1, None, None, None, None, None, kv_seq_array([(0, 3, 0)]), 1, 16, 8, 128,
+                                   None, 1.0, None, None, None, 0, None) == 0
 
 
 def test_gate_rejects_before_launch(lib):

@@ -485,3 +485,73 @@ def test_end_to_end_ragged_four_layers():
         o, _ = oracle.gated_attention(qk.view(m, 16, 128), kk.view(m, 8, 128), vk.view(m, 8, 128), bias, pk,
                                       seg, 16, 8, wl.gain.cpu(), wl.tau, rows=rows)
         assert_rowmax_close(f64(lay.outs[i])[rows], o[rows])
+
+
+# ---------------------------------------------------------------- decode ----
+
+def decode_inputs(segs, hq, hkv, d, seed, dtype=torch.bfloat16, pos_ties=False):
+    """A KV cache holding `segs` (start, len, n_new); the new rows carry bias 0."""
+    rows = max(st + ln for st, ln, _ in segs)
+    a = make_attention_inputs([rows], hq, hkv, d, seed=seed, dtype=dtype, pos_ties=pos_ties)
+    pos = torch.zeros(rows, dtype=torch.int32)
+    bias = a["bias"].clone()
+    for st, ln, nn in segs:
+        pos[st:st + ln] = a["pos"][:ln]
+        bias[st + ln - nn:st + ln] = 0.0
+    r = sum(nn for _, _, nn in segs)
+    gq = torch.Generator().manual_seed(seed + 7)
+    q_new = torch.randn((r, hq, d), generator=gq).to(dtype)
+    return q_new, a["k"], a["v"], bias, pos, a["gain"]
+
+
+def check_decode(segs, hq, hkv, d, seed, dtype=torch.bfloat16, pos_ties=False, tau=1.2):
+    q, k, v, bias, pos, gain = decode_inputs(segs, hq, hkv, d, seed, dtype, pos_ties)
+    out, lse = tg.tg_decode_attention(q.to(DEV), k.to(DEV), v.to(DEV), bias.to(DEV), pos.to(DEV), segs,
+                                      gain.to(DEV), tau, want_lse=True)
+    ref, ref_lse = oracle.decode_attention(f64(q), f64(k), f64(v), f64(bias), pos.numpy(), segs, hq, hkv,
+                                           f64(gain), tau)
+    got = f64(out)
+    if dtype == torch.bfloat16:
+        assert_rowmax_close(got, ref)
+    else:
+        assert np.abs(got - ref).max() <= 1e-4
+    assert np.abs(f64(lse) - ref_lse).max() <= 1e-3 * max(1.0, np.abs(ref_lse).max())
+    return out
+
+
+def test_decode_qwen_shapes_single_and_ragged():
+    note("decode bf16 16/8 heads D=128: one 9152-row cache, then ragged caches with 1..4 new tokens")
+    check_decode([(0, 9152, 1)], 16, 8, 128, seed=1)
+    check_decode([(0, 1, 1), (1, 33, 2), (34, 1000, 3), (1034, 5000, 4), (6034, 77, 1)], 16, 8, 128, seed=2)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (16, 4, 64), (8, 1, 64), (6, 3, 128)])
+def test_decode_head_ratios(hq, hkv, d):
+    note(f"decode bf16 hq={hq} hkv={hkv} D={d}")
+    n_new = max(1, 8 // (hq // hkv))
+    check_decode([(5, 700, n_new), (900, 64, 1), (964, 1, 1)], hq, hkv, d, seed=hq + d)
+
+
+def test_decode_position_ties_and_fp32():
+    note("decode: repeated positions (bf16), fp32 tiny shapes")
+    check_decode([(0, 513, 3), (513, 40, 2)], 4, 2, 64, seed=5, pos_ties=True)
+    check_decode([(0, 176, 1), (176, 90, 2)], 4, 2, 64, seed=6, dtype=torch.float32)
+    check_decode([(0, 300, 2)], 4, 4, 128, seed=7, dtype=torch.float32)
+
+
+def test_decode_deterministic_and_matches_prefill_rows():
+    note("decode: bitwise repeatable; equals the prefill kernel's last rows within the bf16 bar")
+    segs = [(0, 2384, 1), (2384, 1500, 2)]
+    o1 = check_decode(segs, 16, 8, 128, seed=11)
+    o2 = check_decode(segs, 16, 8, 128, seed=11)
+    assert torch.equal(o1, o2)
+    # the prefill kernel over the same cache, its queries filled in for the new rows
+    q, k, v, bias, pos, gain = decode_inputs(segs, 16, 8, 128, seed=11)
+    qfull = torch.zeros((3884, 16, 128), dtype=torch.bfloat16)
+    qfull[2383] = q[0]
+    qfull[3882:3884] = q[1:3]
+    prompts = [Prompt(0, 2384, 0, 0, 0), Prompt(2384, 1500, 0, 0, 0)]
+    pre, _ = tg.tg_gated_attention(qfull.to(DEV), k.to(DEV), v.to(DEV), bias.to(DEV), pos.to(DEV), prompts,
+                                   gain.to(DEV), 1.2)
+    rows = [2383, 3882, 3883]
+    assert_rowmax_close(f64(o1), f64(pre[rows]), rel=2e-2)
