@@ -24,9 +24,10 @@ MUTATIONS = [
     ("SiLU with the wrong sign", "return z * sigmoid(z)", "return z * sigmoid(-z)"),
     ("ties broken towards the higher row", "order = np.lexsort((doc, neg, is_nan))",
      "order = np.lexsort((-doc, neg, is_nan))"),
-    ("query head mapped to the wrong KV head", "kvh = (h * hkv) // hq", "kvh = h % hkv"),
-    ("scale 1/(D tau) instead of 1/(sqrt(D) tau)", "scale = 1.0 / (math.sqrt(dh) * float(tau))",
-     "scale = 1.0 / (dh * float(tau))"),
+    ("query head mapped to the wrong KV head", "kvh = (h * hkv) // hq\n            kh, vh",
+     "kvh = h % hkv\n            kh, vh"),
+    ("scale 1/(D tau) instead of 1/(sqrt(D) tau)", "scale = 1.0 / (math.sqrt(dh) * float(tau))\n    o = np.full",
+     "scale = 1.0 / (dh * float(tau))\n    o = np.full"),
     ("log-sigmoid with the wrong sign of the log term", "np.minimum(s, 0.0) - np.log1p",
      "np.minimum(s, 0.0) + np.log1p"),
     ("bias also on question keys", "bias[is_doc] = logsigmoid(sk[is_doc])", "bias[:] = logsigmoid(sk)"),
@@ -34,6 +35,14 @@ MUTATIONS = [
      "keep_doc = doc[order[-p.k_doc:]] if p.k_doc else doc[:0]"),
     ("second gate bias dropped", "out[r0:r0 + xb.shape[0]] = silu(h) @ w2 + float(b2)",
      "out[r0:r0 + xb.shape[0]] = silu(h) @ w2"),
+    ("decode: kept-token bias dropped", "* scale + g[h] * b[vis]", "* scale"),
+    ("decode: a new token does not see itself", "vis = keys[ps[keys] <= ps[i]]", "vis = keys[ps[keys] < ps[i]]"),
+    ("decode: queries placed at the first rows of the cache", "            i = start + length - n_new + t",
+     "            i = start + t"),
+    ("decode: query head mapped to the wrong KV head", "kvh = (h * hkv) // hq\n                logits",
+     "kvh = h % hkv\n                logits"),
+    ("decode: scale 1/(D tau)", "scale = 1.0 / (math.sqrt(dh) * float(tau))\n    o = np.zeros",
+     "scale = 1.0 / (dh * float(tau))\n    o = np.zeros"),
 ]
 
 
