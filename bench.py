@@ -233,6 +233,8 @@ def measure_extras(torch, tg, layer, w, steps, dev):
                             "p90": round(pct(cold, 0.9), 2),
                             "note": "a 1 GiB device write before each step evicts the Infinity Cache"}
     del src, dst
+    # Decode after this prefill: one new token over the kept K/V cache.
+    out["decode_qwen16k"] = measure_decode(torch, tg, layer, timed, pct)
     # Select on one prompt of 2^24 document rows: the multi-workgroup path
     # (1024 chunks of 16384 rows), arguments marshalled once outside the
     # timed region.
@@ -265,6 +267,60 @@ def measure_extras(torch, tg, layer, w, steps, dev):
     return out
 
 
+def measure_decode(torch, tg, lay, timed, pct, reps=50):
+    """One decode step per prompt over the layer's KV cache: the kept K/V
+    rows of the pruned prefill with one new token appended (bias 0, next
+    position). Algorithmic bytes: every cached K and V row once per KV head,
+    plus its bias and position."""
+    from learned_token_pruning_layer_amd._lib import kv_seq_array
+    _, kk, vk = lay.qkv_kept[0]
+    hq, hkv, dh = lay.hq, lay.hkv, lay.head_dim
+    dev = kk.device
+    segs, rows, off = [], [], 0
+    for p in lay.prompts:
+        n = p.k_doc + p.length - (p.doc_end - p.doc_begin)
+        rows.append((off, n))
+        off += n
+    total = off + len(rows)
+    k = torch.empty((total, hkv, dh), dtype=kk.dtype, device=dev)
+    v = torch.empty_like(k)
+    bias = torch.zeros(total, dtype=torch.float32, device=dev)
+    pos = torch.empty(total, dtype=torch.int32, device=dev)
+    g = torch.Generator(device=dev).manual_seed(5)
+    dst = 0
+    for (src, n) in rows:  # cache of this prompt, then its new token
+        k[dst:dst + n] = kk[src:src + n].view(n, hkv, dh)
+        v[dst:dst + n] = vk[src:src + n].view(n, hkv, dh)
+        bias[dst:dst + n] = lay.bias_kept[src:src + n]
+        pos[dst:dst + n] = lay.pos_kept[src:src + n]
+        k[dst + n] = torch.randn((hkv, dh), generator=g, device=dev).to(kk.dtype)
+        v[dst + n] = torch.randn((hkv, dh), generator=g, device=dev).to(kk.dtype)
+        pos[dst + n] = pos[dst + n - 1] + 1
+        segs.append((dst, n + 1, 1))
+        dst += n + 1
+    q = torch.randn((len(segs), hq, dh), generator=g, device=dev).to(kk.dtype)
+    out = torch.empty_like(q)
+    lib = tg.load()
+    sa = kv_seq_array(segs)
+    wsb = lib.tg_decode_workspace_bytes(sa, len(segs), hq, hkv, dh)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    gain = lay.layers[0].gain
+    st = torch.cuda.current_stream().cuda_stream
+    args = (1 if kk.dtype == torch.bfloat16 else 0, q.data_ptr(), k.data_ptr(), v.data_ptr(), bias.data_ptr(),
+            pos.data_ptr(), sa, len(segs), hq, hkv, dh, gain.data_ptr(), float(lay.layers[0].tau),
+            out.data_ptr(), None, ws.data_ptr(), wsb, st)
+
+    def call():
+        if lib.tg_decode_attention(*args) != 0:
+            raise RuntimeError(lib.tg_last_error().decode())
+
+    call()
+    us = pct(timed(call, reps), 0.5)
+    byts = total * hkv * dh * k.element_size() * 2 + total * 8
+    return {"cache_rows": total, "us": round(us, 2), "algorithmic_gb_s": round(byts / (us * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def measure_configs(torch, tg, dev, timed, pct):
     """The other workloads, timed the same way (whole layer and attention
     alone, p50 of event-timed reps): the 32k budget sweep, 128k at 6.25%
@@ -275,7 +331,7 @@ def measure_configs(torch, tg, dev, timed, pct):
     def causal_flops(prompts, hq, dh):
         return sum(4 * dh * hq * p.n_kept * (p.n_kept + 1) // 2 for p in prompts)
 
-    def run_one(w, prompts, reps, attn_reps=None):
+    def run_one(w, prompts, reps, attn_reps=None, decode=False):
         lay = tg.GatedPrefillLayer(w.x, w.w1, w.w2, prompts, w.layers, w.hq, w.hkv, w.head_dim)
         lay.run()
         t_layer = pct(timed(lay.run, reps), 0.5)
@@ -283,6 +339,8 @@ def measure_configs(torch, tg, dev, timed, pct):
         fl = causal_flops(prompts, w.hq, w.head_dim) * len(w.layers)
         rec = {"kept_rows": lay.m, "layer_us": round(t_layer, 1), "attention_us": round(t_attn, 1),
                "attention_tflops": round(fl / (t_attn * 1e-6) / 1e12, 1)}
+        if decode:
+            rec["decode_one_token"] = measure_decode(torch, tg, lay, timed, pct)
         del lay
         return rec
 
@@ -298,16 +356,17 @@ def measure_configs(torch, tg, dev, timed, pct):
     torch.cuda.empty_cache()
     w = make_workload("long128k", device=dev)
     p0 = w.prompts[0]
-    pruned = run_one(w, w.prompts, 20)
-    full = run_one(w, [p0._replace(k_doc=p0.n_doc)], 3, attn_reps=3)
+    pruned = run_one(w, w.prompts, 20, decode=True)
+    full = run_one(w, [p0._replace(k_doc=p0.n_doc)], 3, attn_reps=3, decode=True)
     out["long128k"] = {"n_rows": w.n_rows, "k_doc": p0.k_doc, **pruned,
-                       "unpruned": {k: full[k] for k in ("kept_rows", "attention_us", "attention_tflops")},
+                       "unpruned": {k: full[k] for k in ("kept_rows", "attention_us", "attention_tflops",
+                                                         "decode_one_token")},
                        "unpruned_attention_over_pruned_layer": round(full["attention_us"] / pruned["layer_us"], 1)}
     del w
     torch.cuda.empty_cache()
     w = make_workload("ragged", device=dev)
     out["ragged"] = {"n_rows": w.n_rows, "prompts": len(w.prompts), "layers": len(w.layers),
-                     **run_one(w, w.prompts, 20),
+                     **run_one(w, w.prompts, 20, decode=True),
                      "note": "layer_us: one gate, one select and one compaction for all prompts, then one "
                              "attention call per layer; attention_us sums the 4 layers"}
     del w
