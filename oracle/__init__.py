@@ -9,10 +9,12 @@ from .tokengate import (  # noqa: F401
     decode_attention,
     gate_scores,
     gated_attention,
+    gated_attention_backward,
     gated_prefill,
     kept_rows,
     logsigmoid,
     prompt_of_rows,
+    score_grad,
     select_topk,
     sigmoid,
     silu,

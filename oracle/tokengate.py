@@ -261,6 +261,87 @@ def gated_attention(q, k, v, bias, pos, seg_lens: Sequence[int], hq: int, hkv: i
 
 
 # ---------------------------------------------------------------------------
+# Backward of token-gated attention, and the bias -> score chain.  [DE-attn]
+# (the bias on the logits is what gives the gradient a path back to the
+# scorer, like a mixture-of-experts router), [TH-how] (same: the kept
+# tokens' scores become the bias so the gradient reaches the scorer).
+# ---------------------------------------------------------------------------
+
+def gated_attention_backward(q, k, v, bias, pos, seg_lens: Sequence[int], hq: int, hkv: int,
+                             gain, tau: float, d_out):
+    """Gradients of sum(d_out * o) through token-gated attention.
+
+    Same inputs as gated_attention, plus d_out[M, hq, D]. With
+    l_ij = q_i.k_j * c + gain[h] * bias[j], c = 1 / (sqrt(D) * tau), over
+    visible keys, p = softmax_j(l), o_i = sum_j p_ij v_j:
+
+        dv_j    = sum_{h in group, i} p_ij do_i
+        dp_ij   = do_i . v_j
+        ds_ij   = p_ij (dp_ij - sum_j' p_ij' dp_ij')     (= p_ij (dp_ij - do_i . o_i))
+        dq_i    = c * sum_j ds_ij k_j
+        dk_j    = c * sum_{h in group, i} ds_ij q_i
+        dbias_j = sum_h gain[h] sum_i ds_ij
+        dgain_h = sum_{i,j} ds_ij bias[j]
+        dtau    = -(1/tau) * sum_{h,i,j} ds_ij (q_i.k_j * c)
+
+    Returns dict(dq, dk, dv, dbias, dgain, dtau) in fp64.
+    """
+    if hq % hkv:
+        raise ValueError("hq must be a multiple of hkv")
+    qd, kd, vd, dod = _f64(q), _f64(k), _f64(v), _f64(d_out)
+    b = _f64(bias).reshape(-1)
+    ps = np.asarray(pos.detach().cpu().numpy() if hasattr(pos, "detach") else pos, dtype=np.int64)
+    g = _f64(gain).reshape(-1)
+    m_tot, _, dh = qd.shape
+    c = 1.0 / (math.sqrt(dh) * float(tau))
+    dq = np.zeros_like(qd)
+    dk = np.zeros_like(kd)
+    dv = np.zeros_like(vd)
+    dbias = np.zeros(m_tot)
+    dgain = np.zeros(hq)
+    dtau = 0.0
+    off = 0
+    for ln in seg_lens:
+        ln = int(ln)
+        seg = slice(off, off + ln)
+        vis = ps[seg][None, :] <= ps[seg][:, None]          # [query, key]
+        for h in range(hq):
+            kvh = (h * hkv) // hq
+            qk = qd[seg, h, :] @ kd[seg, kvh, :].T            # q_i . k_j
+            logits = np.where(vis, qk * c + g[h] * b[seg][None, :], -np.inf)
+            e = np.exp(logits - logits.max(axis=1, keepdims=True))
+            p = e / e.sum(axis=1, keepdims=True)
+            o = p @ vd[seg, kvh, :]
+            do = dod[seg, h, :]
+            dp = do @ vd[seg, kvh, :].T
+            ds = p * (dp - (do * o).sum(axis=1, keepdims=True))
+            dv[seg, kvh, :] += p.T @ do
+            dq[seg, h, :] += c * (ds @ kd[seg, kvh, :])
+            dk[seg, kvh, :] += c * (ds.T @ qd[seg, h, :])
+            dbias[seg] += g[h] * ds.sum(axis=0)
+            dgain[h] += (ds.sum(axis=0) * b[seg]).sum()
+            dtau += -(1.0 / float(tau)) * (ds * qk * c).sum()
+        off += ln
+    return dict(dq=dq, dk=dk, dv=dv, dbias=dbias, dgain=dgain, dtau=dtau)
+
+
+def score_grad(dbias_kept, scores, kept, prompts: Sequence) -> np.ndarray:
+    """d(scores) from d(bias_kept): bias = logsigmoid(s) for kept document
+    rows, whose derivative is sigmoid(-s); question rows carry a constant 0
+    bias and pruned rows no bias at all, so both get 0."""
+    s = _f64(scores).reshape(-1)
+    db = _f64(dbias_kept).reshape(-1)
+    kept = np.asarray(kept, dtype=np.int64)
+    out = np.zeros_like(s)
+    owner = prompt_of_rows(kept, prompts)
+    for m, r in enumerate(kept):
+        p = prompts[owner[m]]
+        if p.start + p.doc_begin <= r < p.start + p.doc_end:
+            out[r] = db[m] * sigmoid(-s[r])
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Next step after prefill: decode over the pruned KV cache.  [DE-prune] (the
 # layers above the gate build no KV for pruned tokens, so their cache holds
 # only the kept rows), [DE-attn] (each kept token's bias sits on the

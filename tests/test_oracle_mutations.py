@@ -43,6 +43,13 @@ MUTATIONS = [
      "kvh = h % hkv\n                logits"),
     ("decode: scale 1/(D tau)", "scale = 1.0 / (math.sqrt(dh) * float(tau))\n    o = np.zeros",
      "scale = 1.0 / (dh * float(tau))\n    o = np.zeros"),
+    ("backward: softmax Jacobian without its row term", "ds = p * (dp - (do * o).sum(axis=1, keepdims=True))",
+     "ds = p * dp"),
+    ("backward: dk without the logit scale", "dk[seg, kvh, :] += c * (ds.T @ qd[seg, h, :])",
+     "dk[seg, kvh, :] += ds.T @ qd[seg, h, :]"),
+    ("backward: bias gradient without the gain", "dbias[seg] += g[h] * ds.sum(axis=0)", "dbias[seg] += ds.sum(axis=0)"),
+    ("backward: temperature gradient with the wrong sign", "dtau += -(1.0 / float(tau))", "dtau += (1.0 / float(tau))"),
+    ("score gradient through sigmoid(+s)", "out[r] = db[m] * sigmoid(-s[r])", "out[r] = db[m] * sigmoid(s[r])"),
 ]
 
 

@@ -357,6 +357,106 @@ def test_attention_sampled_rows_match_full():
     assert np.isnan(part[1]).all()
 
 
+# -------------------------------------------------------------- backward ----
+
+def _bwd_case(seed, seg, hq, hkv, d, pos_ties=True):
+    m = sum(seg)
+    a = make_attention_inputs(seg, hq, hkv, d, seed=seed, dtype=torch.float64, pos_ties=pos_ties, n_query_tail=2)
+    gd = torch.Generator().manual_seed(seed + 3)
+    d_out = torch.randn((m, hq, d), generator=gd, dtype=torch.float64).numpy()
+    return (a["q"].numpy(), a["k"].numpy(), a["v"].numpy(), a["bias"].numpy().astype(np.float64),
+            a["pos"].numpy(), a["gain"].numpy().astype(np.float64), d_out)
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 1), (4, 2), (3, 3)])
+def test_attention_backward_vs_finite_differences(hq, hkv):
+    """Every gradient against central differences of the (pinned) forward:
+    L = sum(d_out * o)."""
+    seg, d, tau = [5, 3], 3, 0.8
+    q, k, v, b, pos, g, do = _bwd_case(31 + hq, seg, hq, hkv, d)
+    grads = oracle.gated_attention_backward(q, k, v, b, pos, seg, hq, hkv, g, tau, do)
+
+    def loss(q_, k_, v_, b_, g_, t_):
+        o, _ = oracle.gated_attention(q_, k_, v_, b_, pos, seg, hq, hkv, g_, t_)
+        return float((o * do).sum())
+
+    eps = 1e-6
+    for name, arr in (("dq", q), ("dk", k), ("dv", v), ("dbias", b), ("dgain", g)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            args = {"dq": (plus, k, v, b, g), "dk": (q, plus, v, b, g), "dv": (q, k, plus, b, g),
+                    "dbias": (q, k, v, plus, g), "dgain": (q, k, v, b, plus)}
+            ap = args[name]
+            am = {"dq": (minus, k, v, b, g), "dk": (q, minus, v, b, g), "dv": (q, k, minus, b, g),
+                  "dbias": (q, k, v, minus, g), "dgain": (q, k, v, b, minus)}[name]
+            num[idx] = (loss(*ap, tau) - loss(*am, tau)) / (2 * eps)
+        np.testing.assert_allclose(grads[name], num, rtol=1e-6, atol=1e-8, err_msg=name)
+    num_tau = (loss(q, k, v, b, g, tau + eps) - loss(q, k, v, b, g, tau - eps)) / (2 * eps)
+    np.testing.assert_allclose(grads["dtau"], num_tau, rtol=1e-6, atol=1e-8)
+
+
+def test_attention_backward_vs_torch_autograd():
+    """torch autograd (fp64, CPU) through SDPA with an additive float mask
+    gain[h] * bias[j] built from leaf tensors: dq, dk, dv, dbias, dgain."""
+    hq, hkv, d, m, tau = 4, 2, 16, 37, 1.3
+    q, k, v, b, pos, g, do = _bwd_case(41, [m], hq, hkv, d)
+    grads = oracle.gated_attention_backward(q, k, v, b, pos, [m], hq, hkv, g, tau, do)
+    tq, tk, tv = (torch.from_numpy(x).clone().requires_grad_() for x in (q, k, v))
+    tb, tg_ = torch.from_numpy(b).clone().requires_grad_(), torch.from_numpy(g).clone().requires_grad_()
+    vis = torch.from_numpy(pos[None, :] <= pos[:, None])
+    mask = torch.where(vis[None], tg_[:, None, None] * tb[None, None, :], torch.tensor(-math.inf, dtype=torch.float64))
+    kk = tk.permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None]
+    vv = tv.permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)[None]
+    o = F.scaled_dot_product_attention(tq.permute(1, 0, 2)[None], kk, vv, attn_mask=mask[None],
+                                       scale=1.0 / (math.sqrt(d) * tau))
+    (o[0].permute(1, 0, 2) * torch.from_numpy(do)).sum().backward()
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv), ("dbias", tb), ("dgain", tg_)):
+        np.testing.assert_allclose(grads[name], t.grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+def test_attention_backward_invariants():
+    """Softmax rows: sum_j ds_ij = 0, so the bias gradient sums to zero over each
+    segment; zero gain gives zero bias gradient; d_out = 0 gives all zeros."""
+    seg, hq, hkv, d = [20, 9, 1], 4, 2, 8
+    q, k, v, b, pos, g, do = _bwd_case(51, seg, hq, hkv, d)
+    gr = oracle.gated_attention_backward(q, k, v, b, pos, seg, hq, hkv, g, 1.2, do)
+    off = 0
+    for ln in seg:
+        assert abs(gr["dbias"][off:off + ln].sum()) < 1e-12
+        off += ln
+    gr0 = oracle.gated_attention_backward(q, k, v, b, pos, seg, hq, hkv, np.zeros(hq), 1.2, do)
+    np.testing.assert_allclose(gr0["dbias"], 0.0, atol=1e-15)
+    grz = oracle.gated_attention_backward(q, k, v, b, pos, seg, hq, hkv, g, 1.2, np.zeros_like(do))
+    for key in ("dq", "dk", "dv", "dbias", "dgain"):
+        assert not np.any(grz[key])
+    # a one-row segment: o = v, so dv = d_out summed over the group and every ds is 0
+    i = seg[0] + seg[1]
+    for h in range(hq):
+        assert np.abs(gr["dq"][i, h]).max() < 1e-14  # ds = p (dp - do.o) = 1 * (do.v - do.v)
+    np.testing.assert_allclose(gr["dv"][i, 0], do[i, 0] + do[i, 1], rtol=1e-14)
+
+
+def test_score_grad_chain():
+    """d(score) = d(bias) * d logsigmoid(s)/ds for kept document rows (central
+    differences of the pinned logsigmoid), 0 for question and pruned rows."""
+    prompts = [Prompt(0, 12, 2, 9, 4), Prompt(12, 6, 0, 4, 2)]
+    s = np.random.default_rng(3).normal(size=18) * 3
+    kept = oracle.select_topk(s, prompts)
+    db = np.random.default_rng(4).normal(size=len(kept))
+    ds = oracle.score_grad(db, s, kept, prompts)
+    eps = 1e-6
+    for m, r in enumerate(kept):
+        p = prompts[0] if r < 12 else prompts[1]
+        doc = p.start + p.doc_begin <= r < p.start + p.doc_end
+        want = db[m] * (oracle.logsigmoid(s[r] + eps) - oracle.logsigmoid(s[r] - eps)) / (2 * eps) if doc else 0.0
+        assert abs(ds[r] - want) < 1e-8
+    pruned = np.setdiff1d(np.arange(18), kept)
+    assert not np.any(ds[pruned])
+
+
 # ---------------------------------------------------------------- decode ----
 
 def _decode_case(seed, segs, hq, hkv, d, n_new_max=3, pos_ties=False):
