@@ -188,6 +188,44 @@ tg_status tg_gated_attention(tg_dtype dt, const void* q, const void* k, const vo
                              float* lse, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* Device workspace tg_gated_attention_backward needs, in bytes (0 for an
+ * invalid table, which the call then reports). */
+size_t tg_attention_backward_workspace_bytes(const tg_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv,
+                                             int32_t head_dim);
+
+/* Backward of token-gated attention: the gradients of sum(d_out * out)
+ * with respect to q, k, v, bias_kept, gain and tau, where out and lse are
+ * what tg_gated_attention returned for the same inputs (lse is required).
+ * With c = 1/(sqrt(head_dim) tau), p = softmax of the visible logits and
+ * dS_ij = p_ij (d_out_i . v_j - d_out_i . out_i):
+ *     d_q_i = c sum_j dS_ij k_j,   d_k_j = c sum_{h,i} dS_ij q_i,
+ *     d_v_j = sum_{h,i} p_ij d_out_i,   d_bias_j = sum_h gain[h] sum_i dS_ij,
+ *     d_gain[h] = sum_ij dS_ij bias_j,  d_tau = -(c/tau) sum dS_ij q_i.k_j.
+ * Inputs as for tg_gated_attention (bf16 only: dt must be TG_BF16), plus
+ * d_out bf16 [M, hq, head_dim]. Outputs fp32: d_q [M, hq, head_dim],
+ * d_k and d_v [M, hkv, head_dim], d_bias [M], d_gain [hq], d_tau [1]
+ * (device). Workspace: tg_attention_backward_workspace_bytes bytes,
+ * 4-byte aligned (scratch). Deterministic (partials are summed in a fixed
+ * order). Sources: section "Was ist token-gated Attention?" (the bias on the
+ * logits is the gradient's path back to the scorer, as for a
+ * mixture-of-experts router). */
+tg_status tg_gated_attention_backward(tg_dtype dt, const void* q, const void* k, const void* v,
+                                      const float* bias_kept, const int32_t* pos_kept,
+                                      const tg_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv,
+                                      int32_t head_dim, const float* gain, float tau, const void* out,
+                                      const float* lse, const void* d_out, float* d_q, float* d_k,
+                                      float* d_v, float* d_bias, float* d_gain, float* d_tau,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Gradient of the gate scores from the gradient of bias_kept: d_scores
+ * fp32 [n_rows] is set to 0 everywhere except the kept document rows,
+ * which get d_bias_kept[m] * sigmoid(-scores[kept_idx[m]]) (the derivative
+ * of the logsigmoid that tg_compact applied). Question rows have a constant
+ * bias and pruned rows none, so both get 0. Same section. */
+tg_status tg_score_grad(const float* d_bias_kept, const float* scores, const int32_t* kept_idx,
+                        const tg_seq* seqs, int32_t n_seqs, int64_t n_rows, float* d_scores,
+                        hipStream_t stream);
+
 /* One cached sequence for decode (host memory): rows [start, start + len)
  * of the KV cache of an above-gate layer (the kept rows of its pruned
  * prefill, then the tokens generated since), whose last n_new rows are the

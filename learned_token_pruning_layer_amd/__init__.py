@@ -21,7 +21,9 @@ from ._lib import (  # noqa: F401
     tg_decode_attention,
     tg_gate_score,
     tg_gated_attention,
+    tg_gated_attention_backward,
     tg_kept_rows,
+    tg_score_grad,
     tg_select_topk,
 )
 from .layer import GatedPrefillLayer  # noqa: F401

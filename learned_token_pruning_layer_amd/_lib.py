@@ -26,6 +26,7 @@ TG_MAX_GATHERS = 16
 EXPORTED = (
     "tg_kept_rows", "tg_gate_score", "tg_select_workspace_bytes", "tg_select_topk", "tg_compact",
     "tg_attention_workspace_bytes", "tg_gated_attention", "tg_decode_workspace_bytes", "tg_decode_attention",
+    "tg_attention_backward_workspace_bytes", "tg_gated_attention_backward", "tg_score_grad",
     "tg_status_string", "tg_last_error",
 )
 
@@ -79,6 +80,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tg_gated_attention.argtypes = [c_int, vp, vp, vp, vp, vp, seqp, i32, i32, i32, i32, vp, f32,
                                        vp, vp, vp, ctypes.c_size_t, vp]
     lib.tg_gated_attention.restype = c_int
+    lib.tg_attention_backward_workspace_bytes.argtypes = [seqp, i32, i32, i32, i32]
+    lib.tg_attention_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.tg_gated_attention_backward.argtypes = [c_int, vp, vp, vp, vp, vp, seqp, i32, i32, i32, i32, vp, f32,
+                                                vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.tg_gated_attention_backward.restype = c_int
+    lib.tg_score_grad.argtypes = [vp, vp, vp, seqp, i32, i64, vp, vp]
+    lib.tg_score_grad.restype = c_int
     kvp = ctypes.POINTER(TgKvSeq)
     lib.tg_decode_workspace_bytes.argtypes = [kvp, i32, i32, i32, i32]
     lib.tg_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -300,3 +308,51 @@ def tg_decode_attention(q_new: torch.Tensor, k: torch.Tensor, v: torch.Tensor, b
                                    float(tau), out.data_ptr(), _ptr(lse if want_lse else None), _ptr(workspace),
                                    ws_have, _stream(stream)))
     return out, (lse if want_lse else None)
+
+
+def tg_gated_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias_kept: torch.Tensor,
+                                pos_kept: torch.Tensor, seqs: Sequence, gain: torch.Tensor, tau: float,
+                                out: torch.Tensor, lse: torch.Tensor, d_out: torch.Tensor,
+                                workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradients of sum(d_out * out) through token-gated attention (bf16 in,
+    fp32 out): dict(dq, dk, dv, dbias, dgain, dtau). out and lse are the
+    forward's results for the same inputs."""
+    lib = load()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (bias_kept, "bias_kept"), (pos_kept, "pos_kept"), (gain, "gain"),
+                  (out, "out"), (lse, "lse"), (d_out, "d_out")):
+        _dev(t, nm)
+    m, hq, dh = q.shape
+    hkv = k.shape[1]
+    if d_out.shape != q.shape or out.shape != q.shape or lse.shape != (hq, m):
+        raise ValueError("out, d_out [M, hq, D] and lse [hq, M] expected")
+    dev = q.device
+    f32 = torch.float32
+    g = dict(dq=torch.empty((m, hq, dh), dtype=f32, device=dev), dk=torch.empty((m, hkv, dh), dtype=f32, device=dev),
+             dv=torch.empty((m, hkv, dh), dtype=f32, device=dev), dbias=torch.empty(m, dtype=f32, device=dev),
+             dgain=torch.empty(hq, dtype=f32, device=dev), dtau=torch.empty(1, dtype=f32, device=dev))
+    sa = seq_array(seqs)
+    ws_bytes = lib.tg_attention_backward_workspace_bytes(sa, len(seqs), hq, hkv, dh)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=dev)
+    ws_have = workspace.numel() * workspace.element_size()
+    _check(lib.tg_gated_attention_backward(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                           bias_kept.data_ptr(), pos_kept.data_ptr(), sa, len(seqs), hq, hkv, dh,
+                                           gain.data_ptr(), float(tau), out.data_ptr(), lse.data_ptr(),
+                                           d_out.data_ptr(), g["dq"].data_ptr(), g["dk"].data_ptr(),
+                                           g["dv"].data_ptr(), g["dbias"].data_ptr(), g["dgain"].data_ptr(),
+                                           g["dtau"].data_ptr(), workspace.data_ptr(), ws_have, _stream(stream)))
+    return g
+
+
+def tg_score_grad(d_bias_kept: torch.Tensor, scores: torch.Tensor, kept_idx: torch.Tensor, seqs: Sequence,
+                  d_scores: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """d(scores) [N] from d(bias_kept) [M]: sigmoid(-s) on kept document rows, 0 elsewhere."""
+    lib = load()
+    for t, nm in ((d_bias_kept, "d_bias_kept"), (scores, "scores"), (kept_idx, "kept_idx")):
+        _dev(t, nm)
+    n = scores.shape[0]
+    if d_scores is None:
+        d_scores = torch.empty(n, dtype=torch.float32, device=scores.device)
+    _check(lib.tg_score_grad(d_bias_kept.data_ptr(), scores.data_ptr(), kept_idx.data_ptr(), seq_array(seqs),
+                             len(seqs), n, d_scores.data_ptr(), _stream(stream)))
+    return d_scores

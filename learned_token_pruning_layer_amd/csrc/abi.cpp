@@ -9,6 +9,8 @@
 
 #include "tg_internal.hpp"
 
+#include <vector>
+
 namespace {
 
 thread_local std::string g_err;
@@ -319,6 +321,84 @@ tg_status build_decode_table(tg_dtype dt, const tg_kv_seq* seqs, int32_t n_seqs,
 }  // namespace
 
 extern "C" {
+
+size_t tg_attention_backward_workspace_bytes(const tg_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv,
+                                             int32_t head_dim) {
+    tg::SeqTable st_;
+    int64_t m = 0;
+    if (hq <= 0 || hkv <= 0 || hq % hkv || (head_dim != 64 && head_dim != 128)) return 0;
+    if (build_seq_table(seqs, n_seqs, &st_, &m) != TG_OK) return 0;
+    g_err.clear();
+    std::vector<char> table(tg::attention_backward_table_bytes());
+    return tg::attention_backward_plan(st_, hq, head_dim, table.data());
+}
+
+tg_status tg_gated_attention_backward(tg_dtype dt, const void* q, const void* k, const void* v, const float* bias_kept,
+                                      const int32_t* pos_kept, const tg_seq* seqs, int32_t n_seqs, int32_t hq,
+                                      int32_t hkv, int32_t head_dim, const float* gain, float tau, const void* out,
+                                      const float* lse, const void* d_out, float* d_q, float* d_k, float* d_v,
+                                      float* d_bias, float* d_gain, float* d_tau, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+    g_err.clear();
+    if (dt != TG_BF16) return fail(TG_ERR_UNSUPPORTED, "the backward is built for bf16 inputs only");
+    if (hq <= 0 || hkv <= 0 || hq % hkv)
+        return fail(TG_ERR_INVALID_ARGUMENT, "hq=%d must be a positive multiple of hkv=%d", hq, hkv);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(TG_ERR_UNSUPPORTED, "head_dim=%d (built: 64, 128)", head_dim);
+    if (!(tau > 0.0f) || tau != tau || tau > 3.0e38f)
+        return fail(TG_ERR_INVALID_ARGUMENT, "tau must be finite and > 0");
+    tg::SeqTable st_;
+    int64_t m = 0;
+    tg_status st = build_seq_table(seqs, n_seqs, &st_, &m);
+    if (st != TG_OK) return st;
+    if (!d_gain || !d_tau) return fail(TG_ERR_INVALID_ARGUMENT, "d_gain, d_tau must be non-NULL");
+    std::vector<char> table(tg::attention_backward_table_bytes());
+    const size_t need = tg::attention_backward_plan(st_, hq, head_dim, table.data());
+    if (m == 0) {
+        hipError_t e = hipMemsetAsync(d_gain, 0, sizeof(float) * hq, stream);
+        if (e == hipSuccess) e = hipMemsetAsync(d_tau, 0, sizeof(float), stream);
+        if (e != hipSuccess) return hip_fail(e, "tg_gated_attention_backward clear");
+        return TG_OK;
+    }
+    if (!q || !k || !v || !bias_kept || !pos_kept || !gain || !out || !lse || !d_out || !d_q || !d_k || !d_v ||
+        !d_bias)
+        return fail(TG_ERR_INVALID_ARGUMENT, "every tensor pointer must be non-NULL");
+    if (!(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out) && aligned16(d_out) && aligned16(d_q)))
+        return fail(TG_ERR_UNSUPPORTED, "q, k, v, out, d_out, d_q must be 16-byte aligned");
+    if ((int64_t)m * hq > (int64_t)INT32_MAX / 2) return fail(TG_ERR_UNSUPPORTED, "too many rows for one launch");
+    if (!workspace || workspace_bytes < need)
+        return fail(TG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                    need);
+    if ((uintptr_t)workspace % 4 != 0) return fail(TG_ERR_INVALID_ARGUMENT, "workspace not 4-byte aligned");
+    tg::AttnBwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.d_out = d_out;
+    a.lse = lse; a.bias = bias_kept; a.pos = pos_kept; a.gain = gain; a.tau = tau;
+    a.hq = hq; a.hkv = hkv; a.head_dim = head_dim;
+    a.d_q = d_q; a.d_k = d_k; a.d_v = d_v; a.d_bias = d_bias; a.d_gain = d_gain; a.d_tau = d_tau;
+    a.workspace = workspace;
+    hipError_t e = tg::launch_attention_backward(a, table.data(), stream);
+    if (e != hipSuccess) return hip_fail(e, "tg_gated_attention_backward launch");
+    return TG_OK;
+}
+
+tg_status tg_score_grad(const float* d_bias_kept, const float* scores, const int32_t* kept_idx, const tg_seq* seqs,
+                        int32_t n_seqs, int64_t n_rows, float* d_scores, hipStream_t stream) {
+    g_err.clear();
+    tg::SeqTable t;
+    int64_t m = 0;
+    tg_status st = build_seq_table(seqs, n_seqs, &t, &m);
+    if (st != TG_OK) return st;
+    if (n_rows < 0) return fail(TG_ERR_INVALID_ARGUMENT, "n_rows=%lld < 0", (long long)n_rows);
+    for (int b = 0; b < n_seqs; ++b)
+        if (seqs[b].start + seqs[b].len > n_rows)
+            return fail(TG_ERR_INVALID_ARGUMENT, "prompt %d ends past n_rows=%lld", b, (long long)n_rows);
+    if (n_rows == 0) return TG_OK;
+    if (!d_scores || (m > 0 && (!d_bias_kept || !scores || !kept_idx)))
+        return fail(TG_ERR_INVALID_ARGUMENT, "d_bias_kept, scores, kept_idx, d_scores must be non-NULL");
+    hipError_t e = tg::launch_score_grad(d_bias_kept, scores, kept_idx, t, m, n_rows, d_scores, stream);
+    if (e != hipSuccess) return hip_fail(e, "tg_score_grad launch");
+    return TG_OK;
+}
 
 size_t tg_decode_workspace_bytes(const tg_kv_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv, int32_t head_dim) {
     tg::DecTable t;

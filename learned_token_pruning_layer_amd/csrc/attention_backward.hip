@@ -1,0 +1,540 @@
+// Backward of token-gated attention: the path by which the gate's scores
+// receive a gradient.
+//
+// Defined by the TokenGate pages: spke.com article, section "Was ist
+// token-gated Attention?" (the score of each kept token becomes a bias on
+// the attention logits, which gives the gradient a way back to the scorer,
+// in the manner of a mixture-of-experts router; per-head gain and a
+// temperature) and the ai4bro.com post, section on how learned token pruning
+// works (same). With l_ij = c q_i.k_j + g_h b_j (c = 1/(sqrt(D) tau)), p =
+// softmax over the visible keys, o = p V and an upstream gradient dO:
+//     dV_j = sum_i p_ij dO_i,   dP_ij = dO_i . v_j,
+//     dS_ij = p_ij (dP_ij - dO_i . o_i),
+//     dQ_i = c sum_j dS_ij k_j,   dK_j = c sum_i dS_ij q_i,
+//     db_j = sum_h g_h sum_i dS_ij,   dg_h = sum_ij dS_ij b_j,
+//     dtau = -(c / tau) sum_hij dS_ij q_i.k_j,
+// and the score of a kept document row gets db_j * sigmoid(-s_j) (the
+// derivative of logsigmoid); question and pruned rows get 0.
+//
+// Kernels (bf16 inputs, fp32 gradients):
+//  1. prep: Dl[h][i] = dO_i . o_i (the softmax row term).
+//  2. dkdv: one wave per (prompt, 32-key block, query head). The key block
+//     sits in LDS; the wave walks the query blocks that can see it and
+//     forms S = Q K^T and dP = dO V^T on 32x32x16 bf16 MFMA (one key per
+//     lane column, 16 queries down its registers), then P and dS, and
+//     accumulates dV += P^T dO and dK += dS^T Q with P^T / dS^T taken
+//     straight from those registers (the query order inside each 16-wide
+//     k-step is permuted the same way on both operands) and dO / Q read
+//     transposed from LDS (ds_read_b64_tr_b16). Per-head partial dK, dV and
+//     db go to a workspace, the head's dg and dtau partials per wave.
+//  3. dq: one wave per (prompt, 32-query block, query head), like the
+//     forward kernel: S^T = K Q^T and dP^T = V dO^T with Q and dO in
+//     registers, dS^T in registers, dQ^T += K^T dS^T with K^T read
+//     transposed from LDS.
+//  4. reduce: sums the per-head partials of each KV head (and of the
+//     gain / temperature) in a fixed order, so the result is deterministic;
+//     the score kernel applies sigmoid(-s).
+// LDS tiles are row-major with a 16-byte pad per row (row stride D*2+16
+// bytes), which spreads both the row reads and the transpose reads over
+// the banks.
+#include "tg_internal.hpp"
+#include "tg_device.hpp"
+
+namespace tg {
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+template <int D>
+struct Tile {
+    static constexpr int RS = D * 2 + 16;  // padded row stride in bytes
+    static constexpr int BYTES = 32 * RS;
+};
+
+__device__ __forceinline__ v4i16 read_tr16(const LDS_AS char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)p);
+}
+
+// Copy 32 rows (row r of the tile <- global row min(row0 + r, n_rows - 1))
+// of D bf16 into a padded LDS tile; `stride` elements between global rows.
+template <int D>
+__device__ __forceinline__ void load_tile(LDS_AS char* tile, const uint16_t* __restrict__ src, int64_t stride,
+                                          int row0, int n_rows, int lane) {
+    constexpr int CH = D / 8;  // 16-byte chunks per row
+#pragma unroll
+    for (int u = 0; u < 32 * CH / 64; ++u) {
+        const int idx = u * 64 + lane;
+        const int r = idx / CH, ch = idx % CH;
+        const int gr = min(row0 + r, n_rows - 1);
+        const u32x4 w = *(const u32x4*)(src + gr * stride + ch * 8);
+        *(LDS_AS u32x4*)(tile + r * Tile<D>::RS + ch * 16) = w;
+    }
+}
+
+// A/B operand for k-step s of a 32x32x16 MFMA whose rows (A) or columns (B)
+// are the tile's columns d = 32b + (lane%32) and whose k-slots (lane/32, e)
+// are tile rows 16s + 8(e/4) + 4(lane/32) + e%4: four transpose reads.
+template <int D>
+__device__ __forceinline__ bf16x8 tile_tr_operand(const LDS_AS char* tile, int b, int s, int lane) {
+    const int g = lane >> 4, r16 = lane & 15;
+    const int dsub = 16 * (g & 1) + 4 * (r16 & 3);
+    const int rowo = 4 * (g >> 1) + (r16 >> 2);
+    const int ra = 16 * s + rowo, rb = ra + 8;
+    const int dd = 32 * b + dsub;
+    const v4i16 lo = read_tr16(tile + ra * Tile<D>::RS + dd * 2);
+    const v4i16 hi = read_tr16(tile + rb * Tile<D>::RS + dd * 2);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Row operand: tile row (lane%32), elements 16s + 8(lane/32) .. +8.
+template <int D>
+__device__ __forceinline__ bf16x8 tile_row_operand(const LDS_AS char* tile, int s, int lane) {
+    return *(const LDS_AS bf16x8*)(tile + (lane & 31) * Tile<D>::RS + (16 * s + 8 * (lane >> 5)) * 2);
+}
+
+struct BwdSeg {
+    int64_t off;     // first kept row
+    int32_t n;       // kept rows
+    int32_t n_blk;   // 32-row blocks
+    int32_t item0;   // first (block, head) work item
+    int32_t pad;
+};
+struct BwdTable {
+    int32_t n_seg;
+    int32_t n_items;  // sum over prompts of n_blk * hq
+    int64_t m_total;
+    BwdSeg s[TG_MAX_SEQS];
+};
+
+// Work item -> (prompt, block, head): item = item0 + order(block) * hq + h,
+// blocks in the order given (the ones with the most work first).
+__device__ __forceinline__ void bwd_item(const BwdTable& t, int item, int hq, bool last_first, int& sg, int& blk,
+                                         int& h) {
+    sg = 0;
+    for (int i = 1; i < t.n_seg; ++i)
+        if (t.s[i].item0 <= item) sg = i;
+    const int local = item - t.s[sg].item0;
+    blk = last_first ? t.s[sg].n_blk - 1 - local / hq : local / hq;
+    h = local % hq;
+}
+
+// 1. Dl[h][i] = dO_i . o_i (fp32), one thread per (row, head).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ d_out,
+                                                      const uint16_t* __restrict__ out, int64_t m, int hq,
+                                                      float* __restrict__ dl) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= m * hq) return;
+    const int64_t row = idx / hq;
+    const int h = (int)(idx % hq);
+    const uint16_t* a = d_out + idx * D;
+    const uint16_t* b = out + idx * D;
+    float acc = 0.0f;
+#pragma unroll 4
+    for (int c = 0; c < D; c += 8) {
+        const uint4 x = *(const uint4*)(a + c), y = *(const uint4*)(b + c);
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = fmaf(__uint_as_float(xs[e] << 16), __uint_as_float(ys[e] << 16), acc);
+            acc = fmaf(__uint_as_float(xs[e] & 0xffff0000u), __uint_as_float(ys[e] & 0xffff0000u), acc);
+        }
+    }
+    dl[(int64_t)h * m + row] = acc;
+}
+
+// 2. Per (prompt, key block, head): partial dK, dV, db of that head, dg and
+// dtau partials. ws layout (fp32): dk [hq][M][D], dv [hq][M][D], db [hq][M],
+// and per item: dg, dtau.
+template <int D>
+__global__ __launch_bounds__(64) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ d_out, const float* __restrict__ lse, const float* __restrict__ dl,
+    const float* __restrict__ bias, const int32_t* __restrict__ pos, BwdTable t, int hq, int hkv,
+    const float* __restrict__ gain, float c, float* __restrict__ ws_dk, float* __restrict__ ws_dv,
+    float* __restrict__ ws_db, float* __restrict__ ws_item) {
+    constexpr int KS = D / 16, DB = D / 32;
+    __shared__ __attribute__((aligned(16))) char kt[Tile<D>::BYTES], vt[Tile<D>::BYTES];
+    __shared__ __attribute__((aligned(16))) char qt[Tile<D>::BYTES], dot[Tile<D>::BYTES];
+    __shared__ __attribute__((aligned(16))) float s_lse[32], s_dl[32];
+    __shared__ __attribute__((aligned(16))) int32_t s_pos[32];
+    const int lane = threadIdx.x;
+    const int hh = lane >> 5, l32 = lane & 31;
+    int sg, jb, h;
+    bwd_item(t, blockIdx.x, hq, false, sg, jb, h);  // early key blocks see the most queries
+    const int64_t off = t.s[sg].off, m = t.m_total;
+    const int n = t.s[sg].n;
+    const int kvh = h / (hq / hkv);
+    const int key0 = 32 * jb;
+    const float c2 = c * LOG2E, gb2 = gain[h] * LOG2E, g = gain[h];
+
+    load_tile<D>((LDS_AS char*)kt, k + (off * hkv + kvh) * D, (int64_t)hkv * D, key0, n, lane);
+    load_tile<D>((LDS_AS char*)vt, v + (off * hkv + kvh) * D, (int64_t)hkv * D, key0, n, lane);
+    const int key = key0 + l32;                       // this lane's key column
+    const bool key_ok = key < n;
+    const float b_key = bias[off + min(key, n - 1)];
+    const int32_t p_key = pos[off + min(key, n - 1)];
+    const int32_t p_key0 = pos[off + key0];
+
+    // First query block that can see a key of this block (positions never
+    // decrease along the kept rows; repeats can reach earlier blocks).
+    int i0 = jb;
+    while (i0 > 0 && pos[off + 32 * i0 - 1] >= p_key0) --i0;
+
+    f32x16 acc_dk[DB], acc_dv[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            acc_dk[b][j] = 0.0f;
+            acc_dv[b][j] = 0.0f;
+        }
+    float db_acc = 0.0f, dg_acc = 0.0f, dt_acc = 0.0f;
+
+    for (int ib = i0; ib < t.s[sg].n_blk; ++ib) {
+        const int qrow0 = 32 * ib;
+        __syncthreads();  // previous iteration's reads of qt / dot are done
+        load_tile<D>((LDS_AS char*)qt, q + (off * hq + h) * D, (int64_t)hq * D, qrow0, n, lane);
+        load_tile<D>((LDS_AS char*)dot, d_out + (off * hq + h) * D, (int64_t)hq * D, qrow0, n, lane);
+        if (lane < 32) {
+            const int qi = min(qrow0 + lane, n - 1);
+            s_lse[lane] = lse[(int64_t)h * m + off + qi] * LOG2E;
+            s_dl[lane] = dl[(int64_t)h * m + off + qi];
+            s_pos[lane] = pos[off + qi];
+        }
+        __syncthreads();
+        f32x16 sacc, pacc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            sacc[j] = 0.0f;
+            pacc[j] = 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row_operand<D>((const LDS_AS char*)qt, s, lane),
+                                                           tile_row_operand<D>((const LDS_AS char*)kt, s, lane), sacc, 0, 0, 0);
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row_operand<D>((const LDS_AS char*)dot, s, lane),
+                                                           tile_row_operand<D>((const LDS_AS char*)vt, s, lane), pacc, 0, 0, 0);
+        }
+        // Register j: query qrow0 + 8(j/4) + 4hh + j%4 of key `key`.
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            u32x4 wp, wd;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                float pv[2], dv_[2];
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) {
+                    const int j = 8 * s + 2 * e2 + t2;
+                    const int qloc = 8 * (j / 4) + 4 * hh + (j % 4);
+                    const bool vis = key_ok & (qrow0 + qloc < n) & (p_key <= s_pos[qloc]);
+                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[j], c2, fmaf(gb2, b_key, -s_lse[qloc])))
+                                        : 0.0f;
+                    const float ds = p * (pacc[j] - s_dl[qloc]);
+                    db_acc += ds;
+                    dt_acc = fmaf(ds, sacc[j], dt_acc);
+                    pv[t2] = p;
+                    dv_[t2] = ds;
+                }
+                wp[e2] = pack_bf16x2(pv[0], pv[1]);
+                wd[e2] = pack_bf16x2(dv_[0], dv_[1]);
+            }
+            pf[s] = __builtin_bit_cast(bf16x8, wp);
+            dsf[s] = __builtin_bit_cast(bf16x8, wd);
+        }
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                acc_dv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[s], tile_tr_operand<D>((const LDS_AS char*)dot, b, s, lane),
+                                                                    acc_dv[b], 0, 0, 0);
+                acc_dk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsf[s], tile_tr_operand<D>((const LDS_AS char*)qt, b, s, lane),
+                                                                    acc_dk[b], 0, 0, 0);
+            }
+    }
+    // Accumulator j of block b: key key0 + 8(j/4) + 4hh + j%4, d = 32b + l32.
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int kr = key0 + 8 * (j / 4) + 4 * hh + (j % 4);
+            if (kr < n) {
+                const int64_t o = ((int64_t)h * m + off + kr) * D + 32 * b + l32;
+                ws_dk[o] = acc_dk[b][j] * c;
+                ws_dv[o] = acc_dv[b][j];
+            }
+        }
+    // db: this lane's key, summed over both query halves.
+    db_acc += __shfl_xor(db_acc, 32);
+    if (hh == 0 && key_ok) ws_db[(int64_t)h * m + off + key] = g * db_acc;
+    dg_acc = db_acc * b_key;  // per key, both halves already added
+    if (hh == 1 || !key_ok) dg_acc = 0.0f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        dg_acc += __shfl_xor(dg_acc, o);
+        dt_acc += __shfl_xor(dt_acc, o);
+    }
+    if (lane == 0) {
+        ws_item[2 * blockIdx.x] = dg_acc;
+        ws_item[2 * blockIdx.x + 1] = dt_acc;
+    }
+}
+
+// 3. dQ of one (prompt, query block, head).
+template <int D>
+__global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                   const uint16_t* __restrict__ v,
+                                                   const uint16_t* __restrict__ d_out, const float* __restrict__ lse,
+                                                   const float* __restrict__ dl, const float* __restrict__ bias,
+                                                   const int32_t* __restrict__ pos, BwdTable t, int hq, int hkv,
+                                                   const float* __restrict__ gain, float c, float* __restrict__ dq) {
+    constexpr int KS = D / 16, DB = D / 32;
+    __shared__ __attribute__((aligned(16))) char kt[Tile<D>::BYTES], vt[Tile<D>::BYTES];
+    __shared__ __attribute__((aligned(16))) float s_b[32];
+    __shared__ __attribute__((aligned(16))) int32_t s_p[32];
+    const int lane = threadIdx.x;
+    const int hh = lane >> 5, l32 = lane & 31;
+    int sg, ib, h;
+    bwd_item(t, blockIdx.x, hq, true, sg, ib, h);  // late query blocks see the most keys
+    const int64_t off = t.s[sg].off, m = t.m_total;
+    const int n = t.s[sg].n;
+    const int kvh = h / (hq / hkv);
+    const int i0 = 32 * ib;
+    const int qi = min(i0 + l32, n - 1);
+    const bool q_ok = i0 + l32 < n;
+    const float c2 = c * LOG2E, gb2 = gain[h] * LOG2E;
+    const float lse2 = lse[(int64_t)h * m + off + qi] * LOG2E;
+    const float dlq = dl[(int64_t)h * m + off + qi];
+    const int32_t my_pos = pos[off + qi];
+    const int32_t pos_last = pos[off + min(i0 + 31, n - 1)];
+
+    bf16x8 qf[KS], df[KS];
+    {
+        const uint16_t* qrow = q + ((off + qi) * hq + h) * D + 8 * hh;
+        const uint16_t* drow = d_out + ((off + qi) * hq + h) * D + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            qf[s] = *(const bf16x8*)(qrow + 16 * s);
+            df[s] = *(const bf16x8*)(drow + 16 * s);
+        }
+    }
+    // Key blocks up to the last one holding a key visible to this block.
+    int n_kt = min(n - 1, i0 + 31) / 32 + 1;
+    while (n_kt * 32 < n && pos[off + n_kt * 32] <= pos_last) ++n_kt;
+
+    f32x16 acc[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[b][j] = 0.0f;
+
+    for (int kb = 0; kb < n_kt; ++kb) {
+        const int key0 = 32 * kb;
+        __syncthreads();
+        load_tile<D>((LDS_AS char*)kt, k + (off * hkv + kvh) * D, (int64_t)hkv * D, key0, n, lane);
+        load_tile<D>((LDS_AS char*)vt, v + (off * hkv + kvh) * D, (int64_t)hkv * D, key0, n, lane);
+        if (lane < 32) {
+            s_b[lane] = bias[off + min(key0 + lane, n - 1)];
+            s_p[lane] = (key0 + lane < n) ? pos[off + key0 + lane] : INT32_MAX;
+        }
+        __syncthreads();
+        f32x16 sacc, pacc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            sacc[j] = 0.0f;
+            pacc[j] = 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row_operand<D>((const LDS_AS char*)kt, s, lane), qf[s], sacc, 0, 0, 0);
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row_operand<D>((const LDS_AS char*)vt, s, lane), df[s], pacc, 0, 0, 0);
+        }
+        // Register j: key key0 + 8(j/4) + 4hh + j%4 of query qi.
+        bf16x8 dsf[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            u32x4 w;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                float dv_[2];
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) {
+                    const int j = 8 * s + 2 * e2 + t2;
+                    const int kl = 8 * (j / 4) + 4 * hh + (j % 4);
+                    const bool vis = q_ok & (s_p[kl] <= my_pos);
+                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[j], c2, fmaf(gb2, s_b[kl], -lse2))) : 0.0f;
+                    dv_[t2] = p * (pacc[j] - dlq);
+                }
+                w[e2] = pack_bf16x2(dv_[0], dv_[1]);
+            }
+            dsf[s] = __builtin_bit_cast(bf16x8, w);
+        }
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr_operand<D>((const LDS_AS char*)kt, b, s, lane), dsf[s], acc[b],
+                                                                 0, 0, 0);
+    }
+    // acc[b] register j: d = 32b + 8(j/4) + 4hh + j%4 of query qi.
+    if (q_ok) {
+        float* row = dq + ((off + i0 + l32) * hq + h) * D;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = acc[b][4 * g4 + e] * c;
+                *(f32x4*)(row + 32 * b + 8 * g4 + 4 * hh) = o;
+            }
+    }
+}
+
+// 4a. dK, dV = sums of the per-head partials over each KV head's query
+// heads (in head order); db = sum over all heads.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ ws_dk,
+                                                        const float* __restrict__ ws_dv,
+                                                        const float* __restrict__ ws_db, int64_t m, int hq, int hkv,
+                                                        float* __restrict__ dk, float* __restrict__ dv,
+                                                        float* __restrict__ db) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over m * hkv * D
+    const int gsz = hq / hkv;
+    if (idx < m * hkv * D) {
+        const int64_t row = idx / (hkv * D);
+        const int kvh = (int)((idx / D) % hkv), d = (int)(idx % D);
+        float a = 0.0f, b = 0.0f;
+        for (int hl = 0; hl < gsz; ++hl) {
+            const int64_t o = (((int64_t)(kvh * gsz + hl)) * m + row) * D + d;
+            a += ws_dk[o];
+            b += ws_dv[o];
+        }
+        dk[idx] = a;
+        dv[idx] = b;
+    }
+    if (idx < m) {
+        float s = 0.0f;
+        for (int h = 0; h < hq; ++h) s += ws_db[(int64_t)h * m + idx];
+        db[idx] = s;
+    }
+}
+
+// 4b. dg_h = sum of the head's item partials (prompt, block order);
+// dtau = -(c/tau) * sum of all dtau partials. One workgroup.
+__global__ __launch_bounds__(256) void bwd_scalars_kernel(const float* __restrict__ ws_item, BwdTable t, int hq,
+                                                         float c_over_tau, float* __restrict__ dgain,
+                                                         float* __restrict__ dtau) {
+    __shared__ float part[256];
+    const int tid = threadIdx.x;
+    for (int h = tid; h < hq; h += 256) {
+        float s = 0.0f;
+        for (int sg = 0; sg < t.n_seg; ++sg)
+            for (int b = 0; b < t.s[sg].n_blk; ++b) s += ws_item[2 * (t.s[sg].item0 + b * hq + h)];
+        dgain[h] = s;
+    }
+    float s = 0.0f;
+    for (int i = tid; i < t.n_items; i += 256) s += ws_item[2 * i + 1];
+    part[tid] = s;
+    __syncthreads();
+    if (tid == 0) {
+        float tot = 0.0f;
+        for (int i = 0; i < 256; ++i) tot += part[i];
+        *dtau = -c_over_tau * tot;
+    }
+}
+
+template <int D>
+hipError_t launch_bwd_d(const AttnBwdArgs& a, const BwdTable& t, float c, hipStream_t st) {
+    const int64_t m = t.m_total;
+    float* ws = (float*)a.workspace;
+    float* dl = ws;
+    float* ws_dk = dl + (int64_t)a.hq * m;
+    float* ws_dv = ws_dk + (int64_t)a.hq * m * D;
+    float* ws_db = ws_dv + (int64_t)a.hq * m * D;
+    float* ws_item = ws_db + (int64_t)a.hq * m;
+    const uint16_t *q = (const uint16_t*)a.q, *k = (const uint16_t*)a.k, *v = (const uint16_t*)a.v;
+    const uint16_t *dout = (const uint16_t*)a.d_out, *out = (const uint16_t*)a.out;
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((m * a.hq + 255) / 256)), dim3(256), 0, st, dout, out, m,
+                       a.hq, dl);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)t.n_items), dim3(64), 0, st, q, k, v, dout, a.lse, dl,
+                       a.bias, a.pos, t, a.hq, a.hkv, a.gain, c, ws_dk, ws_dv, ws_db, ws_item);
+    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)t.n_items), dim3(64), 0, st, q, k, v, dout, a.lse, dl,
+                       a.bias, a.pos, t, a.hq, a.hkv, a.gain, c, a.d_q);
+    hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3((unsigned)((m * a.hkv * D + 255) / 256)), dim3(256), 0, st, ws_dk,
+                       ws_dv, ws_db, m, a.hq, a.hkv, a.d_k, a.d_v, a.d_bias);
+    hipLaunchKernelGGL(bwd_scalars_kernel, dim3(1), dim3(256), 0, st, ws_item, t, a.hq, c / a.tau, a.d_gain, a.d_tau);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attention_backward_plan(const SeqTable& st, int hq, int head_dim, void* table_out) {
+    BwdTable& t = *(BwdTable*)table_out;
+    t = BwdTable{};
+    t.n_seg = st.n;
+    int64_t items = 0, m = 0;
+    for (int b = 0; b < st.n; ++b) {
+        t.s[b].off = st.s[b].kept_off;
+        t.s[b].n = st.s[b].n_kept;
+        t.s[b].n_blk = (st.s[b].n_kept + 31) / 32;
+        t.s[b].item0 = (int32_t)items;
+        items += (int64_t)t.s[b].n_blk * hq;
+        m += st.s[b].n_kept;
+    }
+    t.n_items = (int32_t)items;
+    t.m_total = m;
+    // Dl [hq][M], dk and dv partials [hq][M][D], db partials [hq][M], 2 per item.
+    return ((size_t)hq * m * (2 + 2 * (size_t)head_dim) + 2 * (size_t)items) * sizeof(float);
+}
+
+size_t attention_backward_table_bytes() { return sizeof(BwdTable); }
+
+hipError_t launch_attention_backward(const AttnBwdArgs& a, const void* table, hipStream_t st) {
+    const BwdTable& t = *(const BwdTable*)table;
+    if (t.n_items == 0) return hipSuccess;
+    const float c = 1.0f / (sqrtf((float)a.head_dim) * a.tau);
+    return a.head_dim == 128 ? launch_bwd_d<128>(a, t, c, st) : launch_bwd_d<64>(a, t, c, st);
+}
+
+// Score gradient: zero every row, then d_scores[kept_idx[m]] = d_bias[m] *
+// sigmoid(-s) for kept document rows.
+namespace {
+__global__ __launch_bounds__(256) void score_zero_kernel(float* __restrict__ d, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) d[i] = 0.0f;
+}
+__global__ __launch_bounds__(256) void score_grad_kernel(const float* __restrict__ d_bias,
+                                                        const float* __restrict__ scores,
+                                                        const int32_t* __restrict__ kept, SeqTable t,
+                                                        float* __restrict__ d_scores) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    int b = 0;
+    for (int s = 1; s < t.n; ++s)
+        if (t.s[s].kept_off <= i) b = s;
+    const SeqDesc sd = t.s[b];
+    if (i >= sd.kept_off + sd.n_kept) return;  // past the last prompt
+    const int32_t row = kept[i];
+    const int64_t rel = row - sd.start;
+    if (rel >= sd.doc_begin && rel < sd.doc_end) {
+        const float s = scores[row];
+        // sigmoid(-s), without overflow for large |s|
+        const float e = __expf(-fabsf(s));
+        d_scores[row] = d_bias[i] * (s >= 0.0f ? e / (1.0f + e) : 1.0f / (1.0f + e));
+    }
+}
+}  // namespace
+
+hipError_t launch_score_grad(const float* d_bias, const float* scores, const int32_t* kept, const SeqTable& t,
+                             int64_t m, int64_t n_rows, float* d_scores, hipStream_t st) {
+    if (n_rows > 0)
+        hipLaunchKernelGGL(score_zero_kernel, dim3((unsigned)((n_rows + 255) / 256)), dim3(256), 0, st, d_scores,
+                           n_rows);
+    if (m > 0)
+        hipLaunchKernelGGL(score_grad_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, d_bias, scores,
+                           kept, t, d_scores);
+    return hipGetLastError();
+}
+
+}  // namespace tg

@@ -116,6 +116,26 @@ hipError_t launch_decode(tg_dtype dt, const void* q, const void* k, const void* 
                          const int32_t* pos, const DecTable& t, int hq, int hkv, int head_dim, const float* gain,
                          float tau, void* out, float* lse, int64_t r_total, void* ws, hipStream_t st);
 
+// Backward of token-gated attention (bf16 inputs, fp32 gradients).
+struct AttnBwdArgs {
+    const void *q, *k, *v, *out, *d_out;
+    const float* lse;
+    const float* bias;
+    const int32_t* pos;
+    const float* gain;
+    float tau;
+    int hq, hkv, head_dim;
+    float *d_q, *d_k, *d_v, *d_bias, *d_gain, *d_tau;
+    void* workspace;
+};
+// Fills the opaque work table (attention_backward_table_bytes() bytes) and
+// returns the workspace bytes.
+size_t attention_backward_plan(const SeqTable& st, int hq, int head_dim, void* table_out);
+size_t attention_backward_table_bytes();
+hipError_t launch_attention_backward(const AttnBwdArgs& a, const void* table, hipStream_t st);
+hipError_t launch_score_grad(const float* d_bias, const float* scores, const int32_t* kept, const SeqTable& t,
+                             int64_t m, int64_t n_rows, float* d_scores, hipStream_t st);
+
 // Query-row block per attention work item for a given dtype/head ratio.
 int attention_block_rows(tg_dtype dt, int hq, int hkv);
 int attention_heads_per_item(tg_dtype dt, int hq, int hkv);

@@ -284,7 +284,9 @@ def gated_attention_backward(q, k, v, bias, pos, seg_lens: Sequence[int], hq: in
         dgain_h = sum_{i,j} ds_ij bias[j]
         dtau    = -(1/tau) * sum_{h,i,j} ds_ij (q_i.k_j * c)
 
-    Returns dict(dq, dk, dv, dbias, dgain, dtau) in fp64.
+    Returns dict(dq, dk, dv, dbias, dgain, dtau) in fp64, plus dtau_abs =
+    (1/tau) sum |ds_ij q_i.k_j c|, the size of the terms dtau sums (it can
+    cancel to far less), for setting tolerances.
     """
     if hq % hkv:
         raise ValueError("hq must be a multiple of hkv")
@@ -300,6 +302,7 @@ def gated_attention_backward(q, k, v, bias, pos, seg_lens: Sequence[int], hq: in
     dbias = np.zeros(m_tot)
     dgain = np.zeros(hq)
     dtau = 0.0
+    dtau_abs = 0.0
     off = 0
     for ln in seg_lens:
         ln = int(ln)
@@ -321,8 +324,9 @@ def gated_attention_backward(q, k, v, bias, pos, seg_lens: Sequence[int], hq: in
             dbias[seg] += g[h] * ds.sum(axis=0)
             dgain[h] += (ds.sum(axis=0) * b[seg]).sum()
             dtau += -(1.0 / float(tau)) * (ds * qk * c).sum()
+            dtau_abs += (1.0 / float(tau)) * np.abs(ds * qk * c).sum()
         off += ln
-    return dict(dq=dq, dk=dk, dv=dv, dbias=dbias, dgain=dgain, dtau=dtau)
+    return dict(dq=dq, dk=dk, dv=dv, dbias=dbias, dgain=dgain, dtau=dtau, dtau_abs=dtau_abs)
 
 
 def score_grad(dbias_kept, scores, kept, prompts: Sequence) -> np.ndarray:

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(tg.EXPORTED)
@@ -111,6 +111,27 @@ def test_decode_table_and_rejects_before_launch(lib):
     # nothing to decode: OK without any pointer
     assert lib.tg_decode_attention(1, None, None, None, None, None, kv_seq_array([(0, 3, 0)]), 1, 16, 8, 128,
                                    None, 1.0, None, None, None, 0, None) == 0
+
+
+def test_backward_workspace_and_rejects_before_launch(lib):
+    # Workspace (fp32 words): the softmax row term [hq][M], per-head dK and dV
+    # partials [hq][M][D] each, per-head bias partials [hq][M], and a gain and a
+    # temperature partial per (prompt, 32-row block, head) item.
+    prompts = [Prompt(0, 100, 0, 90, 40), Prompt(100, 70, 0, 0, 0)]  # 50 and 70 kept rows
+    m, hq, d = 120, 16, 128
+    items = (2 + 3) * hq
+    need = lib.tg_attention_backward_workspace_bytes(seq_array(prompts), 2, hq, 8, d)
+    assert need == 4 * (hq * m * (2 + 2 * d) + 2 * items)
+    fake = ctypes.c_void_p(4096)
+    args = [fake, fake, fake, fake, fake, seq_array(prompts), 2, hq, 8, d, fake, 1.2, fake, fake, fake,
+            fake, fake, fake, fake, fake, fake]
+    assert lib.tg_gated_attention_backward(0, *args, fake, need, None) == UNSUPPORTED  # fp32 not built
+    assert lib.tg_gated_attention_backward(1, *args, None, 0, None) == WORKSPACE
+    assert lib.tg_gated_attention_backward(1, *args, fake, need - 4, None) == WORKSPACE
+    bad = list(args)
+    bad[9] = 96
+    assert lib.tg_gated_attention_backward(1, *bad, fake, need, None) == UNSUPPORTED
+    assert lib.tg_score_grad(fake, fake, fake, seq_array(prompts), 2, 100, fake, None) == INVALID  # n_rows short
 
 
 def test_gate_rejects_before_launch(lib):

@@ -555,3 +555,73 @@ def test_decode_deterministic_and_matches_prefill_rows():
                                    gain.to(DEV), 1.2)
     rows = [2383, 3882, 3883]
     assert_rowmax_close(f64(o1), f64(pre[rows]), rel=2e-2)
+
+
+# -------------------------------------------------------------- backward ----
+
+def assert_slice_close(got, ref, rel=2e-2, what=""):
+    """Gradient bar: per head slice [:, h, :], max |got - ref| <= rel * max |ref| of that
+    slice (bf16 operands of the MFMAs: P, dS and dO round to 8 bits; gradients of rows that
+    see little attention are sums with cancellation, so the slice maximum sets the scale)."""
+    for h in range(ref.shape[1]):
+        err = np.abs(got[:, h] - ref[:, h]).max()
+        scale = np.abs(ref[:, h]).max()
+        assert err <= rel * scale, f"{what} head {h}: max err {err:.3e} > {rel} * {scale:.3e}"
+
+
+def check_backward(lens, hq, hkv, d, seed, pos_ties=False, tau=1.2, tail=20):
+    a = make_attention_inputs(lens, hq, hkv, d, seed=seed, dtype=torch.bfloat16, pos_ties=pos_ties,
+                              n_query_tail=tail)
+    ps, st = [], 0
+    for ln in lens:
+        ps.append(Prompt(st, ln, 0, 0, 0))
+        st += ln
+    dv_ = {k: (x.to(DEV) if hasattr(x, "to") else x) for k, x in a.items()}
+    out, lse = tg.tg_gated_attention(dv_["q"], dv_["k"], dv_["v"], dv_["bias"], dv_["pos"], ps, dv_["gain"], tau,
+                                     want_lse=True)
+    dout = torch.randn(out.shape, generator=torch.Generator().manual_seed(seed + 1)).to(torch.bfloat16)
+    g = tg.tg_gated_attention_backward(dv_["q"], dv_["k"], dv_["v"], dv_["bias"], dv_["pos"], ps, dv_["gain"], tau,
+                                       out, lse, dout.to(DEV))
+    ref = oracle.gated_attention_backward(f64(a["q"]), f64(a["k"]), f64(a["v"]), f64(a["bias"]), a["pos"].numpy(),
+                                          lens, hq, hkv, f64(a["gain"]), tau, f64(dout))
+    for key in ("dq", "dk", "dv"):
+        assert_slice_close(f64(g[key]), ref[key], what=key)
+    for key in ("dbias", "dgain"):
+        err = np.abs(f64(g[key]) - ref[key]).max()
+        assert err <= 2e-2 * np.abs(ref[key]).max(), f"{key}: {err:.3e}"
+    # dtau sums terms of both signs: the bar is set by their magnitude, not by the sum
+    assert abs(float(g["dtau"][0]) - ref["dtau"]) <= 2e-2 * ref["dtau_abs"]
+    return g
+
+
+def test_backward_qwen_shapes():
+    note("backward bf16 16/8 heads D=128: one 2384-row prompt; ragged prompts with a one-row prompt")
+    check_backward([2384], 16, 8, 128, seed=71)
+    check_backward([700, 33, 1, 95], 16, 8, 128, seed=72)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 4, 64), (8, 2, 64), (6, 3, 128)])
+def test_backward_head_ratios_and_ties(hq, hkv, d):
+    note(f"backward bf16 hq={hq} hkv={hkv} D={d}, repeated positions")
+    check_backward([300, 129], hq, hkv, d, seed=hq * 7 + d, pos_ties=True)
+
+
+def test_backward_deterministic():
+    note("backward: bitwise repeatable")
+    g1 = check_backward([1000], 16, 8, 128, seed=81)
+    g2 = check_backward([1000], 16, 8, 128, seed=81)
+    for key in g1:
+        assert torch.equal(g1[key], g2[key]), key
+
+
+def test_score_grad_chain_on_gpu():
+    note("score gradient: d_bias * sigmoid(-s) on kept document rows, 0 elsewhere (bit-exact zeros)")
+    prompts = [Prompt(0, 3000, 50, 2900, 400), Prompt(3000, 1000, 0, 744, 100), Prompt(4000, 64, 0, 0, 0)]
+    s = make_scores(4064, seed=91) * 6
+    kept = torch.from_numpy(oracle.select_topk(s.numpy(), prompts).astype(np.int32))
+    db = torch.randn(len(kept), generator=torch.Generator().manual_seed(92))
+    got = tg.tg_score_grad(db.to(DEV), s.to(DEV), kept.to(DEV), prompts).cpu().double().numpy()
+    ref = oracle.score_grad(db.double().numpy(), s.numpy(), kept.numpy(), prompts)
+    zero = ref == 0.0
+    assert np.all(got[zero] == 0.0)
+    np.testing.assert_allclose(got[~zero], ref[~zero], rtol=2e-6, atol=0)
