@@ -235,6 +235,8 @@ def measure_extras(torch, tg, layer, w, steps, dev):
     del src, dst
     # Decode after this prefill: one new token over the kept K/V cache.
     out["decode_qwen16k"] = measure_decode(torch, tg, layer, timed, pct)
+    # Backward of this layer's token-gated attention (the gradient path to the gate).
+    out["backward_qwen16k"] = measure_backward(torch, tg, layer, timed, pct)
     # Select on one prompt of 2^24 document rows: the multi-workgroup path
     # (1024 chunks of 16384 rows), arguments marshalled once outside the
     # timed region.
@@ -319,6 +321,50 @@ def measure_decode(torch, tg, lay, timed, pct, reps=50):
     byts = total * hkv * dh * k.element_size() * 2 + total * 8
     return {"cache_rows": total, "us": round(us, 2), "algorithmic_gb_s": round(byts / (us * 1e-6) / 1e9, 1),
             "frac_hbm_peak": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def measure_backward(torch, tg, lay, timed, pct, reps=20):
+    """Backward of the layer's token-gated attention over its kept rows (the
+    forward's output and lse, a random upstream gradient). Algorithmic work:
+    five products of 2*D*Hq flop per visible pair (S, dP, dV, dK, dQ), 2.5x
+    the forward's."""
+    from learned_token_pruning_layer_amd._lib import seq_array
+    qk, kk, vk = lay.qkv_kept[0]
+    hq, hkv, dh, m = lay.hq, lay.hkv, lay.head_dim, lay.m
+    q3, k3, v3 = qk.view(m, hq, dh), kk.view(m, hkv, dh), vk.view(m, hkv, dh)
+    lay_l = lay.layers[0]
+    out, lse = tg.tg_gated_attention(q3, k3, v3, lay.bias_kept, lay.pos_kept, lay.prompts, lay_l.gain, lay_l.tau,
+                                     want_lse=True)
+    g = torch.Generator(device=q3.device).manual_seed(11)
+    dout = torch.randn(out.shape, generator=g, device=q3.device).to(torch.bfloat16)
+    lib = tg.load()
+    sa = seq_array(lay.prompts)
+    wsb = lib.tg_attention_backward_workspace_bytes(sa, len(lay.prompts), hq, hkv, dh)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=q3.device)
+    f32 = torch.float32
+    dq = torch.empty((m, hq, dh), dtype=f32, device=q3.device)
+    dk = torch.empty((m, hkv, dh), dtype=f32, device=q3.device)
+    dv = torch.empty_like(dk)
+    db = torch.empty(m, dtype=f32, device=q3.device)
+    dg = torch.empty(hq, dtype=f32, device=q3.device)
+    dt = torch.empty(1, dtype=f32, device=q3.device)
+    st = torch.cuda.current_stream().cuda_stream
+    args = (1, q3.data_ptr(), k3.data_ptr(), v3.data_ptr(), lay.bias_kept.data_ptr(), lay.pos_kept.data_ptr(), sa,
+            len(lay.prompts), hq, hkv, dh, lay_l.gain.data_ptr(), float(lay_l.tau), out.data_ptr(), lse.data_ptr(),
+            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), db.data_ptr(), dg.data_ptr(),
+            dt.data_ptr(), ws.data_ptr(), wsb, st)
+
+    def call():
+        if lib.tg_gated_attention_backward(*args) != 0:
+            raise RuntimeError(lib.tg_last_error().decode())
+
+    call()
+    us = pct(timed(call, reps), 0.5)
+    pairs = sum((p.k_doc + p.length - (p.doc_end - p.doc_begin)) * (p.k_doc + p.length - (p.doc_end - p.doc_begin) + 1)
+                // 2 for p in lay.prompts)
+    fl = 5 * 2 * dh * hq * pairs
+    return {"kept_rows": m, "us": round(us, 1), "algorithmic_tflops": round(fl / (us * 1e-6) / 1e12, 1),
+            "frac_bf16_peak": round(fl / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def measure_configs(torch, tg, dev, timed, pct):

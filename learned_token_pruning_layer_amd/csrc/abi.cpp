@@ -355,8 +355,8 @@ tg_status tg_gated_attention_backward(tg_dtype dt, const void* q, const void* k,
     std::vector<char> table(tg::attention_backward_table_bytes());
     const size_t need = tg::attention_backward_plan(st_, hq, head_dim, table.data());
     if (m == 0) {
-        hipError_t e = hipMemsetAsync(d_gain, 0, sizeof(float) * hq, stream);
-        if (e == hipSuccess) e = hipMemsetAsync(d_tau, 0, sizeof(float), stream);
+        hipError_t e = tg::launch_zero_f32(d_gain, hq, stream);
+        if (e == hipSuccess) e = tg::launch_zero_f32(d_tau, 1, stream);
         if (e != hipSuccess) return hip_fail(e, "tg_gated_attention_backward clear");
         return TG_OK;
     }

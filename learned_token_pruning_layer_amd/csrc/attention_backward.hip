@@ -526,6 +526,11 @@ __global__ __launch_bounds__(256) void score_grad_kernel(const float* __restrict
 }
 }  // namespace
 
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st) {
+    if (n > 0) hipLaunchKernelGGL(score_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_score_grad(const float* d_bias, const float* scores, const int32_t* kept, const SeqTable& t,
                              int64_t m, int64_t n_rows, float* d_scores, hipStream_t st) {
     if (n_rows > 0)

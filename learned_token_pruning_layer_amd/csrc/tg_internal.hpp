@@ -133,6 +133,8 @@ struct AttnBwdArgs {
 size_t attention_backward_plan(const SeqTable& st, int hq, int head_dim, void* table_out);
 size_t attention_backward_table_bytes();
 hipError_t launch_attention_backward(const AttnBwdArgs& a, const void* table, hipStream_t st);
+// Fill kernel (graph-capture safe, unlike a memset node): p[0 .. n) = 0.
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st);
 hipError_t launch_score_grad(const float* d_bias, const float* scores, const int32_t* kept, const SeqTable& t,
                              int64_t m, int64_t n_rows, float* d_scores, hipStream_t st);
 
