@@ -71,6 +71,34 @@ __device__ __forceinline__ void load_tile(LDS_AS char* tile, const uint16_t* __r
     }
 }
 
+// The same copy split in two halves, so that the global loads of the next
+// tile can be in flight (in registers) while the current tile is used.
+template <int D>
+struct TileRegs {
+    static constexpr int N = 32 * (D / 8) / 64;  // 16-byte chunks per lane
+    u32x4 w[N];
+};
+template <int D>
+__device__ __forceinline__ void fetch_tile(TileRegs<D>& r, const uint16_t* __restrict__ src, int64_t stride,
+                                           int row0, int n_rows, int lane) {
+    constexpr int CH = D / 8;
+#pragma unroll
+    for (int u = 0; u < TileRegs<D>::N; ++u) {
+        const int idx = u * 64 + lane;
+        const int gr = min(row0 + idx / CH, n_rows - 1);
+        r.w[u] = *(const u32x4*)(src + gr * stride + (idx % CH) * 8);
+    }
+}
+template <int D>
+__device__ __forceinline__ void store_tile(LDS_AS char* tile, const TileRegs<D>& r, int lane) {
+    constexpr int CH = D / 8;
+#pragma unroll
+    for (int u = 0; u < TileRegs<D>::N; ++u) {
+        const int idx = u * 64 + lane;
+        *(LDS_AS u32x4*)(tile + (idx / CH) * Tile<D>::RS + (idx % CH) * 16) = r.w[u];
+    }
+}
+
 // A/B operand for k-step s of a 32x32x16 MFMA whose rows (A) or columns (B)
 // are the tile's columns d = 32b + (lane%32) and whose k-slots (lane/32, e)
 // are tile rows 16s + 8(e/4) + 4(lane/32) + e%4: four transpose reads.
@@ -170,6 +198,14 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
 
     load_tile<D>((LDS_AS char*)kt, k + (off * hkv + kvh) * D, (int64_t)hkv * D, key0, n, lane);
     load_tile<D>((LDS_AS char*)vt, v + (off * hkv + kvh) * D, (int64_t)hkv * D, key0, n, lane);
+    __syncthreads();
+    // The key block's row operands (S = Q K^T, dP = dO V^T) stay in registers.
+    bf16x8 kop[KS], vop[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        kop[s] = tile_row_operand<D>((const LDS_AS char*)kt, s, lane);
+        vop[s] = tile_row_operand<D>((const LDS_AS char*)vt, s, lane);
+    }
     const int key = key0 + l32;                       // this lane's key column
     const bool key_ok = key < n;
     const float b_key = bias[off + min(key, n - 1)];
@@ -191,31 +227,66 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
         }
     float db_acc = 0.0f, dg_acc = 0.0f, dt_acc = 0.0f;
 
-    for (int ib = i0; ib < t.s[sg].n_blk; ++ib) {
+    // Q / dO tiles and the per-query scalars of block ib + 1 are fetched into
+    // registers while block ib is processed.
+    const uint16_t* qsrc = q + (off * hq + h) * D;
+    const uint16_t* dsrc = d_out + (off * hq + h) * D;
+    TileRegs<D> rq, rd;
+    float n_lse = 0.0f, n_dl = 0.0f;
+    int32_t n_pos = 0;
+    auto fetch_q = [&](int ib) __attribute__((always_inline)) {
+        fetch_tile<D>(rq, qsrc, (int64_t)hq * D, 32 * ib, n, lane);
+        fetch_tile<D>(rd, dsrc, (int64_t)hq * D, 32 * ib, n, lane);
+        const int qi = min(32 * ib + (lane & 31), n - 1);
+        n_lse = lse[(int64_t)h * m + off + qi] * LOG2E;
+        n_dl = dl[(int64_t)h * m + off + qi];
+        n_pos = pos[off + qi];
+    };
+    const int n_blk = t.s[sg].n_blk;
+    fetch_q(i0);
+    for (int ib = i0; ib < n_blk; ++ib) {
         const int qrow0 = 32 * ib;
         __syncthreads();  // previous iteration's reads of qt / dot are done
-        load_tile<D>((LDS_AS char*)qt, q + (off * hq + h) * D, (int64_t)hq * D, qrow0, n, lane);
-        load_tile<D>((LDS_AS char*)dot, d_out + (off * hq + h) * D, (int64_t)hq * D, qrow0, n, lane);
+        store_tile<D>((LDS_AS char*)qt, rq, lane);
+        store_tile<D>((LDS_AS char*)dot, rd, lane);
         if (lane < 32) {
-            const int qi = min(qrow0 + lane, n - 1);
-            s_lse[lane] = lse[(int64_t)h * m + off + qi] * LOG2E;
-            s_dl[lane] = dl[(int64_t)h * m + off + qi];
-            s_pos[lane] = pos[off + qi];
+            s_lse[lane] = n_lse;
+            s_dl[lane] = n_dl;
+            s_pos[lane] = n_pos;
         }
         __syncthreads();
+        if (ib + 1 < n_blk) fetch_q(ib + 1);
         f32x16 sacc, pacc;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             sacc[j] = 0.0f;
             pacc[j] = 0.0f;
         }
+        // Operands are read from LDS ahead of their MFMAs (one batch of row
+        // reads, then the transpose reads while the softmax math runs), so the
+        // LDS latency is paid once per batch rather than once per MFMA.
+        bf16x8 qop[KS], dop[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row_operand<D>((const LDS_AS char*)qt, s, lane),
-                                                           tile_row_operand<D>((const LDS_AS char*)kt, s, lane), sacc, 0, 0, 0);
-            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row_operand<D>((const LDS_AS char*)dot, s, lane),
-                                                           tile_row_operand<D>((const LDS_AS char*)vt, s, lane), pacc, 0, 0, 0);
+            qop[s] = tile_row_operand<D>((const LDS_AS char*)qt, s, lane);
+            dop[s] = tile_row_operand<D>((const LDS_AS char*)dot, s, lane);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[s], kop[s], sacc, 0, 0, 0);
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dop[s], vop[s], pacc, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 dotr[DB][2], qtr[DB][2];
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                dotr[b][s] = tile_tr_operand<D>((const LDS_AS char*)dot, b, s, lane);
+                qtr[b][s] = tile_tr_operand<D>((const LDS_AS char*)qt, b, s, lane);
+            }
+        __builtin_amdgcn_sched_barrier(0);
         // Register j: query qrow0 + 8(j/4) + 4hh + j%4 of key `key`.
         bf16x8 pf[2], dsf[2];
 #pragma unroll
@@ -247,10 +318,8 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
         for (int b = 0; b < DB; ++b)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                acc_dv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[s], tile_tr_operand<D>((const LDS_AS char*)dot, b, s, lane),
-                                                                    acc_dv[b], 0, 0, 0);
-                acc_dk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsf[s], tile_tr_operand<D>((const LDS_AS char*)qt, b, s, lane),
-                                                                    acc_dk[b], 0, 0, 0);
+                acc_dv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[s], dotr[b][s], acc_dv[b], 0, 0, 0);
+                acc_dk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsf[s], qtr[b][s], acc_dk[b], 0, 0, 0);
             }
     }
     // Accumulator j of block b: key key0 + 8(j/4) + 4hh + j%4, d = 32b + l32.
@@ -329,27 +398,56 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[b][j] = 0.0f;
 
+    // K / V tiles and the key scalars of block kb + 1 are fetched into
+    // registers while block kb is processed.
+    const uint16_t* ksrc = k + (off * hkv + kvh) * D;
+    const uint16_t* vsrc = v + (off * hkv + kvh) * D;
+    TileRegs<D> rk, rv;
+    float n_b = 0.0f;
+    int32_t n_p = 0;
+    auto fetch_kv = [&](int kb) __attribute__((always_inline)) {
+        fetch_tile<D>(rk, ksrc, (int64_t)hkv * D, 32 * kb, n, lane);
+        fetch_tile<D>(rv, vsrc, (int64_t)hkv * D, 32 * kb, n, lane);
+        const int kr = 32 * kb + (lane & 31);
+        n_b = bias[off + min(kr, n - 1)];
+        n_p = (kr < n) ? pos[off + kr] : INT32_MAX;
+    };
+    fetch_kv(0);
     for (int kb = 0; kb < n_kt; ++kb) {
-        const int key0 = 32 * kb;
         __syncthreads();
-        load_tile<D>((LDS_AS char*)kt, k + (off * hkv + kvh) * D, (int64_t)hkv * D, key0, n, lane);
-        load_tile<D>((LDS_AS char*)vt, v + (off * hkv + kvh) * D, (int64_t)hkv * D, key0, n, lane);
+        store_tile<D>((LDS_AS char*)kt, rk, lane);
+        store_tile<D>((LDS_AS char*)vt, rv, lane);
         if (lane < 32) {
-            s_b[lane] = bias[off + min(key0 + lane, n - 1)];
-            s_p[lane] = (key0 + lane < n) ? pos[off + key0 + lane] : INT32_MAX;
+            s_b[lane] = n_b;
+            s_p[lane] = n_p;
         }
         __syncthreads();
+        if (kb + 1 < n_kt) fetch_kv(kb + 1);
         f32x16 sacc, pacc;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             sacc[j] = 0.0f;
             pacc[j] = 0.0f;
         }
+        bf16x8 kop[KS], vop[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row_operand<D>((const LDS_AS char*)kt, s, lane), qf[s], sacc, 0, 0, 0);
-            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row_operand<D>((const LDS_AS char*)vt, s, lane), df[s], pacc, 0, 0, 0);
+            kop[s] = tile_row_operand<D>((const LDS_AS char*)kt, s, lane);
+            vop[s] = tile_row_operand<D>((const LDS_AS char*)vt, s, lane);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s], qf[s], sacc, 0, 0, 0);
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[s], df[s], pacc, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 ktr[DB][2];
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) ktr[b][s] = tile_tr_operand<D>((const LDS_AS char*)kt, b, s, lane);
+        __builtin_amdgcn_sched_barrier(0);
         // Register j: key key0 + 8(j/4) + 4hh + j%4 of query qi.
         bf16x8 dsf[2];
 #pragma unroll
@@ -374,8 +472,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__
         for (int b = 0; b < DB; ++b)
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr_operand<D>((const LDS_AS char*)kt, b, s, lane), dsf[s], acc[b],
-                                                                 0, 0, 0);
+                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktr[b][s], dsf[s], acc[b], 0, 0, 0);
     }
     // acc[b] register j: d = 32b + 8(j/4) + 4hh + j%4 of query qi.
     if (q_ok) {
