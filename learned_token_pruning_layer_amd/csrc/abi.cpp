@@ -330,7 +330,7 @@ size_t tg_attention_backward_workspace_bytes(const tg_seq* seqs, int32_t n_seqs,
     if (build_seq_table(seqs, n_seqs, &st_, &m) != TG_OK) return 0;
     g_err.clear();
     std::vector<char> table(tg::attention_backward_table_bytes());
-    return tg::attention_backward_plan(st_, hq, head_dim, table.data());
+    return tg::attention_backward_plan(st_, hq, hkv, head_dim, table.data());
 }
 
 tg_status tg_gated_attention_backward(tg_dtype dt, const void* q, const void* k, const void* v, const float* bias_kept,
@@ -353,7 +353,7 @@ tg_status tg_gated_attention_backward(tg_dtype dt, const void* q, const void* k,
     if (st != TG_OK) return st;
     if (!d_gain || !d_tau) return fail(TG_ERR_INVALID_ARGUMENT, "d_gain, d_tau must be non-NULL");
     std::vector<char> table(tg::attention_backward_table_bytes());
-    const size_t need = tg::attention_backward_plan(st_, hq, head_dim, table.data());
+    const size_t need = tg::attention_backward_plan(st_, hq, hkv, head_dim, table.data());
     if (m == 0) {
         hipError_t e = tg::launch_zero_f32(d_gain, hq, stream);
         if (e == hipSuccess) e = tg::launch_zero_f32(d_tau, 1, stream);

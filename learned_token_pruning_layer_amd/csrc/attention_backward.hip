@@ -12,7 +12,7 @@
 //     dS_ij = p_ij (dP_ij - dO_i . o_i),
 //     dQ_i = c sum_j dS_ij k_j,   dK_j = c sum_i dS_ij q_i,
 //     db_j = sum_h g_h sum_i dS_ij,   dg_h = sum_ij dS_ij b_j,
-//     dtau = -(c / tau) sum_hij dS_ij q_i.k_j,
+//     dtau = -(c / tau) sum_hij dS_ij q_i.k_j = -(1 / tau) sum_j k_j . dK_j,
 // and the score of a kept document row gets db_j * sigmoid(-s_j) (the
 // derivative of logsigmoid); question and pruned rows get 0.
 //
@@ -26,14 +26,17 @@
 //     straight from those registers (the query order inside each 16-wide
 //     k-step is permuted the same way on both operands) and dO / Q read
 //     transposed from LDS (ds_read_b64_tr_b16). Per-head partial dK, dV and
-//     db go to a workspace, the head's dg and dtau partials per wave.
+//     sum_i dS_ij go to a workspace. Blocks that every query of the query
+//     block can fully see take a path without the causal and ragged masks.
 //  3. dq: one wave per (prompt, 32-query block, query head), like the
 //     forward kernel: S^T = K Q^T and dP^T = V dO^T with Q and dO in
 //     registers, dS^T in registers, dQ^T += K^T dS^T with K^T read
 //     transposed from LDS.
-//  4. reduce: sums the per-head partials of each KV head (and of the
-//     gain / temperature) in a fixed order, so the result is deterministic;
-//     the score kernel applies sigmoid(-s).
+//  4. reduce: sums the per-head partials of each KV head in a fixed order
+//     (so the result is deterministic), applies the gains to db, and forms
+//     per-workgroup partials of sum k . dK; a last kernel reduces dg_h =
+//     sum_j b_j sum_i dS_ij per head and dtau from those partials, each in
+//     a fixed order. The score kernel applies sigmoid(-s).
 // LDS tiles are row-major with a 16-byte pad per row (row stride D*2+16
 // bytes), which spreads both the row reads and the transpose reads over
 // the banks.
@@ -180,11 +183,11 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ d_out, const float* __restrict__ lse, const float* __restrict__ dl,
     const float* __restrict__ bias, const int32_t* __restrict__ pos, BwdTable t, int hq, int hkv,
     const float* __restrict__ gain, float c, float* __restrict__ ws_dk, float* __restrict__ ws_dv,
-    float* __restrict__ ws_db, float* __restrict__ ws_item) {
+    float* __restrict__ ws_db) {
     constexpr int KS = D / 16, DB = D / 32;
     __shared__ __attribute__((aligned(16))) char kt[Tile<D>::BYTES], vt[Tile<D>::BYTES];
     __shared__ __attribute__((aligned(16))) char qt[Tile<D>::BYTES], dot[Tile<D>::BYTES];
-    __shared__ __attribute__((aligned(16))) float s_lse[32], s_dl[32];
+    __shared__ __attribute__((aligned(16))) float s_nlse[32], s_dl[32];
     __shared__ __attribute__((aligned(16))) int32_t s_pos[32];
     const int lane = threadIdx.x;
     const int hh = lane >> 5, l32 = lane & 31;
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
     const int n = t.s[sg].n;
     const int kvh = h / (hq / hkv);
     const int key0 = 32 * jb;
-    const float c2 = c * LOG2E, gb2 = gain[h] * LOG2E, g = gain[h];
+    const float c2 = c * LOG2E, gb2 = gain[h] * LOG2E;
 
     load_tile<D>((LDS_AS char*)kt, k + (off * hkv + kvh) * D, (int64_t)hkv * D, key0, n, lane);
     load_tile<D>((LDS_AS char*)vt, v + (off * hkv + kvh) * D, (int64_t)hkv * D, key0, n, lane);
@@ -208,9 +211,12 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
     }
     const int key = key0 + l32;                       // this lane's key column
     const bool key_ok = key < n;
-    const float b_key = bias[off + min(key, n - 1)];
+    const float kterm = gb2 * bias[off + min(key, n - 1)];
     const int32_t p_key = pos[off + min(key, n - 1)];
     const int32_t p_key0 = pos[off + key0];
+    // Every query of a full query block at or after this position sees every
+    // key of a full key block.
+    const int32_t p_key_last = key0 + 32 <= n ? pos[off + key0 + 31] : INT32_MAX;
 
     // First query block that can see a key of this block (positions never
     // decrease along the kept rows; repeats can reach earlier blocks).
@@ -225,20 +231,20 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
             acc_dk[b][j] = 0.0f;
             acc_dv[b][j] = 0.0f;
         }
-    float db_acc = 0.0f, dg_acc = 0.0f, dt_acc = 0.0f;
+    float db_acc = 0.0f;
 
     // Q / dO tiles and the per-query scalars of block ib + 1 are fetched into
     // registers while block ib is processed.
     const uint16_t* qsrc = q + (off * hq + h) * D;
     const uint16_t* dsrc = d_out + (off * hq + h) * D;
     TileRegs<D> rq, rd;
-    float n_lse = 0.0f, n_dl = 0.0f;
+    float n_nlse = 0.0f, n_dl = 0.0f;
     int32_t n_pos = 0;
     auto fetch_q = [&](int ib) __attribute__((always_inline)) {
         fetch_tile<D>(rq, qsrc, (int64_t)hq * D, 32 * ib, n, lane);
         fetch_tile<D>(rd, dsrc, (int64_t)hq * D, 32 * ib, n, lane);
         const int qi = min(32 * ib + (lane & 31), n - 1);
-        n_lse = lse[(int64_t)h * m + off + qi] * LOG2E;
+        n_nlse = -lse[(int64_t)h * m + off + qi] * LOG2E;
         n_dl = dl[(int64_t)h * m + off + qi];
         n_pos = pos[off + qi];
     };
@@ -250,10 +256,12 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
         store_tile<D>((LDS_AS char*)qt, rq, lane);
         store_tile<D>((LDS_AS char*)dot, rd, lane);
         if (lane < 32) {
-            s_lse[lane] = n_lse;
+            s_nlse[lane] = n_nlse;
             s_dl[lane] = n_dl;
             s_pos[lane] = n_pos;
         }
+        // Lane 0 holds the position of the block's first (lowest) query.
+        const bool full = qrow0 + 32 <= n && __builtin_amdgcn_readfirstlane(n_pos) >= p_key_last;
         __syncthreads();
         if (ib + 1 < n_blk) fetch_q(ib + 1);
         f32x16 sacc, pacc;
@@ -287,33 +295,52 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
                 qtr[b][s] = tile_tr_operand<D>((const LDS_AS char*)qt, b, s, lane);
             }
         __builtin_amdgcn_sched_barrier(0);
-        // Register j: query qrow0 + 8(j/4) + 4hh + j%4 of key `key`.
-        bf16x8 pf[2], dsf[2];
+        // Register j: query qrow0 + 8(j/4) + 4hh + j%4 of key `key`; the
+        // per-query scalars of four consecutive queries come in one read.
+        f32x4 nl[4], dlq[4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            u32x4 wp, wd;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                float pv[2], dv_[2];
-#pragma unroll
-                for (int t2 = 0; t2 < 2; ++t2) {
-                    const int j = 8 * s + 2 * e2 + t2;
-                    const int qloc = 8 * (j / 4) + 4 * hh + (j % 4);
-                    const bool vis = key_ok & (qrow0 + qloc < n) & (p_key <= s_pos[qloc]);
-                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[j], c2, fmaf(gb2, b_key, -s_lse[qloc])))
-                                        : 0.0f;
-                    const float ds = p * (pacc[j] - s_dl[qloc]);
-                    db_acc += ds;
-                    dt_acc = fmaf(ds, sacc[j], dt_acc);
-                    pv[t2] = p;
-                    dv_[t2] = ds;
-                }
-                wp[e2] = pack_bf16x2(pv[0], pv[1]);
-                wd[e2] = pack_bf16x2(dv_[0], dv_[1]);
-            }
-            pf[s] = __builtin_bit_cast(bf16x8, wp);
-            dsf[s] = __builtin_bit_cast(bf16x8, wd);
+        for (int g4 = 0; g4 < 4; ++g4) {
+            nl[g4] = *(const LDS_AS f32x4*)(s_nlse + 8 * g4 + 4 * hh);
+            dlq[g4] = *(const LDS_AS f32x4*)(s_dl + 8 * g4 + 4 * hh);
         }
+        bf16x8 pf[2], dsf[2];
+        auto softmax = [&](auto masked) __attribute__((always_inline)) {
+            i32x4 pq[4];
+            if constexpr (decltype(masked)::value) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) pq[g4] = *(const LDS_AS i32x4*)(s_pos + 8 * g4 + 4 * hh);
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u32x4 wp, wd;
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    float pv[2], dv_[2];
+#pragma unroll
+                    for (int t2 = 0; t2 < 2; ++t2) {
+                        const int j = 8 * s + 2 * e2 + t2;
+                        float p = __builtin_amdgcn_exp2f(fmaf(sacc[j], c2, kterm + nl[j / 4][j % 4]));
+                        if constexpr (decltype(masked)::value) {
+                            const int qloc = 8 * (j / 4) + 4 * hh + (j % 4);
+                            const bool vis = key_ok & (qrow0 + qloc < n) & (p_key <= pq[j / 4][j % 4]);
+                            p = vis ? p : 0.0f;
+                        }
+                        const float ds = p * (pacc[j] - dlq[j / 4][j % 4]);
+                        db_acc += ds;
+                        pv[t2] = p;
+                        dv_[t2] = ds;
+                    }
+                    wp[e2] = pack_bf16x2(pv[0], pv[1]);
+                    wd[e2] = pack_bf16x2(dv_[0], dv_[1]);
+                }
+                pf[s] = __builtin_bit_cast(bf16x8, wp);
+                dsf[s] = __builtin_bit_cast(bf16x8, wd);
+            }
+        };
+        if (full)
+            softmax(std::false_type{});
+        else
+            softmax(std::true_type{});
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -334,20 +361,10 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
                 ws_dv[o] = acc_dv[b][j];
             }
         }
-    // db: this lane's key, summed over both query halves.
+    // sum_i dS_ij of this lane's key, over both query halves (the gain is
+    // applied when the heads are summed).
     db_acc += __shfl_xor(db_acc, 32);
-    if (hh == 0 && key_ok) ws_db[(int64_t)h * m + off + key] = g * db_acc;
-    dg_acc = db_acc * b_key;  // per key, both halves already added
-    if (hh == 1 || !key_ok) dg_acc = 0.0f;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        dg_acc += __shfl_xor(dg_acc, o);
-        dt_acc += __shfl_xor(dt_acc, o);
-    }
-    if (lane == 0) {
-        ws_item[2 * blockIdx.x] = dg_acc;
-        ws_item[2 * blockIdx.x + 1] = dt_acc;
-    }
+    if (hh == 0 && key_ok) ws_db[(int64_t)h * m + off + key] = db_acc;
 }
 
 // 3. dQ of one (prompt, query block, head).
@@ -360,7 +377,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__
                                                    const float* __restrict__ gain, float c, float* __restrict__ dq) {
     constexpr int KS = D / 16, DB = D / 32;
     __shared__ __attribute__((aligned(16))) char kt[Tile<D>::BYTES], vt[Tile<D>::BYTES];
-    __shared__ __attribute__((aligned(16))) float s_b[32];
+    __shared__ __attribute__((aligned(16))) float s_kb[32];
     __shared__ __attribute__((aligned(16))) int32_t s_p[32];
     const int lane = threadIdx.x;
     const int hh = lane >> 5, l32 = lane & 31;
@@ -373,10 +390,13 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__
     const int qi = min(i0 + l32, n - 1);
     const bool q_ok = i0 + l32 < n;
     const float c2 = c * LOG2E, gb2 = gain[h] * LOG2E;
-    const float lse2 = lse[(int64_t)h * m + off + qi] * LOG2E;
+    const float nlse2 = -lse[(int64_t)h * m + off + qi] * LOG2E;
     const float dlq = dl[(int64_t)h * m + off + qi];
     const int32_t my_pos = pos[off + qi];
     const int32_t pos_last = pos[off + min(i0 + 31, n - 1)];
+    // Lowest query position of the block, if the block is full: a full key
+    // block whose last key is at or before it is visible to every query.
+    const int32_t pos_first = i0 + 32 <= n ? pos[off + i0] : INT32_MIN;
 
     bf16x8 qf[KS], df[KS];
     {
@@ -403,13 +423,13 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__
     const uint16_t* ksrc = k + (off * hkv + kvh) * D;
     const uint16_t* vsrc = v + (off * hkv + kvh) * D;
     TileRegs<D> rk, rv;
-    float n_b = 0.0f;
+    float n_kb = 0.0f;
     int32_t n_p = 0;
     auto fetch_kv = [&](int kb) __attribute__((always_inline)) {
         fetch_tile<D>(rk, ksrc, (int64_t)hkv * D, 32 * kb, n, lane);
         fetch_tile<D>(rv, vsrc, (int64_t)hkv * D, 32 * kb, n, lane);
         const int kr = 32 * kb + (lane & 31);
-        n_b = bias[off + min(kr, n - 1)];
+        n_kb = gb2 * bias[off + min(kr, n - 1)];
         n_p = (kr < n) ? pos[off + kr] : INT32_MAX;
     };
     fetch_kv(0);
@@ -418,9 +438,11 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__
         store_tile<D>((LDS_AS char*)kt, rk, lane);
         store_tile<D>((LDS_AS char*)vt, rv, lane);
         if (lane < 32) {
-            s_b[lane] = n_b;
+            s_kb[lane] = n_kb;
             s_p[lane] = n_p;
         }
+        // Lane 31 holds the position of the block's last key (INT32_MAX past the end).
+        const bool full = __builtin_amdgcn_readlane(n_p, 31) <= pos_first;
         __syncthreads();
         if (kb + 1 < n_kt) fetch_kv(kb + 1);
         f32x16 sacc, pacc;
@@ -448,26 +470,40 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__
 #pragma unroll
             for (int s = 0; s < 2; ++s) ktr[b][s] = tile_tr_operand<D>((const LDS_AS char*)kt, b, s, lane);
         __builtin_amdgcn_sched_barrier(0);
-        // Register j: key key0 + 8(j/4) + 4hh + j%4 of query qi.
+        // Register j: key 32kb + 8(j/4) + 4hh + j%4 of query qi; the key
+        // scalars of four consecutive keys come in one read.
+        f32x4 kb4[4];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) kb4[g4] = *(const LDS_AS f32x4*)(s_kb + 8 * g4 + 4 * hh);
         bf16x8 dsf[2];
+        auto softmax = [&](auto masked) __attribute__((always_inline)) {
+            i32x4 pk[4];
+            if constexpr (decltype(masked)::value) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            u32x4 w;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                float dv_[2];
-#pragma unroll
-                for (int t2 = 0; t2 < 2; ++t2) {
-                    const int j = 8 * s + 2 * e2 + t2;
-                    const int kl = 8 * (j / 4) + 4 * hh + (j % 4);
-                    const bool vis = q_ok & (s_p[kl] <= my_pos);
-                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[j], c2, fmaf(gb2, s_b[kl], -lse2))) : 0.0f;
-                    dv_[t2] = p * (pacc[j] - dlq);
-                }
-                w[e2] = pack_bf16x2(dv_[0], dv_[1]);
+                for (int g4 = 0; g4 < 4; ++g4) pk[g4] = *(const LDS_AS i32x4*)(s_p + 8 * g4 + 4 * hh);
             }
-            dsf[s] = __builtin_bit_cast(bf16x8, w);
-        }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u32x4 w;
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    float dv_[2];
+#pragma unroll
+                    for (int t2 = 0; t2 < 2; ++t2) {
+                        const int j = 8 * s + 2 * e2 + t2;
+                        float p = __builtin_amdgcn_exp2f(fmaf(sacc[j], c2, kb4[j / 4][j % 4] + nlse2));
+                        if constexpr (decltype(masked)::value) p = (q_ok & (pk[j / 4][j % 4] <= my_pos)) ? p : 0.0f;
+                        dv_[t2] = p * (pacc[j] - dlq);
+                    }
+                    w[e2] = pack_bf16x2(dv_[0], dv_[1]);
+                }
+                dsf[s] = __builtin_bit_cast(bf16x8, w);
+            }
+        };
+        if (full)
+            softmax(std::false_type{});
+        else
+            softmax(std::true_type{});
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -490,15 +526,21 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__
 }
 
 // 4a. dK, dV = sums of the per-head partials over each KV head's query
-// heads (in head order); db = sum over all heads.
+// heads (in head order); db = sum over heads of g_h times the head's
+// sum_i dS_ij; per workgroup, the partial sum of k . dK over its elements
+// (a fixed-order tree) for the temperature.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ ws_dk,
                                                         const float* __restrict__ ws_dv,
-                                                        const float* __restrict__ ws_db, int64_t m, int hq, int hkv,
+                                                        const float* __restrict__ ws_db,
+                                                        const uint16_t* __restrict__ k,
+                                                        const float* __restrict__ gain, int64_t m, int hq, int hkv,
                                                         float* __restrict__ dk, float* __restrict__ dv,
-                                                        float* __restrict__ db) {
+                                                        float* __restrict__ db, float* __restrict__ ws_part) {
+    __shared__ float part[4];
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over m * hkv * D
     const int gsz = hq / hkv;
+    float kd = 0.0f;
     if (idx < m * hkv * D) {
         const int64_t row = idx / (hkv * D);
         const int kvh = (int)((idx / D) % hkv), d = (int)(idx % D);
@@ -510,35 +552,64 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict
         }
         dk[idx] = a;
         dv[idx] = b;
+        kd = __uint_as_float((uint32_t)k[idx] << 16) * a;
     }
     if (idx < m) {
         float s = 0.0f;
-        for (int h = 0; h < hq; ++h) s += ws_db[(int64_t)h * m + idx];
+        for (int h = 0; h < hq; ++h) s = fmaf(gain[h], ws_db[(int64_t)h * m + idx], s);
         db[idx] = s;
     }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) kd += __shfl_xor(kd, o);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = kd;
+    __syncthreads();
+    if (threadIdx.x == 0) ws_part[blockIdx.x] = (part[0] + part[1]) + (part[2] + part[3]);
 }
 
-// 4b. dg_h = sum of the head's item partials (prompt, block order);
-// dtau = -(c/tau) * sum of all dtau partials. One workgroup.
-__global__ __launch_bounds__(256) void bwd_scalars_kernel(const float* __restrict__ ws_item, BwdTable t, int hq,
-                                                         float c_over_tau, float* __restrict__ dgain,
-                                                         float* __restrict__ dtau) {
-    __shared__ float part[256];
-    const int tid = threadIdx.x;
-    for (int h = tid; h < hq; h += 256) {
-        float s = 0.0f;
-        for (int sg = 0; sg < t.n_seg; ++sg)
-            for (int b = 0; b < t.s[sg].n_blk; ++b) s += ws_item[2 * (t.s[sg].item0 + b * hq + h)];
-        dgain[h] = s;
-    }
-    float s = 0.0f;
-    for (int i = tid; i < t.n_items; i += 256) s += ws_item[2 * i + 1];
-    part[tid] = s;
+// Fixed-order sum of one 1024-thread workgroup's values (a butterfly per
+// wave, then the sixteen wave sums in order); valid in thread 0.
+__device__ __forceinline__ float block_sum_1024(float v, float* part) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
     __syncthreads();
-    if (tid == 0) {
-        float tot = 0.0f;
-        for (int i = 0; i < 256; ++i) tot += part[i];
-        *dtau = -c_over_tau * tot;
+    float s = 0.0f;
+    if (threadIdx.x == 0)
+        for (int i = 0; i < 16; ++i) s += part[i];
+    return s;
+}
+
+// 4b. Workgroup h < hq: dg_h = sum_j b_j sum_i dS_ij over all kept rows.
+// Workgroup hq: dtau = -(1/tau) * sum of the k . dK partials. Each thread
+// keeps four loads in flight; the summation order is fixed.
+__global__ __launch_bounds__(1024) void bwd_scalars_kernel(const float* __restrict__ ws_db,
+                                                          const float* __restrict__ bias, int64_t m, int hq,
+                                                          const float* __restrict__ ws_part, int64_t n_part,
+                                                          float inv_tau, float* __restrict__ dgain,
+                                                          float* __restrict__ dtau) {
+    __shared__ float part[16];
+    const int h = blockIdx.x;
+    const bool gain_wg = h < hq;
+    const float* x = gain_wg ? ws_db + (int64_t)h * m : ws_part;
+    const int64_t len = gain_wg ? m : n_part;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t j0 = threadIdx.x; j0 < len; j0 += 4 * 1024) {
+        float xv[4], bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t j = j0 + (int64_t)u * 1024;
+            xv[u] = j < len ? x[j] : 0.0f;
+            bv[u] = (gain_wg && j < len) ? bias[j] : 1.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] = fmaf(bv[u], xv[u], acc[u]);
+    }
+    const float tot = block_sum_1024((acc[0] + acc[1]) + (acc[2] + acc[3]), part);
+    if (threadIdx.x == 0) {
+        if (gain_wg)
+            dgain[h] = tot;
+        else
+            *dtau = -inv_tau * tot;
     }
 }
 
@@ -550,24 +621,26 @@ hipError_t launch_bwd_d(const AttnBwdArgs& a, const BwdTable& t, float c, hipStr
     float* ws_dk = dl + (int64_t)a.hq * m;
     float* ws_dv = ws_dk + (int64_t)a.hq * m * D;
     float* ws_db = ws_dv + (int64_t)a.hq * m * D;
-    float* ws_item = ws_db + (int64_t)a.hq * m;
+    float* ws_part = ws_db + (int64_t)a.hq * m;
+    const int64_t n_red = (m * a.hkv * D + 255) / 256;
     const uint16_t *q = (const uint16_t*)a.q, *k = (const uint16_t*)a.k, *v = (const uint16_t*)a.v;
     const uint16_t *dout = (const uint16_t*)a.d_out, *out = (const uint16_t*)a.out;
     hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((m * a.hq + 255) / 256)), dim3(256), 0, st, dout, out, m,
                        a.hq, dl);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)t.n_items), dim3(64), 0, st, q, k, v, dout, a.lse, dl,
-                       a.bias, a.pos, t, a.hq, a.hkv, a.gain, c, ws_dk, ws_dv, ws_db, ws_item);
+                       a.bias, a.pos, t, a.hq, a.hkv, a.gain, c, ws_dk, ws_dv, ws_db);
     hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)t.n_items), dim3(64), 0, st, q, k, v, dout, a.lse, dl,
                        a.bias, a.pos, t, a.hq, a.hkv, a.gain, c, a.d_q);
-    hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3((unsigned)((m * a.hkv * D + 255) / 256)), dim3(256), 0, st, ws_dk,
-                       ws_dv, ws_db, m, a.hq, a.hkv, a.d_k, a.d_v, a.d_bias);
-    hipLaunchKernelGGL(bwd_scalars_kernel, dim3(1), dim3(256), 0, st, ws_item, t, a.hq, c / a.tau, a.d_gain, a.d_tau);
+    hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3((unsigned)n_red), dim3(256), 0, st, ws_dk, ws_dv, ws_db, k,
+                       a.gain, m, a.hq, a.hkv, a.d_k, a.d_v, a.d_bias, ws_part);
+    hipLaunchKernelGGL(bwd_scalars_kernel, dim3((unsigned)(a.hq + 1)), dim3(1024), 0, st, ws_db, a.bias, m, a.hq,
+                       ws_part, n_red, 1.0f / a.tau, a.d_gain, a.d_tau);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t attention_backward_plan(const SeqTable& st, int hq, int head_dim, void* table_out) {
+size_t attention_backward_plan(const SeqTable& st, int hq, int hkv, int head_dim, void* table_out) {
     BwdTable& t = *(BwdTable*)table_out;
     t = BwdTable{};
     t.n_seg = st.n;
@@ -582,8 +655,10 @@ size_t attention_backward_plan(const SeqTable& st, int hq, int head_dim, void* t
     }
     t.n_items = (int32_t)items;
     t.m_total = m;
-    // Dl [hq][M], dk and dv partials [hq][M][D], db partials [hq][M], 2 per item.
-    return ((size_t)hq * m * (2 + 2 * (size_t)head_dim) + 2 * (size_t)items) * sizeof(float);
+    // Dl [hq][M], dk and dv partials [hq][M][D], sum_i dS partials [hq][M],
+    // one k . dK partial per 256 elements of dK.
+    const size_t n_red = ((size_t)m * hkv * head_dim + 255) / 256;
+    return ((size_t)hq * m * (2 + 2 * (size_t)head_dim) + n_red) * sizeof(float);
 }
 
 size_t attention_backward_table_bytes() { return sizeof(BwdTable); }

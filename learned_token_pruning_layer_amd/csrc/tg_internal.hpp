@@ -130,7 +130,7 @@ struct AttnBwdArgs {
 };
 // Fills the opaque work table (attention_backward_table_bytes() bytes) and
 // returns the workspace bytes.
-size_t attention_backward_plan(const SeqTable& st, int hq, int head_dim, void* table_out);
+size_t attention_backward_plan(const SeqTable& st, int hq, int hkv, int head_dim, void* table_out);
 size_t attention_backward_table_bytes();
 hipError_t launch_attention_backward(const AttnBwdArgs& a, const void* table, hipStream_t st);
 // Fill kernel (graph-capture safe, unlike a memset node): p[0 .. n) = 0.

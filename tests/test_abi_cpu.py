@@ -115,13 +115,12 @@ def test_decode_table_and_rejects_before_launch(lib):
 
 def test_backward_workspace_and_rejects_before_launch(lib):
     # Workspace (fp32 words): the softmax row term [hq][M], per-head dK and dV
-    # partials [hq][M][D] each, per-head bias partials [hq][M], and a gain and a
-    # temperature partial per (prompt, 32-row block, head) item.
+    # partials [hq][M][D] each, per-head bias partials [hq][M], and one partial
+    # of sum k . dK per 256 elements of dK [M][hkv][D].
     prompts = [Prompt(0, 100, 0, 90, 40), Prompt(100, 70, 0, 0, 0)]  # 50 and 70 kept rows
-    m, hq, d = 120, 16, 128
-    items = (2 + 3) * hq
-    need = lib.tg_attention_backward_workspace_bytes(seq_array(prompts), 2, hq, 8, d)
-    assert need == 4 * (hq * m * (2 + 2 * d) + 2 * items)
+    m, hq, hkv, d = 120, 16, 8, 128
+    need = lib.tg_attention_backward_workspace_bytes(seq_array(prompts), 2, hq, hkv, d)
+    assert need == 4 * (hq * m * (2 + 2 * d) + (m * hkv * d + 255) // 256)
     fake = ctypes.c_void_p(4096)
     args = [fake, fake, fake, fake, fake, seq_array(prompts), 2, hq, 8, d, fake, 1.2, fake, fake, fake,
             fake, fake, fake, fake, fake, fake]
