@@ -7,6 +7,7 @@ import this package; the HIP library never does.
 from .tokengate import (  # noqa: F401
     compact,
     decode_attention,
+    gate_backward,
     gate_scores,
     gated_attention,
     gated_attention_backward,

@@ -345,6 +345,40 @@ def score_grad(dbias_kept, scores, kept, prompts: Sequence) -> np.ndarray:
     return out
 
 
+def gate_backward(x, w1, w2, d_scores, rows=None, b1=None):
+    """Gradients of sum_r d_scores[r] * s_r through the gate MLP, the last
+    link of the path from the attention bias back to the scorer.
+
+    With z_r = W1 x_r + b1, a_r = SiLU(z_r) and s_r = w2 . a_r + b2:
+
+        dz_r  = d_scores[r] * w2 * SiLU'(z_r),   SiLU'(z) = sig(z) (1 + z (1 - sig(z)))
+        dW1   = sum_r dz_r x_r^T        db1 = sum_r dz_r
+        dw2   = sum_r d_scores[r] a_r   db2 = sum_r d_scores[r]
+        dx_r  = W1^T dz_r
+
+    The sums run over `rows` (every row if None); rows outside it are taken
+    to have d_scores = 0. Returns dict(dx [len(rows), d] in the order of
+    `rows`, dw1 [H, d], db1 [H], dw2 [H], db2) in fp64.
+    """
+    xd = _f64(x)
+    w1d = _f64(w1)
+    w2d = _f64(w2).reshape(-1)
+    ds = _f64(d_scores).reshape(-1)
+    n = xd.shape[0]
+    idx = np.arange(n, dtype=np.int64) if rows is None else np.asarray(
+        rows.detach().cpu().numpy() if hasattr(rows, "detach") else rows, dtype=np.int64)
+    xr = xd[idx]
+    z = xr @ w1d.T
+    if b1 is not None:
+        z = z + _f64(b1).reshape(-1)
+    sg = sigmoid(z)
+    a = z * sg
+    dsr = ds[idx]
+    dz = dsr[:, None] * w2d[None, :] * (sg * (1.0 + z * (1.0 - sg)))
+    return dict(dx=dz @ w1d, dw1=dz.T @ xr, db1=dz.sum(axis=0), dw2=(dsr[:, None] * a).sum(axis=0),
+                db2=float(dsr.sum()))
+
+
 # ---------------------------------------------------------------------------
 # Next step after prefill: decode over the pruned KV cache.  [DE-prune] (the
 # layers above the gate build no KV for pruned tokens, so their cache holds

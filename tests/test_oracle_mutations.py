@@ -50,6 +50,11 @@ MUTATIONS = [
     ("backward: bias gradient without the gain", "dbias[seg] += g[h] * ds.sum(axis=0)", "dbias[seg] += ds.sum(axis=0)"),
     ("backward: temperature gradient with the wrong sign", "dtau += -(1.0 / float(tau))", "dtau += (1.0 / float(tau))"),
     ("score gradient through sigmoid(+s)", "out[r] = db[m] * sigmoid(-s[r])", "out[r] = db[m] * sigmoid(s[r])"),
+    ("gate backward: SiLU' taken as sigmoid", "(sg * (1.0 + z * (1.0 - sg)))", "(sg)"),
+    ("gate backward: dz without w2", "dz = dsr[:, None] * w2d[None, :] * ", "dz = dsr[:, None] * "),
+    ("gate backward: first bias left out of the recomputed pre-activation", "        z = z + _f64(b1).reshape(-1)\n    sg",
+     "        z = z\n    sg"),
+    ("gate backward: dw2 from the pre-activation", "dw2=(dsr[:, None] * a).sum(axis=0)", "dw2=(dsr[:, None] * z).sum(axis=0)"),
 ]
 
 

@@ -457,6 +457,77 @@ def test_score_grad_chain():
     assert not np.any(ds[pruned])
 
 
+def _gate_bwd_case(seed, n=9, d=6, h=4):
+    rng = np.random.default_rng(seed)
+    return (rng.normal(size=(n, d)), rng.normal(size=(h, d)) / np.sqrt(d), rng.normal(size=h) / np.sqrt(h),
+            rng.normal(size=h) * 0.3, rng.normal(size=n))
+
+
+def test_gate_backward_vs_finite_differences():
+    """Every gradient of L = sum_r ds_r s_r against central differences of the
+    pinned forward (gate_scores), on a tiny gate with biases and a row list."""
+    x, w1, w2, b1, ds = _gate_bwd_case(5)
+    rows = np.array([7, 1, 4, 8])
+    dsm = np.zeros_like(ds)
+    dsm[rows] = ds[rows]  # rows outside the list count as d_scores = 0
+
+    def loss(x_=x, w1_=w1, w2_=w2, b1_=b1, b2=0.25):
+        return float(dsm @ oracle.gate_scores(x_, w1_, w2_, b1_, b2))
+
+    g = oracle.gate_backward(x, w1, w2, ds, rows=rows, b1=b1)
+    eps = 1e-6
+
+    def fd(name, arr, idx):
+        a = arr.copy()
+        a[idx] += eps
+        up = loss(**{name: a})
+        a[idx] -= 2 * eps
+        return (up - loss(**{name: a})) / (2 * eps)
+
+    for idx in [(0, 0), (2, 5), (3, 1)]:
+        assert abs(g["dw1"][idx] - fd("w1_", w1, idx)) < 1e-7
+    for i in range(4):
+        assert abs(g["db1"][i] - fd("b1_", b1, i)) < 1e-7
+        assert abs(g["dw2"][i] - fd("w2_", w2, i)) < 1e-7
+    for m, r in enumerate(rows):
+        for c in (0, 3, 5):
+            assert abs(g["dx"][m, c] - fd("x_", x, (r, c))) < 1e-7
+    assert abs(g["db2"] - (loss(b2=0.25 + eps) - loss(b2=0.25 - eps)) / (2 * eps)) < 1e-7
+
+
+def test_gate_backward_vs_torch_autograd():
+    """The same gradients from torch autograd through a gate written with
+    torch ops (not the oracle), all rows listed."""
+    x, w1, w2, b1, ds = _gate_bwd_case(6, n=11, d=8, h=5)
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in
+         dict(x=x, w1=w1, w2=w2, b1=b1).items()}
+    b2 = torch.tensor(0.5, dtype=torch.float64, requires_grad=True)
+    s = torch.nn.functional.silu(t["x"] @ t["w1"].T + t["b1"]) @ t["w2"] + b2
+    (s * torch.tensor(ds)).sum().backward()
+    g = oracle.gate_backward(x, w1, w2, ds, b1=b1)
+    for mine, ref in (("dx", t["x"]), ("dw1", t["w1"]), ("db1", t["b1"]), ("dw2", t["w2"])):
+        np.testing.assert_allclose(g[mine], ref.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert abs(g["db2"] - b2.grad.item()) < 1e-12
+
+
+def test_gate_backward_invariants():
+    """Zero w2 blocks every gradient but dw2 and db2; unlisted rows change
+    nothing; the gradients are linear in d_scores."""
+    x, w1, w2, b1, ds = _gate_bwd_case(7)
+    g0 = oracle.gate_backward(x, w1, np.zeros_like(w2), ds, b1=b1)
+    assert not np.any(g0["dw1"]) and not np.any(g0["db1"]) and not np.any(g0["dx"])
+    rows = np.array([2, 3, 6])
+    ds2 = ds.copy()
+    ds2[[0, 1, 4]] = 99.0  # rows outside the list
+    ga, gb = (oracle.gate_backward(x, w1, w2, d, rows=rows, b1=b1) for d in (ds, ds2))
+    for k in ("dx", "dw1", "db1", "dw2"):
+        np.testing.assert_array_equal(ga[k], gb[k])
+    g2 = oracle.gate_backward(x, w1, w2, 2.0 * ds, b1=b1)
+    g1 = oracle.gate_backward(x, w1, w2, ds, b1=b1)
+    for k in ("dx", "dw1", "db1", "dw2"):
+        np.testing.assert_allclose(g2[k], 2.0 * g1[k], rtol=1e-14, atol=1e-14)
+
+
 # ---------------------------------------------------------------- decode ----
 
 def _decode_case(seed, segs, hq, hkv, d, n_new_max=3, pos_ties=False):
