@@ -13,6 +13,11 @@
  *   4. tg_gated_attention  causal attention over the kept rows only, with the
  *                          bias of every kept key added to its logits.
  *
+ * Beyond the forward pass: tg_gated_attention_backward, tg_score_grad and
+ * tg_gate_backward carry a gradient from the attention output through the
+ * bias back to the gate's weights (training); tg_decode_attention attends new
+ * tokens over the kept rows' cache (generation).
+ *
  * Sources: the pages about "TokenGate: Adapting LLMs for Fast and
  * Memory-Efficient Prefill with Learned Token Pruning". The spke.com article
  * (German) defines the steps in its section "Wie hat TokenGate das Pruning von
@@ -237,6 +242,35 @@ typedef struct {
     int32_t len;
     int32_t n_new;
 } tg_kv_seq;
+
+/* Device workspace tg_gate_backward needs, in bytes (0 when n_list is 0 or
+ * the shape is not built, which the call then reports). */
+size_t tg_gate_backward_workspace_bytes(int64_t n_rows, int32_t d_model, int32_t d_hidden, int64_t n_list);
+
+/* Backward of the gate MLP of step 1: the gradients of sum_r d_scores[r] *
+ * scores[r] for the rows listed in rows[0..n_list). With z_r = W1 x_r + b1:
+ *     dz_r = d_scores[r] * w2 * SiLU'(z_r),
+ *     d_w1 = sum_r dz_r x_r^T [d_hidden, d_model],  d_b1 = sum_r dz_r,
+ *     d_w2 = sum_r d_scores[r] SiLU(z_r),  d_b2 = sum_r d_scores[r],
+ *     d_x[r] += W1^T dz_r  (fp32 [n_rows, d_model], added to; nullable: skip).
+ * x, W1, b1 (nullable: zero), w2 as for tg_gate_score (bf16 only: dt must be
+ * TG_BF16; d_model a multiple of 64; d_hidden one of 64, 128, 192, 256; x and
+ * w1 16-byte aligned). d_scores fp32 [n_rows] (device), e.g. from
+ * tg_score_grad. rows: device int32, distinct row ids in [0, n_rows) (rows
+ * with nonzero score gradient, such as kept_idx), or NULL for every row
+ * (n_list == n_rows) or for none (n_list == 0); unlisted rows count as d_scores = 0 and their d_x rows
+ * are not touched. d_w1, d_b1, d_w2, d_b2 fp32 (device) are overwritten.
+ * Workspace: tg_gate_backward_workspace_bytes bytes, 256-byte aligned
+ * (scratch). Deterministic (partials summed in a fixed order); a repeated
+ * row id makes d_x undefined. Sources: section "Was ist token-gated
+ * Attention?" (the score's bias on the logits carries the gradient back to
+ * the scorer) and section "Wie hat TokenGate das Pruning von Tokens
+ * verstanden?" (the scorer is the small MLP of step 1). */
+tg_status tg_gate_backward(tg_dtype dt, const void* x, int64_t n_rows, int32_t d_model, const void* w1,
+                           const void* b1, const void* w2, int32_t d_hidden, const float* d_scores,
+                           const int32_t* rows, int64_t n_list, float* d_x, float* d_w1, float* d_b1,
+                           float* d_w2, float* d_b2, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /* Device workspace tg_decode_attention needs, in bytes (0 if no sequence
  * has new tokens; also 0 for an invalid table, which the call reports). */

@@ -1,9 +1,10 @@
 """TokenGate pruned-prefill layer for MI355X (gfx950).
 
 The four steps (gate score, top-K select, compaction, token-gated
-attention) and decode over the pruned KV cache are HIP kernels behind the
-C ABI in include/tokengate.h; this package is the thin ctypes binding over
-it (argument marshalling only).
+attention), their backward (attention, bias -> score, gate MLP) and decode
+over the pruned KV cache are HIP kernels behind the C ABI in
+include/tokengate.h; this package is the thin ctypes binding over it
+(argument marshalling only).
 """
 
 from ._lib import (  # noqa: F401
@@ -19,6 +20,7 @@ from ._lib import (  # noqa: F401
     kv_seq_array,
     tg_compact,
     tg_decode_attention,
+    tg_gate_backward,
     tg_gate_score,
     tg_gated_attention,
     tg_gated_attention_backward,

@@ -27,7 +27,7 @@ EXPORTED = (
     "tg_kept_rows", "tg_gate_score", "tg_select_workspace_bytes", "tg_select_topk", "tg_compact",
     "tg_attention_workspace_bytes", "tg_gated_attention", "tg_decode_workspace_bytes", "tg_decode_attention",
     "tg_attention_backward_workspace_bytes", "tg_gated_attention_backward", "tg_score_grad",
-    "tg_status_string", "tg_last_error",
+    "tg_gate_backward_workspace_bytes", "tg_gate_backward", "tg_status_string", "tg_last_error",
 )
 
 
@@ -87,6 +87,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tg_gated_attention_backward.restype = c_int
     lib.tg_score_grad.argtypes = [vp, vp, vp, seqp, i32, i64, vp, vp]
     lib.tg_score_grad.restype = c_int
+    lib.tg_gate_backward_workspace_bytes.argtypes = [i64, i32, i32, i64]
+    lib.tg_gate_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.tg_gate_backward.argtypes = [c_int, vp, i64, i32, vp, vp, vp, i32, vp, vp, i64, vp, vp, vp, vp, vp, vp,
+                                     ctypes.c_size_t, vp]
+    lib.tg_gate_backward.restype = c_int
     kvp = ctypes.POINTER(TgKvSeq)
     lib.tg_decode_workspace_bytes.argtypes = [kvp, i32, i32, i32, i32]
     lib.tg_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -356,3 +361,45 @@ def tg_score_grad(d_bias_kept: torch.Tensor, scores: torch.Tensor, kept_idx: tor
     _check(lib.tg_score_grad(d_bias_kept.data_ptr(), scores.data_ptr(), kept_idx.data_ptr(), seq_array(seqs),
                              len(seqs), n, d_scores.data_ptr(), _stream(stream)))
     return d_scores
+
+
+def tg_gate_backward(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, d_scores: torch.Tensor,
+                     rows: Optional[torch.Tensor] = None, b1: Optional[torch.Tensor] = None,
+                     d_x: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> dict:
+    """Gradients of sum_r d_scores[r] * scores[r] through the gate MLP over the
+    listed rows (every row if rows is None): dict(dw1 [H, d], db1 [H], dw2 [H],
+    db2 [1]) in fp32, plus dx when d_x (fp32 [N, d], added to) is given."""
+    lib = load()
+    for t, nm in ((x, "x"), (w1, "w1"), (w2, "w2"), (d_scores, "d_scores")):
+        _dev(t, nm)
+    n, d = x.shape
+    h = w1.shape[0]
+    if w1.shape != (h, d) or w2.numel() != h or w1.dtype != x.dtype or w2.dtype != x.dtype:
+        raise ValueError("w1 must be [H, d] and w2 [H], same dtype as x")
+    if d_scores.dtype != torch.float32 or d_scores.numel() != n:
+        raise ValueError("d_scores must be fp32 [N]")
+    if b1 is not None:
+        _dev(b1, "b1")
+    if rows is not None:
+        _dev(rows, "rows")
+        if rows.dtype != torch.int32:
+            raise ValueError("rows must be int32")
+    if d_x is not None:
+        _dev(d_x, "d_x")
+        if d_x.dtype != torch.float32 or d_x.shape != (n, d):
+            raise ValueError("d_x must be fp32 [N, d]")
+    n_list = n if rows is None else rows.numel()
+    f32 = torch.float32
+    g = dict(dw1=torch.empty((h, d), dtype=f32, device=x.device), db1=torch.empty(h, dtype=f32, device=x.device),
+             dw2=torch.empty(h, dtype=f32, device=x.device), db2=torch.empty(1, dtype=f32, device=x.device))
+    ws_need = lib.tg_gate_backward_workspace_bytes(n, d, h, n_list)
+    if workspace is None:
+        workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib.tg_gate_backward(_dtype_code(x), x.data_ptr(), n, d, w1.data_ptr(), _ptr(b1), w2.data_ptr(), h,
+                                d_scores.data_ptr(), _ptr(rows), n_list, _ptr(d_x), g["dw1"].data_ptr(),
+                                g["db1"].data_ptr(), g["dw2"].data_ptr(), g["db2"].data_ptr(),
+                                workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    if d_x is not None:
+        g["dx"] = d_x
+    return g

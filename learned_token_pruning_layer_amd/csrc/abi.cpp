@@ -400,6 +400,48 @@ tg_status tg_score_grad(const float* d_bias_kept, const float* scores, const int
     return TG_OK;
 }
 
+static tg_status check_gate_backward_shape(int64_t n_rows, int32_t d_model, int32_t d_hidden, int64_t n_list) {
+    if (n_rows < 0 || n_list < 0 || n_list > n_rows)
+        return fail(TG_ERR_INVALID_ARGUMENT, "need 0 <= n_list=%lld <= n_rows=%lld", (long long)n_list,
+                    (long long)n_rows);
+    if (d_model <= 0 || d_model % 64)
+        return fail(TG_ERR_UNSUPPORTED, "d_model=%d (built: positive multiples of 64)", d_model);
+    if (d_hidden <= 0 || d_hidden % 64 || d_hidden > 256)
+        return fail(TG_ERR_UNSUPPORTED, "d_hidden=%d (built: 64, 128, 192, 256)", d_hidden);
+    return TG_OK;
+}
+
+size_t tg_gate_backward_workspace_bytes(int64_t n_rows, int32_t d_model, int32_t d_hidden, int64_t n_list) {
+    if (check_gate_backward_shape(n_rows, d_model, d_hidden, n_list) != TG_OK) return 0;
+    g_err.clear();
+    return tg::gate_backward_workspace_bytes(n_list, d_model, d_hidden);
+}
+
+tg_status tg_gate_backward(tg_dtype dt, const void* x, int64_t n_rows, int32_t d_model, const void* w1,
+                           const void* b1, const void* w2, int32_t d_hidden, const float* d_scores,
+                           const int32_t* rows, int64_t n_list, float* d_x, float* d_w1, float* d_b1, float* d_w2,
+                           float* d_b2, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_err.clear();
+    if (dt != TG_BF16) return fail(TG_ERR_UNSUPPORTED, "the gate backward is built for bf16 inputs only");
+    tg_status st = check_gate_backward_shape(n_rows, d_model, d_hidden, n_list);
+    if (st != TG_OK) return st;
+    if (!w1 || !w2 || !d_w1 || !d_b1 || !d_w2 || !d_b2)
+        return fail(TG_ERR_INVALID_ARGUMENT, "w1, w2, d_w1, d_b1, d_w2, d_b2 must be non-NULL");
+    if (n_list > 0 && (!x || !d_scores)) return fail(TG_ERR_INVALID_ARGUMENT, "x and d_scores must be non-NULL");
+    if (!rows && n_list > 0 && n_list != n_rows)
+        return fail(TG_ERR_INVALID_ARGUMENT, "rows may be NULL only when n_list == n_rows (every row)");
+    if (!(aligned16(x) && aligned16(w1))) return fail(TG_ERR_UNSUPPORTED, "x and w1 must be 16-byte aligned");
+    const size_t need = tg::gate_backward_workspace_bytes(n_list, d_model, d_hidden);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(TG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                    need);
+    if ((uintptr_t)workspace % 256 != 0) return fail(TG_ERR_INVALID_ARGUMENT, "workspace not 256-byte aligned");
+    hipError_t e = tg::launch_gate_backward(x, n_rows, d_model, w1, b1, w2, d_hidden, d_scores, rows, n_list, d_x,
+                                            d_w1, d_b1, d_w2, d_b2, workspace, stream);
+    if (e != hipSuccess) return hip_fail(e, "tg_gate_backward launch");
+    return TG_OK;
+}
+
 size_t tg_decode_workspace_bytes(const tg_kv_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv, int32_t head_dim) {
     tg::DecTable t;
     int64_t r = 0;

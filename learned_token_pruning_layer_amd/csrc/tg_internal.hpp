@@ -132,6 +132,13 @@ struct AttnBwdArgs {
 // returns the workspace bytes.
 size_t attention_backward_plan(const SeqTable& st, int hq, int hkv, int head_dim, void* table_out);
 size_t attention_backward_table_bytes();
+
+// Gate MLP backward (bf16, d_model % 64 == 0, d_hidden % 64 == 0 and <= 256).
+size_t gate_backward_workspace_bytes(int64_t n_list, int d_model, int d_hidden);
+hipError_t launch_gate_backward(const void* x, int64_t n_rows, int d, const void* w1, const void* b1,
+                                const void* w2, int hdim, const float* d_scores, const int32_t* rows,
+                                int64_t n_list, float* d_x, float* d_w1, float* d_b1, float* d_w2, float* d_b2,
+                                void* workspace, hipStream_t st);
 hipError_t launch_attention_backward(const AttnBwdArgs& a, const void* table, hipStream_t st);
 // Fill kernel (graph-capture safe, unlike a memset node): p[0 .. n) = 0.
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st);

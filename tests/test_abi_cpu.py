@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(tg.EXPORTED)
@@ -175,6 +175,37 @@ def test_attention_rejects_before_launch(lib):
     assert call(dt=5) == INVALID
     assert call() == INVALID  # NULL tensors
     assert lib.tg_attention_workspace_bytes(sa, 1, 16, 8, 128) == 0
+
+
+def test_gate_backward_workspace_and_rejects_before_launch(lib):
+    # Workspace: dZ and dZ^T in bf16 over the list padded to 64 rows, per
+    # 32-row tile partials of dw2 and db1, per 256-row chunk partials of dW1,
+    # each region rounded up to 256 bytes.
+    def up(b):
+        return (b + 255) // 256 * 256
+
+    n, d, h, nl = 16384, 2048, 256, 2384
+    pad = 2432
+    need = lib.tg_gate_backward_workspace_bytes(n, d, h, nl)
+    assert need == 2 * up(pad * h * 2) + 2 * up(pad // 32 * h * 4) + up(((pad + 255) // 256) * h * d * 4)
+    assert lib.tg_gate_backward_workspace_bytes(n, d, h, 0) == 0
+    assert lib.tg_gate_backward_workspace_bytes(n, 96, h, nl) == 0      # d_model not a multiple of 64
+    assert lib.tg_gate_backward_workspace_bytes(n, d, 320, nl) == 0     # d_hidden above 256
+    assert lib.tg_gate_backward_workspace_bytes(n, d, h, n + 1) == 0    # list longer than the rows
+    fake = ctypes.c_void_p(4096)
+    args = [fake, n, d, fake, None, fake, h, fake, fake, nl, fake, fake, fake, fake, fake]
+    assert lib.tg_gate_backward(0, *args, fake, need, None) == UNSUPPORTED  # fp32 not built
+    assert lib.tg_gate_backward(1, *args, None, 0, None) == WORKSPACE
+    assert lib.tg_gate_backward(1, *args, fake, need - 1, None) == WORKSPACE
+    bad = list(args)
+    bad[8] = None  # rows NULL with a shorter list
+    assert lib.tg_gate_backward(1, *bad, fake, need, None) == INVALID
+    bad = list(args)
+    bad[6] = 192 + 32  # d_hidden not a multiple of 64
+    assert lib.tg_gate_backward(1, *bad, fake, need, None) == UNSUPPORTED
+    bad = list(args)
+    bad[11] = None  # d_w1
+    assert lib.tg_gate_backward(1, *bad, fake, need, None) == INVALID
 
 
 def test_binding_refuses_cpu_tensors():

@@ -625,3 +625,69 @@ def test_score_grad_chain_on_gpu():
     zero = ref == 0.0
     assert np.all(got[zero] == 0.0)
     np.testing.assert_allclose(got[~zero], ref[~zero], rtol=2e-6, atol=0)
+
+
+# --------------------------------------------------------- gate backward ----
+
+def check_gate_backward(n, d, h, n_list, seed, with_b1=True, with_dx=True):
+    """Gate MLP backward over a row list (every row when n_list == n) against the oracle.
+    Bars: dW1 and dx within 2e-2 of their maxima (dz enters the MFMAs in bf16); dw2, db1,
+    db2 (fp32 sums of fp32 terms) within 1e-3 of their maxima; unlisted rows of dx
+    untouched, bit for bit."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(n, d, generator=g).to(torch.bfloat16)
+    w1 = (torch.randn(h, d, generator=g) / math.sqrt(d)).to(torch.bfloat16)
+    w2 = (torch.randn(h, generator=g) / math.sqrt(h)).to(torch.bfloat16)
+    b1 = (torch.randn(h, generator=g) * 0.5).to(torch.bfloat16) if with_b1 else None
+    ds = torch.randn(n, generator=g)  # unlisted rows carry junk that must be ignored
+    if n_list < n:
+        rows = torch.randperm(n, generator=g)[:n_list].sort().values.to(torch.int32)
+        rows_np = rows.numpy().astype(np.int64)
+    else:
+        rows, rows_np = None, np.arange(n)
+    dx0 = torch.randn(n, d, generator=g) * 0.1
+    dxd = dx0.to(DEV) if with_dx else None
+    got = tg.tg_gate_backward(x.to(DEV), w1.to(DEV), w2.to(DEV), ds.to(DEV),
+                              rows=None if rows is None else rows.to(DEV),
+                              b1=None if b1 is None else b1.to(DEV), d_x=dxd)
+    ref = oracle.gate_backward(f64(x), f64(w1), f64(w2), ds.double().numpy(), rows=rows_np,
+                               b1=None if b1 is None else f64(b1))
+    if n_list == 0:
+        for k in ("dw1", "db1", "dw2", "db2"):
+            assert not torch.any(got[k]), k
+    else:
+        for k, rel in (("dw1", 2e-2), ("dw2", 1e-3), ("db1", 1e-3)):
+            err = np.abs(f64(got[k]) - ref[k]).max()
+            assert err <= rel * np.abs(ref[k]).max(), f"{k}: {err:.3e} vs max {np.abs(ref[k]).max():.3e}"
+        assert abs(float(got["db2"][0]) - ref["db2"]) <= 1e-5 * np.abs(ds.numpy()[rows_np]).sum()
+    if with_dx:
+        dxg = got["dx"].cpu()
+        listed = np.zeros(n, dtype=bool)
+        listed[rows_np] = True
+        assert torch.equal(dxg[~torch.from_numpy(listed)], dx0[~torch.from_numpy(listed)])
+        if n_list:
+            delta = dxg[torch.from_numpy(rows_np)].double().numpy() - dx0[torch.from_numpy(rows_np)].double().numpy()
+            err = np.abs(delta - ref["dx"]).max()
+            assert err <= 2e-2 * np.abs(ref["dx"]).max(), f"dx: {err:.3e}"
+    return got
+
+
+def test_gate_backward_qwen16k_kept_rows():
+    note("gate backward bf16 N=16384 d=2048 H=256 over 2384 listed rows, b1, dx accumulated")
+    check_gate_backward(16384, 2048, 256, 2384, seed=101)
+
+
+@pytest.mark.parametrize("n,d,h,n_list,with_b1", [(1000, 192, 64, 77, False), (300, 320, 128, 300, True),
+                                                  (513, 64, 192, 1, True), (700, 2048, 256, 700, False),
+                                                  (64, 128, 64, 0, True)])
+def test_gate_backward_shapes(n, d, h, n_list, with_b1):
+    note(f"gate backward bf16 n={n} d={d} H={h} listed={n_list} b1={with_b1}")
+    check_gate_backward(n, d, h, n_list, seed=n + d + h + n_list, with_b1=with_b1)
+
+
+def test_gate_backward_without_dx_and_deterministic():
+    note("gate backward: no dx; bitwise repeatable")
+    a = check_gate_backward(2000, 512, 128, 333, seed=7, with_dx=False)
+    b = check_gate_backward(2000, 512, 128, 333, seed=7, with_dx=False)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
