@@ -237,6 +237,8 @@ def measure_extras(torch, tg, layer, w, steps, dev):
     out["decode_qwen16k"] = measure_decode(torch, tg, layer, timed, pct)
     # Backward of this layer's token-gated attention (the gradient path to the gate).
     out["backward_qwen16k"] = measure_backward(torch, tg, layer, timed, pct)
+    # ... and on through the score chain into the gate MLP's weights.
+    out["gate_backward_qwen16k"] = measure_gate_backward(torch, tg, layer, timed, pct)
     # Select on one prompt of 2^24 document rows: the multi-workgroup path
     # (1024 chunks of 16384 rows), arguments marshalled once outside the
     # timed region.
@@ -364,6 +366,40 @@ def measure_backward(torch, tg, lay, timed, pct, reps=20):
                 // 2 for p in lay.prompts)
     fl = 5 * 2 * dh * hq * pairs
     return {"kept_rows": m, "us": round(us, 1), "algorithmic_tflops": round(fl / (us * 1e-6) / 1e12, 1),
+            "frac_bf16_peak": round(fl / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def measure_gate_backward(torch, tg, lay, timed, pct, reps=20):
+    """Backward of the gate MLP over the layer's kept rows: the score gradient of
+    a random bias gradient (sigmoid(-s) on kept document rows), then dW1, db1,
+    dw2, db2 and dx (added to an fp32 [N, d] buffer). Algorithmic work: three
+    products of 2*M*d*H flop (recomputed pre-activation, dx, dW1)."""
+    from learned_token_pruning_layer_amd._lib import seq_array
+    n, d = lay.x.shape
+    h = lay.w1.shape[0]
+    m = lay.m
+    g = torch.Generator(device=lay.x.device).manual_seed(12)
+    dbias = torch.randn(m, generator=g, device=lay.x.device)
+    dsc = tg.tg_score_grad(dbias, lay.scores, lay.kept, lay.prompts)
+    dx = torch.zeros((n, d), dtype=torch.float32, device=lay.x.device)
+    lib = tg.load()
+    wsb = lib.tg_gate_backward_workspace_bytes(n, d, h, m)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=lay.x.device)
+    f32 = torch.float32
+    outs = [torch.empty(s, dtype=f32, device=lay.x.device) for s in ((h, d), (h,), (h,), (1,))]
+    st = torch.cuda.current_stream().cuda_stream
+    args = (1, lay.x.data_ptr(), n, d, lay.w1.data_ptr(), None if lay.b1 is None else lay.b1.data_ptr(),
+            lay.w2.data_ptr(), h, dsc.data_ptr(), lay.kept.data_ptr(), m, dx.data_ptr(),
+            *[t.data_ptr() for t in outs], ws.data_ptr(), ws.numel(), st)
+
+    def call():
+        if lib.tg_gate_backward(*args) != 0:
+            raise RuntimeError(lib.tg_last_error().decode())
+
+    call()
+    us = pct(timed(call, reps), 0.5)
+    fl = 3 * 2 * m * d * h
+    return {"listed_rows": m, "us": round(us, 1), "algorithmic_tflops": round(fl / (us * 1e-6) / 1e12, 1),
             "frac_bf16_peak": round(fl / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
