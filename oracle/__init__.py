@@ -7,6 +7,7 @@ import this package; the HIP library never does.
 from .tokengate import (  # noqa: F401
     compact,
     decode_attention,
+    dense_layer,
     gate_backward,
     gate_scores,
     gated_attention,
@@ -15,6 +16,8 @@ from .tokengate import (  # noqa: F401
     kept_rows,
     logsigmoid,
     prompt_of_rows,
+    rms_norm,
+    rope,
     score_grad,
     select_topk,
     sigmoid,

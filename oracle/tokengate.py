@@ -440,6 +440,62 @@ def decode_attention(q_new, k, v, bias, pos, segs: Sequence, hq: int, hkv: int, 
 # ---------------------------------------------------------------------------
 # The whole layer, in the pages' order.
 # ---------------------------------------------------------------------------
+# The full above-gate layer over the kept rows.  [DE-prune] (the layers above
+# the gate process only the kept tokens and build no KV for the others),
+# [IT-keep] (only the kept tokens' representations go up). The layer itself is
+# the model's own decoder layer, unchanged: for the Qwen3 family, RMSNorm, a
+# QKV projection, RMSNorm of every query and key head, rotary position
+# embedding by the token's original position, attention (here token-gated),
+# the output projection and a residual add, then RMSNorm, a SwiGLU MLP and a
+# second residual add.
+# ---------------------------------------------------------------------------
+
+def rms_norm(x, w, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * w over the last axis."""
+    xd = _f64(x)
+    return xd / np.sqrt((xd * xd).mean(axis=-1, keepdims=True) + eps) * _f64(w)
+
+
+def rope(x, pos, theta: float) -> np.ndarray:
+    """Rotary embedding of x [M, heads, D] at positions pos [M]: element i of
+    the first half pairs with element i + D/2 and the pair turns by the angle
+    pos * theta^(-2i/D)."""
+    xd = _f64(x)
+    dh = xd.shape[-1]
+    half = dh // 2
+    inv = float(theta) ** (-2.0 * np.arange(half) / dh)
+    ps = np.asarray(pos.detach().cpu().numpy() if hasattr(pos, "detach") else pos, dtype=np.float64)
+    ang = ps[:, None] * inv[None, :]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    x1, x2 = xd[..., :half], xd[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def dense_layer(h, pos_kept, bias_kept, seg_lens: Sequence[int], w: dict, hq: int, hkv: int,
+                head_dim: int) -> dict:
+    """One decoder layer above the gate, over the kept rows h [M, d] at their
+    original positions, with token-gated attention. w: ln1 [d], wqkv
+    [(hq + 2 hkv) D, d] (q rows, then k, then v), q_norm [D], k_norm [D], wo
+    [d, hq D], ln2 [d], w_gate [I, d], w_up [I, d], w_down [d, I], gain [hq],
+    tau, eps, theta. Returns the layer output and the intermediates in fp64."""
+    hd = _f64(h)
+    m = hd.shape[0]
+    dq = hq * head_dim
+    dk = hkv * head_dim
+    eps, theta = float(w["eps"]), float(w["theta"])
+    a = rms_norm(hd, w["ln1"], eps)
+    qkv = a @ _f64(w["wqkv"]).T
+    q = rope(rms_norm(qkv[:, :dq].reshape(m, hq, head_dim), w["q_norm"], eps), pos_kept, theta)
+    k = rope(rms_norm(qkv[:, dq:dq + dk].reshape(m, hkv, head_dim), w["k_norm"], eps), pos_kept, theta)
+    v = qkv[:, dq + dk:].reshape(m, hkv, head_dim)
+    o, _ = gated_attention(q, k, v, bias_kept, pos_kept, seg_lens, hq, hkv, w["gain"], w["tau"])
+    h2 = hd + o.reshape(m, dq) @ _f64(w["wo"]).T
+    a2 = rms_norm(h2, w["ln2"], eps)
+    mlp = silu(a2 @ _f64(w["w_gate"]).T) * (a2 @ _f64(w["w_up"]).T)
+    return dict(out=h2 + mlp @ _f64(w["w_down"]).T, h2=h2, q=q, k=k, v=v, attn=o, mlp=mlp)
+
+
+# ---------------------------------------------------------------------------
 
 def gated_prefill(x, w1, w2, prompts: Sequence, layers: Sequence = (), b1=None, b2: float = 0.0,
                   hq: int = 0, hkv: int = 0, head_dim: int = 0, pos=None,

@@ -322,3 +322,49 @@ def make_attention_inputs(seg_lens: List[int], hq: int, hkv: int, head_dim: int,
     gain = torch.rand((hq,), generator=gen) * 1.5 + 0.5
     return dict(q=q.to(device), k=k.to(device), v=v.to(device), bias=bias.to(device),
                 pos=pos.to(device), gain=gain.to(device), tau=TAU, seg_lens=list(seg_lens))
+
+
+def make_dense_layer(d: int, hq: int, hkv: int, head_dim: int, d_ff: int, seed: int,
+                     dtype=torch.bfloat16, device="cpu") -> dict:
+    """Weights of one above-gate decoder layer (Qwen3 layout: RMSNorm, fused
+    QKV projection, per-head Q/K RMSNorm, output projection, RMSNorm, SwiGLU
+    MLP), all nn.Linear [out, in]: projections N(0, 1/fan_in), norm weights
+    1 + N(0, 0.1^2), gains U(0.5, 2); tau 1.2, eps 1e-6, rope theta 1e6."""
+    gen = _torch_gen("cpu", seed)
+
+    def lin(n_out, n_in):
+        return (torch.randn((n_out, n_in), generator=gen) / math.sqrt(n_in)).to(dtype).to(device)
+
+    def norm_w(n):
+        return (1.0 + 0.1 * torch.randn((n,), generator=gen)).to(dtype).to(device)
+
+    w = dict(ln1=norm_w(d), wqkv=lin((hq + 2 * hkv) * head_dim, d), q_norm=norm_w(head_dim),
+             k_norm=norm_w(head_dim), wo=lin(d, hq * head_dim), ln2=norm_w(d), w_gate=lin(d_ff, d),
+             w_up=lin(d_ff, d), w_down=lin(d, d_ff))
+    w["gain"] = (torch.rand((hq,), generator=gen) * 1.5 + 0.5).to(device)
+    w.update(tau=TAU, eps=1e-6, theta=1.0e6)
+    return w
+
+
+def make_kept_hidden(seg_lens: List[int], d: int, seed: int, dtype=torch.bfloat16, device="cpu",
+                     n_query_tail: int = 0) -> dict:
+    """Kept rows entering an above-gate layer: hidden states N(0, 1), original
+    positions strictly increasing within each segment (random gaps 1..8),
+    bias -|N(0, 1.5^2)| for document rows and 0 for the last n_query_tail rows
+    of each segment."""
+    m = int(sum(seg_lens))
+    gen = _torch_gen("cpu", seed)
+    h = torch.randn((m, d), generator=gen).to(dtype)
+    bias = -(torch.randn((m,), generator=gen) * 1.5).abs()
+    pos = torch.empty((m,), dtype=torch.int32)
+    off = 0
+    for ln in seg_lens:
+        if ln:
+            gaps = torch.randint(1, 9, (ln,), generator=gen)
+            gaps[0] = torch.randint(0, 5, (1,), generator=gen)[0]
+            pos[off:off + ln] = torch.cumsum(gaps, 0).to(torch.int32)
+            tail = min(n_query_tail, ln)
+            if tail:
+                bias[off + ln - tail: off + ln] = 0.0
+        off += ln
+    return dict(h=h.to(device), pos=pos.to(device), bias=bias.to(device), seg_lens=list(seg_lens))

@@ -55,6 +55,18 @@ MUTATIONS = [
     ("gate backward: first bias left out of the recomputed pre-activation", "        z = z + _f64(b1).reshape(-1)\n    sg",
      "        z = z\n    sg"),
     ("gate backward: dw2 from the pre-activation", "dw2=(dsr[:, None] * a).sum(axis=0)", "dw2=(dsr[:, None] * z).sum(axis=0)"),
+    ("rms norm without eps", "np.sqrt((xd * xd).mean(axis=-1, keepdims=True) + eps)",
+     "np.sqrt((xd * xd).mean(axis=-1, keepdims=True))"),
+    ("rope pairs adjacent elements", "x1, x2 = xd[..., :half], xd[..., half:]", "x1, x2 = xd[..., 0::2], xd[..., 1::2]"),
+    ("rope turns the wrong way", "[x1 * c - x2 * s, x2 * c + x1 * s]", "[x1 * c + x2 * s, x2 * c - x1 * s]"),
+    ("rope frequency exponent -i/D", "inv = float(theta) ** (-2.0 * np.arange(half) / dh)",
+     "inv = float(theta) ** (-1.0 * np.arange(half) / dh)"),
+    ("key heads left without their norm", "k = rope(rms_norm(qkv[:, dq:dq + dk].reshape(m, hkv, head_dim), w[\"k_norm\"], eps)",
+     "k = rope(qkv[:, dq:dq + dk].reshape(m, hkv, head_dim)"),
+    ("SiLU on the up projection instead of the gate", "mlp = silu(a2 @ _f64(w[\"w_gate\"]).T) * (a2 @ _f64(w[\"w_up\"]).T)",
+     "mlp = (a2 @ _f64(w[\"w_gate\"]).T) * silu(a2 @ _f64(w[\"w_up\"]).T)"),
+    ("second norm over the layer input instead of the attention residual", "a2 = rms_norm(h2, w[\"ln2\"], eps)",
+     "a2 = rms_norm(hd, w[\"ln2\"], eps)"),
 ]
 
 

@@ -528,6 +528,102 @@ def test_gate_backward_invariants():
         np.testing.assert_allclose(g2[k], 2.0 * g1[k], rtol=1e-14, atol=1e-14)
 
 
+# ----------------------------------------------------- full above-gate layer ----
+
+def test_rms_norm_vs_library_and_closed_form():
+    """RMSNorm against torch's own rms_norm, and a constant row c against
+    c / sqrt(c^2 + eps) * w."""
+    rng = np.random.default_rng(11)
+    x, w = rng.normal(size=(7, 24)), rng.normal(size=24)
+    ref = torch.nn.functional.rms_norm(torch.tensor(x), (24,), torch.tensor(w), eps=1e-6).numpy()
+    np.testing.assert_allclose(oracle.rms_norm(x, w, 1e-6), ref, rtol=1e-12, atol=1e-12)
+    c = np.full((1, 24), -3.0)
+    np.testing.assert_allclose(oracle.rms_norm(c, w, 0.5), -3.0 / np.sqrt(9.5) * w[None, :], rtol=1e-14)
+
+
+def test_rope_vs_complex_bruteforce_and_invariants():
+    """Rotary embedding against a pure-Python complex rotation of each (i, i + D/2)
+    pair by e^{i pos theta^(-2i/D)}; position 0 is the identity; norms are kept; the
+    product of a rotated query and key depends only on the position difference."""
+    rng = np.random.default_rng(12)
+    m, heads, dh, theta = 5, 3, 8, 1.0e4
+    x = rng.normal(size=(m, heads, dh))
+    pos = np.array([0, 3, 17, 250, 40000])
+    got = oracle.rope(x, pos, theta)
+    for r in range(m):
+        for hh in range(heads):
+            for i in range(dh // 2):
+                z = complex(x[r, hh, i], x[r, hh, i + dh // 2])
+                z *= complex(math.cos(pos[r] * theta ** (-2 * i / dh)), math.sin(pos[r] * theta ** (-2 * i / dh)))
+                assert abs(got[r, hh, i] - z.real) < 1e-12 and abs(got[r, hh, i + dh // 2] - z.imag) < 1e-12
+    np.testing.assert_allclose(got[0], x[0], rtol=0, atol=0)
+    np.testing.assert_allclose(np.linalg.norm(got, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    q, k = rng.normal(size=(1, 1, dh)), rng.normal(size=(1, 1, dh))
+    d1 = (oracle.rope(q, [100], theta) * oracle.rope(k, [60], theta)).sum()
+    d2 = (oracle.rope(q, [1040], theta) * oracle.rope(k, [1000], theta)).sum()
+    assert abs(d1 - d2) < 1e-12
+
+
+def _dense_case(seed, segs=(30, 1, 17), d=64, hq=4, hkv=2, dh=16, d_ff=96):
+    from synthetic import make_dense_layer, make_kept_hidden
+    w = make_dense_layer(d, hq, hkv, dh, d_ff, seed=seed, dtype=torch.float64)
+    x = make_kept_hidden(list(segs), d, seed=seed + 1, dtype=torch.float64, n_query_tail=3)
+    return w, x
+
+
+def test_dense_layer_vs_torch_reference():
+    """The layer against the same layer written with torch ops in fp64: torch's
+    rms_norm, rotary embedding through complex multiplication of (i, i + D/2) pairs,
+    SDPA with an additive float mask for the token-gated attention, torch's silu."""
+    hq, hkv, dh = 4, 2, 16
+    w, x = _dense_case(21)
+    got = oracle.dense_layer(x["h"], x["pos"], x["bias"], x["seg_lens"], w, hq, hkv, dh)
+    F = torch.nn.functional
+    h = x["h"]
+    m, d = h.shape
+    eps = w["eps"]
+
+    def rot(t):  # [m, heads, dh]
+        half = dh // 2
+        inv = torch.tensor(w["theta"], dtype=torch.float64) ** (-2.0 * torch.arange(half, dtype=torch.float64) / dh)
+        ang = x["pos"].double()[:, None] * inv[None, :]
+        z = torch.complex(t[..., :half], t[..., half:]) * torch.polar(torch.ones_like(ang), ang)[:, None, :]
+        return torch.cat([z.real, z.imag], dim=-1)
+
+    a = F.rms_norm(h, (d,), w["ln1"], eps=eps)
+    qkv = a @ w["wqkv"].T
+    q = rot(F.rms_norm(qkv[:, :hq * dh].reshape(m, hq, dh), (dh,), w["q_norm"], eps=eps))
+    k = rot(F.rms_norm(qkv[:, hq * dh:(hq + hkv) * dh].reshape(m, hkv, dh), (dh,), w["k_norm"], eps=eps))
+    v = qkv[:, (hq + hkv) * dh:].reshape(m, hkv, dh)
+    o = torch.empty(m, hq, dh, dtype=torch.float64)
+    off = 0
+    for ln in x["seg_lens"]:
+        sl = slice(off, off + ln)
+        p = x["pos"][sl]
+        for hh in range(hq):
+            kv = hh // (hq // hkv)
+            mask = torch.where(p[None, :] <= p[:, None], w["gain"][hh].double() * x["bias"][sl].double()[None, :],
+                               torch.tensor(-math.inf, dtype=torch.float64))
+            o[sl, hh] = F.scaled_dot_product_attention(q[None, None, sl, hh], k[None, None, sl, kv], v[None, None, sl, kv],
+                                                       attn_mask=mask[None, None], scale=1.0 / (math.sqrt(dh) * w["tau"]))[0, 0]
+        off += ln
+    h2 = h + o.reshape(m, hq * dh) @ w["wo"].T
+    a2 = F.rms_norm(h2, (d,), w["ln2"], eps=eps)
+    out = h2 + (F.silu(a2 @ w["w_gate"].T) * (a2 @ w["w_up"].T)) @ w["w_down"].T
+    np.testing.assert_allclose(got["q"], q.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got["out"], out.numpy(), rtol=1e-10, atol=1e-11)
+
+
+def test_dense_layer_residual_only_without_output_projections():
+    """With zero output and down projections the layer returns its input."""
+    hq, hkv, dh = 4, 2, 16
+    w, x = _dense_case(22)
+    w["wo"] = torch.zeros_like(w["wo"])
+    w["w_down"] = torch.zeros_like(w["w_down"])
+    got = oracle.dense_layer(x["h"], x["pos"], x["bias"], x["seg_lens"], w, hq, hkv, dh)
+    np.testing.assert_array_equal(got["out"], x["h"].numpy())
+
+
 # ---------------------------------------------------------------- decode ----
 
 def _decode_case(seed, segs, hq, hkv, d, n_new_max=3, pos_ties=False):
