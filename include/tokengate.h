@@ -243,6 +243,65 @@ typedef struct {
     int32_t n_new;
 } tg_kv_seq;
 
+/* Epilogues of tg_linear. */
+#define TG_LINEAR_STORE 0    /* out = x W^T                              */
+#define TG_LINEAR_RESIDUAL 1 /* out = residual + x W^T                   */
+#define TG_LINEAR_SWIGLU 2   /* out = SiLU(x W^T) * (x W_up^T)           */
+
+/* A linear layer of the above-gate model on MFMA: for the m rows of x (bf16
+ * [m, k] row-major) and weights in the nn.Linear layout (bf16 [n, k]),
+ * out (bf16 [m, n]) per the epilogue; accumulation fp32, one bf16 rounding
+ * of the result. residual bf16 [m, n] (TG_LINEAR_RESIDUAL; may not alias
+ * out), w_up bf16 [n, k] (TG_LINEAR_SWIGLU: w holds the gate rows, w_up the
+ * matching up rows). k a multiple of 64; n a multiple of 128 (SwiGLU: 64);
+ * all pointers device, 16-byte aligned. bf16 only. Source: the layers above
+ * the gate are the model's own (section "Wie hat TokenGate das Pruning von
+ * Tokens verstanden?": they run on the kept tokens only). */
+tg_status tg_linear(tg_dtype dt, int32_t epilogue, const void* x, int64_t m, int32_t k, const void* w,
+                    const void* w_up, int32_t n, const void* residual, void* out, hipStream_t stream);
+
+/* Weights of one above-gate decoder layer (Qwen3 layout), all bf16 device
+ * pointers in the nn.Linear layout [out, in], 16-byte aligned: ln1, ln2
+ * [d_model] (RMSNorm), wqkv [(hq + 2 hkv) head_dim, d_model] (query rows,
+ * then key rows, then value rows), q_norm, k_norm [head_dim] (per-head
+ * RMSNorm), wo [d_model, hq head_dim], w_gate, w_up [d_ff, d_model], w_down
+ * [d_model, d_ff]; gain fp32 [hq] and tau of the token-gated attention; eps
+ * of every RMSNorm; rope_theta of the rotary embedding. Built: head_dim 64
+ * or 128, d_model a multiple of 128, d_ff a multiple of 64, (hq + 2 hkv)
+ * head_dim a multiple of 128. */
+typedef struct {
+    int32_t d_model, hq, hkv, head_dim, d_ff;
+    float eps, rope_theta, tau;
+    const void *ln1, *wqkv, *q_norm, *k_norm, *wo, *ln2, *w_gate, *w_up, *w_down;
+    const float* gain;
+} tg_dense_weights;
+
+/* Device workspace tg_dense_layer needs, in bytes (0 for invalid weights or
+ * prompts, which the call then reports). */
+size_t tg_dense_layer_workspace_bytes(const tg_seq* seqs, int32_t n_seqs, const tg_dense_weights* w);
+
+/* One full decoder layer above the gate over the kept rows (the model's own
+ * layer with token-gated attention):
+ *     a = RMSNorm(h) ln1;  q|k|v = a Wqkv^T;
+ *     q, k = rotary(RMSNorm_head(q) q_norm | RMSNorm_head(k) k_norm, pos);
+ *     h2 = h + TokenGatedAttention(q, k, v; bias, pos, gain, tau) Wo^T;
+ *     out = h2 + (SiLU(a2 Wg^T) * (a2 Wu^T)) Wd^T,  a2 = RMSNorm(h2) ln2.
+ * RMSNorm: x / sqrt(mean(x^2) + eps); rotary: element i < head_dim/2 pairs
+ * with i + head_dim/2 and turns by pos * rope_theta^(-2i/head_dim). hidden_kept
+ * bf16 [M, d_model] (tg_compact's output), bias_kept, pos_kept and seqs as
+ * for tg_gated_attention; out bf16 [M, d_model]. k_out, v_out (nullable)
+ * receive the layer's keys (normalised and rotated) and values, bf16
+ * [M, hkv, head_dim]: the layer's pruned KV cache, for tg_decode_attention.
+ * Intermediates are stored in bf16. Workspace:
+ * tg_dense_layer_workspace_bytes bytes, 256-byte aligned (scratch). Sources:
+ * section "Wie hat TokenGate das Pruning von Tokens verstanden?" (layers
+ * above the gate process only the kept tokens and build no KV for the
+ * pruned ones) and "Was ist token-gated Attention?" (the bias on their
+ * logits). */
+tg_status tg_dense_layer(tg_dtype dt, const void* hidden_kept, const float* bias_kept, const int32_t* pos_kept,
+                         const tg_seq* seqs, int32_t n_seqs, const tg_dense_weights* w, void* out, void* k_out,
+                         void* v_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Device workspace tg_gate_backward needs, in bytes (0 when n_list is 0 or
  * the shape is not built, which the call then reports). */
 size_t tg_gate_backward_workspace_bytes(int64_t n_rows, int32_t d_model, int32_t d_hidden, int64_t n_list);

@@ -1,8 +1,8 @@
 """TokenGate pruned-prefill layer for MI355X (gfx950).
 
 The four steps (gate score, top-K select, compaction, token-gated
-attention), their backward (attention, bias -> score, gate MLP) and decode
-over the pruned KV cache are HIP kernels behind the C ABI in
+attention), their backward (attention, bias -> score, gate MLP), the full
+above-gate decoder layer and decode over the pruned KV cache are HIP kernels behind the C ABI in
 include/tokengate.h; this package is the thin ctypes binding over it
 (argument marshalling only).
 """
@@ -20,11 +20,13 @@ from ._lib import (  # noqa: F401
     kv_seq_array,
     tg_compact,
     tg_decode_attention,
+    tg_dense_layer,
     tg_gate_backward,
     tg_gate_score,
     tg_gated_attention,
     tg_gated_attention_backward,
     tg_kept_rows,
+    tg_linear,
     tg_score_grad,
     tg_select_topk,
 )

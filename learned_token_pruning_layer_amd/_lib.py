@@ -27,7 +27,8 @@ EXPORTED = (
     "tg_kept_rows", "tg_gate_score", "tg_select_workspace_bytes", "tg_select_topk", "tg_compact",
     "tg_attention_workspace_bytes", "tg_gated_attention", "tg_decode_workspace_bytes", "tg_decode_attention",
     "tg_attention_backward_workspace_bytes", "tg_gated_attention_backward", "tg_score_grad",
-    "tg_gate_backward_workspace_bytes", "tg_gate_backward", "tg_status_string", "tg_last_error",
+    "tg_gate_backward_workspace_bytes", "tg_gate_backward", "tg_linear", "tg_dense_layer_workspace_bytes",
+    "tg_dense_layer", "tg_status_string", "tg_last_error",
 )
 
 
@@ -45,6 +46,14 @@ class TgSeq(ctypes.Structure):
 
 class TgKvSeq(ctypes.Structure):
     _fields_ = [("start", ctypes.c_int64), ("len", ctypes.c_int32), ("n_new", ctypes.c_int32)]
+
+
+class TgDenseWeights(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("rope_theta", ctypes.c_float), ("tau", ctypes.c_float)] + \
+               [(nm, ctypes.c_void_p) for nm in ("ln1", "wqkv", "q_norm", "k_norm", "wo", "ln2", "w_gate", "w_up",
+                                                 "w_down", "gain")]
 
 
 class TgGather(ctypes.Structure):
@@ -92,6 +101,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tg_gate_backward.argtypes = [c_int, vp, i64, i32, vp, vp, vp, i32, vp, vp, i64, vp, vp, vp, vp, vp, vp,
                                      ctypes.c_size_t, vp]
     lib.tg_gate_backward.restype = c_int
+    lib.tg_linear.argtypes = [c_int, i32, vp, i64, i32, vp, vp, i32, vp, vp, vp]
+    lib.tg_linear.restype = c_int
+    dwp = ctypes.POINTER(TgDenseWeights)
+    lib.tg_dense_layer_workspace_bytes.argtypes = [seqp, i32, dwp]
+    lib.tg_dense_layer_workspace_bytes.restype = ctypes.c_size_t
+    lib.tg_dense_layer.argtypes = [c_int, vp, vp, vp, seqp, i32, dwp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.tg_dense_layer.restype = c_int
     kvp = ctypes.POINTER(TgKvSeq)
     lib.tg_decode_workspace_bytes.argtypes = [kvp, i32, i32, i32, i32]
     lib.tg_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -403,3 +419,60 @@ def tg_gate_backward(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, d_scor
     if d_x is not None:
         g["dx"] = d_x
     return g
+
+
+LINEAR_STORE, LINEAR_RESIDUAL, LINEAR_SWIGLU = 0, 1, 2
+
+
+def tg_linear(x: torch.Tensor, w: torch.Tensor, residual: Optional[torch.Tensor] = None,
+              w_up: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """bf16 out = x W^T (+ residual), or SiLU(x W^T) * (x W_up^T) when w_up is given."""
+    lib = load()
+    _dev(x, "x")
+    _dev(w, "w")
+    m, k = x.shape
+    n = w.shape[0]
+    if w.shape != (n, k) or (w_up is not None and w_up.shape != (n, k)):
+        raise ValueError("weights must be [n, k]")
+    epi = LINEAR_SWIGLU if w_up is not None else (LINEAR_RESIDUAL if residual is not None else LINEAR_STORE)
+    if out is None:
+        out = torch.empty((m, n), dtype=x.dtype, device=x.device)
+    _check(lib.tg_linear(_dtype_code(x), epi, x.data_ptr(), m, k, w.data_ptr(), _ptr(w_up), n, _ptr(residual),
+                         out.data_ptr(), _stream(stream)))
+    return out
+
+
+def dense_weights(w: dict, d_model: int, hq: int, hkv: int, head_dim: int) -> TgDenseWeights:
+    """The C descriptor of a layer's weights (dict of device tensors plus tau, eps, theta)."""
+    for nm in ("ln1", "wqkv", "q_norm", "k_norm", "wo", "ln2", "w_gate", "w_up", "w_down", "gain"):
+        _dev(w[nm], nm)
+    return TgDenseWeights(d_model, hq, hkv, head_dim, int(w["w_gate"].shape[0]), float(w["eps"]),
+                          float(w["theta"]), float(w["tau"]),
+                          *[w[nm].data_ptr() for nm in ("ln1", "wqkv", "q_norm", "k_norm", "wo", "ln2", "w_gate",
+                                                        "w_up", "w_down", "gain")])
+
+
+def tg_dense_layer(h: torch.Tensor, bias_kept: torch.Tensor, pos_kept: torch.Tensor, seqs: Sequence, w: dict,
+                   hq: int, hkv: int, head_dim: int, out: Optional[torch.Tensor] = None, want_kv: bool = False,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """One above-gate decoder layer over the kept rows h [M, d] (bf16); returns out [M, d],
+    or (out, k, v) with the layer's keys and values [M, hkv, D] when want_kv."""
+    lib = load()
+    for t, nm in ((h, "h"), (bias_kept, "bias_kept"), (pos_kept, "pos_kept")):
+        _dev(t, nm)
+    m, d = h.shape
+    desc = dense_weights(w, d, hq, hkv, head_dim)
+    sa = seq_array(seqs)
+    if out is None:
+        out = torch.empty_like(h)
+    k = v = None
+    if want_kv:
+        k = torch.empty((m, hkv, head_dim), dtype=h.dtype, device=h.device)
+        v = torch.empty_like(k)
+    need = lib.tg_dense_layer_workspace_bytes(sa, len(seqs), ctypes.byref(desc))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
+    _check(lib.tg_dense_layer(_dtype_code(h), h.data_ptr(), bias_kept.data_ptr(), pos_kept.data_ptr(), sa, len(seqs),
+                              ctypes.byref(desc), out.data_ptr(), _ptr(k), _ptr(v), workspace.data_ptr(),
+                              workspace.numel(), _stream(stream)))
+    return (out, k, v) if want_kv else out

@@ -442,6 +442,134 @@ tg_status tg_gate_backward(tg_dtype dt, const void* x, int64_t n_rows, int32_t d
     return TG_OK;
 }
 
+tg_status tg_linear(tg_dtype dt, int32_t epilogue, const void* x, int64_t m, int32_t k, const void* w,
+                    const void* w_up, int32_t n, const void* residual, void* out, hipStream_t stream) {
+    g_err.clear();
+    if (dt != TG_BF16) return fail(TG_ERR_UNSUPPORTED, "tg_linear is built for bf16 only");
+    if (epilogue < TG_LINEAR_STORE || epilogue > TG_LINEAR_SWIGLU)
+        return fail(TG_ERR_INVALID_ARGUMENT, "epilogue %d unknown", epilogue);
+    if (m < 0) return fail(TG_ERR_INVALID_ARGUMENT, "m=%lld < 0", (long long)m);
+    if (k <= 0 || k % 64) return fail(TG_ERR_UNSUPPORTED, "k=%d (built: positive multiples of 64)", k);
+    const int n_align = epilogue == TG_LINEAR_SWIGLU ? 64 : 128;
+    if (n <= 0 || n % n_align) return fail(TG_ERR_UNSUPPORTED, "n=%d (built: positive multiples of %d)", n, n_align);
+    if (m > INT32_MAX / 2) return fail(TG_ERR_UNSUPPORTED, "m=%lld too large", (long long)m);
+    if (m == 0) return TG_OK;
+    if (!x || !w || !out || (epilogue == TG_LINEAR_SWIGLU && !w_up) || (epilogue == TG_LINEAR_RESIDUAL && !residual))
+        return fail(TG_ERR_INVALID_ARGUMENT, "x, w, out (and w_up or residual for that epilogue) must be non-NULL");
+    if (!(aligned16(x) && aligned16(w) && aligned16(w_up) && aligned16(out) && aligned16(residual)))
+        return fail(TG_ERR_UNSUPPORTED, "x, w, w_up, residual, out must be 16-byte aligned");
+    hipError_t e = tg::launch_linear(epilogue, x, m, k, w, w_up, n, residual, out, stream);
+    if (e != hipSuccess) return hip_fail(e, "tg_linear launch");
+    return TG_OK;
+}
+
+}  // extern "C"
+
+namespace {
+struct DenseLayout {
+    size_t a, qkv, q, k, v, o, h2, mlp, total;
+};
+DenseLayout dense_layout(int64_t m, const tg_dense_weights& w) {
+    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    const size_t d = (size_t)w.d_model, dh = (size_t)w.head_dim;
+    DenseLayout l{};
+    size_t o = 0;
+    auto take = [&](size_t elems) {
+        const size_t at = o;
+        o += up(elems * 2 * (size_t)m);
+        return at;
+    };
+    l.a = take(d);
+    l.qkv = take((size_t)(w.hq + 2 * w.hkv) * dh);
+    l.q = take((size_t)w.hq * dh);
+    l.k = take((size_t)w.hkv * dh);
+    l.v = take((size_t)w.hkv * dh);
+    l.o = take((size_t)w.hq * dh);
+    l.h2 = take(d);
+    l.mlp = take((size_t)w.d_ff);
+    l.total = o;
+    return l;
+}
+tg_status check_dense_weights(const tg_dense_weights* w) {
+    if (!w) return fail(TG_ERR_INVALID_ARGUMENT, "weights must be non-NULL");
+    if (w->hq <= 0 || w->hkv <= 0 || w->hq % w->hkv)
+        return fail(TG_ERR_INVALID_ARGUMENT, "hq=%d must be a positive multiple of hkv=%d", w->hq, w->hkv);
+    if (w->head_dim != 64 && w->head_dim != 128)
+        return fail(TG_ERR_UNSUPPORTED, "head_dim=%d (built: 64, 128)", w->head_dim);
+    if (w->d_model <= 0 || w->d_model % 128)
+        return fail(TG_ERR_UNSUPPORTED, "d_model=%d (built: positive multiples of 128)", w->d_model);
+    if (w->d_ff <= 0 || w->d_ff % 64) return fail(TG_ERR_UNSUPPORTED, "d_ff=%d (built: positive multiples of 64)", w->d_ff);
+    if (((w->hq + 2 * w->hkv) * w->head_dim) % 128)
+        return fail(TG_ERR_UNSUPPORTED, "(hq + 2 hkv) * head_dim must be a multiple of 128");
+    if (!(w->eps > 0.0f) || !(w->rope_theta > 1.0f) || !(w->tau > 0.0f) || w->tau > 3.0e38f ||
+        w->rope_theta > 3.0e38f)
+        return fail(TG_ERR_INVALID_ARGUMENT, "eps and tau must be > 0, rope_theta > 1, all finite");
+    const void* ptrs[] = {w->ln1, w->wqkv, w->q_norm, w->k_norm, w->wo, w->ln2, w->w_gate, w->w_up, w->w_down};
+    for (const void* p : ptrs) {
+        if (!p) return fail(TG_ERR_INVALID_ARGUMENT, "every weight pointer must be non-NULL");
+        if (!aligned16(p)) return fail(TG_ERR_UNSUPPORTED, "weights must be 16-byte aligned");
+    }
+    if (!w->gain) return fail(TG_ERR_INVALID_ARGUMENT, "gain must be non-NULL");
+    return TG_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t tg_dense_layer_workspace_bytes(const tg_seq* seqs, int32_t n_seqs, const tg_dense_weights* w) {
+    tg::SeqTable st_;
+    int64_t m = 0;
+    if (check_dense_weights(w) != TG_OK || build_seq_table(seqs, n_seqs, &st_, &m) != TG_OK) return 0;
+    g_err.clear();
+    return dense_layout(m, *w).total;
+}
+
+tg_status tg_dense_layer(tg_dtype dt, const void* hidden_kept, const float* bias_kept, const int32_t* pos_kept,
+                         const tg_seq* seqs, int32_t n_seqs, const tg_dense_weights* w, void* out, void* k_out,
+                         void* v_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_err.clear();
+    if (dt != TG_BF16) return fail(TG_ERR_UNSUPPORTED, "the dense layer is built for bf16 only");
+    tg_status st = check_dense_weights(w);
+    if (st != TG_OK) return st;
+    tg::SeqTable st_;
+    int64_t m = 0;
+    st = build_seq_table(seqs, n_seqs, &st_, &m);
+    if (st != TG_OK) return st;
+    if (m == 0) return TG_OK;
+    if (!hidden_kept || !bias_kept || !pos_kept || !out)
+        return fail(TG_ERR_INVALID_ARGUMENT, "hidden_kept, bias_kept, pos_kept, out must be non-NULL");
+    if (!(aligned16(hidden_kept) && aligned16(out) && aligned16(k_out) && aligned16(v_out)))
+        return fail(TG_ERR_UNSUPPORTED, "hidden_kept, out, k_out, v_out must be 16-byte aligned");
+    const DenseLayout l = dense_layout(m, *w);
+    if (!workspace || workspace_bytes < l.total)
+        return fail(TG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                    l.total);
+    if ((uintptr_t)workspace % 256) return fail(TG_ERR_INVALID_ARGUMENT, "workspace not 256-byte aligned");
+    char* ws = (char*)workspace;
+    void *a = ws + l.a, *qkv = ws + l.qkv, *q = ws + l.q, *o = ws + l.o, *h2 = ws + l.h2, *mlp = ws + l.mlp;
+    void* k = k_out ? k_out : ws + l.k;
+    void* v = v_out ? v_out : ws + l.v;
+    const int d = w->d_model, dh = w->head_dim, hq = w->hq, hkv = w->hkv;
+    hipError_t e = tg::launch_rmsnorm(hidden_kept, m, d, w->ln1, w->eps, a, stream);
+    if (e == hipSuccess)
+        e = tg::launch_linear(TG_LINEAR_STORE, a, m, d, w->wqkv, nullptr, (hq + 2 * hkv) * dh, nullptr, qkv, stream);
+    if (e == hipSuccess)
+        e = tg::launch_qk_norm_rope(qkv, m, hq, hkv, dh, w->q_norm, w->k_norm, pos_kept, w->eps, w->rope_theta, q, k,
+                                    v, stream);
+    if (e != hipSuccess) return hip_fail(e, "tg_dense_layer launch");
+    st = tg_gated_attention(TG_BF16, q, k, v, bias_kept, pos_kept, seqs, n_seqs, hq, hkv, dh, w->gain, w->tau, o,
+                            nullptr, nullptr, 0, stream);
+    if (st != TG_OK) return st;
+    e = tg::launch_linear(TG_LINEAR_RESIDUAL, o, m, hq * dh, w->wo, nullptr, d, hidden_kept, h2, stream);
+    if (e == hipSuccess) e = tg::launch_rmsnorm(h2, m, d, w->ln2, w->eps, a, stream);
+    if (e == hipSuccess)
+        e = tg::launch_linear(TG_LINEAR_SWIGLU, a, m, d, w->w_gate, w->w_up, w->d_ff, nullptr, mlp, stream);
+    if (e == hipSuccess)
+        e = tg::launch_linear(TG_LINEAR_RESIDUAL, mlp, m, w->d_ff, w->w_down, nullptr, d, h2, out, stream);
+    if (e != hipSuccess) return hip_fail(e, "tg_dense_layer launch");
+    return TG_OK;
+}
+
 size_t tg_decode_workspace_bytes(const tg_kv_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv, int32_t head_dim) {
     tg::DecTable t;
     int64_t r = 0;

@@ -133,6 +133,15 @@ struct AttnBwdArgs {
 size_t attention_backward_plan(const SeqTable& st, int hq, int hkv, int head_dim, void* table_out);
 size_t attention_backward_table_bytes();
 
+// Dense decoder layer pieces (bf16).
+hipError_t launch_rmsnorm(const void* x, int64_t m, int d, const void* w, float eps, void* out, hipStream_t st);
+hipError_t launch_qk_norm_rope(const void* qkv, int64_t m, int hq, int hkv, int head_dim, const void* qn,
+                               const void* kn, const int32_t* pos, float eps, float theta, void* q, void* k, void* v,
+                               hipStream_t st);
+// epi: 0 store, 1 add residual, 2 SwiGLU (w = gate rows, w_up = up rows).
+hipError_t launch_linear(int epi, const void* a, int64_t m, int k, const void* w, const void* w_up, int n_out,
+                         const void* resid, void* out, hipStream_t st);
+
 // Gate MLP backward (bf16, d_model % 64 == 0, d_hidden % 64 == 0 and <= 256).
 size_t gate_backward_workspace_bytes(int64_t n_list, int d_model, int d_hidden);
 hipError_t launch_gate_backward(const void* x, int64_t n_rows, int d, const void* w1, const void* b1,

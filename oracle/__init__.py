@@ -14,6 +14,7 @@ from .tokengate import (  # noqa: F401
     gated_attention_backward,
     gated_prefill,
     kept_rows,
+    linear,
     logsigmoid,
     prompt_of_rows,
     rms_norm,
@@ -21,5 +22,6 @@ from .tokengate import (  # noqa: F401
     score_grad,
     select_topk,
     sigmoid,
+    swiglu,
     silu,
 )

@@ -471,6 +471,17 @@ def rope(x, pos, theta: float) -> np.ndarray:
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
+def linear(x, w, residual=None) -> np.ndarray:
+    """x W^T (+ residual), W in the nn.Linear layout [out, in]."""
+    y = _f64(x) @ _f64(w).T
+    return y if residual is None else y + _f64(residual)
+
+
+def swiglu(x, w_gate, w_up) -> np.ndarray:
+    """SiLU(x Wg^T) * (x Wu^T), the gated input of the MLP's down projection."""
+    return silu(linear(x, w_gate)) * linear(x, w_up)
+
+
 def dense_layer(h, pos_kept, bias_kept, seg_lens: Sequence[int], w: dict, hq: int, hkv: int,
                 head_dim: int) -> dict:
     """One decoder layer above the gate, over the kept rows h [M, d] at their
@@ -489,10 +500,10 @@ def dense_layer(h, pos_kept, bias_kept, seg_lens: Sequence[int], w: dict, hq: in
     k = rope(rms_norm(qkv[:, dq:dq + dk].reshape(m, hkv, head_dim), w["k_norm"], eps), pos_kept, theta)
     v = qkv[:, dq + dk:].reshape(m, hkv, head_dim)
     o, _ = gated_attention(q, k, v, bias_kept, pos_kept, seg_lens, hq, hkv, w["gain"], w["tau"])
-    h2 = hd + o.reshape(m, dq) @ _f64(w["wo"]).T
+    h2 = linear(o.reshape(m, dq), w["wo"], hd)
     a2 = rms_norm(h2, w["ln2"], eps)
-    mlp = silu(a2 @ _f64(w["w_gate"]).T) * (a2 @ _f64(w["w_up"]).T)
-    return dict(out=h2 + mlp @ _f64(w["w_down"]).T, h2=h2, q=q, k=k, v=v, attn=o, mlp=mlp)
+    mlp = swiglu(a2, w["w_gate"], w["w_up"])
+    return dict(out=linear(mlp, w["w_down"], h2), h2=h2, q=q, k=k, v=v, attn=o, mlp=mlp)
 
 
 # ---------------------------------------------------------------------------

@@ -15,7 +15,7 @@ from synthetic import Prompt
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tokengate.h")
 
-INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 
 
 def declared_functions():
@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 19, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(tg.EXPORTED)
@@ -206,6 +206,34 @@ def test_gate_backward_workspace_and_rejects_before_launch(lib):
     bad = list(args)
     bad[11] = None  # d_w1
     assert lib.tg_gate_backward(1, *bad, fake, need, None) == INVALID
+
+
+def test_linear_and_dense_layer_reject_before_launch(lib):
+    fake = ctypes.c_void_p(4096)
+    assert lib.tg_linear(0, 0, fake, 10, 64, fake, None, 128, None, fake, None) == UNSUPPORTED  # fp32
+    assert lib.tg_linear(1, 3, fake, 10, 64, fake, None, 128, None, fake, None) == INVALID      # epilogue
+    assert lib.tg_linear(1, 0, fake, 10, 96, fake, None, 128, None, fake, None) == UNSUPPORTED  # k % 64
+    assert lib.tg_linear(1, 0, fake, 10, 64, fake, None, 192, None, fake, None) == UNSUPPORTED  # n % 128
+    assert lib.tg_linear(1, 1, fake, 10, 64, fake, None, 128, None, fake, None) == INVALID      # residual missing
+    assert lib.tg_linear(1, 2, fake, 10, 64, fake, None, 128, None, fake, None) == INVALID      # w_up missing
+    assert lib.tg_linear(1, 0, fake, 0, 64, None, None, 128, None, None, None) == OK            # nothing to do
+    w = tg._lib.TgDenseWeights(2048, 16, 8, 128, 6144, 1e-6, 1e6, 1.2, *([4096] * 10))
+    prompts = [Prompt(0, 100, 0, 90, 40)]
+    m = 50
+    need = lib.tg_dense_layer_workspace_bytes(seq_array(prompts), 1, ctypes.byref(w))
+    up = lambda b: (b + 255) // 256 * 256
+    assert need == sum(up(m * e * 2) for e in (2048, 4096, 2048, 1024, 1024, 2048, 2048, 6144))
+    for field, bad, code in (("head_dim", 96, UNSUPPORTED), ("hkv", 3, INVALID), ("d_ff", 100, UNSUPPORTED),
+                             ("d_model", 2000, UNSUPPORTED), ("tau", 0.0, INVALID), ("rope_theta", 1.0, INVALID)):
+        wb = tg._lib.TgDenseWeights(2048, 16, 8, 128, 6144, 1e-6, 1e6, 1.2, *([4096] * 10))
+        setattr(wb, field, bad)
+        assert lib.tg_dense_layer_workspace_bytes(seq_array(prompts), 1, ctypes.byref(wb)) == 0
+        assert lib.tg_dense_layer(1, fake, fake, fake, seq_array(prompts), 1, ctypes.byref(wb), fake, None, None,
+                                  fake, need, None) == code, field
+    assert lib.tg_dense_layer(1, fake, fake, fake, seq_array(prompts), 1, ctypes.byref(w), fake, None, None,
+                              fake, need - 1, None) == WORKSPACE
+    assert lib.tg_dense_layer(0, fake, fake, fake, seq_array(prompts), 1, ctypes.byref(w), fake, None, None,
+                              fake, need, None) == UNSUPPORTED
 
 
 def test_binding_refuses_cpu_tensors():

@@ -691,3 +691,59 @@ def test_gate_backward_without_dx_and_deterministic():
     b = check_gate_backward(2000, 512, 128, 333, seed=7, with_dx=False)
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+# ------------------------------------------------------- full above-gate layer ----
+
+@pytest.mark.parametrize("m,k,n", [(1, 64, 128), (77, 2048, 384), (300, 128, 4096), (2384, 2048, 256)])
+def test_linear_epilogues(m, k, n):
+    """tg_linear against the oracle's linear / swiglu: store, residual add, SwiGLU.
+    Bar: per row, max |err| <= 1e-2 * max |ref| (fp32 sums of exact bf16 products, one
+    bf16 rounding of the result; SwiGLU: two such sums and an fp32 SiLU)."""
+    note(f"linear m={m} k={k} n={n}: store, residual, swiglu")
+    g = torch.Generator().manual_seed(m + k + n)
+    x = torch.randn(m, k, generator=g).to(torch.bfloat16)
+    w = (torch.randn(n, k, generator=g) / math.sqrt(k)).to(torch.bfloat16)
+    wu = (torch.randn(n, k, generator=g) / math.sqrt(k)).to(torch.bfloat16)
+    r = torch.randn(m, n, generator=g).to(torch.bfloat16)
+    xd, wd, wud, rd = x.to(DEV), w.to(DEV), wu.to(DEV), r.to(DEV)
+    assert_rowmax_close(f64(tg.tg_linear(xd, wd)), oracle.linear(f64(x), f64(w)), rel=1e-2)
+    assert_rowmax_close(f64(tg.tg_linear(xd, wd, residual=rd)), oracle.linear(f64(x), f64(w), f64(r)), rel=1e-2)
+    assert_rowmax_close(f64(tg.tg_linear(xd, wd, w_up=wud)), oracle.swiglu(f64(x), f64(w), f64(wu)), rel=1e-2)
+
+
+def check_dense_layer(segs, d, hq, hkv, dh, d_ff, seed, pos_offset=0):
+    from synthetic import make_dense_layer, make_kept_hidden
+    w = make_dense_layer(d, hq, hkv, dh, d_ff, seed=seed)
+    x = make_kept_hidden(list(segs), d, seed=seed + 1, n_query_tail=16)
+    pos = x["pos"] + pos_offset
+    ps, st = [], 0
+    for ln in segs:
+        ps.append(Prompt(st, ln, 0, 0, 0))
+        st += ln
+    wd = {kk: (t.to(DEV) if hasattr(t, "to") else t) for kk, t in w.items()}
+    out, kc, vc = tg.tg_dense_layer(x["h"].to(DEV), x["bias"].to(DEV), pos.to(DEV), ps, wd, hq, hkv, dh,
+                                    want_kv=True)
+    ref = oracle.dense_layer(x["h"], pos, x["bias"], list(segs), w, hq, hkv, dh)
+    # bf16 storage between the steps: per (row, head) and per row against the row maximum
+    rk = assert_rowmax_close(f64(kc), ref["k"])
+    rv = assert_rowmax_close(f64(vc), ref["v"])
+    ro = assert_rowmax_close(f64(out), ref["out"])
+    return out, (rk, rv, ro)
+
+
+def test_dense_layer_small_ragged():
+    note("dense layer d=256 hq=4 hkv=2 D=64 d_ff=384, prompts 100 + 1 + 37")
+    check_dense_layer([100, 1, 37], 256, 4, 2, 64, 384, seed=31)
+
+
+def test_dense_layer_qwen_shapes_far_positions():
+    note("dense layer Qwen3-1.7B shapes (d=2048, 16/8 heads, D=128, d_ff=6144), 600 kept rows at positions ~120k")
+    check_dense_layer([500, 100], 2048, 16, 8, 128, 6144, seed=32, pos_offset=120000)
+
+
+def test_dense_layer_deterministic():
+    note("dense layer: bitwise repeatable")
+    a, _ = check_dense_layer([300], 512, 8, 4, 128, 1024, seed=33)
+    b, _ = check_dense_layer([300], 512, 8, 4, 128, 1024, seed=33)
+    assert torch.equal(a, b)

@@ -63,8 +63,10 @@ MUTATIONS = [
      "inv = float(theta) ** (-1.0 * np.arange(half) / dh)"),
     ("key heads left without their norm", "k = rope(rms_norm(qkv[:, dq:dq + dk].reshape(m, hkv, head_dim), w[\"k_norm\"], eps)",
      "k = rope(qkv[:, dq:dq + dk].reshape(m, hkv, head_dim)"),
-    ("SiLU on the up projection instead of the gate", "mlp = silu(a2 @ _f64(w[\"w_gate\"]).T) * (a2 @ _f64(w[\"w_up\"]).T)",
-     "mlp = (a2 @ _f64(w[\"w_gate\"]).T) * silu(a2 @ _f64(w[\"w_up\"]).T)"),
+    ("SiLU on the up projection instead of the gate", "return silu(linear(x, w_gate)) * linear(x, w_up)",
+     "return linear(x, w_gate) * silu(linear(x, w_up))"),
+    ("output projection without the residual", "h2 = linear(o.reshape(m, dq), w[\"wo\"], hd)",
+     "h2 = linear(o.reshape(m, dq), w[\"wo\"])"),
     ("second norm over the layer input instead of the attention residual", "a2 = rms_norm(h2, w[\"ln2\"], eps)",
      "a2 = rms_norm(hd, w[\"ln2\"], eps)"),
 ]
