@@ -239,6 +239,8 @@ def measure_extras(torch, tg, layer, w, steps, dev):
     out["backward_qwen16k"] = measure_backward(torch, tg, layer, timed, pct)
     # ... and on through the score chain into the gate MLP's weights.
     out["gate_backward_qwen16k"] = measure_gate_backward(torch, tg, layer, timed, pct)
+    # The full above-gate decoder layer over the kept rows, against the same layer over all rows.
+    out["dense_layer_qwen16k"] = measure_dense_layer(torch, tg, layer, w, timed, pct)
     # Select on one prompt of 2^24 document rows: the multi-workgroup path
     # (1024 chunks of 16384 rows), arguments marshalled once outside the
     # timed region.
@@ -401,6 +403,55 @@ def measure_gate_backward(torch, tg, lay, timed, pct, reps=20):
     fl = 3 * 2 * m * d * h
     return {"listed_rows": m, "us": round(us, 1), "algorithmic_tflops": round(fl / (us * 1e-6) / 1e12, 1),
             "frac_bf16_peak": round(fl / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def measure_dense_layer(torch, tg, lay, w, timed, pct, reps=10):
+    """One Qwen3-1.7B-shaped decoder layer above the gate (RMSNorm, QKV, per-head
+    Q/K norm + rotary embedding at the original positions, token-gated attention,
+    output projection, SwiGLU MLP; random weights) over the 16k layer's kept rows,
+    and the same layer over all 16384 rows (every row kept, zero bias) for
+    comparison. Memory: the layer's device workspace plus its K/V cache and output
+    (bf16), the part of the above-gate footprint that scales with the rows."""
+    import ctypes
+    from synthetic import Prompt, make_dense_layer
+    from learned_token_pruning_layer_amd._lib import dense_weights, seq_array
+    d, hq, hkv, dh, d_ff = lay.x.shape[1], lay.hq, lay.hkv, lay.head_dim, 6144
+    wts = make_dense_layer(d, hq, hkv, dh, d_ff, seed=5, device=lay.x.device)
+    lib = tg.load()
+    desc = dense_weights(wts, d, hq, hkv, dh)
+
+    def one(h, bias, pos, prompts):
+        m = h.shape[0]
+        sa = seq_array(prompts)
+        need = lib.tg_dense_layer_workspace_bytes(sa, len(prompts), ctypes.byref(desc))
+        ws = torch.empty(need, dtype=torch.uint8, device=h.device)
+        out = torch.empty_like(h)
+        kc = torch.empty((m, hkv, dh), dtype=h.dtype, device=h.device)
+        vc = torch.empty_like(kc)
+        st = torch.cuda.current_stream().cuda_stream
+        args = (1, h.data_ptr(), bias.data_ptr(), pos.data_ptr(), sa, len(prompts), ctypes.byref(desc),
+                out.data_ptr(), kc.data_ptr(), vc.data_ptr(), ws.data_ptr(), need, st)
+
+        def call():
+            if lib.tg_dense_layer(*args) != 0:
+                raise RuntimeError(lib.tg_last_error().decode())
+
+        call()
+        us = pct(timed(call, reps), 0.5)
+        pairs = sum((p.k_doc + p.length - (p.doc_end - p.doc_begin)) * (p.k_doc + p.length - (p.doc_end - p.doc_begin)
+                                                                        + 1) // 2 for p in prompts)
+        fl = 2 * m * d * ((hq + 2 * hkv) * dh + hq * dh + 3 * d_ff) + 4 * dh * hq * pairs
+        mem = need + (2 * kc.numel() + out.numel()) * 2
+        return {"rows": m, "us": round(us, 1), "tflops": round(fl / (us * 1e-6) / 1e12, 1),
+                "row_scaled_bytes": int(mem)}
+
+    pruned = one(lay.hidden_kept if lay.hidden_kept is not None else lay.x[lay.kept.long()].contiguous(),
+                 lay.bias_kept, lay.pos_kept, lay.prompts)
+    n = w.x.shape[0]
+    full = one(w.x, torch.zeros(n, dtype=torch.float32, device=w.x.device),
+               torch.arange(n, dtype=torch.int32, device=w.x.device), [Prompt(0, n, 0, 0, 0)])
+    return {"pruned": pruned, "unpruned": full, "speedup": round(full["us"] / pruned["us"], 2),
+            "memory_ratio": round(full["row_scaled_bytes"] / pruned["row_scaled_bytes"], 2), "d_ff": d_ff}
 
 
 def measure_configs(torch, tg, dev, timed, pct):
