@@ -19,15 +19,16 @@
 //    at a time (lane i holds the rotary pair (i, i + D/2)), rotates it by
 //    the row's original position (angle reduced in fp64, sin/cos in fp32)
 //    and writes q, k and v as separate [M, heads, D] tensors.
-//  * linear_kernel<EPI>: C = A W^T on 32x32x16 bf16 MFMA for 128 activation
-//    rows x 128 weight rows per workgroup (4 waves of 64 x 64), 64-wide k
+//  * linear_kernel<EPI, ...>: C = A W^T on 32x32x16 bf16 MFMA, waves of 64
+//    weight rows x 64 activation rows: 256 x 128 per workgroup of 8 waves
+//    (one per CU) or 128 x 128 per workgroup of 4 (two per CU); 64-wide k
 //    chunks streamed global -> LDS with direct loads through a two-stage
-//    ring (the gate kernel's swizzled 128-byte LDS rows and permuted k-step
-//    order), tiles ordered so the workgroups of one XCD share weight tiles.
-//    The weights are the MFMA A operand, so each lane's accumulators hold 4
-//    consecutive output columns of one row (8-byte stores). Epilogues: plain
-//    store, residual add, and SwiGLU (the 128 weight rows are 64 gate rows
-//    and the matching 64 up rows; a wave holds both halves of its columns).
+//    ring (swizzled 128-byte LDS rows, permuted k-step order), tiles ordered
+//    so the workgroups of one XCD share weight tiles. The weights are the
+//    MFMA A operand, so each lane's accumulators hold 4 consecutive output
+//    columns of one row (8-byte stores). Epilogues: plain store, residual
+//    add, and SwiGLU (a tile's weight rows are gate rows and the matching up
+//    rows; a wave holds both halves of its columns).
 #include "tg_internal.hpp"
 #include "tg_device.hpp"
 
@@ -126,8 +127,6 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(const uint16_t* __res
 // ------------------------------------------------------------------- GEMM
 
 enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
-constexpr int LBM = 128;  // activation rows per workgroup
-constexpr int LBN = 128;  // weight rows per workgroup
 constexpr int LBK = 64;   // k per chunk
 constexpr int LNS = 2;    // ring stages
 
@@ -135,72 +134,76 @@ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // out[m, n] = sum_k a[m, k] w[n, k] (+ resid[m, n]); SwiGLU: out[m, n] =
 // SiLU(a . wg[n]) * (a . wu[n]). a [m, k], weights [*, k] row-major, k % 64
-// == 0; n_out % 128 == 0 (SwiGLU: % 64). Tile t = (m tile, n tile), m tile
-// fastest; the 8 XCDs each take a contiguous range of tiles.
-template <int EPI>
-__global__ __launch_bounds__(256) void linear_kernel(const uint16_t* __restrict__ a, int64_t m, int k,
+// == 0. Workgroup: WN x WM waves, each wave SN x SM sub-tiles of 32 x 32
+// (weight rows x activation rows), so TN = 32 SN WN weight rows and TM =
+// 32 SM WM activation rows per tile; SwiGLU: the first TN/2 weight rows are gate
+// rows and the rest the matching up rows, so a tile makes TN/2 output
+// columns. Tile t = (m tile, n tile), m tile fastest; the 8 XCDs each take
+// a contiguous range of tiles.
+template <int EPI, int SN, int SM, int WN, int WM>
+__global__ __launch_bounds__(64 * WN * WM) void linear_kernel(const uint16_t* __restrict__ a, int64_t m, int k,
                                                      const uint16_t* __restrict__ w,
                                                      const uint16_t* __restrict__ w_up, int n_out,
                                                      const uint16_t* __restrict__ resid, uint16_t* __restrict__ out,
                                                      int n_mt, int n_nt) {
-    constexpr int OPS = 8;  // direct loads per wave per chunk (4 for A, 4 for W)
-    constexpr int NPT = EPI == EPI_SWIGLU ? LBN / 2 : LBN;  // output columns per tile
-    __shared__ __attribute__((aligned(1024))) char as_[LNS][LBM * 128];
-    __shared__ __attribute__((aligned(1024))) char ws_[LNS][LBN * 128];
+    constexpr int NW = WN * WM;                    // waves
+    constexpr int TN = 32 * SN * WN, TM = 32 * SM * WM;
+    constexpr int AI = TM / (8 * NW), WI = TN / (8 * NW);  // direct loads per wave per chunk (8 rows each)
+    static_assert(AI * 8 * NW == TM && WI * 8 * NW == TN, "tile rows must split evenly over the waves");
+    constexpr int OPS = AI + WI;
+    constexpr int NPT = EPI == EPI_SWIGLU ? TN / 2 : TN;  // output columns per tile
+    __shared__ __attribute__((aligned(1024))) char as_[LNS][TM * 128];
+    __shared__ __attribute__((aligned(1024))) char ws_[LNS][TN * 128];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
     const int n_tiles = n_mt * n_nt;
     int t = blockIdx.x;
     if ((n_tiles & 7) == 0) t = (t & 7) * (n_tiles >> 3) + (t >> 3);
     const int mt = t % n_mt, nt = t / n_mt;
-    const int64_t m0 = (int64_t)mt * LBM;
+    const int64_t m0 = (int64_t)mt * TM;
     const int n0 = nt * NPT;
     const int nchunk = k / LBK;
 
-    // Per-lane load rows (fixed across chunks): instruction i of this wave
-    // moves 8 rows x 128 bytes; lane >> 3 picks the row, lane & 7 its chunk.
-    const uint16_t* asrc[4];
-    const uint16_t* wsrc[4];
+    // Per-lane load rows (fixed across chunks): load instruction i of this
+    // wave moves 8 rows x 128 bytes; lane >> 3 picks the row, lane & 7 its
+    // 16-byte chunk.
+    const uint16_t* asrc[AI];
+    const uint16_t* wsrc[WI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = (wave * 4 + i) * 8 + (lane >> 3);
-        const int ch = (lane & 7) ^ swz(row);
-        const int64_t ar = min(m0 + row, m - 1);
-        asrc[i] = a + ar * k + ch * 8;
-        const uint16_t* wb;
-        int wr;
-        if (EPI == EPI_SWIGLU) {
-            wb = row < 64 ? w : w_up;
-            wr = n0 + (row & 63);
-        } else {
-            wb = w;
-            wr = n0 + row;
-        }
-        wsrc[i] = wb + (int64_t)wr * k + ch * 8;
+    for (int i = 0; i < AI; ++i) {
+        const int row = (wave * AI + i) * 8 + (lane >> 3);
+        asrc[i] = a + min(m0 + row, m - 1) * k + ((lane & 7) ^ swz(row)) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < WI; ++i) {
+        const int row = (wave * WI + i) * 8 + (lane >> 3);
+        const uint16_t* wb = (EPI == EPI_SWIGLU && row >= TN / 2) ? w_up : w;
+        const int wr = EPI == EPI_SWIGLU ? n0 + (row % (TN / 2)) : n0 + row;
+        wsrc[i] = wb + (int64_t)wr * k + ((lane & 7) ^ swz(row)) * 8;
     }
     auto issue = [&](int c, int slot) __attribute__((always_inline)) {
         const int k0 = (c < nchunk ? c : nchunk - 1) * LBK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int inst = wave * 4 + i;
-            dma16(asrc[i] + k0, (const LDS_AS void*)&as_[slot][inst * 1024]);
-            dma16(wsrc[i] + k0, (const LDS_AS void*)&ws_[slot][inst * 1024]);
-        }
+        for (int i = 0; i < AI; ++i) dma16(asrc[i] + k0, (const LDS_AS void*)&as_[slot][(wave * AI + i) * 1024]);
+#pragma unroll
+        for (int i = 0; i < WI; ++i) dma16(wsrc[i] + k0, (const LDS_AS void*)&ws_[slot][(wave * WI + i) * 1024]);
     };
 
-    // Wave tile: weight rows 64 wn .. +64 (SwiGLU: gate rows 32 wn .. +32 and
-    // the up rows 64 + 32 wn .. +32), activation rows 64 wm .. +64.
-    const int wn = wave & 1, wm = wave >> 1;
-    int wrow[2], arow[2];
+    // Wave tile: weight sub-tiles i (rows 32 SN wn + 32 i; SwiGLU: gate rows
+    // 16 SN wn + 32 i for i < SN/2 and the matching up rows TN/2 + ...), and
+    // activation sub-tiles j (rows 32 SM wm + 32 j).
+    const int wn = wave % WN, wm = wave / WN;
+    int wrow[SN], arow[SM];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        wrow[i] = EPI == EPI_SWIGLU ? 64 * i + 32 * wn + l32 : 64 * wn + 32 * i + l32;
-        arow[i] = 64 * wm + 32 * i + l32;
-    }
-    f32x16 acc[2][2];
+    for (int i = 0; i < SN; ++i)
+        wrow[i] = (EPI == EPI_SWIGLU ? (i < SN / 2 ? 16 * SN * wn + 32 * i : TN / 2 + 16 * SN * wn + 32 * (i - SN / 2))
+                                     : 32 * SN * wn + 32 * i) + l32;  // (TN / 2 = 16 SN WN)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < SM; ++j) arow[j] = 32 * SM * wm + 32 * j + l32;
+    f32x16 acc[SN][SM];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < SN; ++i)
+#pragma unroll
+        for (int j = 0; j < SM; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -215,16 +218,17 @@ __global__ __launch_bounds__(256) void linear_kernel(const uint16_t* __restrict_
         const LDS_AS char* wt = (const LDS_AS char*)ws_[slot];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 wa[2], xa[2];
+            bf16x8 wa[SN], xa[SM];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < SN; ++i)
                 wa[i] = *(const LDS_AS bf16x8*)(wt + wrow[i] * 128 + (((hh * 4 + ks) ^ swz(wrow[i])) << 4));
-                xa[i] = *(const LDS_AS bf16x8*)(at + arow[i] * 128 + (((hh * 4 + ks) ^ swz(arow[i])) << 4));
-            }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < SM; ++j)
+                xa[j] = *(const LDS_AS bf16x8*)(at + arow[j] * 128 + (((hh * 4 + ks) ^ swz(arow[j])) << 4));
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+            for (int i = 0; i < SN; ++i)
+#pragma unroll
+                for (int j = 0; j < SM; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[i], xa[j], acc[i][j], 0, 0, 0);
         }
     }
@@ -233,27 +237,25 @@ __global__ __launch_bounds__(256) void linear_kernel(const uint16_t* __restrict_
     // acc[i][j] register r: weight row wrow[i] - l32 + 8(r/4) + 4hh + r%4 of
     // activation row m0 + arow[j]: 4 consecutive output columns per group.
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < SM; ++j) {
         const int64_t mr = m0 + arow[j];
         if (mr >= m) continue;
         uint16_t* orow = out + mr * n_out;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            if (EPI == EPI_SWIGLU) {
-                const int col = n0 + 32 * wn + 8 * g + 4 * hh;
+        for (int i = 0; i < (EPI == EPI_SWIGLU ? SN / 2 : SN); ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
                 float o[4];
+                int col;
+                if (EPI == EPI_SWIGLU) {
+                    col = n0 + 16 * SN * wn + 32 * i + 8 * g + 4 * hh;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float gt = acc[0][j][4 * g + e], up = acc[1][j][4 * g + e];
-                    o[e] = gt / (1.0f + __expf(-gt)) * up;
-                }
-                uint2 st = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-                *(uint2*)(orow + col) = st;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int col = n0 + 64 * wn + 32 * i + 8 * g + 4 * hh;
-                    float o[4];
+                    for (int e = 0; e < 4; ++e) {
+                        const float gt = acc[i][j][4 * g + e], up = acc[i + SN / 2][j][4 * g + e];
+                        o[e] = gt / (1.0f + __expf(-gt)) * up;
+                    }
+                } else {
+                    col = n0 + 32 * SN * wn + 32 * i + 8 * g + 4 * hh;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * g + e];
                     if (EPI == EPI_RESID) {
@@ -263,11 +265,10 @@ __global__ __launch_bounds__(256) void linear_kernel(const uint16_t* __restrict_
                         o[2] += __uint_as_float(rv.y << 16);
                         o[3] += __uint_as_float(rv.y & 0xffff0000u);
                     }
-                    uint2 st = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-                    *(uint2*)(orow + col) = st;
                 }
+                uint2 st = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                *(uint2*)(orow + col) = st;
             }
-        }
     }
 }
 
@@ -296,22 +297,37 @@ hipError_t launch_qk_norm_rope(const void* qkv, int64_t m, int hq, int hkv, int 
     return hipGetLastError();
 }
 
-hipError_t launch_linear(int epi, const void* a, int64_t m, int k, const void* w, const void* w_up, int n_out,
-                         const void* resid, void* out, hipStream_t st) {
-    if (m == 0) return hipSuccess;
-    const int n_mt = (int)((m + LBM - 1) / LBM);
-    const int n_nt = n_out / (epi == EPI_SWIGLU ? LBN / 2 : LBN);
-    const dim3 grid((unsigned)(n_mt * n_nt)), block(256);
+template <int SN, int SM, int WN, int WM>
+hipError_t launch_linear_t(int epi, const void* a, int64_t m, int k, const void* w, const void* w_up, int n_out,
+                           const void* resid, void* out, hipStream_t st) {
+    const int tm = 32 * SM * WM, npt = (epi == EPI_SWIGLU ? 16 : 32) * SN * WN;
+    const int n_mt = (int)((m + tm - 1) / tm);
+    const int n_nt = n_out / npt;
+    const dim3 grid((unsigned)(n_mt * n_nt)), block(64 * WN * WM);
     const uint16_t *ab = (const uint16_t*)a, *wb = (const uint16_t*)w, *ub = (const uint16_t*)w_up;
     const uint16_t* rb = (const uint16_t*)resid;
     uint16_t* ob = (uint16_t*)out;
     if (epi == EPI_SWIGLU)
-        hipLaunchKernelGGL(linear_kernel<EPI_SWIGLU>, grid, block, 0, st, ab, m, k, wb, ub, n_out, rb, ob, n_mt, n_nt);
+        hipLaunchKernelGGL((linear_kernel<EPI_SWIGLU, SN, SM, WN, WM>), grid, block, 0, st, ab, m, k, wb, ub, n_out,
+                           rb, ob, n_mt, n_nt);
     else if (epi == EPI_RESID)
-        hipLaunchKernelGGL(linear_kernel<EPI_RESID>, grid, block, 0, st, ab, m, k, wb, ub, n_out, rb, ob, n_mt, n_nt);
+        hipLaunchKernelGGL((linear_kernel<EPI_RESID, SN, SM, WN, WM>), grid, block, 0, st, ab, m, k, wb, ub, n_out, rb,
+                           ob, n_mt, n_nt);
     else
-        hipLaunchKernelGGL(linear_kernel<EPI_STORE>, grid, block, 0, st, ab, m, k, wb, ub, n_out, rb, ob, n_mt, n_nt);
+        hipLaunchKernelGGL((linear_kernel<EPI_STORE, SN, SM, WN, WM>), grid, block, 0, st, ab, m, k, wb, ub, n_out, rb,
+                           ob, n_mt, n_nt);
     return hipGetLastError();
+}
+
+hipError_t launch_linear(int epi, const void* a, int64_t m, int k, const void* w, const void* w_up, int n_out,
+                         const void* resid, void* out, hipStream_t st) {
+    if (m == 0) return hipSuccess;
+    // 256 weight rows x 128 activation rows per workgroup (8 waves, one
+    // workgroup per CU, shared loads) where the output width allows it;
+    // 128 x 128 (4 waves, two workgroups per CU) otherwise.
+    const int wide = epi == EPI_SWIGLU ? 128 : 256;
+    if (n_out % wide == 0) return launch_linear_t<2, 2, 4, 2>(epi, a, m, k, w, w_up, n_out, resid, out, st);
+    return launch_linear_t<2, 2, 2, 2>(epi, a, m, k, w, w_up, n_out, resid, out, st);
 }
 
 }  // namespace tg
