@@ -12,6 +12,7 @@ from .tokengate import (  # noqa: F401
     gate_scores,
     gated_attention,
     gated_attention_backward,
+    gated_delta_scan,
     gated_prefill,
     kept_rows,
     linear,

@@ -30,6 +30,9 @@ Memory-Efficient Prefill with Learned Token Pruning"):
   [IT-keep]  ai.info news, section "TokenGate impara quali token mantenere":
              the component ranks tokens at an intermediate layer and sends
              only the kept tokens' representations upward.
+  [TH-hybrid], [DE-hybrid], [IT-hybrid]  the sections of the same three
+             pages on hybrid-attention models: TokenGate also prunes at a
+             Gated-DeltaNet layer of the Qwen3.5 hybrid.
 
 The pages fix the bias only qualitatively. The form used here, on both
 sides, is: logit_ij = q_i.k_j / (sqrt(D) * tau) + g_h * logsigmoid(s_j) for
@@ -504,6 +507,43 @@ def dense_layer(h, pos_kept, bias_kept, seg_lens: Sequence[int], w: dict, hq: in
     a2 = rms_norm(h2, w["ln2"], eps)
     mlp = swiglu(a2, w["w_gate"], w["w_up"])
     return dict(out=linear(mlp, w["w_down"], h2), h2=h2, q=q, k=k, v=v, attn=o, mlp=mlp)
+
+
+# ---------------------------------------------------------------------------
+# Pruning at a Gated-DeltaNet layer.  [TH-hybrid] ai4bro.com post, section on
+# hybrid-attention models, [DE-hybrid] spke.com article, section on hybrid
+# attention, [IT-hybrid] ai.info news, section on hybrid models: the gate can
+# sit on a Gated-DeltaNet layer of the Qwen3.5 hybrid, and the layers above it
+# then run on the kept tokens only. A Gated-DeltaNet layer's token mixer is
+# the gated delta rule (its published definition), run here over the kept
+# rows of each prompt in their order:
+#     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+#     o_t = S_t q_t,
+# with a state S [dv, dk] per prompt and head.
+# ---------------------------------------------------------------------------
+
+def gated_delta_scan(q, k, v, g, beta, seg_lens: Sequence[int], state0=None):
+    """The gated delta rule over packed prompts. q, k [M, H, dk], v [M, H, dv],
+    g (log decay) and beta [M, H]; state0 [n_prompts, H, dv, dk] or None
+    (zero). Returns (o [M, H, dv], states [n_prompts, H, dv, dk]) in fp64.
+    The product S (I - beta k k^T) is applied as S - beta (S k) k^T."""
+    qd, kd, vd = _f64(q), _f64(k), _f64(v)
+    gd, bd = _f64(g), _f64(beta)
+    m_tot, nh, dk = kd.shape
+    dv = vd.shape[2]
+    o = np.zeros((m_tot, nh, dv))
+    states = np.zeros((len(seg_lens), nh, dv, dk)) if state0 is None else _f64(state0).copy()
+    off = 0
+    for p, ln in enumerate(seg_lens):
+        for t in range(off, off + int(ln)):
+            for h in range(nh):
+                sm = states[p, h]
+                a, b = math.exp(gd[t, h]), bd[t, h]
+                sm = a * (sm - b * np.outer(sm @ kd[t, h], kd[t, h])) + b * np.outer(vd[t, h], kd[t, h])
+                states[p, h] = sm
+                o[t, h] = sm @ qd[t, h]
+        off += int(ln)
+    return o, states
 
 
 # ---------------------------------------------------------------------------

@@ -368,3 +368,21 @@ def make_kept_hidden(seg_lens: List[int], d: int, seed: int, dtype=torch.bfloat1
                 bias[off + ln - tail: off + ln] = 0.0
         off += ln
     return dict(h=h.to(device), pos=pos.to(device), bias=bias.to(device), seg_lens=list(seg_lens))
+
+
+def make_delta_inputs(seg_lens: List[int], n_heads: int, dk: int, dv: int, seed: int, dtype=torch.bfloat16,
+                      device="cpu") -> dict:
+    """Kept-row inputs of a Gated-DeltaNet token mixer: q and k L2-normalised per
+    head (then rounded to dtype), v ~ N(0, 1), decay alpha ~ U(0.9, 1) given as
+    g = log(alpha), beta ~ U(0.05, 0.95), both fp32 [M, H]."""
+    m = int(sum(seg_lens))
+    gen = _torch_gen("cpu", seed)
+    q = torch.randn((m, n_heads, dk), generator=gen)
+    k = torch.randn((m, n_heads, dk), generator=gen)
+    q = q / torch.linalg.vector_norm(q, dim=-1, keepdim=True)
+    k = k / torch.linalg.vector_norm(k, dim=-1, keepdim=True)
+    v = torch.randn((m, n_heads, dv), generator=gen)
+    g = torch.log(torch.rand((m, n_heads), generator=gen) * 0.1 + 0.9)
+    beta = torch.rand((m, n_heads), generator=gen) * 0.9 + 0.05
+    return dict(q=q.to(dtype).to(device), k=k.to(dtype).to(device), v=v.to(dtype).to(device), g=g.to(device),
+                beta=beta.to(device), seg_lens=list(seg_lens))

@@ -67,6 +67,13 @@ MUTATIONS = [
      "return linear(x, w_gate) * silu(linear(x, w_up))"),
     ("output projection without the residual", "h2 = linear(o.reshape(m, dq), w[\"wo\"], hd)",
      "h2 = linear(o.reshape(m, dq), w[\"wo\"])"),
+    ("delta rule: decay applied after the new value is written",
+     "sm = a * (sm - b * np.outer(sm @ kd[t, h], kd[t, h])) + b * np.outer(vd[t, h], kd[t, h])",
+     "sm = a * (sm - b * np.outer(sm @ kd[t, h], kd[t, h]) + b * np.outer(vd[t, h], kd[t, h]))"),
+    ("delta rule: erase term added instead of subtracted", "sm = a * (sm - b * np.outer(sm @ kd[t, h]",
+     "sm = a * (sm + b * np.outer(sm @ kd[t, h]"),
+    ("delta rule: output read from the state before the update", "                states[p, h] = sm\n                o[t, h] = sm @ qd[t, h]",
+     "                o[t, h] = states[p, h] @ qd[t, h]\n                states[p, h] = sm"),
     ("second norm over the layer input instead of the attention residual", "a2 = rms_norm(h2, w[\"ln2\"], eps)",
      "a2 = rms_norm(hd, w[\"ln2\"], eps)"),
 ]

@@ -624,6 +624,71 @@ def test_dense_layer_residual_only_without_output_projections():
     np.testing.assert_array_equal(got["out"], x["h"].numpy())
 
 
+# ------------------------------------------------------ gated delta rule ----
+
+def test_delta_scan_vs_explicit_products():
+    """Against the definition with the transition matrix written out:
+    S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T, in pure Python lists."""
+    rng = np.random.default_rng(41)
+    segs, nh, dk, dv = [4, 3], 2, 3, 2
+    m = sum(segs)
+    q, k, v = rng.normal(size=(m, nh, dk)), rng.normal(size=(m, nh, dk)), rng.normal(size=(m, nh, dv))
+    g, beta = np.log(rng.uniform(0.5, 1.0, size=(m, nh))), rng.uniform(0.0, 1.0, size=(m, nh))
+    s0 = rng.normal(size=(2, nh, dv, dk))
+    o, st = oracle.gated_delta_scan(q, k, v, g, beta, segs, state0=s0)
+    off = 0
+    for p, ln in enumerate(segs):
+        for h in range(nh):
+            sm = [[s0[p, h, i, j] for j in range(dk)] for i in range(dv)]
+            for t in range(off, off + ln):
+                a, b = math.exp(g[t, h]), beta[t, h]
+                tr = [[(1.0 if i == j else 0.0) - b * k[t, h, i] * k[t, h, j] for j in range(dk)] for i in range(dk)]
+                sm = [[a * sum(sm[i][r] * tr[r][j] for r in range(dk)) + b * v[t, h, i] * k[t, h, j]
+                       for j in range(dk)] for i in range(dv)]
+                for i in range(dv):
+                    assert abs(o[t, h, i] - sum(sm[i][j] * q[t, h, j] for j in range(dk))) < 1e-12
+            np.testing.assert_allclose(st[p, h], np.array(sm), rtol=1e-12, atol=1e-12)
+        off += ln
+
+
+def test_delta_scan_closed_forms():
+    """beta = 0: the state only decays, o_t = exp(sum of g so far) S_0 q_t. Orthonormal keys
+    with no decay and beta = 1: the delta rule stores each value exactly, so the final
+    state maps key i to value i. One dimension: s_t = a (1 - b k^2) s + b v k."""
+    rng = np.random.default_rng(42)
+    nh, dk, dv, m = 1, 4, 3, 5
+    q, k, v = rng.normal(size=(m, nh, dk)), rng.normal(size=(m, nh, dk)), rng.normal(size=(m, nh, dv))
+    g = np.log(rng.uniform(0.6, 1.0, size=(m, nh)))
+    s0 = rng.normal(size=(1, nh, dv, dk))
+    o, _ = oracle.gated_delta_scan(q, k, v, g, np.zeros((m, nh)), [m], state0=s0)
+    for t in range(m):
+        np.testing.assert_allclose(o[t, 0], math.exp(g[: t + 1, 0].sum()) * s0[0, 0] @ q[t, 0], rtol=1e-12)
+    basis = np.linalg.qr(rng.normal(size=(dk, dk)))[0].T  # orthonormal rows
+    kk = basis[:, None, :]
+    _, st = oracle.gated_delta_scan(kk, kk, v[:4], np.zeros((4, 1)), np.ones((4, 1)), [4])
+    for i in range(4):
+        np.testing.assert_allclose(st[0, 0] @ basis[i], v[i, 0], rtol=1e-12, atol=1e-12)
+    q1, k1, v1 = rng.normal(size=(m, 1, 1)), rng.normal(size=(m, 1, 1)), rng.normal(size=(m, 1, 1))
+    b1 = rng.uniform(0, 1, size=(m, 1))
+    o1, _ = oracle.gated_delta_scan(q1, k1, v1, g, b1, [m])
+    sv = 0.0
+    for t in range(m):
+        sv = math.exp(g[t, 0]) * (1 - b1[t, 0] * k1[t, 0, 0] ** 2) * sv + b1[t, 0] * v1[t, 0, 0] * k1[t, 0, 0]
+        assert abs(o1[t, 0, 0] - sv * q1[t, 0, 0]) < 1e-12
+
+
+def test_delta_scan_state_carries_across_calls():
+    """A prompt split in two calls, the second starting from the first's final state,
+    gives the outputs and final state of one call."""
+    from synthetic import make_delta_inputs
+    a = make_delta_inputs([20], 2, 8, 6, seed=43, dtype=torch.float64)
+    full_o, full_s = oracle.gated_delta_scan(a["q"], a["k"], a["v"], a["g"], a["beta"], [20])
+    o1, s1 = oracle.gated_delta_scan(a["q"][:7], a["k"][:7], a["v"][:7], a["g"][:7], a["beta"][:7], [7])
+    o2, s2 = oracle.gated_delta_scan(a["q"][7:], a["k"][7:], a["v"][7:], a["g"][7:], a["beta"][7:], [13], state0=s1)
+    np.testing.assert_allclose(np.concatenate([o1, o2]), full_o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(s2, full_s, rtol=1e-12, atol=1e-13)
+
+
 # ---------------------------------------------------------------- decode ----
 
 def _decode_case(seed, segs, hq, hkv, d, n_new_max=3, pos_ties=False):
