@@ -302,6 +302,31 @@ tg_status tg_dense_layer(tg_dtype dt, const void* hidden_kept, const float* bias
                          const tg_seq* seqs, int32_t n_seqs, const tg_dense_weights* w, void* out, void* k_out,
                          void* v_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Device workspace tg_gated_delta_scan needs, in bytes (0 for invalid
+ * arguments, which the call then reports, or no rows). */
+size_t tg_delta_scan_workspace_bytes(const tg_seq* seqs, int32_t n_seqs, int32_t n_heads, int32_t dk, int32_t dv);
+
+/* The gated delta rule (the token mixer of a Gated-DeltaNet layer) over the
+ * kept rows of each prompt, in their packed order:
+ *     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     out_t = S_t q_t,
+ * per prompt and head, with the state S [dv, dk] starting at state_in (fp32
+ * [n_seqs, n_heads, dv, dk], nullable: zero) and ending in state_out
+ * (nullable). q, k bf16 [M, n_heads, dk], v bf16 [M, n_heads, dv], g (log
+ * decay) and beta fp32 [M, n_heads], out bf16 [M, n_heads, dv]; q and k are
+ * used as given (a Gated-DeltaNet layer L2-normalises them first). Built: dk =
+ * dv = 128, bf16. Computed in 64-row chunks: per chunk, a triangular solve
+ * independent of the state (all chunks at once), then the chunks in order on
+ * MFMA with the state in fp32. Workspace: tg_delta_scan_workspace_bytes bytes,
+ * 16-byte aligned (scratch). Sources: the pages' sections on hybrid-attention
+ * models (ai4bro.com post, spke.com article, ai.info news): the gate also
+ * prunes at Gated-DeltaNet layers, whose mixers then run over the kept rows
+ * only. */
+tg_status tg_gated_delta_scan(tg_dtype dt, const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const tg_seq* seqs, int32_t n_seqs, int32_t n_heads, int32_t dk,
+                              int32_t dv, const float* state_in, void* out, float* state_out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* Device workspace tg_gate_backward needs, in bytes (0 when n_list is 0 or
  * the shape is not built, which the call then reports). */
 size_t tg_gate_backward_workspace_bytes(int64_t n_rows, int32_t d_model, int32_t d_hidden, int64_t n_list);

@@ -2,7 +2,8 @@
 
 The four steps (gate score, top-K select, compaction, token-gated
 attention), their backward (attention, bias -> score, gate MLP), the full
-above-gate decoder layer and decode over the pruned KV cache are HIP kernels behind the C ABI in
+above-gate decoder layer, the gated delta rule of a Gated-DeltaNet layer over
+the kept rows and decode over the pruned KV cache are HIP kernels behind the C ABI in
 include/tokengate.h; this package is the thin ctypes binding over it
 (argument marshalling only).
 """
@@ -25,6 +26,7 @@ from ._lib import (  # noqa: F401
     tg_gate_score,
     tg_gated_attention,
     tg_gated_attention_backward,
+    tg_gated_delta_scan,
     tg_kept_rows,
     tg_linear,
     tg_score_grad,

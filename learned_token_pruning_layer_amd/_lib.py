@@ -28,7 +28,7 @@ EXPORTED = (
     "tg_attention_workspace_bytes", "tg_gated_attention", "tg_decode_workspace_bytes", "tg_decode_attention",
     "tg_attention_backward_workspace_bytes", "tg_gated_attention_backward", "tg_score_grad",
     "tg_gate_backward_workspace_bytes", "tg_gate_backward", "tg_linear", "tg_dense_layer_workspace_bytes",
-    "tg_dense_layer", "tg_status_string", "tg_last_error",
+    "tg_dense_layer", "tg_delta_scan_workspace_bytes", "tg_gated_delta_scan", "tg_status_string", "tg_last_error",
 )
 
 
@@ -101,6 +101,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tg_gate_backward.argtypes = [c_int, vp, i64, i32, vp, vp, vp, i32, vp, vp, i64, vp, vp, vp, vp, vp, vp,
                                      ctypes.c_size_t, vp]
     lib.tg_gate_backward.restype = c_int
+    lib.tg_delta_scan_workspace_bytes.argtypes = [seqp, i32, i32, i32, i32]
+    lib.tg_delta_scan_workspace_bytes.restype = ctypes.c_size_t
+    lib.tg_gated_delta_scan.argtypes = [c_int, vp, vp, vp, vp, vp, seqp, i32, i32, i32, i32, vp, vp, vp, vp,
+                                        ctypes.c_size_t, vp]
+    lib.tg_gated_delta_scan.restype = c_int
     lib.tg_linear.argtypes = [c_int, i32, vp, i64, i32, vp, vp, i32, vp, vp, vp]
     lib.tg_linear.restype = c_int
     dwp = ctypes.POINTER(TgDenseWeights)
@@ -476,3 +481,29 @@ def tg_dense_layer(h: torch.Tensor, bias_kept: torch.Tensor, pos_kept: torch.Ten
                               ctypes.byref(desc), out.data_ptr(), _ptr(k), _ptr(v), workspace.data_ptr(),
                               workspace.numel(), _stream(stream)))
     return (out, k, v) if want_kv else out
+
+
+def tg_gated_delta_scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                        seqs: Sequence, state_in: Optional[torch.Tensor] = None, want_state: bool = False,
+                        workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gated delta rule over the kept rows: out bf16 [M, H, dv], plus the final states fp32
+    [n_seqs, H, dv, dk] when want_state."""
+    lib = load()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta")):
+        _dev(t, nm)
+    m, nh, dk = k.shape
+    dv = v.shape[2]
+    if g.dtype != torch.float32 or beta.dtype != torch.float32 or g.shape != (m, nh) or beta.shape != (m, nh):
+        raise ValueError("g and beta must be fp32 [M, H]")
+    if state_in is not None:
+        _dev(state_in, "state_in")
+    sa = seq_array(seqs)
+    out = torch.empty((m, nh, dv), dtype=v.dtype, device=v.device)
+    st = torch.empty((len(seqs), nh, dv, dk), dtype=torch.float32, device=v.device) if want_state else None
+    need = lib.tg_delta_scan_workspace_bytes(sa, len(seqs), nh, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=v.device)
+    _check(lib.tg_gated_delta_scan(_dtype_code(v), q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                                   beta.data_ptr(), sa, len(seqs), nh, dk, dv, _ptr(state_in), out.data_ptr(),
+                                   _ptr(st), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return (out, st) if want_state else out

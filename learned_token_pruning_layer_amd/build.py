@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "gate_score.hip", "select_topk.hip", "compact.hip", "gated_attention.hip", "decode_attention.hip",
-           "attention_backward.hip", "gate_backward.hip", "dense_layer.hip"]
+           "attention_backward.hip", "gate_backward.hip", "dense_layer.hip", "delta_scan.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

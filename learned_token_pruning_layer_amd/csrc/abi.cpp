@@ -570,6 +570,41 @@ tg_status tg_dense_layer(tg_dtype dt, const void* hidden_kept, const float* bias
     return TG_OK;
 }
 
+size_t tg_delta_scan_workspace_bytes(const tg_seq* seqs, int32_t n_seqs, int32_t n_heads, int32_t dk, int32_t dv) {
+    tg::SeqTable st_;
+    int64_t m = 0;
+    if (n_heads <= 0 || dk != 128 || dv != 128 || build_seq_table(seqs, n_seqs, &st_, &m) != TG_OK) return 0;
+    g_err.clear();
+    return tg::delta_scan_workspace_bytes(st_, n_heads);
+}
+
+tg_status tg_gated_delta_scan(tg_dtype dt, const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const tg_seq* seqs, int32_t n_seqs, int32_t n_heads, int32_t dk,
+                              int32_t dv, const float* state_in, void* out, float* state_out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    g_err.clear();
+    if (dt != TG_BF16) return fail(TG_ERR_UNSUPPORTED, "the delta scan is built for bf16 q, k, v only");
+    if (n_heads <= 0 || n_heads > 65535) return fail(TG_ERR_INVALID_ARGUMENT, "n_heads=%d out of range", n_heads);
+    if (dk != 128 || dv != 128) return fail(TG_ERR_UNSUPPORTED, "dk=%d dv=%d (built: 128, 128)", dk, dv);
+    tg::SeqTable st_;
+    int64_t m = 0;
+    tg_status st = build_seq_table(seqs, n_seqs, &st_, &m);
+    if (st != TG_OK) return st;
+    if (m == 0 && !state_out) return TG_OK;
+    if (m > 0 && (!q || !k || !v || !g || !beta || !out))
+        return fail(TG_ERR_INVALID_ARGUMENT, "q, k, v, g, beta, out must be non-NULL");
+    if (!(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out)))
+        return fail(TG_ERR_UNSUPPORTED, "q, k, v, out must be 16-byte aligned");
+    const size_t need = tg::delta_scan_workspace_bytes(st_, n_heads);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(TG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                    need);
+    if ((uintptr_t)workspace % 16) return fail(TG_ERR_INVALID_ARGUMENT, "workspace not 16-byte aligned");
+    hipError_t e = tg::launch_delta_scan(q, k, v, g, beta, st_, n_heads, state_in, out, state_out, workspace, stream);
+    if (e != hipSuccess) return hip_fail(e, "tg_gated_delta_scan launch");
+    return TG_OK;
+}
+
 size_t tg_decode_workspace_bytes(const tg_kv_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv, int32_t head_dim) {
     tg::DecTable t;
     int64_t r = 0;

@@ -142,6 +142,12 @@ hipError_t launch_qk_norm_rope(const void* qkv, int64_t m, int hq, int hkv, int 
 hipError_t launch_linear(int epi, const void* a, int64_t m, int k, const void* w, const void* w_up, int n_out,
                          const void* resid, void* out, hipStream_t st);
 
+// Gated delta rule over the kept rows (bf16, dk = dv = 128).
+size_t delta_scan_workspace_bytes(const SeqTable& t, int nh);
+hipError_t launch_delta_scan(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             const SeqTable& t, int nh, const float* state_in, void* out, float* state_out,
+                             void* workspace, hipStream_t st);
+
 // Gate MLP backward (bf16, d_model % 64 == 0, d_hidden % 64 == 0 and <= 256).
 size_t gate_backward_workspace_bytes(int64_t n_list, int d_model, int d_hidden);
 hipError_t launch_gate_backward(const void* x, int64_t n_rows, int d, const void* w1, const void* b1,

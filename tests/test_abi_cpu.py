@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(tg.EXPORTED)

@@ -747,3 +747,50 @@ def test_dense_layer_deterministic():
     a, _ = check_dense_layer([300], 512, 8, 4, 128, 1024, seed=33)
     b, _ = check_dense_layer([300], 512, 8, 4, 128, 1024, seed=33)
     assert torch.equal(a, b)
+
+
+# -------------------------------------------------------- gated delta rule ----
+
+def check_delta_scan(segs, nh, seed, with_state=True):
+    """Bars: outputs per (row, head) within 2e-2 of their maximum over the row's dv values,
+    final states per (prompt, head) within 2e-2 of their maximum (bf16 operands of the
+    chunk products: the state copy, Y, P and W round to 8 bits; the state itself is kept
+    in fp32)."""
+    from synthetic import make_delta_inputs
+    a = make_delta_inputs(list(segs), nh, 128, 128, seed=seed)
+    s0 = (torch.randn(len(segs), nh, 128, 128, generator=torch.Generator().manual_seed(seed + 1)) * 0.05
+          if with_state else None)
+    ps, st = [], 0
+    for ln in segs:
+        ps.append(Prompt(st, ln, 0, 0, 0))
+        st += ln
+    out, fs = tg.tg_gated_delta_scan(a["q"].to(DEV), a["k"].to(DEV), a["v"].to(DEV), a["g"].to(DEV),
+                                     a["beta"].to(DEV), ps, state_in=None if s0 is None else s0.to(DEV),
+                                     want_state=True)
+    ref_o, ref_s = oracle.gated_delta_scan(f64(a["q"]), f64(a["k"]), f64(a["v"]), a["g"].double().numpy(),
+                                           a["beta"].double().numpy(), list(segs),
+                                           state0=None if s0 is None else s0.double().numpy())
+    r1 = assert_rowmax_close(f64(out), ref_o)
+    got_s = fs.cpu().double().numpy()
+    for p in range(len(segs)):
+        for h in range(nh):
+            err = np.abs(got_s[p, h] - ref_s[p, h]).max()
+            assert err <= 2e-2 * np.abs(ref_s[p, h]).max() + 1e-6, f"state {p},{h}: {err:.3e}"
+    return out, fs
+
+
+def test_delta_scan_ragged_prompts_with_state():
+    note("gated delta rule: prompts of 200, 1, 77 and 64 kept rows, 4 heads, initial states")
+    check_delta_scan([200, 1, 77, 64], 4, seed=51)
+
+
+def test_delta_scan_16k_kept_rows():
+    note("gated delta rule: 2384 kept rows, 16 heads, zero initial state")
+    check_delta_scan([2384], 16, seed=52, with_state=False)
+
+
+def test_delta_scan_deterministic():
+    note("gated delta rule: bitwise repeatable")
+    a = check_delta_scan([300, 50], 2, seed=53)
+    b = check_delta_scan([300, 50], 2, seed=53)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
