@@ -24,9 +24,10 @@
 //
 // Kernels:
 //  * delta_prep_kernel: one workgroup per (chunk, head), independent of the
-//    state, so all chunks run at once: L, the triangular solve for T (one
-//    wave, row by row), U, Y and P in fp32; U is kept in fp32, Y and P in
-//    bf16 for the MFMAs of the next kernel.
+//    state, so all chunks run at once: K K^T and Q K^T on bf16 MFMA, L and
+//    P, the triangular solve for T in fp32 (one wave, a column per lane),
+//    then U = T V and Y = T diag(exp(G)) K on bf16 MFMA; U is kept in fp32,
+//    Y and P in bf16 for the MFMAs of the next kernel.
 //  * delta_scan_kernel: one wave per (prompt, head, 32 state rows), walking
 //    the chunks in order on 32x32x16 bf16 MFMA with the state in fp32
 //    registers: W = U - Y S^T, O = diag(exp(G)) Q S^T + P W, and
@@ -40,9 +41,9 @@ namespace tg {
 namespace {
 
 constexpr int DC = 64;   // rows per chunk
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int DD = 128;  // dk = dv
 
-__device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
 __device__ __forceinline__ uint16_t f2bf(float x) { return (uint16_t)(pack_bf16x2(x, 0.0f) & 0xffffu); }
 
 // Chunk c of the whole call -> (prompt, first kept row, rows in the chunk).
@@ -73,25 +74,49 @@ struct DeltaRec {
     static constexpr size_t BYTES = E + DC * 4;
 };
 
+__device__ __forceinline__ int sw16(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+__device__ __forceinline__ int sw8(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+// B operand from a swizzled 256-byte-row tile (16-byte chunk c of row r at
+// c ^ (r % 16)): column 32b + lane%32, k-slots = tile rows 16s + 8(e/4) +
+// 4(lane/32) + e%4.
+__device__ __forceinline__ bf16x8 k_tr_operand(const LDS_AS char* tile, int b, int s, int lane) {
+    const int gq = lane >> 4, r16 = lane & 15;
+    const int ra = 16 * s + 4 * (gq >> 1) + (r16 >> 2);
+    const int col = 32 * b + 16 * (gq & 1) + 4 * (r16 & 3);  // element; chunk col / 8, half (col % 8) / 4
+    const int off = ((col & 7) >> 2) * 8;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(tile + sw16(ra, col >> 3) + off));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(tile + sw16(ra + 8, col >> 3) + off));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Per (chunk, head), 4 waves. K K^T and Q K^T on MFMA (operands straight
+// from memory; wave w takes the 32 x 32 tile (w/2, w%2)), then L and P; the
+// triangular solve for T in one wave (lane c holds column c in registers);
+// U = T V and Y = T diag(exp(G)) K on MFMA (A = T rows in the permuted k
+// order of the transpose reads of V and K; wave w takes 32 rows x 64
+// columns). Accumulator layout: row 8(r/4) + 4hh + r%4 of the tile, column
+// lane%32.
 __global__ __launch_bounds__(256) void delta_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v, const float* __restrict__ g,
                                                          const float* __restrict__ beta, SeqTable t, int nh,
                                                          char* __restrict__ ws) {
-    __shared__ float ks[DC][DD + 1], qs[DC][DD + 1], vs[DC][DD + 1];
-    __shared__ float lm[DC][DC + 1], tm[DC][DC + 1];
+    __shared__ __attribute__((aligned(16))) char kt[DC * DD * 2], vt[DC * DD * 2];  // swizzled rows
+    __shared__ __attribute__((aligned(16))) float lm[DC][DC + 4], tm[DC][DC + 4];
     __shared__ float gc[DC], bl[DC];
-    const int tid = threadIdx.x;
+    __shared__ __attribute__((aligned(16))) float gm[DC];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
     const int chunk = blockIdx.x, h = blockIdx.y;
     int sg, len, c_in;
     int64_t row0;
     delta_chunk(t, chunk, sg, row0, len, c_in);
-    for (int idx = tid; idx < DC * DD; idx += 256) {
-        const int r = idx / DD, c = idx % DD;
-        const int64_t o = ((row0 + min(r, len - 1)) * nh + h) * DD + c;
-        const bool in = r < len;
-        ks[r][c] = in ? bf2f(k[o]) : 0.0f;
-        qs[r][c] = in ? bf2f(q[o]) : 0.0f;
-        vs[r][c] = in ? bf2f(v[o]) : 0.0f;
+    auto grow = [&](int r) __attribute__((always_inline)) { return ((row0 + min(r, len - 1)) * nh + h) * DD; };
+    // K and V tiles (bf16) into LDS; rows past the chunk repeat its last row
+    // (their beta is 0, so they never contribute).
+    for (int idx = tid; idx < DC * DD / 8; idx += 256) {
+        const int r = idx >> 4, cc = idx & 15;
+        *(LDS_AS u32x4*)(kt + sw16(r, cc)) = *(const u32x4*)(k + grow(r) + cc * 8);
+        *(LDS_AS u32x4*)(vt + sw16(r, cc)) = *(const u32x4*)(v + grow(r) + cc * 8);
     }
     if (tid < DC) {
         const bool in = tid < len;
@@ -105,70 +130,120 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(const uint16_t* __restr
             if (tid >= d) x += y;
         }
         gc[tid] = x;
+        gm[tid] = __expf(x);
     }
-    __syncthreads();
-    // L (strictly lower) and P (lower with the diagonal), 16 entries per thread.
+    // K K^T and Q K^T: tile (tm_, tn_) of wave w.
+    const int tm_ = wave >> 1, tn_ = wave & 1;
+    f32x16 kk, qk;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        kk[r] = 0.0f;
+        qk[r] = 0.0f;
+    }
+    {
+        const uint16_t* ka = k + grow(32 * tm_ + l32) + 8 * hh;
+        const uint16_t* qa = q + grow(32 * tm_ + l32) + 8 * hh;
+        const uint16_t* kb = k + grow(32 * tn_ + l32) + 8 * hh;
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) {
+            const bf16x8 a1 = *(const bf16x8*)(ka + 16 * s2), a2 = *(const bf16x8*)(qa + 16 * s2);
+            const bf16x8 b1 = *(const bf16x8*)(kb + 16 * s2);
+            kk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, kk, 0, 0, 0);
+            qk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b1, qk, 0, 0, 0);
+        }
+    }
+    __syncthreads();  // gc, bl, gm and the tiles are ready
     char* rec = ws + ((size_t)chunk * nh + h) * DeltaRec::BYTES;
     uint16_t* prec = (uint16_t*)(rec + DeltaRec::P);
-    for (int idx = tid; idx < DC * DC; idx += 256) {
-        const int r = idx / DC, s = idx % DC;
-        float kk = 0.0f, qk = 0.0f;
-        if (s <= r) {
-#pragma unroll 8
-            for (int c = 0; c < DD; ++c) {
-                kk = fmaf(ks[r][c], ks[s][c], kk);
-                qk = fmaf(qs[r][c], ks[s][c], qk);
-            }
-        }
-        const float dec = s <= r ? __expf(gc[r] - gc[s]) : 0.0f;
-        lm[r][s] = s < r ? bl[r] * dec * kk : 0.0f;
-        prec[r * DC + s] = f2bf(dec * qk);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int rr = 32 * tm_ + 8 * (r >> 2) + 4 * hh + (r & 3), ss = 32 * tn_ + l32;
+        const float dec = ss <= rr ? __expf(gc[rr] - gc[ss]) : 0.0f;
+        lm[rr][ss] = ss < rr ? bl[rr] * dec * kk[r] : 0.0f;
+        prec[rr * DC + ss] = f2bf(dec * qk[r]);
     }
     __syncthreads();
-    // T = (I + L)^-1 diag(b), row by row (one wave; lane c holds column c).
+    // T = (I + L)^-1 diag(b), row by row: one wave, lane c holds column c of
+    // T in registers (fully unrolled; the row entries of L are the same for
+    // every lane, two partial sums shorten the dependence chain).
     if (tid < DC) {
         const int c = tid;
+        float tcol[DC];
+#pragma unroll
         for (int r = 0; r < DC; ++r) {
-            float x = r == c ? bl[r] : 0.0f;
-            for (int s = c; s < r; ++s) x = fmaf(-lm[r][s], tm[s][c], x);
-            tm[r][c] = x;  // read back by this wave only, in order
+            float x0 = r == c ? bl[r] : 0.0f, x1 = 0.0f;
+#pragma unroll
+            for (int s2 = 0; s2 + 1 < r; s2 += 2) {
+                x0 = fmaf(-lm[r][s2], tcol[s2], x0);
+                x1 = fmaf(-lm[r][s2 + 1], tcol[s2 + 1], x1);
+            }
+            if (r & 1) x0 = fmaf(-lm[r][r - 1], tcol[r - 1], x0);
+            tcol[r] = x0 + x1;
         }
+#pragma unroll
+        for (int r = 0; r < DC; ++r) tm[r][c] = tcol[r];
     }
     __syncthreads();
-    // U = T V (fp32) and Y = T diag(exp(G)) K (bf16), 32 entries each per thread.
+    // U = T V and Y = T diag(exp(G)) K: wave w takes rows 32 (w/2) .. +32 and
+    // columns 64 (w%2) .. +64 (two 32-column tiles).
     float* urec = (float*)(rec + DeltaRec::U);
     uint16_t* yrec = (uint16_t*)(rec + DeltaRec::Y);
-    for (int idx = tid; idx < DC * DD; idx += 256) {
-        const int r = idx / DD, c = idx % DD;
-        float u = 0.0f, y = 0.0f;
-        for (int s = 0; s <= r; ++s) {
-            const float ts = tm[r][s];
-            u = fmaf(ts, vs[s][c], u);
-            y = fmaf(ts * __expf(gc[s]), ks[s][c], y);
+    const int ur = 32 * (wave >> 1) + l32;  // this lane's A-operand row of T
+    bf16x8 ta[4], tg[4];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+        // k-slots (hh, e) <-> T columns 16 s2 + 8(e/4) + 4hh + e%4
+        const f32x4 lo = *(const LDS_AS f32x4*)(&tm[ur][16 * s2 + 4 * hh]);
+        const f32x4 hi = *(const LDS_AS f32x4*)(&tm[ur][16 * s2 + 8 + 4 * hh]);
+        const f32x4 glo = *(const LDS_AS f32x4*)(&gm[16 * s2 + 4 * hh]);
+        const f32x4 ghi = *(const LDS_AS f32x4*)(&gm[16 * s2 + 8 + 4 * hh]);
+        const u32x4 w1 = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                          pack_bf16x2(hi[2], hi[3])};
+        const u32x4 w2 = {pack_bf16x2(lo[0] * glo[0], lo[1] * glo[1]), pack_bf16x2(lo[2] * glo[2], lo[3] * glo[3]),
+                          pack_bf16x2(hi[0] * ghi[0], hi[1] * ghi[1]), pack_bf16x2(hi[2] * ghi[2], hi[3] * ghi[3])};
+        ta[s2] = __builtin_bit_cast(bf16x8, w1);
+        tg[s2] = __builtin_bit_cast(bf16x8, w2);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const int ct = 2 * (wave & 1) + cb;  // 32-column tile
+        f32x16 ua, ya;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            ua[r] = 0.0f;
+            ya[r] = 0.0f;
         }
-        urec[idx] = u;
-        yrec[idx] = f2bf(y);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            ua = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[s2], k_tr_operand((const LDS_AS char*)vt, ct, s2, lane), ua,
+                                                         0, 0, 0);
+            ya = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tg[s2], k_tr_operand((const LDS_AS char*)kt, ct, s2, lane), ya,
+                                                         0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int rr = 32 * (wave >> 1) + 8 * (r >> 2) + 4 * hh + (r & 3);
+            urec[rr * DD + 32 * ct + l32] = ua[r];
+            yrec[rr * DD + 32 * ct + l32] = f2bf(ya[r]);
+        }
     }
     if (tid < DC) {
-        ((float*)(rec + DeltaRec::GAM))[tid] = __expf(gc[tid]);
+        ((float*)(rec + DeltaRec::GAM))[tid] = gm[tid];
         ((float*)(rec + DeltaRec::E))[tid] = __expf(gc[DC - 1] - gc[tid]);
     }
 }
 
-// B operand of a 32x32x16 MFMA from an LDS tile of bf16 rows with the given
-// byte stride: column 32b + lane%32, k-slots = tile rows 16s + 8(e/4) +
-// 4(lane/32) + e%4.
-__device__ __forceinline__ bf16x8 tr_operand(const LDS_AS char* tile, int stride, int b, int s, int lane) {
-    const int gq = lane >> 4, r16 = lane & 15;
-    const int ra = 16 * s + 4 * (gq >> 1) + (r16 >> 2);
-    const int col = 32 * b + 16 * (gq & 1) + 4 * (r16 & 3);
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(tile + ra * stride + col * 2));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(tile + (ra + 8) * stride + col * 2));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
+// LDS stage of one chunk for the scan kernel: Y, Q and K rows (256-byte
+// rows, 16-byte chunk c of row r at c ^ (r % 16)), P rows (128-byte rows,
+// chunk c at c ^ (r % 8)), the state-row block of U (64 x 32 fp32) and
+// exp(G), e (64 fp32 each).
+struct DeltaStage {
+    static constexpr int Y = 0, Q = Y + DC * DD * 2, K = Q + DC * DD * 2, P = K + DC * DD * 2;
+    static constexpr int U = P + DC * DC * 2, GAM = U + DC * 32 * 4, E = GAM + DC * 4, BYTES = E + DC * 4;
+};
 // One wave per (prompt, head, 32 state rows i0 .. i0+31): the chunks in
-// order, the state rows on the lanes:
+// order, the state rows on the lanes; the next chunk's operands stream into
+// the other half of a two-stage LDS ring (direct loads) while a chunk runs.
 //     W (64 x 32)   = U - Y S^T                 (A = Y rows, B = S rows)
 //     O (64 x 32)   = diag(gam) Q S^T + P W     (B = W from registers)
 //     S (32 x 128)  = e_last S + (diag(e) W)^T K
@@ -181,13 +256,58 @@ __global__ __launch_bounds__(64) void delta_scan_kernel(const uint16_t* __restri
                                                         const uint16_t* __restrict__ k, SeqTable t, int nh,
                                                         const char* __restrict__ ws, const float* __restrict__ state_in,
                                                         uint16_t* __restrict__ out, float* __restrict__ state_out) {
-    __shared__ __attribute__((aligned(16))) char kt[DC * DD * 2];  // K rows of the chunk, bf16
+    __shared__ __attribute__((aligned(1024))) char stage[2][DeltaStage::BYTES];
     __shared__ __attribute__((aligned(16))) char st[32 * DD * 2];  // S rows (bf16), row-major
     const int lane = threadIdx.x, hh = lane >> 5, l32 = lane & 31;
     const int sg = blockIdx.x, h = blockIdx.y, i0 = 32 * blockIdx.z;
     int c0 = 0;
     for (int i = 0; i < sg; ++i) c0 += (t.s[i].n_kept + DC - 1) / DC;
     const int n_chunks = (t.s[sg].n_kept + DC - 1) / DC;
+
+    // Direct loads of chunk c into stage b: 16 + 16 + 16 + 8 + 8 + 2
+    // instructions, each from a wave-uniform base plus a fixed per-lane
+    // offset. Load ins of a 256-byte-row tile covers rows 4 ins .. +4: lane
+    // l takes row 4 ins + l/16 and the logical chunk (l%16) ^ (row%16), which
+    // depends on ins only through ins % 4.
+    uint32_t oy[4], oq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int lc = (lane & 15) ^ ((4 * j + (lane >> 4)) & 15);
+        oy[j] = (uint32_t)((lane >> 4) * 256 + lc * 16);
+        oq[j] = (uint32_t)((lane >> 4) * nh * 256 + lc * 16);
+    }
+    const uint32_t op = (uint32_t)((lane >> 3) * 128 + (((lane & 7) ^ ((lane >> 3) & 7)) * 16));
+    const uint32_t ou = (uint32_t)((lane >> 3) * DD * 4 + i0 * 4 + (lane & 7) * 16);
+    const uint32_t o4 = (uint32_t)(lane * 4);
+    auto issue = [&](int c, int b) __attribute__((always_inline)) {
+        const int64_t row0 = t.s[sg].kept_off + (int64_t)c * DC;
+        const int len = min(DC, t.s[sg].n_kept - c * DC);
+        const char* rec = ws + ((size_t)(c0 + c) * nh + h) * DeltaRec::BYTES;
+        const uint32_t sb = LDS_ADDR(stage[b]);
+        const char* qb = (const char*)(q + (row0 * nh + h) * DD);
+        const char* kb = (const char*)(k + (row0 * nh + h) * DD);
+#pragma unroll
+        for (int ins = 0; ins < 16; ++ins) {
+            dma16_so(rec + DeltaRec::Y + ins * 1024, oy[ins & 3], sb + DeltaStage::Y + ins * 1024);
+            if (len == DC) {
+                dma16_so(qb + (size_t)ins * 4 * nh * 256, oq[ins & 3], sb + DeltaStage::Q + ins * 1024);
+                dma16_so(kb + (size_t)ins * 4 * nh * 256, oq[ins & 3], sb + DeltaStage::K + ins * 1024);
+            } else {  // the prompt's last, partial chunk: rows past its end repeat its last row
+                const int row = ins * 4 + (lane >> 4);
+                const int lc = (lane & 15) ^ (row & 15);
+                const uint32_t o = (uint32_t)(min(row, len - 1) * nh * 256 + lc * 16);
+                dma16_so(qb, o, sb + DeltaStage::Q + ins * 1024);
+                dma16_so(kb, o, sb + DeltaStage::K + ins * 1024);
+            }
+        }
+#pragma unroll
+        for (int ins = 0; ins < 8; ++ins) {
+            dma16_so(rec + DeltaRec::P + ins * 1024, op, sb + DeltaStage::P + ins * 1024);
+            dma16_so(rec + DeltaRec::U + ins * 8 * DD * 4, ou, sb + DeltaStage::U + ins * 1024);
+        }
+        dma4_so(rec + DeltaRec::GAM, o4, sb + DeltaStage::GAM);
+        dma4_so(rec + DeltaRec::E, o4, sb + DeltaStage::E);
+    };
 
     f32x16 sacc[4];
 #pragma unroll
@@ -198,17 +318,12 @@ __global__ __launch_bounds__(64) void delta_scan_kernel(const uint16_t* __restri
             sacc[jt][r] = state_in ? state_in[(((int64_t)sg * nh + h) * DD + i) * DD + 32 * jt + l32] : 0.0f;
         }
 
+    if (n_chunks > 0) issue(0, 0);
     for (int c = 0; c < n_chunks; ++c) {
         const int64_t row0 = t.s[sg].kept_off + (int64_t)c * DC;
         const int len = min(DC, t.s[sg].n_kept - c * DC);
-        const char* rec = ws + ((size_t)(c0 + c) * nh + h) * DeltaRec::BYTES;
-        const float* urec = (const float*)(rec + DeltaRec::U);
-        const uint16_t* yrec = (const uint16_t*)(rec + DeltaRec::Y);
-        const uint16_t* prec = (const uint16_t*)(rec + DeltaRec::P);
-        const float* gam = (const float*)(rec + DeltaRec::GAM);
-        const float* ee = (const float*)(rec + DeltaRec::E);
-
-        // The state (bf16) and the chunk's K rows into LDS.
+        const LDS_AS char* sb = (const LDS_AS char*)stage[c & 1];
+        // The state (bf16) into LDS for its row reads.
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
@@ -216,24 +331,22 @@ __global__ __launch_bounds__(64) void delta_scan_kernel(const uint16_t* __restri
                 const int il = 8 * (r >> 2) + 4 * hh + (r & 3);
                 *(LDS_AS uint16_t*)(st + (il * DD + 32 * jt + l32) * 2) = f2bf(sacc[jt][r]);
             }
-        for (int idx = lane; idx < DC * DD / 8; idx += 64) {
-            const int r = idx / (DD / 8), cc = idx % (DD / 8);
-            *(LDS_AS u32x4*)(kt + (r * DD + cc * 8) * 2) =
-                *(const u32x4*)(k + ((row0 + min(r, len - 1)) * nh + h) * DD + cc * 8);
-        }
-        __syncthreads();
+        wait_vmcnt<0>();  // chunk c's loads (and the previous chunk's stores) are done
+        ring_barrier();   // ... and the other stage's reads of chunk c - 1 too
+        if (c + 1 < n_chunks) issue(c + 1, (c + 1) & 1);
 
         // S rows as the B operand (lane = state row, k = key column).
         bf16x8 sop[8];
 #pragma unroll
         for (int s2 = 0; s2 < 8; ++s2)
             sop[s2] = *(const LDS_AS bf16x8*)(st + (l32 * DD + 16 * s2 + 8 * hh) * 2);
+        const float* gam = (const float*)(sb + DeltaStage::GAM);
+        const float* ee = (const float*)(sb + DeltaStage::E);
+        const float* us = (const float*)(sb + DeltaStage::U);
         f32x16 wt[2], ot[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int rr = 32 * tt + l32;  // this lane's A-operand chunk row
-            const uint16_t* yrow = yrec + rr * DD + 8 * hh;
-            const uint16_t* qrow = q + ((row0 + min(rr, len - 1)) * nh + h) * DD + 8 * hh;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 wt[tt][r] = 0.0f;
@@ -241,8 +354,9 @@ __global__ __launch_bounds__(64) void delta_scan_kernel(const uint16_t* __restri
             }
 #pragma unroll
             for (int s2 = 0; s2 < 8; ++s2) {
-                const bf16x8 yb = *(const bf16x8*)(yrow + 16 * s2);
-                const bf16x8 qb = *(const bf16x8*)(qrow + 16 * s2);
+                const int ch = 2 * s2 + hh;
+                const bf16x8 yb = *(const LDS_AS bf16x8*)(sb + DeltaStage::Y + sw16(rr, ch));
+                const bf16x8 qb = *(const LDS_AS bf16x8*)(sb + DeltaStage::Q + sw16(rr, ch));
                 wt[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(yb, sop[s2], wt[tt], 0, 0, 0);
                 ot[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb, sop[s2], ot[tt], 0, 0, 0);
             }
@@ -250,7 +364,7 @@ __global__ __launch_bounds__(64) void delta_scan_kernel(const uint16_t* __restri
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int tr = 32 * tt + 8 * (r >> 2) + 4 * hh + (r & 3);
-                wt[tt][r] = urec[tr * DD + i0 + l32] - wt[tt][r];
+                wt[tt][r] = us[tr * 32 + l32] - wt[tt][r];
                 ot[tt][r] *= gam[tr];
             }
         }
@@ -273,11 +387,14 @@ __global__ __launch_bounds__(64) void delta_scan_kernel(const uint16_t* __restri
         }
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const uint16_t* prow = prec + (32 * tt + l32) * DC + 4 * hh;
+            const int pr = 32 * tt + l32;
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2) {
-                const uint2 lo = *(const uint2*)(prow + 16 * s2), hi = *(const uint2*)(prow + 16 * s2 + 8);
-                const u32x4 pw = {lo.x, lo.y, hi.x, hi.y};
+                // columns 16 s2 + 4hh .. +4 and 16 s2 + 8 + 4hh .. +4 of P row pr
+                const int e0 = 16 * s2 + 4 * hh, e1 = e0 + 8;
+                const u32x2 lo = *(const LDS_AS u32x2*)(sb + DeltaStage::P + sw8(pr, e0 >> 3) + (e0 & 7) * 2);
+                const u32x2 hi = *(const LDS_AS u32x2*)(sb + DeltaStage::P + sw8(pr, e1 >> 3) + (e1 & 7) * 2);
+                const u32x4 pw = {lo[0], lo[1], hi[0], hi[1]};
                 ot[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pw), wop[s2], ot[tt], 0,
                                                                  0, 0);
             }
@@ -298,10 +415,11 @@ __global__ __launch_bounds__(64) void delta_scan_kernel(const uint16_t* __restri
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2)
                 sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    wsc[s2], tr_operand((const LDS_AS char*)kt, DD * 2, jt, s2, lane), sacc[jt], 0, 0, 0);
+                    wsc[s2], k_tr_operand(sb + DeltaStage::K, jt, s2, lane), sacc[jt], 0, 0, 0);
         }
-        __syncthreads();  // LDS tiles are rewritten by the next chunk
+        ring_barrier();  // the state copy and this stage are rewritten later
     }
+    wait_vmcnt<0>();
     if (state_out) {
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
