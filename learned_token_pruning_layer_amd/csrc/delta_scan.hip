@@ -28,12 +28,12 @@
 //    P, the triangular solve for T in fp32 (one wave, a column per lane),
 //    then U = T V and Y = T diag(exp(G)) K on bf16 MFMA; U is kept in fp32,
 //    Y and P in bf16 for the MFMAs of the next kernel.
-//  * delta_scan_kernel: one wave per (prompt, head, 32 state rows), walking
-//    the chunks in order on 32x32x16 bf16 MFMA with the state in fp32
-//    registers: W = U - Y S^T, O = diag(exp(G)) Q S^T + P W, and
-//    S = exp(G_last) S + (diag(e) W)^T K with K read transposed from LDS.
-//    W's registers feed the next two products directly (the row order
-//    inside each 16-wide k step is permuted the same way on both operands).
+//  * delta_scan_kernel: one workgroup of four waves per (prompt, head, 32
+//    state rows), walking the chunks in order on 32x32x16 bf16 MFMA with the
+//    state in fp32 registers (32 key columns per wave): W = U - Y S^T,
+//    O = diag(exp(G)) Q S^T + P W, and S = exp(G_last) S + (diag(e) W)^T K
+//    with K read transposed from LDS; W goes through LDS transposed, read
+//    in the permuted row order of the other operand of each product.
 #include "tg_internal.hpp"
 #include "tg_device.hpp"
 
@@ -241,34 +241,41 @@ struct DeltaStage {
     static constexpr int Y = 0, Q = Y + DC * DD * 2, K = Q + DC * DD * 2, P = K + DC * DD * 2;
     static constexpr int U = P + DC * DC * 2, GAM = U + DC * 32 * 4, E = GAM + DC * 4, BYTES = E + DC * 4;
 };
-// One wave per (prompt, head, 32 state rows i0 .. i0+31): the chunks in
-// order, the state rows on the lanes; the next chunk's operands stream into
-// the other half of a two-stage LDS ring (direct loads) while a chunk runs.
-//     W (64 x 32)   = U - Y S^T                 (A = Y rows, B = S rows)
-//     O (64 x 32)   = diag(gam) Q S^T + P W     (B = W from registers)
-//     S (32 x 128)  = e_last S + (diag(e) W)^T K
+// One workgroup of four waves per (prompt, head, 32 state rows i0 .. +32):
+// the chunks in order, the state rows on the lanes; the next chunk's
+// operands stream into the other half of a two-stage LDS ring (direct
+// loads, a quarter per wave) while a chunk runs. Per chunk:
+//   A: waves 0, 1: W tile tt = U - Y S^T, written transposed to LDS (plain
+//      and scaled by e); waves 2, 3: O tile tt = diag(gam) Q S^T.
+//   B: waves 2, 3: O += P W, stored; every wave: its 32 key columns of
+//      S = e_last S + (diag(e) W)^T K, written back (bf16) for the next A.
 // Accumulator layouts: W, O tile tt: chunk row 32tt + 8(r/4) + 4hh + r%4,
-// state row i0 + lane%32; S tile jt: state row i0 + 8(r/4) + 4hh + r%4,
-// key column 32jt + lane%32. The chunk-row order of W's registers inside a
-// 16-wide k step is the permuted order of the transpose reads of K and of
-// the P column reads.
-__global__ __launch_bounds__(64) void delta_scan_kernel(const uint16_t* __restrict__ q,
-                                                        const uint16_t* __restrict__ k, SeqTable t, int nh,
-                                                        const char* __restrict__ ws, const float* __restrict__ state_in,
-                                                        uint16_t* __restrict__ out, float* __restrict__ state_out) {
+// state row i0 + lane%32; S tile jt: state row i0 + 8(r/4) + 4hh + r%4, key
+// column 32jt + lane%32. W^T in LDS is read in the permuted chunk-row order
+// of the transpose reads of K and of the P column reads.
+constexpr int WTS = 72;  // W^T row stride (bf16): 144-byte rows spread 32 rows over the banks
+
+__global__ __launch_bounds__(256) void delta_scan_kernel(const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ k, SeqTable t, int nh,
+                                                         const char* __restrict__ ws, const float* __restrict__ state_in,
+                                                         uint16_t* __restrict__ out, float* __restrict__ state_out) {
     __shared__ __attribute__((aligned(1024))) char stage[2][DeltaStage::BYTES];
-    __shared__ __attribute__((aligned(16))) char st[32 * DD * 2];  // S rows (bf16), row-major
-    const int lane = threadIdx.x, hh = lane >> 5, l32 = lane & 31;
+    __shared__ __attribute__((aligned(16))) char st[32 * DD * 2];     // S rows (bf16), row-major
+    __shared__ __attribute__((aligned(16))) char wtt[32 * WTS * 2];   // W^T (bf16)
+    __shared__ __attribute__((aligned(16))) char wse[32 * WTS * 2];   // (diag(e) W)^T (bf16)
+    const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (load bases live in SGPRs)
     const int sg = blockIdx.x, h = blockIdx.y, i0 = 32 * blockIdx.z;
     int c0 = 0;
     for (int i = 0; i < sg; ++i) c0 += (t.s[i].n_kept + DC - 1) / DC;
     const int n_chunks = (t.s[sg].n_kept + DC - 1) / DC;
 
-    // Direct loads of chunk c into stage b: 16 + 16 + 16 + 8 + 8 + 2
-    // instructions, each from a wave-uniform base plus a fixed per-lane
-    // offset. Load ins of a 256-byte-row tile covers rows 4 ins .. +4: lane
-    // l takes row 4 ins + l/16 and the logical chunk (l%16) ^ (row%16), which
-    // depends on ins only through ins % 4.
+    // Direct loads of chunk c into stage b, this wave's quarter: loads 4w ..
+    // 4w+3 of the Y, Q and K tiles (256-byte rows, 4 rows per load), 2w,
+    // 2w+1 of the P and U tiles (128-byte rows, 8 rows per load), and exp(G)
+    // (wave 0) or e (wave 1). Each from a wave-uniform base plus a fixed
+    // per-lane offset: load ins takes row 4 ins + l/16 and the logical chunk
+    // (l%16) ^ (row%16), which depends on ins only through ins % 4 = j.
     uint32_t oy[4], oq[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -287,11 +294,12 @@ __global__ __launch_bounds__(64) void delta_scan_kernel(const uint16_t* __restri
         const char* qb = (const char*)(q + (row0 * nh + h) * DD);
         const char* kb = (const char*)(k + (row0 * nh + h) * DD);
 #pragma unroll
-        for (int ins = 0; ins < 16; ++ins) {
-            dma16_so(rec + DeltaRec::Y + ins * 1024, oy[ins & 3], sb + DeltaStage::Y + ins * 1024);
+        for (int j = 0; j < 4; ++j) {
+            const int ins = 4 * wave + j;
+            dma16_so(rec + DeltaRec::Y + ins * 1024, oy[j], sb + DeltaStage::Y + ins * 1024);
             if (len == DC) {
-                dma16_so(qb + (size_t)ins * 4 * nh * 256, oq[ins & 3], sb + DeltaStage::Q + ins * 1024);
-                dma16_so(kb + (size_t)ins * 4 * nh * 256, oq[ins & 3], sb + DeltaStage::K + ins * 1024);
+                dma16_so(qb + (size_t)ins * 4 * nh * 256, oq[j], sb + DeltaStage::Q + ins * 1024);
+                dma16_so(kb + (size_t)ins * 4 * nh * 256, oq[j], sb + DeltaStage::K + ins * 1024);
             } else {  // the prompt's last, partial chunk: rows past its end repeat its last row
                 const int row = ins * 4 + (lane >> 4);
                 const int lc = (lane & 15) ^ (row & 15);
@@ -301,133 +309,116 @@ __global__ __launch_bounds__(64) void delta_scan_kernel(const uint16_t* __restri
             }
         }
 #pragma unroll
-        for (int ins = 0; ins < 8; ++ins) {
+        for (int j = 0; j < 2; ++j) {
+            const int ins = 2 * wave + j;
             dma16_so(rec + DeltaRec::P + ins * 1024, op, sb + DeltaStage::P + ins * 1024);
             dma16_so(rec + DeltaRec::U + ins * 8 * DD * 4, ou, sb + DeltaStage::U + ins * 1024);
         }
-        dma4_so(rec + DeltaRec::GAM, o4, sb + DeltaStage::GAM);
-        dma4_so(rec + DeltaRec::E, o4, sb + DeltaStage::E);
+        if (wave == 0) dma4_so(rec + DeltaRec::GAM, o4, sb + DeltaStage::GAM);
+        if (wave == 1) dma4_so(rec + DeltaRec::E, o4, sb + DeltaStage::E);
     };
 
-    f32x16 sacc[4];
+    // This wave's 32 key columns of the state (fp32), and their bf16 copy.
+    const int jt = wave;
+    f32x16 sacc;
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
+    for (int r = 0; r < 16; ++r) {
+        const int i = i0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        sacc[r] = state_in ? state_in[(((int64_t)sg * nh + h) * DD + i) * DD + 32 * jt + l32] : 0.0f;
+    }
+    auto put_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int i = i0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            sacc[jt][r] = state_in ? state_in[(((int64_t)sg * nh + h) * DD + i) * DD + 32 * jt + l32] : 0.0f;
+            const int il = 8 * (r >> 2) + 4 * hh + (r & 3);
+            *(LDS_AS uint16_t*)(st + (il * DD + 32 * jt + l32) * 2) = f2bf(sacc[r]);
         }
-
+    };
+    put_state();
     if (n_chunks > 0) issue(0, 0);
     for (int c = 0; c < n_chunks; ++c) {
         const int64_t row0 = t.s[sg].kept_off + (int64_t)c * DC;
         const int len = min(DC, t.s[sg].n_kept - c * DC);
         const LDS_AS char* sb = (const LDS_AS char*)stage[c & 1];
-        // The state (bf16) into LDS for its row reads.
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int il = 8 * (r >> 2) + 4 * hh + (r & 3);
-                *(LDS_AS uint16_t*)(st + (il * DD + 32 * jt + l32) * 2) = f2bf(sacc[jt][r]);
-            }
-        wait_vmcnt<0>();  // chunk c's loads (and the previous chunk's stores) are done
-        ring_barrier();   // ... and the other stage's reads of chunk c - 1 too
+        wait_vmcnt<0>();  // this wave's loads of chunk c (and its earlier stores) are done
+        ring_barrier();   // ... every wave's; the other stage and W^T are free again
         if (c + 1 < n_chunks) issue(c + 1, (c + 1) & 1);
 
-        // S rows as the B operand (lane = state row, k = key column).
+        // A: S rows as the B operand (lane = state row, k = key column).
         bf16x8 sop[8];
 #pragma unroll
         for (int s2 = 0; s2 < 8; ++s2)
             sop[s2] = *(const LDS_AS bf16x8*)(st + (l32 * DD + 16 * s2 + 8 * hh) * 2);
         const float* gam = (const float*)(sb + DeltaStage::GAM);
         const float* ee = (const float*)(sb + DeltaStage::E);
-        const float* us = (const float*)(sb + DeltaStage::U);
-        f32x16 wt[2], ot[2];
+        const int tt = wave & 1;
+        const int rr = 32 * tt + l32;  // this lane's A-operand chunk row
+        const int src = wave < 2 ? DeltaStage::Y : DeltaStage::Q;
+        f32x16 acc;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int rr = 32 * tt + l32;  // this lane's A-operand chunk row
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                wt[tt][r] = 0.0f;
-                ot[tt][r] = 0.0f;
-            }
+        for (int s2 = 0; s2 < 8; ++s2) {
+            const bf16x8 ab = *(const LDS_AS bf16x8*)(sb + src + sw16(rr, 2 * s2 + hh));
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, sop[s2], acc, 0, 0, 0);
+        }
+        if (wave < 2) {
+            // W = U - Y S^T, stored transposed (plain and scaled by e), pairs of rows.
+            const float* us = (const float*)(sb + DeltaStage::U);
 #pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2) {
-                const int ch = 2 * s2 + hh;
-                const bf16x8 yb = *(const LDS_AS bf16x8*)(sb + DeltaStage::Y + sw16(rr, ch));
-                const bf16x8 qb = *(const LDS_AS bf16x8*)(sb + DeltaStage::Q + sw16(rr, ch));
-                wt[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(yb, sop[s2], wt[tt], 0, 0, 0);
-                ot[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb, sop[s2], ot[tt], 0, 0, 0);
-            }
-            // W = U - Y S^T; O's rows scaled by exp(G).
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int r = 0; r < 16; r += 2) {
                 const int tr = 32 * tt + 8 * (r >> 2) + 4 * hh + (r & 3);
-                wt[tt][r] = us[tr * 32 + l32] - wt[tt][r];
-                ot[tt][r] *= gam[tr];
+                const float w0 = us[tr * 32 + l32] - acc[r], w1 = us[(tr + 1) * 32 + l32] - acc[r + 1];
+                *(LDS_AS uint32_t*)(wtt + (l32 * WTS + tr) * 2) = pack_bf16x2(w0, w1);
+                *(LDS_AS uint32_t*)(wse + (l32 * WTS + tr) * 2) = pack_bf16x2(w0 * ee[tr], w1 * ee[tr + 1]);
             }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] *= gam[32 * tt + 8 * (r >> 2) + 4 * hh + (r & 3)];
         }
-        // O += P W: A = P rows (k = chunk rows in the permuted order), B = W
-        // from its registers (k-step s2: tile s2/2, registers 8(s2%2) .. +8).
-        bf16x8 wop[4], wsc[4];
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-            u32x4 w, ws2;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const int r0 = 8 * (s2 & 1) + 2 * e2;
-                const float x0 = wt[s2 >> 1][r0], x1 = wt[s2 >> 1][r0 + 1];
-                const int t0 = 32 * (s2 >> 1) + 8 * (r0 >> 2) + 4 * hh + (r0 & 3);
-                w[e2] = pack_bf16x2(x0, x1);
-                ws2[e2] = pack_bf16x2(x0 * ee[t0], x1 * ee[t0 + 1]);
-            }
-            wop[s2] = __builtin_bit_cast(bf16x8, w);
-            wsc[s2] = __builtin_bit_cast(bf16x8, ws2);
-        }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int pr = 32 * tt + l32;
+        ring_barrier();  // W^T is complete; every wave's reads of the state copy are done
+
+        // B operands from W^T: lane = state row, k-slots (hh, e) = chunk rows
+        // 16 s2 + 8(e/4) + 4hh + e%4.
+        auto wt_operand = [&](const char* base, int s2) __attribute__((always_inline)) {
+            const LDS_AS char* rowp = (const LDS_AS char*)(base) + (l32 * WTS + 16 * s2 + 4 * hh) * 2;
+            const u32x2 lo = *(const LDS_AS u32x2*)rowp, hi = *(const LDS_AS u32x2*)(rowp + 16);
+            const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+            return __builtin_bit_cast(bf16x8, w);
+        };
+        if (wave >= 2) {
+            // O += P W; store the chunk's own rows.
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2) {
-                // columns 16 s2 + 4hh .. +4 and 16 s2 + 8 + 4hh .. +4 of P row pr
                 const int e0 = 16 * s2 + 4 * hh, e1 = e0 + 8;
-                const u32x2 lo = *(const LDS_AS u32x2*)(sb + DeltaStage::P + sw8(pr, e0 >> 3) + (e0 & 7) * 2);
-                const u32x2 hi = *(const LDS_AS u32x2*)(sb + DeltaStage::P + sw8(pr, e1 >> 3) + (e1 & 7) * 2);
+                const u32x2 lo = *(const LDS_AS u32x2*)(sb + DeltaStage::P + sw8(rr, e0 >> 3) + (e0 & 7) * 2);
+                const u32x2 hi = *(const LDS_AS u32x2*)(sb + DeltaStage::P + sw8(rr, e1 >> 3) + (e1 & 7) * 2);
                 const u32x4 pw = {lo[0], lo[1], hi[0], hi[1]};
-                ot[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pw), wop[s2], ot[tt], 0,
-                                                                 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pw), wt_operand(wtt, s2), acc,
+                                                              0, 0, 0);
             }
-            // Output rows of the chunk (only the prompt's own rows).
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int tr = 32 * tt + 8 * (r >> 2) + 4 * hh + (r & 3);
-                if (tr < len) out[((row0 + tr) * nh + h) * DD + i0 + l32] = f2bf(ot[tt][r]);
+                if (tr < len) out[((row0 + tr) * nh + h) * DD + i0 + l32] = f2bf(acc[r]);
             }
         }
-        // S = e_last S + (diag(e) W)^T K: A = diag(e) W from registers (lane =
-        // state row, k = chunk rows), B = K read transposed from LDS.
+        // S (this wave's key columns) = e_last S + (diag(e) W)^T K.
         const float elast = gam[DC - 1];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
+        for (int r = 0; r < 16; ++r) sacc[r] *= elast;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[jt][r] *= elast;
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2)
-                sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    wsc[s2], k_tr_operand(sb + DeltaStage::K, jt, s2, lane), sacc[jt], 0, 0, 0);
-        }
-        ring_barrier();  // the state copy and this stage are rewritten later
+        for (int s2 = 0; s2 < 4; ++s2)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wt_operand(wse, s2), k_tr_operand(sb + DeltaStage::K, jt, s2, lane),
+                                                           sacc, 0, 0, 0);
+        put_state();
     }
     wait_vmcnt<0>();
     if (state_out) {
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = i0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                state_out[(((int64_t)sg * nh + h) * DD + i) * DD + 32 * jt + l32] = sacc[jt][r];
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int i = i0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            state_out[(((int64_t)sg * nh + h) * DD + i) * DD + 32 * jt + l32] = sacc[r];
+        }
     }
 }
 
@@ -449,7 +440,7 @@ hipError_t launch_delta_scan(const void* q, const void* k, const void* v, const 
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, g, beta, t, nh,
                            (char*)workspace);
     if (t.n > 0)
-        hipLaunchKernelGGL(delta_scan_kernel, dim3((unsigned)t.n, (unsigned)nh, DD / 32), dim3(64), 0, st,
+        hipLaunchKernelGGL(delta_scan_kernel, dim3((unsigned)t.n, (unsigned)nh, DD / 32), dim3(256), 0, st,
                            (const uint16_t*)q, (const uint16_t*)k, t, nh, (const char*)workspace, state_in,
                            (uint16_t*)out, state_out);
     return hipGetLastError();
