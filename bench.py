@@ -241,6 +241,8 @@ def measure_extras(torch, tg, layer, w, steps, dev):
     out["gate_backward_qwen16k"] = measure_gate_backward(torch, tg, layer, timed, pct)
     # The full above-gate decoder layer over the kept rows, against the same layer over all rows.
     out["dense_layer_qwen16k"] = measure_dense_layer(torch, tg, layer, w, timed, pct)
+    # The gated delta rule of a Gated-DeltaNet layer over the kept rows, against all rows.
+    out["delta_scan_qwen16k"] = measure_delta_scan(torch, tg, layer, timed, pct)
     # Select on one prompt of 2^24 document rows: the multi-workgroup path
     # (1024 chunks of 16384 rows), arguments marshalled once outside the
     # timed region.
@@ -452,6 +454,40 @@ def measure_dense_layer(torch, tg, lay, w, timed, pct, reps=10):
                torch.arange(n, dtype=torch.int32, device=w.x.device), [Prompt(0, n, 0, 0, 0)])
     return {"pruned": pruned, "unpruned": full, "speedup": round(full["us"] / pruned["us"], 2),
             "memory_ratio": round(full["row_scaled_bytes"] / pruned["row_scaled_bytes"], 2), "d_ff": d_ff}
+
+
+def measure_delta_scan(torch, tg, lay, timed, pct, reps=10):
+    """The gated delta rule (the token mixer of a Gated-DeltaNet layer; 16 heads,
+    dk = dv = 128, synthetic normalised q/k, decays in (0.9, 1)) over the 16k
+    layer's 2384 kept rows, and over all 16384 rows for comparison. Algorithmic
+    work of the recurrence: 8 dk dv flop per row and head (S k, the rank-1 update,
+    S q)."""
+    from synthetic import Prompt, make_delta_inputs
+    from learned_token_pruning_layer_amd._lib import seq_array
+    lib = tg.load()
+    nh = 16
+    res = {}
+    for name, prompts, m in (("pruned", lay.prompts, lay.m), ("unpruned", [Prompt(0, lay.x.shape[0], 0, 0, 0)],
+                                                               lay.x.shape[0])):
+        a = make_delta_inputs([m], nh, 128, 128, seed=7, device=lay.x.device)
+        sa = seq_array(prompts)
+        need = lib.tg_delta_scan_workspace_bytes(sa, len(prompts), nh, 128, 128)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=lay.x.device)
+        out = torch.empty_like(a["v"])
+        st = torch.cuda.current_stream().cuda_stream
+        args = (1, a["q"].data_ptr(), a["k"].data_ptr(), a["v"].data_ptr(), a["g"].data_ptr(), a["beta"].data_ptr(),
+                sa, len(prompts), nh, 128, 128, None, out.data_ptr(), None, ws.data_ptr(), ws.numel(), st)
+
+        def call():
+            if lib.tg_gated_delta_scan(*args) != 0:
+                raise RuntimeError(lib.tg_last_error().decode())
+
+        call()
+        us = pct(timed(call, reps), 0.5)
+        res[name] = {"rows": m, "us": round(us, 1),
+                     "recurrence_tflops": round(8 * 128 * 128 * nh * m / (us * 1e-6) / 1e12, 2)}
+    res["speedup"] = round(res["unpruned"]["us"] / res["pruned"]["us"], 2)
+    return res
 
 
 def measure_configs(torch, tg, dev, timed, pct):
