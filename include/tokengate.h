@@ -15,8 +15,10 @@
  *
  * Beyond the forward pass: tg_gated_attention_backward, tg_score_grad and
  * tg_gate_backward carry a gradient from the attention output through the
- * bias back to the gate's weights (training); tg_decode_attention attends new
- * tokens over the kept rows' cache (generation).
+ * bias back to the gate's weights (training); tg_dense_layer runs a whole
+ * above-gate decoder layer over the kept rows and tg_gated_delta_scan the token
+ * mixer of a Gated-DeltaNet layer; tg_decode_attention attends new tokens over
+ * the kept rows' cache (generation).
  *
  * Sources: the pages about "TokenGate: Adapting LLMs for Fast and
  * Memory-Efficient Prefill with Learned Token Pruning". The spke.com article
