@@ -79,17 +79,37 @@ MUTATIONS = [
 ]
 
 
-@pytest.mark.parametrize("what,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_pins_catch_planted_mistake(tmp_path, what, old, new):
+def _run_one(tmp_root, idx, old, new):
+    """Plant one mistake into a scratch copy of the oracle and run the pins on it."""
     src = open(os.path.join(ROOT, "oracle", "tokengate.py")).read()
-    assert src.count(old) == 1, f"mutation text not found once in the oracle: {old!r}"
+    if src.count(old) != 1:
+        return None
+    work = os.path.join(tmp_root, f"m{idx}")
     for d in ("oracle", "synthetic", "tests"):
-        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+        shutil.copytree(os.path.join(ROOT, d), os.path.join(work, d),
                         ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutations.py"))
-    (tmp_path / "oracle" / "tokengate.py").write_text(src.replace(old, new))
-    env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
-    r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle_pins.py", "-x", "-q",
-                        "-p", "no:cacheprovider", "-m", "not gpu"],
-                       cwd=tmp_path, env=env, capture_output=True, text=True, timeout=600)
+    with open(os.path.join(work, "oracle", "tokengate.py"), "w") as f:
+        f.write(src.replace(old, new))
+    env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1", OMP_NUM_THREADS="1")
+    return subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle_pins.py", "-x", "-q",
+                           "-p", "no:cacheprovider", "-m", "not gpu"],
+                          cwd=work, env=env, capture_output=True, text=True, timeout=900)
+
+
+@pytest.fixture(scope="module")
+def mutation_runs(tmp_path_factory):
+    """Every planted mistake's pin run, several at a time (each is its own process)."""
+    import concurrent.futures
+    root = str(tmp_path_factory.mktemp("mutations"))
+    workers = max(1, min(8, (os.cpu_count() or 2) - 1))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        futs = {m[0]: ex.submit(_run_one, root, i, m[1], m[2]) for i, m in enumerate(MUTATIONS)}
+        return {k: f.result() for k, f in futs.items()}
+
+
+@pytest.mark.parametrize("what,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(mutation_runs, what, old, new):
+    r = mutation_runs[what]
+    assert r is not None, f"mutation text not found once in the oracle: {old!r}"
     assert r.returncode != 0, f"planted mistake survived every pin: {what}\n{r.stdout[-2000:]}"
     assert "failed" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]
