@@ -794,3 +794,25 @@ def test_delta_scan_deterministic():
     a = check_delta_scan([300, 50], 2, seed=53)
     b = check_delta_scan([300, 50], 2, seed=53)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_delta_scan_empty_prompts_pass_state_through():
+    """A prompt with no kept rows leaves its state as given; the others run as usual."""
+    note("gated delta rule: prompts of 0, 70 and 0 kept rows with initial states")
+    from synthetic import make_delta_inputs
+    a = make_delta_inputs([70], 2, 128, 128, seed=61)
+    s0 = torch.randn(3, 2, 128, 128, generator=torch.Generator().manual_seed(62)) * 0.05
+    ps = [Prompt(0, 0, 0, 0, 0), Prompt(0, 70, 0, 0, 0), Prompt(70, 0, 0, 0, 0)]
+    out, fs = tg.tg_gated_delta_scan(a["q"].to(DEV), a["k"].to(DEV), a["v"].to(DEV), a["g"].to(DEV),
+                                     a["beta"].to(DEV), ps, state_in=s0.to(DEV), want_state=True)
+    ref_o, ref_s = oracle.gated_delta_scan(f64(a["q"]), f64(a["k"]), f64(a["v"]), a["g"].double().numpy(),
+                                           a["beta"].double().numpy(), [0, 70, 0], state0=s0.double().numpy())
+    assert_rowmax_close(f64(out), ref_o)
+    got = fs.cpu()
+    assert torch.equal(got[0], s0[0]) and torch.equal(got[2], s0[2])
+    np.testing.assert_allclose(got[1].double().numpy(), ref_s[1], atol=2e-2 * np.abs(ref_s[1]).max())
+
+
+def test_dense_layer_16k_kept_rows():
+    note("dense layer at the 16k layer's size: 2384 kept rows, Qwen3-1.7B shapes, d_ff 6144")
+    check_dense_layer([2384], 2048, 16, 8, 128, 6144, seed=34)
