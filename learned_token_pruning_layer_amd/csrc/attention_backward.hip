@@ -32,6 +32,9 @@
 //     forward kernel: S^T = K Q^T and dP^T = V dO^T with Q and dO in
 //     registers, dS^T in registers, dQ^T += K^T dS^T with K^T read
 //     transposed from LDS.
+//  When the (block, head) items are too few to fill the chip, each item of 2
+//  and 3 is split over two waves, each walking half of the blocks; their
+//  partials are summed in a fixed order below.
 //  4. reduce: sums the per-head partials of each KV head in a fixed order
 //     (so the result is deterministic), applies the gains to db, and forms
 //     per-workgroup partials of sum k . dK; a last kernel reduces dg_h =
@@ -123,30 +126,41 @@ __device__ __forceinline__ bf16x8 tile_row_operand(const LDS_AS char* tile, int 
     return *(const LDS_AS bf16x8*)(tile + (lane & 31) * Tile<D>::RS + (16 * s + 8 * (lane >> 5)) * 2);
 }
 
+// When the (block, head) items alone would leave the chip short of waves,
+// each is split in two work items over halves of the blocks it walks, so
+// the longest chains (the earliest key blocks, the latest query blocks) are
+// half as long; the partial results are summed in a fixed order afterwards.
+constexpr int BWD_SPLIT_BELOW = 2048;  // (block, head) items under which the split pays
+
 struct BwdSeg {
     int64_t off;     // first kept row
     int32_t n;       // kept rows
     int32_t n_blk;   // 32-row blocks
-    int32_t item0;   // first (block, head) work item
+    int32_t item0;   // first (block, head, part) work item
     int32_t pad;
 };
 struct BwdTable {
     int32_t n_seg;
-    int32_t n_items;  // sum over prompts of n_blk * hq
+    int32_t n_items;  // sum over prompts of n_blk * hq * parts
     int64_t m_total;
+    int32_t parts;    // work items per (block, head): 1 or 2
+    int32_t pad;
     BwdSeg s[TG_MAX_SEQS];
 };
 
-// Work item -> (prompt, block, head): item = item0 + order(block) * hq + h,
-// blocks in the order given (the ones with the most work first).
+// Work item -> (prompt, block, head, part): item = item0 + (order(block) *
+// hq + h) * parts + part, blocks in the order given (the ones with the most
+// work first).
 __device__ __forceinline__ void bwd_item(const BwdTable& t, int item, int hq, bool last_first, int& sg, int& blk,
-                                         int& h) {
+                                         int& h, int& part) {
     sg = 0;
     for (int i = 1; i < t.n_seg; ++i)
         if (t.s[i].item0 <= item) sg = i;
     const int local = item - t.s[sg].item0;
-    blk = last_first ? t.s[sg].n_blk - 1 - local / hq : local / hq;
-    h = local % hq;
+    part = local % t.parts;
+    const int bh = local / t.parts;
+    blk = last_first ? t.s[sg].n_blk - 1 - bh / hq : bh / hq;
+    h = bh % hq;
 }
 
 // 1. Dl[h][i] = dO_i . o_i (fp32), one thread per (row, head).
@@ -191,8 +205,8 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
     __shared__ __attribute__((aligned(16))) int32_t s_pos[32];
     const int lane = threadIdx.x;
     const int hh = lane >> 5, l32 = lane & 31;
-    int sg, jb, h;
-    bwd_item(t, blockIdx.x, hq, false, sg, jb, h);  // early key blocks see the most queries
+    int sg, jb, h, part;
+    bwd_item(t, blockIdx.x, hq, false, sg, jb, h, part);  // early key blocks see the most queries
     const int64_t off = t.s[sg].off, m = t.m_total;
     const int n = t.s[sg].n;
     const int kvh = h / (hq / hkv);
@@ -248,9 +262,12 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
         n_dl = dl[(int64_t)h * m + off + qi];
         n_pos = pos[off + qi];
     };
+    // This item's half of the query blocks i0 .. n_blk - 1.
     const int n_blk = t.s[sg].n_blk;
-    fetch_q(i0);
-    for (int ib = i0; ib < n_blk; ++ib) {
+    const int half = t.parts == 1 ? n_blk - i0 : (n_blk - i0 + 1) / 2;
+    const int lo = part == 0 ? i0 : i0 + half, hi = part == 0 ? i0 + half : n_blk;
+    if (lo < hi) fetch_q(lo);
+    for (int ib = lo; ib < hi; ++ib) {
         const int qrow0 = 32 * ib;
         __syncthreads();  // previous iteration's reads of qt / dot are done
         store_tile<D>((LDS_AS char*)qt, rq, lane);
@@ -263,7 +280,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
         // Lane 0 holds the position of the block's first (lowest) query.
         const bool full = qrow0 + 32 <= n && __builtin_amdgcn_readfirstlane(n_pos) >= p_key_last;
         __syncthreads();
-        if (ib + 1 < n_blk) fetch_q(ib + 1);
+        if (ib + 1 < hi) fetch_q(ib + 1);
         f32x16 sacc, pacc;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -356,7 +373,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
         for (int j = 0; j < 16; ++j) {
             const int kr = key0 + 8 * (j / 4) + 4 * hh + (j % 4);
             if (kr < n) {
-                const int64_t o = ((int64_t)h * m + off + kr) * D + 32 * b + l32;
+                const int64_t o = (((int64_t)part * hq + h) * m + off + kr) * D + 32 * b + l32;
                 ws_dk[o] = acc_dk[b][j] * c;
                 ws_dv[o] = acc_dv[b][j];
             }
@@ -364,7 +381,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
     // sum_i dS_ij of this lane's key, over both query halves (the gain is
     // applied when the heads are summed).
     db_acc += __shfl_xor(db_acc, 32);
-    if (hh == 0 && key_ok) ws_db[(int64_t)h * m + off + key] = db_acc;
+    if (hh == 0 && key_ok) ws_db[((int64_t)part * hq + h) * m + off + key] = db_acc;
 }
 
 // 3. dQ of one (prompt, query block, head).
@@ -381,8 +398,8 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__
     __shared__ __attribute__((aligned(16))) int32_t s_p[32];
     const int lane = threadIdx.x;
     const int hh = lane >> 5, l32 = lane & 31;
-    int sg, ib, h;
-    bwd_item(t, blockIdx.x, hq, true, sg, ib, h);  // late query blocks see the most keys
+    int sg, ib, h, part;
+    bwd_item(t, blockIdx.x, hq, true, sg, ib, h, part);  // late query blocks see the most keys
     const int64_t off = t.s[sg].off, m = t.m_total;
     const int n = t.s[sg].n;
     const int kvh = h / (hq / hkv);
@@ -432,8 +449,11 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__
         n_kb = gb2 * bias[off + min(kr, n - 1)];
         n_p = (kr < n) ? pos[off + kr] : INT32_MAX;
     };
-    fetch_kv(0);
-    for (int kb = 0; kb < n_kt; ++kb) {
+    // This item's half of the key blocks 0 .. n_kt - 1.
+    const int half = t.parts == 1 ? n_kt : (n_kt + 1) / 2;
+    const int lo = part == 0 ? 0 : half, hi = part == 0 ? half : n_kt;
+    if (lo < hi) fetch_kv(lo);
+    for (int kb = lo; kb < hi; ++kb) {
         __syncthreads();
         store_tile<D>((LDS_AS char*)kt, rk, lane);
         store_tile<D>((LDS_AS char*)vt, rv, lane);
@@ -444,7 +464,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__
         // Lane 31 holds the position of the block's last key (INT32_MAX past the end).
         const bool full = __builtin_amdgcn_readlane(n_p, 31) <= pos_first;
         __syncthreads();
-        if (kb + 1 < n_kt) fetch_kv(kb + 1);
+        if (kb + 1 < hi) fetch_kv(kb + 1);
         f32x16 sacc, pacc;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -512,7 +532,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__
     }
     // acc[b] register j: d = 32b + 8(j/4) + 4hh + j%4 of query qi.
     if (q_ok) {
-        float* row = dq + ((off + i0 + l32) * hq + h) * D;
+        float* row = dq + (((int64_t)part * m + off + i0 + l32) * hq + h) * D;  // this part's partial
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -535,7 +555,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict
                                                         const float* __restrict__ ws_db,
                                                         const uint16_t* __restrict__ k,
                                                         const float* __restrict__ gain, int64_t m, int hq, int hkv,
-                                                        float* __restrict__ dk, float* __restrict__ dv,
+                                                        int parts, float* __restrict__ dk, float* __restrict__ dv,
                                                         float* __restrict__ db, float* __restrict__ ws_part) {
     __shared__ float part[4];
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over m * hkv * D
@@ -545,18 +565,23 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict
         const int64_t row = idx / (hkv * D);
         const int kvh = (int)((idx / D) % hkv), d = (int)(idx % D);
         float a = 0.0f, b = 0.0f;
-        for (int hl = 0; hl < gsz; ++hl) {
-            const int64_t o = (((int64_t)(kvh * gsz + hl)) * m + row) * D + d;
-            a += ws_dk[o];
-            b += ws_dv[o];
-        }
+        for (int pt = 0; pt < parts; ++pt)
+            for (int hl = 0; hl < gsz; ++hl) {
+                const int64_t o = (((int64_t)pt * hq + kvh * gsz + hl) * m + row) * D + d;
+                a += ws_dk[o];
+                b += ws_dv[o];
+            }
         dk[idx] = a;
         dv[idx] = b;
         kd = __uint_as_float((uint32_t)k[idx] << 16) * a;
     }
     if (idx < m) {
         float s = 0.0f;
-        for (int h = 0; h < hq; ++h) s = fmaf(gain[h], ws_db[(int64_t)h * m + idx], s);
+        for (int h = 0; h < hq; ++h) {
+            float sh = 0.0f;
+            for (int pt = 0; pt < parts; ++pt) sh += ws_db[((int64_t)pt * hq + h) * m + idx];
+            s = fmaf(gain[h], sh, s);
+        }
         db[idx] = s;
     }
 #pragma unroll
@@ -579,11 +604,18 @@ __device__ __forceinline__ float block_sum_1024(float v, float* part) {
     return s;
 }
 
+// dQ = the sum of its parts, in part order.
+__global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const float* __restrict__ ws_dq, int64_t n,
+                                                        float* __restrict__ dq) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) dq[i] = ws_dq[i] + ws_dq[n + i];
+}
+
 // 4b. Workgroup h < hq: dg_h = sum_j b_j sum_i dS_ij over all kept rows.
 // Workgroup hq: dtau = -(1/tau) * sum of the k . dK partials. Each thread
 // keeps four loads in flight; the summation order is fixed.
 __global__ __launch_bounds__(1024) void bwd_scalars_kernel(const float* __restrict__ ws_db,
-                                                          const float* __restrict__ bias, int64_t m, int hq,
+                                                          const float* __restrict__ bias, int64_t m, int hq, int parts,
                                                           const float* __restrict__ ws_part, int64_t n_part,
                                                           float inv_tau, float* __restrict__ dgain,
                                                           float* __restrict__ dtau) {
@@ -598,7 +630,13 @@ __global__ __launch_bounds__(1024) void bwd_scalars_kernel(const float* __restri
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int64_t j = j0 + (int64_t)u * 1024;
-            xv[u] = j < len ? x[j] : 0.0f;
+            float xs = 0.0f;
+            if (j < len) {
+                xs = x[j];
+                if (gain_wg)  // the other parts of the head's sum_i dS row
+                    for (int pt = 1; pt < parts; ++pt) xs += x[(int64_t)pt * hq * m + j];
+            }
+            xv[u] = xs;
             bv[u] = (gain_wg && j < len) ? bias[j] : 1.0f;
         }
 #pragma unroll
@@ -618,10 +656,12 @@ hipError_t launch_bwd_d(const AttnBwdArgs& a, const BwdTable& t, float c, hipStr
     const int64_t m = t.m_total;
     float* ws = (float*)a.workspace;
     float* dl = ws;
+    const int np = t.parts;
     float* ws_dk = dl + (int64_t)a.hq * m;
-    float* ws_dv = ws_dk + (int64_t)a.hq * m * D;
-    float* ws_db = ws_dv + (int64_t)a.hq * m * D;
-    float* ws_part = ws_db + (int64_t)a.hq * m;
+    float* ws_dv = ws_dk + (int64_t)np * a.hq * m * D;
+    float* ws_db = ws_dv + (int64_t)np * a.hq * m * D;
+    float* ws_dq = ws_db + (int64_t)np * a.hq * m;  // split: the dq parts; else dq is written directly
+    float* ws_part = ws_dq + (np > 1 ? (int64_t)np * a.hq * m * D : 0);
     const int64_t n_red = (m * a.hkv * D + 255) / 256;
     const uint16_t *q = (const uint16_t*)a.q, *k = (const uint16_t*)a.k, *v = (const uint16_t*)a.v;
     const uint16_t *dout = (const uint16_t*)a.d_out, *out = (const uint16_t*)a.out;
@@ -630,10 +670,13 @@ hipError_t launch_bwd_d(const AttnBwdArgs& a, const BwdTable& t, float c, hipStr
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)t.n_items), dim3(64), 0, st, q, k, v, dout, a.lse, dl,
                        a.bias, a.pos, t, a.hq, a.hkv, a.gain, c, ws_dk, ws_dv, ws_db);
     hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)t.n_items), dim3(64), 0, st, q, k, v, dout, a.lse, dl,
-                       a.bias, a.pos, t, a.hq, a.hkv, a.gain, c, a.d_q);
+                       a.bias, a.pos, t, a.hq, a.hkv, a.gain, c, np > 1 ? ws_dq : a.d_q);
+    if (np > 1)
+        hipLaunchKernelGGL(bwd_dq_sum_kernel, dim3((unsigned)((m * a.hq * D + 255) / 256)), dim3(256), 0, st, ws_dq,
+                           m * a.hq * D, a.d_q);
     hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3((unsigned)n_red), dim3(256), 0, st, ws_dk, ws_dv, ws_db, k,
-                       a.gain, m, a.hq, a.hkv, a.d_k, a.d_v, a.d_bias, ws_part);
-    hipLaunchKernelGGL(bwd_scalars_kernel, dim3((unsigned)(a.hq + 1)), dim3(1024), 0, st, ws_db, a.bias, m, a.hq,
+                       a.gain, m, a.hq, a.hkv, np, a.d_k, a.d_v, a.d_bias, ws_part);
+    hipLaunchKernelGGL(bwd_scalars_kernel, dim3((unsigned)(a.hq + 1)), dim3(1024), 0, st, ws_db, a.bias, m, a.hq, np,
                        ws_part, n_red, 1.0f / a.tau, a.d_gain, a.d_tau);
     return hipGetLastError();
 }
@@ -644,21 +687,27 @@ size_t attention_backward_plan(const SeqTable& st, int hq, int hkv, int head_dim
     BwdTable& t = *(BwdTable*)table_out;
     t = BwdTable{};
     t.n_seg = st.n;
+    int64_t blocks = 0;
+    for (int b = 0; b < st.n; ++b) blocks += (st.s[b].n_kept + 31) / 32;
+    t.parts = blocks * hq < BWD_SPLIT_BELOW ? 2 : 1;
     int64_t items = 0, m = 0;
     for (int b = 0; b < st.n; ++b) {
         t.s[b].off = st.s[b].kept_off;
         t.s[b].n = st.s[b].n_kept;
         t.s[b].n_blk = (st.s[b].n_kept + 31) / 32;
         t.s[b].item0 = (int32_t)items;
-        items += (int64_t)t.s[b].n_blk * hq;
+        items += (int64_t)t.s[b].n_blk * hq * t.parts;
         m += st.s[b].n_kept;
     }
     t.n_items = (int32_t)items;
     t.m_total = m;
-    // Dl [hq][M], dk and dv partials [hq][M][D], sum_i dS partials [hq][M],
-    // one k . dK partial per 256 elements of dK.
+    // Dl [hq][M]; per part: dk and dv partials [hq][M][D] and sum_i dS
+    // partials [hq][M]; when split, dq partials [parts][M][hq][D]; one k . dK
+    // partial per 256 elements of dK.
     const size_t n_red = ((size_t)m * hkv * head_dim + 255) / 256;
-    return ((size_t)hq * m * (2 + 2 * (size_t)head_dim) + n_red) * sizeof(float);
+    const size_t per_part = (size_t)hq * m * (2 * (size_t)head_dim + 1);
+    const size_t dq_parts = t.parts > 1 ? (size_t)t.parts * hq * m * head_dim : 0;
+    return ((size_t)hq * m + t.parts * per_part + dq_parts + n_red) * sizeof(float);
 }
 
 size_t attention_backward_table_bytes() { return sizeof(BwdTable); }

@@ -606,6 +606,11 @@ def test_backward_head_ratios_and_ties(hq, hkv, d):
     check_backward([300, 129], hq, hkv, d, seed=hq * 7 + d, pos_ties=True)
 
 
+def test_backward_without_the_split():
+    note("backward bf16 16/8 heads D=128, one 4200-row prompt (enough blocks that items are not split)")
+    check_backward([4200], 16, 8, 128, seed=73)
+
+
 def test_backward_deterministic():
     note("backward: bitwise repeatable")
     g1 = check_backward([1000], 16, 8, 128, seed=81)
