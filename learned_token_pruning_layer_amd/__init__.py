@@ -32,4 +32,5 @@ from ._lib import (  # noqa: F401
     tg_score_grad,
     tg_select_topk,
 )
+from .budget import PromptSpec, doc_budget, pack_prompts, prompt_with_budget  # noqa: F401
 from .layer import GatedPrefillLayer  # noqa: F401
