@@ -142,9 +142,12 @@ def cpu_baseline(w, budget_s):
     import numpy as np
     import oracle
 
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip() for i in info})) or blas
     except Exception:
         threads = os.cpu_count() or 1
     lay = w.layers[0]
@@ -181,7 +184,8 @@ def cpu_baseline(w, budget_s):
                   f"evenly spaced query rows of {m}, scaled by visible (query, key) pairs")
     total_ms = (t_front + t_attn) * 1e3
     return dict(value=round(total_ms, 3), unit="ms", cores=int(threads), kind="oracle", sample=sample,
-                split_ms=dict(gate_select_compact=round(t_front * 1e3, 3), attention=round(t_attn * 1e3, 3)))
+                split_ms=dict(gate_select_compact=round(t_front * 1e3, 3), attention=round(t_attn * 1e3, 3)),
+                blas=blas, host_cpus=len(os.sched_getaffinity(0)))
 
 
 def measure_extras(torch, tg, layer, w, steps, dev):
