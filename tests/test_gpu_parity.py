@@ -700,7 +700,10 @@ def test_gate_backward_without_dx_and_deterministic():
 
 # ------------------------------------------------------- full above-gate layer ----
 
-@pytest.mark.parametrize("m,k,n", [(1, 64, 128), (77, 2048, 384), (300, 128, 4096), (2384, 2048, 256)])
+# (3000, 128, 8192) runs every epilogue on the 256 x 256 tiles (384 and more of
+# them) with a ragged last row tile; the other cases on the smaller tiles.
+@pytest.mark.parametrize("m,k,n", [(1, 64, 128), (77, 2048, 384), (300, 128, 4096), (2384, 2048, 256),
+                                   (3000, 128, 8192)])
 def test_linear_epilogues(m, k, n):
     """tg_linear against the oracle's linear / swiglu: store, residual add, SwiGLU.
     Bar: per row, max |err| <= 1e-2 * max |ref| (fp32 sums of exact bf16 products, one
