@@ -20,10 +20,10 @@
 //    the row's original position (angle reduced in fp64, sin/cos in fp32)
 //    and writes q, k and v as separate [M, heads, D] tensors.
 //  * linear_kernel<EPI, ...>: C = A W^T on 32x32x16 bf16 MFMA: 256 x 256
-//    per workgroup of 8 waves of 128 weight rows x 64 activation rows where
-//    the grid still gives every CU 1.5 tiles (half the loads per MFMA of
-//    the next size), else 256 x 128 of 8 waves of 64 x 64 (one workgroup per
-//    CU), or 128 x 128 of 4 such waves (two per CU) for narrow outputs; 64-wide k
+//    per workgroup of 8 waves of 128 weight rows x 64 activation rows when
+//    that makes at least 128 tiles (half the loads per MFMA of the next
+//    size), else 256 x 128 of 8 waves of 64 x 64 (one workgroup per CU), or
+//    128 x 128 of 4 such waves (two per CU) for narrow outputs; 64-wide k
 //    chunks streamed global -> LDS with direct loads through a two-stage
 //    ring (swizzled 128-byte LDS rows, permuted k-step order), tiles ordered
 //    so the workgroups of one XCD share weight tiles. The weights are the
@@ -329,8 +329,9 @@ hipError_t launch_linear(int epi, const void* a, int64_t m, int k, const void* w
     // 128 x 128 (4 waves, two workgroups per CU) otherwise.
     const int wide = epi == EPI_SWIGLU ? 128 : 256;
     // 256 x 256 tiles (8 waves of 128 weight rows x 64 activation rows) halve
-    // the loads per MFMA; used where they still give every CU 1.5 tiles.
-    if (n_out % wide == 0 && ((m + 255) / 256) * (n_out / wide) >= 384)
+    // the loads per MFMA; measured faster than twice as many 256 x 128 tiles
+    // once there are at least 128 of them (half the CUs).
+    if (n_out % wide == 0 && ((m + 255) / 256) * (n_out / wide) >= 128)
         return launch_linear_t<4, 2, 2, 4>(epi, a, m, k, w, w_up, n_out, resid, out, st);
     if (n_out % wide == 0) return launch_linear_t<2, 2, 4, 2>(epi, a, m, k, w, w_up, n_out, resid, out, st);
     return launch_linear_t<2, 2, 2, 2>(epi, a, m, k, w, w_up, n_out, resid, out, st);

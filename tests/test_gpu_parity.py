@@ -700,8 +700,9 @@ def test_gate_backward_without_dx_and_deterministic():
 
 # ------------------------------------------------------- full above-gate layer ----
 
-# (3000, 128, 8192) runs every epilogue on the 256 x 256 tiles (384 and more of
-# them) with a ragged last row tile; the other cases on the smaller tiles.
+# (3000, 128, 8192) runs every epilogue on the 256 x 256 tiles with a ragged
+# last row tile; the other cases run on 256 x 128 tiles, or on 128 x 128 for
+# outputs that are not a multiple of 256 (store and residual at n = 128, 384).
 @pytest.mark.parametrize("m,k,n", [(1, 64, 128), (77, 2048, 384), (300, 128, 4096), (2384, 2048, 256),
                                    (3000, 128, 8192)])
 def test_linear_epilogues(m, k, n):
