@@ -545,6 +545,9 @@ tg_status tg_dense_layer(tg_dtype dt, const void* hidden_kept, const float* bias
         return fail(TG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
                     l.total);
     if ((uintptr_t)workspace % 256) return fail(TG_ERR_INVALID_ARGUMENT, "workspace not 256-byte aligned");
+    // The attention step's own checks, done here so that a refused call enqueues nothing.
+    if ((m / 32 + n_seqs) * (int64_t)w->hq > (int64_t)INT32_MAX)
+        return fail(TG_ERR_UNSUPPORTED, "too many attention work items for one launch");
     char* ws = (char*)workspace;
     void *a = ws + l.a, *qkv = ws + l.qkv, *q = ws + l.q, *o = ws + l.o, *h2 = ws + l.h2, *mlp = ws + l.mlp;
     void* k = k_out ? k_out : ws + l.k;
