@@ -339,10 +339,12 @@ def tg_decode_attention(q_new: torch.Tensor, k: torch.Tensor, v: torch.Tensor, b
 def tg_gated_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias_kept: torch.Tensor,
                                 pos_kept: torch.Tensor, seqs: Sequence, gain: torch.Tensor, tau: float,
                                 out: torch.Tensor, lse: torch.Tensor, d_out: torch.Tensor,
-                                workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+                                workspace: Optional[torch.Tensor] = None, stream=None,
+                                grads: Optional[dict] = None) -> dict:
     """Gradients of sum(d_out * out) through token-gated attention (bf16 in,
     fp32 out): dict(dq, dk, dv, dbias, dgain, dtau). out and lse are the
-    forward's results for the same inputs."""
+    forward's results for the same inputs. `grads` may hold the output
+    tensors to write (same keys, fp32, contiguous)."""
     lib = load()
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (bias_kept, "bias_kept"), (pos_kept, "pos_kept"), (gain, "gain"),
                   (out, "out"), (lse, "lse"), (d_out, "d_out")):
@@ -353,9 +355,14 @@ def tg_gated_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
         raise ValueError("out, d_out [M, hq, D] and lse [hq, M] expected")
     dev = q.device
     f32 = torch.float32
-    g = dict(dq=torch.empty((m, hq, dh), dtype=f32, device=dev), dk=torch.empty((m, hkv, dh), dtype=f32, device=dev),
-             dv=torch.empty((m, hkv, dh), dtype=f32, device=dev), dbias=torch.empty(m, dtype=f32, device=dev),
-             dgain=torch.empty(hq, dtype=f32, device=dev), dtau=torch.empty(1, dtype=f32, device=dev))
+    shapes = dict(dq=(m, hq, dh), dk=(m, hkv, dh), dv=(m, hkv, dh), dbias=(m,), dgain=(hq,), dtau=(1,))
+    g = {}
+    for key, shp in shapes.items():
+        t = grads[key] if grads is not None else torch.empty(shp, dtype=f32, device=dev)
+        _dev(t, key)
+        if t.dtype != f32 or t.numel() != math.prod(shp):
+            raise ValueError(f"{key} must be fp32 with {math.prod(shp)} elements")
+        g[key] = t
     sa = seq_array(seqs)
     ws_bytes = lib.tg_attention_backward_workspace_bytes(sa, len(seqs), hq, hkv, dh)
     if workspace is None:
@@ -387,10 +394,11 @@ def tg_score_grad(d_bias_kept: torch.Tensor, scores: torch.Tensor, kept_idx: tor
 def tg_gate_backward(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, d_scores: torch.Tensor,
                      rows: Optional[torch.Tensor] = None, b1: Optional[torch.Tensor] = None,
                      d_x: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                     stream=None) -> dict:
+                     stream=None, grads: Optional[dict] = None) -> dict:
     """Gradients of sum_r d_scores[r] * scores[r] through the gate MLP over the
     listed rows (every row if rows is None): dict(dw1 [H, d], db1 [H], dw2 [H],
-    db2 [1]) in fp32, plus dx when d_x (fp32 [N, d], added to) is given."""
+    db2 [1]) in fp32, plus dx when d_x (fp32 [N, d], added to) is given.
+    `grads` may hold the output tensors to write (same keys)."""
     lib = load()
     for t, nm in ((x, "x"), (w1, "w1"), (w2, "w2"), (d_scores, "d_scores")):
         _dev(t, nm)
@@ -412,8 +420,14 @@ def tg_gate_backward(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, d_scor
             raise ValueError("d_x must be fp32 [N, d]")
     n_list = n if rows is None else rows.numel()
     f32 = torch.float32
-    g = dict(dw1=torch.empty((h, d), dtype=f32, device=x.device), db1=torch.empty(h, dtype=f32, device=x.device),
-             dw2=torch.empty(h, dtype=f32, device=x.device), db2=torch.empty(1, dtype=f32, device=x.device))
+    shapes = dict(dw1=(h, d), db1=(h,), dw2=(h,), db2=(1,))
+    g = {}
+    for key, shp in shapes.items():
+        t = grads[key] if grads is not None else torch.empty(shp, dtype=f32, device=x.device)
+        _dev(t, key)
+        if t.dtype != f32 or t.numel() != math.prod(shp):
+            raise ValueError(f"{key} must be fp32 with {math.prod(shp)} elements")
+        g[key] = t
     ws_need = lib.tg_gate_backward_workspace_bytes(n, d, h, n_list)
     if workspace is None:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=x.device)
@@ -459,7 +473,8 @@ def dense_weights(w: dict, d_model: int, hq: int, hkv: int, head_dim: int) -> Tg
 
 def tg_dense_layer(h: torch.Tensor, bias_kept: torch.Tensor, pos_kept: torch.Tensor, seqs: Sequence, w: dict,
                    hq: int, hkv: int, head_dim: int, out: Optional[torch.Tensor] = None, want_kv: bool = False,
-                   workspace: Optional[torch.Tensor] = None, stream=None):
+                   workspace: Optional[torch.Tensor] = None, stream=None, k_out: Optional[torch.Tensor] = None,
+                   v_out: Optional[torch.Tensor] = None):
     """One above-gate decoder layer over the kept rows h [M, d] (bf16); returns out [M, d],
     or (out, k, v) with the layer's keys and values [M, hkv, D] when want_kv."""
     lib = load()
@@ -472,8 +487,8 @@ def tg_dense_layer(h: torch.Tensor, bias_kept: torch.Tensor, pos_kept: torch.Ten
         out = torch.empty_like(h)
     k = v = None
     if want_kv:
-        k = torch.empty((m, hkv, head_dim), dtype=h.dtype, device=h.device)
-        v = torch.empty_like(k)
+        k = k_out if k_out is not None else torch.empty((m, hkv, head_dim), dtype=h.dtype, device=h.device)
+        v = v_out if v_out is not None else torch.empty_like(k)
     need = lib.tg_dense_layer_workspace_bytes(sa, len(seqs), ctypes.byref(desc))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
@@ -485,7 +500,8 @@ def tg_dense_layer(h: torch.Tensor, bias_kept: torch.Tensor, pos_kept: torch.Ten
 
 def tg_gated_delta_scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
                         seqs: Sequence, state_in: Optional[torch.Tensor] = None, want_state: bool = False,
-                        workspace: Optional[torch.Tensor] = None, stream=None):
+                        workspace: Optional[torch.Tensor] = None, stream=None, out: Optional[torch.Tensor] = None,
+                        state_out: Optional[torch.Tensor] = None):
     """Gated delta rule over the kept rows: out bf16 [M, H, dv], plus the final states fp32
     [n_seqs, H, dv, dk] when want_state."""
     lib = load()
@@ -498,8 +514,12 @@ def tg_gated_delta_scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
     if state_in is not None:
         _dev(state_in, "state_in")
     sa = seq_array(seqs)
-    out = torch.empty((m, nh, dv), dtype=v.dtype, device=v.device)
-    st = torch.empty((len(seqs), nh, dv, dk), dtype=torch.float32, device=v.device) if want_state else None
+    if out is None:
+        out = torch.empty((m, nh, dv), dtype=v.dtype, device=v.device)
+    st = None
+    if want_state:
+        st = state_out if state_out is not None else torch.empty((len(seqs), nh, dv, dk), dtype=torch.float32,
+                                                                 device=v.device)
     need = lib.tg_delta_scan_workspace_bytes(sa, len(seqs), nh, dk, dv)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=v.device)

@@ -12,7 +12,7 @@
 //     dS_ij = p_ij (dP_ij - dO_i . o_i),
 //     dQ_i = c sum_j dS_ij k_j,   dK_j = c sum_i dS_ij q_i,
 //     db_j = sum_h g_h sum_i dS_ij,   dg_h = sum_ij dS_ij b_j,
-//     dtau = -(c / tau) sum_hij dS_ij q_i.k_j = -(1 / tau) sum_j k_j . dK_j,
+//     dtau = -(c / tau) sum_hij dS_ij q_i.k_j,
 // and the score of a kept document row gets db_j * sigmoid(-s_j) (the
 // derivative of logsigmoid); question and pruned rows get 0.
 //
@@ -26,8 +26,12 @@
 //     straight from those registers (the query order inside each 16-wide
 //     k-step is permuted the same way on both operands) and dO / Q read
 //     transposed from LDS (ds_read_b64_tr_b16). Per-head partial dK, dV and
-//     sum_i dS_ij go to a workspace. Blocks that every query of the query
-//     block can fully see take a path without the causal and ragged masks.
+//     sum_i dS_ij go to a workspace, with the fp32 sum_i dS_ij (q_i . k_j) of
+//     the unrounded dS and S registers per key and head (the temperature's
+//     gradient: taken from the bf16-rounded products of dK instead, it loses
+//     the digits that survive its cancellation). Blocks that every query of
+//     the query block can fully see take a path without the causal and
+//     ragged masks.
 //  3. dq: one wave per (prompt, 32-query block, query head), like the
 //     forward kernel: S^T = K Q^T and dP^T = V dO^T with Q and dO in
 //     registers, dS^T in registers, dQ^T += K^T dS^T with K^T read
@@ -36,10 +40,10 @@
 //  and 3 is split over two waves, each walking half of the blocks; their
 //  partials are summed in a fixed order below.
 //  4. reduce: sums the per-head partials of each KV head in a fixed order
-//     (so the result is deterministic), applies the gains to db, and forms
-//     per-workgroup partials of sum k . dK; a last kernel reduces dg_h =
-//     sum_j b_j sum_i dS_ij per head and dtau from those partials, each in
-//     a fixed order. The score kernel applies sigmoid(-s).
+//     (so the result is deterministic) and applies the gains to db; a last
+//     kernel reduces dg_h = sum_j b_j sum_i dS_ij per head and dtau from the
+//     per-key sums of dS_ij (q_i . k_j), each in a fixed order. The score
+//     kernel applies sigmoid(-s).
 // LDS tiles are row-major with a 16-byte pad per row (row stride D*2+16
 // bytes), which spreads both the row reads and the transpose reads over
 // the banks.
@@ -188,16 +192,16 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
     dl[(int64_t)h * m + row] = acc;
 }
 
-// 2. Per (prompt, key block, head): partial dK, dV, db of that head, dg and
-// dtau partials. ws layout (fp32): dk [hq][M][D], dv [hq][M][D], db [hq][M],
-// and per item: dg, dtau.
+// 2. Per (prompt, key block, head): partial dK, dV of that head, and per key
+// sum_i dS_ij and sum_i dS_ij (q_i . k_j). ws layout per part (fp32): dk
+// [hq][M][D], dv [hq][M][D], db [hq][M], dt [hq][M].
 template <int D>
 __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ d_out, const float* __restrict__ lse, const float* __restrict__ dl,
     const float* __restrict__ bias, const int32_t* __restrict__ pos, BwdTable t, int hq, int hkv,
     const float* __restrict__ gain, float c, float* __restrict__ ws_dk, float* __restrict__ ws_dv,
-    float* __restrict__ ws_db) {
+    float* __restrict__ ws_db, float* __restrict__ ws_dt) {
     constexpr int KS = D / 16, DB = D / 32;
     __shared__ __attribute__((aligned(16))) char kt[Tile<D>::BYTES], vt[Tile<D>::BYTES];
     __shared__ __attribute__((aligned(16))) char qt[Tile<D>::BYTES], dot[Tile<D>::BYTES];
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
             acc_dk[b][j] = 0.0f;
             acc_dv[b][j] = 0.0f;
         }
-    float db_acc = 0.0f;
+    float db_acc = 0.0f, dt_acc = 0.0f;
 
     // Q / dO tiles and the per-query scalars of block ib + 1 are fetched into
     // registers while block ib is processed.
@@ -344,6 +348,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
                         }
                         const float ds = p * (pacc[j] - dlq[j / 4][j % 4]);
                         db_acc += ds;
+                        dt_acc = fmaf(ds, sacc[j], dt_acc);
                         pv[t2] = p;
                         dv_[t2] = ds;
                     }
@@ -381,7 +386,11 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
     // sum_i dS_ij of this lane's key, over both query halves (the gain is
     // applied when the heads are summed).
     db_acc += __shfl_xor(db_acc, 32);
-    if (hh == 0 && key_ok) ws_db[((int64_t)part * hq + h) * m + off + key] = db_acc;
+    dt_acc += __shfl_xor(dt_acc, 32);
+    if (hh == 0 && key_ok) {
+        ws_db[((int64_t)part * hq + h) * m + off + key] = db_acc;
+        ws_dt[((int64_t)part * hq + h) * m + off + key] = dt_acc;
+    }
 }
 
 // 3. dQ of one (prompt, query block, head).
@@ -547,20 +556,16 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__
 
 // 4a. dK, dV = sums of the per-head partials over each KV head's query
 // heads (in head order); db = sum over heads of g_h times the head's
-// sum_i dS_ij; per workgroup, the partial sum of k . dK over its elements
-// (a fixed-order tree) for the temperature.
+// sum_i dS_ij.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ ws_dk,
                                                         const float* __restrict__ ws_dv,
                                                         const float* __restrict__ ws_db,
-                                                        const uint16_t* __restrict__ k,
                                                         const float* __restrict__ gain, int64_t m, int hq, int hkv,
                                                         int parts, float* __restrict__ dk, float* __restrict__ dv,
-                                                        float* __restrict__ db, float* __restrict__ ws_part) {
-    __shared__ float part[4];
+                                                        float* __restrict__ db) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over m * hkv * D
     const int gsz = hq / hkv;
-    float kd = 0.0f;
     if (idx < m * hkv * D) {
         const int64_t row = idx / (hkv * D);
         const int kvh = (int)((idx / D) % hkv), d = (int)(idx % D);
@@ -573,7 +578,6 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict
             }
         dk[idx] = a;
         dv[idx] = b;
-        kd = __uint_as_float((uint32_t)k[idx] << 16) * a;
     }
     if (idx < m) {
         float s = 0.0f;
@@ -584,11 +588,6 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict
         }
         db[idx] = s;
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) kd += __shfl_xor(kd, o);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = kd;
-    __syncthreads();
-    if (threadIdx.x == 0) ws_part[blockIdx.x] = (part[0] + part[1]) + (part[2] + part[3]);
 }
 
 // Fixed-order sum of one 1024-thread workgroup's values (a butterfly per
@@ -612,18 +611,18 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const float* __restrict
 }
 
 // 4b. Workgroup h < hq: dg_h = sum_j b_j sum_i dS_ij over all kept rows.
-// Workgroup hq: dtau = -(1/tau) * sum of the k . dK partials. Each thread
-// keeps four loads in flight; the summation order is fixed.
+// Workgroup hq: dtau = -(c/tau) times the sum of the per-key, per-head sums
+// of dS_ij (q_i . k_j) over every part. Each thread keeps four loads in
+// flight; the summation order is fixed.
 __global__ __launch_bounds__(1024) void bwd_scalars_kernel(const float* __restrict__ ws_db,
                                                           const float* __restrict__ bias, int64_t m, int hq, int parts,
-                                                          const float* __restrict__ ws_part, int64_t n_part,
-                                                          float inv_tau, float* __restrict__ dgain,
-                                                          float* __restrict__ dtau) {
+                                                          const float* __restrict__ ws_dt, float dtau_scale,
+                                                          float* __restrict__ dgain, float* __restrict__ dtau) {
     __shared__ float part[16];
     const int h = blockIdx.x;
     const bool gain_wg = h < hq;
-    const float* x = gain_wg ? ws_db + (int64_t)h * m : ws_part;
-    const int64_t len = gain_wg ? m : n_part;
+    const float* x = gain_wg ? ws_db + (int64_t)h * m : ws_dt;
+    const int64_t len = gain_wg ? m : (int64_t)parts * hq * m;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int64_t j0 = threadIdx.x; j0 < len; j0 += 4 * 1024) {
         float xv[4], bv[4];
@@ -647,7 +646,7 @@ __global__ __launch_bounds__(1024) void bwd_scalars_kernel(const float* __restri
         if (gain_wg)
             dgain[h] = tot;
         else
-            *dtau = -inv_tau * tot;
+            *dtau = dtau_scale * tot;
     }
 }
 
@@ -660,24 +659,24 @@ hipError_t launch_bwd_d(const AttnBwdArgs& a, const BwdTable& t, float c, hipStr
     float* ws_dk = dl + (int64_t)a.hq * m;
     float* ws_dv = ws_dk + (int64_t)np * a.hq * m * D;
     float* ws_db = ws_dv + (int64_t)np * a.hq * m * D;
-    float* ws_dq = ws_db + (int64_t)np * a.hq * m;  // split: the dq parts; else dq is written directly
-    float* ws_part = ws_dq + (np > 1 ? (int64_t)np * a.hq * m * D : 0);
+    float* ws_dt = ws_db + (int64_t)np * a.hq * m;
+    float* ws_dq = ws_dt + (int64_t)np * a.hq * m;  // split: the dq parts; else dq is written directly
     const int64_t n_red = (m * a.hkv * D + 255) / 256;
     const uint16_t *q = (const uint16_t*)a.q, *k = (const uint16_t*)a.k, *v = (const uint16_t*)a.v;
     const uint16_t *dout = (const uint16_t*)a.d_out, *out = (const uint16_t*)a.out;
     hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((m * a.hq + 255) / 256)), dim3(256), 0, st, dout, out, m,
                        a.hq, dl);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)t.n_items), dim3(64), 0, st, q, k, v, dout, a.lse, dl,
-                       a.bias, a.pos, t, a.hq, a.hkv, a.gain, c, ws_dk, ws_dv, ws_db);
+                       a.bias, a.pos, t, a.hq, a.hkv, a.gain, c, ws_dk, ws_dv, ws_db, ws_dt);
     hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)t.n_items), dim3(64), 0, st, q, k, v, dout, a.lse, dl,
                        a.bias, a.pos, t, a.hq, a.hkv, a.gain, c, np > 1 ? ws_dq : a.d_q);
     if (np > 1)
         hipLaunchKernelGGL(bwd_dq_sum_kernel, dim3((unsigned)((m * a.hq * D + 255) / 256)), dim3(256), 0, st, ws_dq,
                            m * a.hq * D, a.d_q);
-    hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3((unsigned)n_red), dim3(256), 0, st, ws_dk, ws_dv, ws_db, k,
-                       a.gain, m, a.hq, a.hkv, np, a.d_k, a.d_v, a.d_bias, ws_part);
+    hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3((unsigned)n_red), dim3(256), 0, st, ws_dk, ws_dv, ws_db,
+                       a.gain, m, a.hq, a.hkv, np, a.d_k, a.d_v, a.d_bias);
     hipLaunchKernelGGL(bwd_scalars_kernel, dim3((unsigned)(a.hq + 1)), dim3(1024), 0, st, ws_db, a.bias, m, a.hq, np,
-                       ws_part, n_red, 1.0f / a.tau, a.d_gain, a.d_tau);
+                       ws_dt, -c / a.tau, a.d_gain, a.d_tau);
     return hipGetLastError();
 }
 
@@ -701,13 +700,13 @@ size_t attention_backward_plan(const SeqTable& st, int hq, int hkv, int head_dim
     }
     t.n_items = (int32_t)items;
     t.m_total = m;
-    // Dl [hq][M]; per part: dk and dv partials [hq][M][D] and sum_i dS
-    // partials [hq][M]; when split, dq partials [parts][M][hq][D]; one k . dK
-    // partial per 256 elements of dK.
-    const size_t n_red = ((size_t)m * hkv * head_dim + 255) / 256;
-    const size_t per_part = (size_t)hq * m * (2 * (size_t)head_dim + 1);
+    // Dl [hq][M]; per part: dk and dv partials [hq][M][D], sum_i dS and
+    // sum_i dS (q . k) partials [hq][M] each; when split, dq partials
+    // [parts][M][hq][D].
+    (void)hkv;
+    const size_t per_part = (size_t)hq * m * (2 * (size_t)head_dim + 2);
     const size_t dq_parts = t.parts > 1 ? (size_t)t.parts * hq * m * head_dim : 0;
-    return ((size_t)hq * m + t.parts * per_part + dq_parts + n_red) * sizeof(float);
+    return ((size_t)hq * m + t.parts * per_part + dq_parts) * sizeof(float);
 }
 
 size_t attention_backward_table_bytes() { return sizeof(BwdTable); }

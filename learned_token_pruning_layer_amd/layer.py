@@ -18,19 +18,68 @@ import math
 from ._lib import TG_BF16, TG_F32, TgGather, _check, load, seq_array, tg_kept_rows
 
 
+def _dense_rows(t: torch.Tensor) -> bool:
+    """Each row (index over dim 0) is one dense block: the inner dimensions
+    are laid out contiguously; the row stride itself may be larger."""
+    exp = 1
+    for size, stride in zip(reversed(t.shape[1:]), reversed(t.stride()[1:])):
+        if size != 1 and stride != exp:
+            return False
+        exp *= size
+    return t.stride(0) >= exp or t.shape[0] <= 1
+
+
+def _validate(x, w1, w2, b1, layers, hq, hkv, head_dim, pos):
+    if not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [N, d] GPU tensor")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"x: unsupported dtype {x.dtype}")
+    n, d = x.shape
+    dev = x.device
+    for t, nm in ((w1, "w1"), (w2, "w2")) + (((b1, "b1"),) if b1 is not None else ()):
+        if t.device != dev or t.dtype != x.dtype or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous tensor of x's dtype on x's device")
+    h = w1.shape[0]
+    if tuple(w1.shape) != (h, d) or w2.numel() != h or (b1 is not None and b1.numel() != h):
+        raise ValueError("w1 must be [H, d], w2 and b1 [H]")
+    if hq <= 0 or hkv <= 0 or hq % hkv:
+        raise ValueError("hq must be a positive multiple of hkv")
+    for li, lay in enumerate(layers):
+        for nm, heads in (("q", hq), ("k", hkv), ("v", hkv)):
+            t = getattr(lay, nm)
+            if t.device != dev or t.dtype != x.dtype:
+                raise ValueError(f"layer {li} {nm}: must be on x's device with x's dtype")
+            if t.dim() < 2 or t.shape[0] != n or math.prod(t.shape[1:]) != heads * head_dim:
+                raise ValueError(f"layer {li} {nm}: expected {n} rows of {heads}x{head_dim}, got {tuple(t.shape)}")
+            if not _dense_rows(t):
+                raise ValueError(f"layer {li} {nm}: each row must be dense (inner dimensions contiguous)")
+        g = lay.gain
+        if g.device != dev or g.dtype != torch.float32 or g.numel() != hq or not g.is_contiguous():
+            raise ValueError(f"layer {li} gain: must be a contiguous fp32 [hq] tensor on x's device")
+    if pos is not None and (pos.device != dev or pos.dtype != torch.int32 or pos.numel() != n
+                            or not pos.is_contiguous()):
+        raise ValueError("pos must be a contiguous int32 [N] tensor on x's device")
+
+
 class GatedPrefillLayer:
     """Preallocated pruned-prefill layer.
 
-    x [N, d] residual at the gate layer; w1 [H, d], w2 [H] (b1 [H] optional)
-    gate weights; prompts: packed prompt descriptors; layers: objects with
-    q [N, hq*D], k/v [N, hkv*D], gain [hq] fp32 and tau (one per above-gate
-    layer sharing this kept set); pos [N] int32 or None (row - start).
+    x [N, d] residual at the gate layer (contiguous); w1 [H, d], w2 [H]
+    (b1 [H] optional) gate weights of x's dtype; prompts: packed prompt
+    descriptors; layers: objects with q [N, hq*D], k/v [N, hkv*D] (or
+    [N, heads, D]), gain [hq] fp32 and tau (one per above-gate layer sharing
+    this kept set); pos [N] int32 or None (row - start). A layer tensor may
+    be a row-strided view (q, k, v sliced from one fused projection): its
+    rows are gathered with its own row stride, as long as each row is dense.
+    Every tensor is checked here (device, dtype, shape, layout), so a step
+    cannot gather from a wrongly laid out buffer.
     """
 
     def __init__(self, x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prompts: Sequence,
                  layers: Sequence, hq: int, hkv: int, head_dim: int, b1: Optional[torch.Tensor] = None,
                  b2: float = 0.0, pos: Optional[torch.Tensor] = None, gather_hidden: bool = True,
                  want_lse: bool = False):
+        _validate(x, w1, w2, b1, layers, hq, hkv, head_dim, pos)
         self.x, self.w1, self.w2, self.b1, self.b2 = x, w1, w2, b1, float(b2)
         self.prompts = list(prompts)
         self.layers = list(layers)
@@ -83,7 +132,7 @@ class GatedPrefillLayer:
         garr = (TgGather * max(1, len(self.srcs)))()
         for i, (src, dst) in enumerate(zip(self.srcs, self.dsts)):
             rb = int(math.prod(src.shape[1:])) * src.element_size()
-            garr[i] = TgGather(src.data_ptr(), dst.data_ptr(), rb, rb, rb)
+            garr[i] = TgGather(src.data_ptr(), dst.data_ptr(), rb, src.stride(0) * src.element_size(), rb)
         self._garr = garr
         self._comp_args = (self.kept.data_ptr(), self.m, self._seqs, ns, garr, len(self.srcs),
                            None if self.pos is None else self.pos.data_ptr(), self.pos_kept.data_ptr(),

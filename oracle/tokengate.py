@@ -271,7 +271,7 @@ def gated_attention(q, k, v, bias, pos, seg_lens: Sequence[int], hq: int, hkv: i
 # ---------------------------------------------------------------------------
 
 def gated_attention_backward(q, k, v, bias, pos, seg_lens: Sequence[int], hq: int, hkv: int,
-                             gain, tau: float, d_out):
+                             gain, tau: float, d_out, o=None):
     """Gradients of sum(d_out * o) through token-gated attention.
 
     Same inputs as gated_attention, plus d_out[M, hq, D]. With
@@ -287,9 +287,16 @@ def gated_attention_backward(q, k, v, bias, pos, seg_lens: Sequence[int], hq: in
         dgain_h = sum_{i,j} ds_ij bias[j]
         dtau    = -(1/tau) * sum_{h,i,j} ds_ij (q_i.k_j * c)
 
-    Returns dict(dq, dk, dv, dbias, dgain, dtau) in fp64, plus dtau_abs =
-    (1/tau) sum |ds_ij q_i.k_j c|, the size of the terms dtau sums (it can
-    cancel to far less), for setting tolerances.
+    `o`, if given [M, hq, D], is the forward output handed to the backward
+    (the attention call's stored result, e.g. rounded to bf16); the row term
+    do_i . o_i is then taken from it, as a backward that receives the
+    forward's output does, instead of from the exact p @ v.
+
+    Returns dict(dq, dk, dv, dbias, dgain, dtau) in fp64, plus, for setting
+    tolerances, the sizes of the terms the scalar gradients sum (they can
+    cancel to far less): dtau_abs = (1/tau) sum |ds_ij q_i.k_j c|;
+    dtau_mag = (1/tau) sum p_ij (|dp_ij| + |do_i . o_i|) |q_i.k_j c| (the
+    same terms before ds is formed); dgain_abs[h] = sum_ij |ds_ij bias[j]|.
     """
     if hq % hkv:
         raise ValueError("hq must be a multiple of hkv")
@@ -304,8 +311,11 @@ def gated_attention_backward(q, k, v, bias, pos, seg_lens: Sequence[int], hq: in
     dv = np.zeros_like(vd)
     dbias = np.zeros(m_tot)
     dgain = np.zeros(hq)
+    dgain_abs = np.zeros(hq)
     dtau = 0.0
     dtau_abs = 0.0
+    dtau_mag = 0.0
+    od = None if o is None else _f64(o)
     off = 0
     for ln in seg_lens:
         ln = int(ln)
@@ -317,19 +327,23 @@ def gated_attention_backward(q, k, v, bias, pos, seg_lens: Sequence[int], hq: in
             logits = np.where(vis, qk * c + g[h] * b[seg][None, :], -np.inf)
             e = np.exp(logits - logits.max(axis=1, keepdims=True))
             p = e / e.sum(axis=1, keepdims=True)
-            o = p @ vd[seg, kvh, :]
+            o_h = p @ vd[seg, kvh, :] if od is None else od[seg, h, :]
             do = dod[seg, h, :]
             dp = do @ vd[seg, kvh, :].T
-            ds = p * (dp - (do * o).sum(axis=1, keepdims=True))
+            row = (do * o_h).sum(axis=1, keepdims=True)
+            ds = p * (dp - row)
             dv[seg, kvh, :] += p.T @ do
             dq[seg, h, :] += c * (ds @ kd[seg, kvh, :])
             dk[seg, kvh, :] += c * (ds.T @ qd[seg, h, :])
             dbias[seg] += g[h] * ds.sum(axis=0)
             dgain[h] += (ds.sum(axis=0) * b[seg]).sum()
+            dgain_abs[h] += np.abs(ds * b[seg][None, :]).sum()
             dtau += -(1.0 / float(tau)) * (ds * qk * c).sum()
             dtau_abs += (1.0 / float(tau)) * np.abs(ds * qk * c).sum()
+            dtau_mag += (1.0 / float(tau)) * (p * (np.abs(dp) + np.abs(row)) * np.abs(qk * c)).sum()
         off += ln
-    return dict(dq=dq, dk=dk, dv=dv, dbias=dbias, dgain=dgain, dtau=dtau, dtau_abs=dtau_abs)
+    return dict(dq=dq, dk=dk, dv=dv, dbias=dbias, dgain=dgain, dtau=dtau, dtau_abs=dtau_abs,
+                dtau_mag=dtau_mag, dgain_abs=dgain_abs)
 
 
 def score_grad(dbias_kept, scores, kept, prompts: Sequence) -> np.ndarray:

@@ -116,17 +116,17 @@ def test_decode_table_and_rejects_before_launch(lib):
 def test_backward_workspace_and_rejects_before_launch(lib):
     # Workspace (fp32 words): the softmax row term [hq][M]; for each of the two
     # halves a (block, head) is split into when the items are few (here: 5 blocks
-    # x 16 heads): dK and dV partials [hq][M][D], bias partials [hq][M] and dQ
-    # partials [M][hq][D]; and one partial of sum k . dK per 256 elements of dK.
+    # x 16 heads): dK and dV partials [hq][M][D], bias partials and
+    # sum_i dS (q . k) partials [hq][M] each, and dQ partials [M][hq][D].
     prompts = [Prompt(0, 100, 0, 90, 40), Prompt(100, 70, 0, 0, 0)]  # 50 and 70 kept rows
     m, hq, hkv, d = 120, 16, 8, 128
     need = lib.tg_attention_backward_workspace_bytes(seq_array(prompts), 2, hq, hkv, d)
-    assert need == 4 * (hq * m * (1 + 2 * (3 * d + 1)) + (m * hkv * d + 255) // 256)
+    assert need == 4 * (hq * m * (1 + 2 * (3 * d + 2)))
     # Without the split (enough blocks): no dQ partials, one set of the others.
     big = [Prompt(0, 5000, 0, 0, 0)]
     mb = 5000
     need_big = lib.tg_attention_backward_workspace_bytes(seq_array(big), 1, hq, hkv, d)
-    assert need_big == 4 * (hq * mb * (1 + 2 * d + 1) + (mb * hkv * d + 255) // 256)
+    assert need_big == 4 * (hq * mb * (1 + 2 * d + 2))
     fake = ctypes.c_void_p(4096)
     args = [fake, fake, fake, fake, fake, seq_array(prompts), 2, hq, 8, d, fake, 1.2, fake, fake, fake,
             fake, fake, fake, fake, fake, fake]
@@ -257,3 +257,13 @@ def test_product_never_touches_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", src, re.M), f
                 assert "oracle" not in src or f.endswith(".py") is False or "import oracle" not in src, f
+
+
+def test_layer_rejects_host_tensors():
+    """The preallocated layer validates its inputs before touching the library:
+    host tensors are refused (there is no CPU path)."""
+    import torch
+    from learned_token_pruning_layer_amd.layer import GatedPrefillLayer
+    x = torch.zeros(8, 64)
+    with pytest.raises(ValueError):
+        GatedPrefillLayer(x, torch.zeros(4, 64), torch.zeros(4), [], [], 4, 2, 64)

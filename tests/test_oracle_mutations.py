@@ -43,8 +43,10 @@ MUTATIONS = [
      "kvh = h % hkv\n                logits"),
     ("decode: scale 1/(D tau)", "scale = 1.0 / (math.sqrt(dh) * float(tau))\n    o = np.zeros",
      "scale = 1.0 / (dh * float(tau))\n    o = np.zeros"),
-    ("backward: softmax Jacobian without its row term", "ds = p * (dp - (do * o).sum(axis=1, keepdims=True))",
-     "ds = p * dp"),
+    ("backward: softmax Jacobian without its row term", "ds = p * (dp - row)", "ds = p * dp"),
+    ("backward: row term from the exact output although one is given",
+     "o_h = p @ vd[seg, kvh, :] if od is None else od[seg, h, :]", "o_h = p @ vd[seg, kvh, :]"),
+    ("backward: given output read at the KV head", "else od[seg, h, :]", "else od[seg, kvh, :]"),
     ("backward: dk without the logit scale", "dk[seg, kvh, :] += c * (ds.T @ qd[seg, h, :])",
      "dk[seg, kvh, :] += ds.T @ qd[seg, h, :]"),
     ("backward: bias gradient without the gain", "dbias[seg] += g[h] * ds.sum(axis=0)", "dbias[seg] += ds.sum(axis=0)"),

@@ -439,6 +439,39 @@ def test_attention_backward_invariants():
     np.testing.assert_allclose(gr["dv"][i, 0], do[i, 0] + do[i, 1], rtol=1e-14)
 
 
+def test_attention_backward_given_forward_output():
+    """The row term taken from a given forward output o: the exact output (from the
+    pinned forward) reproduces the default gradients; a change of o orthogonal to
+    d_out changes nothing; a change beta_i d_out_i / |d_out_i|^2 moves each row term
+    do_i . o_i by beta_i, so sum_j ds_ij = -beta_i: the bias gradient of each segment
+    sums to -sum_h g_h sum_i beta_ih, and dv (no row term) stays as it was."""
+    seg, hq, hkv, d, tau = [11, 6], 4, 2, 8, 0.9
+    q, k, v, b, pos, g, do = _bwd_case(57, seg, hq, hkv, d)
+    o_exact, _ = oracle.gated_attention(q, k, v, b, pos, seg, hq, hkv, g, tau)
+    ref = oracle.gated_attention_backward(q, k, v, b, pos, seg, hq, hkv, g, tau, do)
+    same = oracle.gated_attention_backward(q, k, v, b, pos, seg, hq, hkv, g, tau, do, o=o_exact)
+    for key in ("dq", "dk", "dv", "dbias", "dgain", "dtau"):
+        np.testing.assert_allclose(same[key], ref[key], rtol=1e-10, atol=1e-13, err_msg=key)
+    rng = np.random.default_rng(5)
+    w = rng.standard_normal(do.shape)
+    w -= ((w * do).sum(-1, keepdims=True) / (do * do).sum(-1, keepdims=True)) * do
+    orth = oracle.gated_attention_backward(q, k, v, b, pos, seg, hq, hkv, g, tau, do, o=o_exact + w)
+    for key in ("dq", "dk", "dv", "dbias", "dgain", "dtau"):
+        np.testing.assert_allclose(orth[key], ref[key], rtol=1e-10, atol=1e-12, err_msg=key)
+    beta = rng.standard_normal(do.shape[:2])
+    shift = o_exact + beta[..., None] * do / (do * do).sum(-1, keepdims=True)
+    sh = oracle.gated_attention_backward(q, k, v, b, pos, seg, hq, hkv, g, tau, do, o=shift)
+    np.testing.assert_allclose(sh["dv"], ref["dv"], rtol=1e-12, atol=1e-14)
+    off = 0
+    for ln in seg:
+        want = -(g[None, :] * beta[off:off + ln]).sum()
+        assert abs(sh["dbias"][off:off + ln].sum() - want) < 1e-10 * max(1.0, abs(want))
+        off += ln
+    # the magnitudes returned for tolerances bound the sums they describe
+    assert abs(ref["dtau"]) <= ref["dtau_abs"] <= ref["dtau_mag"] * (1 + 1e-12)
+    assert np.all(np.abs(ref["dgain"]) <= ref["dgain_abs"] * (1 + 1e-12))
+
+
 def test_score_grad_chain():
     """d(score) = d(bias) * d logsigmoid(s)/ds for kept document rows (central
     differences of the pinned logsigmoid), 0 for question and pruned rows."""
