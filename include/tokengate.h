@@ -43,7 +43,9 @@
  *  - The library allocates nothing and keeps no state other than a
  *    thread-local error string. Scratch memory, where a call needs any, is a
  *    caller-provided device workspace whose size the matching
- *    *_workspace_bytes function returns.
+ *    *_workspace_bytes function returns. The one exception is
+ *    tg_decode_attention_noalloc, whose scratch is a static device array
+ *    (see there).
  *  - Every call validates its arguments on the host first. A status other
  *    than TG_OK means nothing was enqueued; tg_last_error() gives details.
  *    A failed launch returns TG_ERR_HIP. Faults inside a kernel surface at the
@@ -384,6 +386,28 @@ tg_status tg_decode_attention(tg_dtype dt, const void* q_new, const void* k, con
                               int32_t n_seqs, int32_t hq, int32_t hkv, int32_t head_dim,
                               const float* gain, float tau, void* out, float* lse, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of the static per-device scratch behind tg_decode_attention_noalloc. */
+#define TG_DECODE_SCRATCH_BYTES (16u << 20)
+
+/* tg_decode_attention without a workspace argument and without any device
+ * allocation, for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same inputs,
+ * outputs, validation and kernels as tg_decode_attention; the split-KV
+ * partials go to a static scratch array of TG_DECODE_SCRATCH_BYTES bytes that
+ * the library holds on each GPU it runs on until the process ends (its
+ * device address is looked up on the first call on each device; that first
+ * call must therefore not be made under graph capture). A call whose
+ * partials need more than that (tg_decode_workspace_bytes > 16 MiB, e.g. more
+ * than ~8000 (split, KV head) pairs at 8 query slots) is refused with
+ * TG_ERR_WORKSPACE before anything is enqueued. Every call on one GPU shares
+ * that GPU's scratch, whose contents are scratch after each call: calls that
+ * overlap on one GPU (two streams, two host threads) race and give undefined
+ * results; serialise them, or use tg_decode_attention with a workspace each. */
+tg_status tg_decode_attention_noalloc(tg_dtype dt, const void* q_new, const void* k, const void* v,
+                                      const float* bias, const int32_t* pos, const tg_kv_seq* seqs, int32_t n_seqs,
+                                      int32_t hq, int32_t hkv, int32_t head_dim, const float* gain, float tau,
+                                      void* out, float* lse, hipStream_t stream);
 
 /* Static text of a status code. */
 const char* tg_status_string(tg_status status);

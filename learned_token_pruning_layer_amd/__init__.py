@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     kv_seq_array,
     tg_compact,
     tg_decode_attention,
+    tg_decode_attention_noalloc,
     tg_dense_layer,
     tg_gate_backward,
     tg_gate_score,

@@ -28,7 +28,8 @@ EXPORTED = (
     "tg_attention_workspace_bytes", "tg_gated_attention", "tg_decode_workspace_bytes", "tg_decode_attention",
     "tg_attention_backward_workspace_bytes", "tg_gated_attention_backward", "tg_score_grad",
     "tg_gate_backward_workspace_bytes", "tg_gate_backward", "tg_linear", "tg_dense_layer_workspace_bytes",
-    "tg_dense_layer", "tg_delta_scan_workspace_bytes", "tg_gated_delta_scan", "tg_status_string", "tg_last_error",
+    "tg_dense_layer", "tg_delta_scan_workspace_bytes", "tg_gated_delta_scan", "tg_decode_attention_noalloc",
+    "tg_status_string", "tg_last_error",
 )
 
 
@@ -119,6 +120,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tg_decode_attention.argtypes = [c_int, vp, vp, vp, vp, vp, kvp, i32, i32, i32, i32, vp, f32,
                                         vp, vp, vp, ctypes.c_size_t, vp]
     lib.tg_decode_attention.restype = c_int
+    lib.tg_decode_attention_noalloc.argtypes = [c_int, vp, vp, vp, vp, vp, kvp, i32, i32, i32, i32, vp, f32, vp, vp,
+                                                vp]
+    lib.tg_decode_attention_noalloc.restype = c_int
     lib.tg_status_string.argtypes = [c_int]
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_last_error.argtypes = []
@@ -333,6 +337,35 @@ def tg_decode_attention(q_new: torch.Tensor, k: torch.Tensor, v: torch.Tensor, b
                                    bias.data_ptr(), pos.data_ptr(), sa, len(seqs), hq, hkv, dh, gain.data_ptr(),
                                    float(tau), out.data_ptr(), _ptr(lse if want_lse else None), _ptr(workspace),
                                    ws_have, _stream(stream)))
+    return out, (lse if want_lse else None)
+
+
+def tg_decode_attention_noalloc(q_new: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias: torch.Tensor,
+                                pos: torch.Tensor, seqs: Sequence, gain: torch.Tensor, tau: float,
+                                out: Optional[torch.Tensor] = None, want_lse: bool = False,
+                                lse: Optional[torch.Tensor] = None,
+                                stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """tg_decode_attention with the library's static scratch instead of a workspace
+    (nothing is allocated by the call; outputs are allocated here only if not given)."""
+    lib = load()
+    for t, nm in ((q_new, "q_new"), (k, "k"), (v, "v"), (bias, "bias"), (pos, "pos"), (gain, "gain")):
+        _dev(t, nm)
+    r, hq, dh = q_new.shape
+    hkv = k.shape[1]
+    if k.dim() != 3 or k.shape[2] != dh or v.shape != k.shape:
+        raise ValueError("k and v must be [rows, hkv, D] matching q_new")
+    if k.dtype != q_new.dtype or v.dtype != q_new.dtype:
+        raise ValueError("q_new, k, v must share a dtype")
+    if bias.dtype != torch.float32 or pos.dtype != torch.int32 or gain.dtype != torch.float32:
+        raise ValueError("bias fp32, pos int32, gain fp32 expected")
+    if out is None:
+        out = torch.empty_like(q_new)
+    if want_lse and lse is None:
+        lse = torch.empty((hq, r), dtype=torch.float32, device=q_new.device)
+    _check(lib.tg_decode_attention_noalloc(_dtype_code(q_new), q_new.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                           bias.data_ptr(), pos.data_ptr(), kv_seq_array(seqs), len(seqs), hq, hkv,
+                                           dh, gain.data_ptr(), float(tau), out.data_ptr(),
+                                           _ptr(lse if want_lse else None), _stream(stream)))
     return out, (lse if want_lse else None)
 
 

@@ -619,10 +619,16 @@ size_t tg_decode_workspace_bytes(const tg_kv_seq* seqs, int32_t n_seqs, int32_t 
     return ws > ws32 ? ws : ws32;  // enough for either dtype
 }
 
-tg_status tg_decode_attention(tg_dtype dt, const void* q_new, const void* k, const void* v, const float* bias,
-                              const int32_t* pos, const tg_kv_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv,
-                              int32_t head_dim, const float* gain, float tau, void* out, float* lse,
-                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by both decode entry points. workspace == nullptr with use_static
+// selects the library's static per-device scratch.
+tg_status decode_common(tg_dtype dt, const void* q_new, const void* k, const void* v, const float* bias,
+                        const int32_t* pos, const tg_kv_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv,
+                        int32_t head_dim, const float* gain, float tau, void* out, float* lse, void* workspace,
+                        size_t workspace_bytes, bool use_static, hipStream_t stream) {
     g_err.clear();
     if (!(tau > 0.0f) || tau != tau || tau > 3.0e38f)
         return fail(TG_ERR_INVALID_ARGUMENT, "tau must be finite and > 0");
@@ -636,14 +642,42 @@ tg_status tg_decode_attention(tg_dtype dt, const void* q_new, const void* k, con
         return fail(TG_ERR_INVALID_ARGUMENT, "q_new, k, v, bias, pos, gain, out must be non-NULL");
     if (!(aligned16(q_new) && aligned16(k) && aligned16(v)))
         return fail(TG_ERR_UNSUPPORTED, "q_new, k, v must be 16-byte aligned");
-    if (!workspace || workspace_bytes < need)
-        return fail(TG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
-                    need);
-    if ((uintptr_t)workspace % 4 != 0) return fail(TG_ERR_INVALID_ARGUMENT, "workspace not 4-byte aligned");
+    if (use_static) {
+        if (need > (size_t)TG_DECODE_SCRATCH_BYTES)
+            return fail(TG_ERR_WORKSPACE, "this call needs %zu bytes of scratch, the static scratch holds %zu; "
+                        "use tg_decode_attention with a workspace", need, (size_t)TG_DECODE_SCRATCH_BYTES);
+        hipError_t e = tg::decode_scratch(&workspace);
+        if (e != hipSuccess) return hip_fail(e, "tg_decode_attention_noalloc scratch address");
+    } else {
+        if (!workspace || workspace_bytes < need)
+            return fail(TG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                        need);
+        if ((uintptr_t)workspace % 4 != 0) return fail(TG_ERR_INVALID_ARGUMENT, "workspace not 4-byte aligned");
+    }
     hipError_t e = tg::launch_decode(dt, q_new, k, v, bias, pos, t, hq, hkv, head_dim, gain, tau, out, lse, r_total,
                                      workspace, stream);
     if (e != hipSuccess) return hip_fail(e, "tg_decode_attention launch");
     return TG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tg_status tg_decode_attention(tg_dtype dt, const void* q_new, const void* k, const void* v, const float* bias,
+                              const int32_t* pos, const tg_kv_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv,
+                              int32_t head_dim, const float* gain, float tau, void* out, float* lse,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return decode_common(dt, q_new, k, v, bias, pos, seqs, n_seqs, hq, hkv, head_dim, gain, tau, out, lse, workspace,
+                         workspace_bytes, false, stream);
+}
+
+tg_status tg_decode_attention_noalloc(tg_dtype dt, const void* q_new, const void* k, const void* v,
+                                      const float* bias, const int32_t* pos, const tg_kv_seq* seqs, int32_t n_seqs,
+                                      int32_t hq, int32_t hkv, int32_t head_dim, const float* gain, float tau,
+                                      void* out, float* lse, hipStream_t stream) {
+    return decode_common(dt, q_new, k, v, bias, pos, seqs, n_seqs, hq, hkv, head_dim, gain, tau, out, lse, nullptr, 0,
+                         true, stream);
 }
 
 }  // extern "C"

@@ -31,6 +31,9 @@
 #include "tg_internal.hpp"
 #include "tg_device.hpp"
 
+#include <atomic>
+#include <mutex>
+
 namespace tg {
 namespace {
 
@@ -345,6 +348,40 @@ hipError_t launch_decode_d(int nq, const void* q, const void* k, const void* v, 
 }  // namespace
 
 int decode_query_slots(int nq) { return nq <= 1 ? 1 : nq <= 2 ? 2 : nq <= 4 ? 4 : nq <= 8 ? 8 : 0; }
+
+// Scratch of the allocation-free decode entry point: the split-KV partials
+// live in this file-scope device array instead of a caller workspace. Each
+// GPU the library runs on holds its own copy until the process ends. Host
+// code never uses the array's name as an address (on the host it is only a
+// stand-in for the symbol): the device address is looked up once per device
+// with hipGetSymbolAddress, with that device current, and cached here.
+static __device__ __align__(256) unsigned char scratch[TG_DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::atomic<void*> g_scratch_ptr[SCRATCH_MAX_DEVICES];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 hipError_t launch_decode(tg_dtype dt, const void* q, const void* k, const void* v, const float* bias,
                          const int32_t* pos, const DecTable& t, int hq, int hkv, int head_dim, const float* gain,

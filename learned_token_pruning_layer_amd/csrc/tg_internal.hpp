@@ -115,6 +115,9 @@ int decode_query_slots(int nq);
 hipError_t launch_decode(tg_dtype dt, const void* q, const void* k, const void* v, const float* bias,
                          const int32_t* pos, const DecTable& t, int hq, int hkv, int head_dim, const float* gain,
                          float tau, void* out, float* lse, int64_t r_total, void* ws, hipStream_t st);
+// Device address of this device's static decode scratch (TG_DECODE_SCRATCH_BYTES
+// bytes), looked up on the first call on each device.
+hipError_t decode_scratch(void** ptr);
 
 // Backward of token-gated attention (bf16 inputs, fp32 gradients).
 struct AttnBwdArgs {

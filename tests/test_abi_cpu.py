@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(tg.EXPORTED)
@@ -267,3 +267,21 @@ def test_layer_rejects_host_tensors():
     x = torch.zeros(8, 64)
     with pytest.raises(ValueError):
         GatedPrefillLayer(x, torch.zeros(4, 64), torch.zeros(4), [], [], 4, 2, 64)
+
+
+def test_noalloc_decode_refuses_beyond_its_scratch(lib):
+    """The allocation-free decode call checks its static scratch's size on the host,
+    before any HIP call: more partials than TG_DECODE_SCRATCH_BYTES hold is refused."""
+    from learned_token_pruning_layer_amd._lib import kv_seq_array
+    segs = [(i << 20, 1 << 20, 4) for i in range(64)]  # 64 caches of 2^20 rows, 8 query slots
+    sa = kv_seq_array(segs)
+    need = lib.tg_decode_workspace_bytes(sa, len(segs), 16, 8, 128)
+    assert need > (16 << 20)
+    fake = ctypes.c_void_p(4096)
+    st = lib.tg_decode_attention_noalloc(1, fake, fake, fake, fake, fake, sa, len(segs), 16, 8, 128, fake, 1.2, fake,
+                                         None, None)
+    assert st == 3
+    assert b"static scratch" in lib.tg_last_error()
+    # an invalid table is still reported as such first
+    assert lib.tg_decode_attention_noalloc(1, fake, fake, fake, fake, fake, kv_seq_array([(0, 3, 4)]), 1, 16, 8, 128,
+                                           fake, 1.0, fake, None, None) == 1
