@@ -228,13 +228,16 @@ tg_status tg_gated_attention(tg_dtype dt, const void* q, const void* k, const vo
         return fail(TG_ERR_INVALID_ARGUMENT, "q, k, v, bias_kept, pos_kept, gain, out must be non-NULL");
     if (dt == TG_BF16 && !(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out)))
         return fail(TG_ERR_UNSUPPORTED, "bf16 q, k, v, out must be 16-byte aligned");
-    const int bm = tg::attention_block_rows(dt, hq, hkv);
-    const int hw = tg::attention_heads_per_item(dt, hq, hkv);
-    const int64_t items_per_blk = hq / hw;
+    int64_t max_rows = 0;
+    for (int b = 0; b < n_seqs; ++b) max_rows = st_.s[b].n_kept > max_rows ? st_.s[b].n_kept : max_rows;
+    const tg::AttnConfig cfg = tg::attention_config(dt, hq, hkv, max_rows);
+    const int bm = cfg.block_rows;
+    const int64_t items_per_blk = hq / cfg.heads_per_item;
     tg::AttnTable t;
     memset(&t, 0, sizeof t);
     t.n_seg = n_seqs;
     t.m_total = m;
+    t.cfg = cfg.kind;
     int64_t items = 0;
     for (int b = 0; b < n_seqs; ++b) {
         const tg::SeqDesc& d = st_.s[b];

@@ -9,10 +9,11 @@
 //     logit_ij = q_i.k_j / (sqrt(D) tau) + gain[h] * bias[j],  pos_j <= pos_i.
 //
 // bf16 path (flash-attention style, online softmax, v_mfma_f32_32x32x16_bf16):
-//  * A workgroup is 4 waves; each wave owns 32 query rows of one query head.
-//    The 4 waves of a workgroup share one KV head (GQA): with G = Hq/Hkv
-//    query heads per KV head, a workgroup holds gcd(G,4) heads x (4/gcd)
-//    32-row slabs, so each K/V tile staged in LDS feeds 4 waves.
+//  * Each wave owns 32 query rows of one query head. A workgroup holds the
+//    query heads of one KV head that share its K/V (GQA; 2 when Hq/Hkv is
+//    even), times query slabs, times key splits; two shapes (see
+//    attention_config): short prompts take 32 rows x 2 key splits, long
+//    prompts 2 slabs of 32 rows sharing every K/V tile with one split.
 //  * S^T = K Q^T: K (keys x d) is the A operand read from LDS, Q^T the B
 //    operand kept in registers for the whole key loop. The 32x32 result
 //    layout puts one query column in each lane (keys down its registers),
@@ -20,11 +21,12 @@
 //    lanes l and l^32.
 //  * O^T += V^T P^T: the lane's own S^T registers, rounded to bf16, are
 //    exactly the B operand once keys are taken in the order
-//    16s + 8(e/4) + 4(l/32) + e%4. V is written to LDS transposed with the
-//    same key order (bits 2 and 3 of the key index swapped), so each A
-//    operand is one 16-byte LDS read.
-//  * Logits are built in the exp2 domain with one FMA per element:
-//    x = acc * (log2 e / (sqrt(D) tau)) + gain[h] log2 e * bias[j].
+//    16s + 8(e/4) + 4(l/32) + e%4; V^T operands come from transposing LDS
+//    reads (ds_read_b64_tr_b16) of row-major V tiles.
+//  * Logits are built in the exp2 domain: the S^T accumulators start from
+//    the key's bias term gain[h] * bias[j] / scale (read from LDS into the
+//    accumulator registers), and each element takes one FMA with the scale
+//    log2 e / (sqrt(D) tau) and the running max before exp2.
 //  * Causality compares original positions element-wise (exact for any
 //    non-decreasing positions, repeats included); key tiles past the
 //    workgroup's last visible key are skipped, and waves whose queries
@@ -104,21 +106,25 @@ __device__ __forceinline__ int swz_k(int row) { return CH == 16 ? (row & 15) : (
 template <int CH>
 __device__ __forceinline__ int swz_v(int row) { return CH == 16 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
 
-// Workgroup = HW query heads of one KV head x SPL key splits, 32 query rows.
-// Wave w: head slot w % HW, split w / HW; split p owns key tiles kt = SPL*i + p.
-// K and V tiles (64 keys x D) stream straight from global memory into LDS
-// (global_load_lds, 16 bytes per lane, no staging registers) through a
-// two-stage ring; 16-byte chunk c of key row r is stored at position
-// c ^ swz(r), which keeps both the K operand reads (ds_read_b128) and the
-// V^T operand reads (ds_read_b64_tr_b16) free of bank conflicts. The
-// splits' (max, sum, O) are merged through LDS at the end, in split order.
-template <int D, int HW, int BN, int SPL>
-__global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_kernel(
+// Workgroup = HW query heads of one KV head x QS slabs of 32 query rows x SPL
+// key splits; each wave owns 32 query rows of one head. Wave w: head slot
+// w % HW, slab (w / HW) % QS, split w / (HW QS); split p owns key tiles
+// kt = SPL*i + p. Every K/V tile staged in LDS feeds the HW x QS waves of its
+// split. K and V tiles (32 keys x D) stream straight from global memory into
+// LDS (global_load_lds, 16 bytes per lane, no staging registers) through an
+// NSTG-stage ring filled NSTG-1 tiles ahead; 16-byte chunk c of key row r is
+// stored at position c ^ swz(r), which keeps both the K operand reads
+// (ds_read_b128) and the V^T operand reads (ds_read_b64_tr_b16) free of
+// bank conflicts. The splits' (max, sum, O) are merged through LDS at the
+// end, in split order.
+template <int D, int HW, int QS, int SPL, int NSTG, int OCC>
+__global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ bias, const int32_t* __restrict__ pos, AttnTable t, int hq, int hkv,
     const float* __restrict__ gain, float qk_scale, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
-    constexpr int NW = HW * SPL;                  // waves
+    constexpr int BN = 32;                        // keys per tile
+    constexpr int NW = HW * QS * SPL;             // waves
     constexpr int ROWB = D * 2;                   // bytes per K/V row
     constexpr int CH = ROWB / 16;                 // 16-byte chunks per row
     constexpr int TILEB = BN * ROWB;              // bytes per K or V tile
@@ -126,18 +132,22 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
     constexpr int IPT = TILEB / 1024;             // load instructions per tile
     constexpr int NTL = 2 * SPL;                  // K and V tiles per stage
     constexpr int TPW = NTL * IPT / NW;           // tile load instructions per wave per stage
-    constexpr int SPW = NTL / NW;                 // small (bias/pos) loads per wave per stage
-    static_assert((NTL * IPT) % NW == 0 && NTL % NW == 0, "loads must split evenly over waves");
+    constexpr int NSM = 2 * SPL;                  // small loads per stage: bias and position per split
+    // Small loads per wave per stage: every wave issues the same number (a
+    // wave past the last small load repeats one, same data to the same place),
+    // so every wave's vmcnt bookkeeping is the same.
+    constexpr int SPW = NSM >= NW ? NSM / NW : 1;
+    constexpr int LPS = TPW + SPW;                // vector-memory instructions per wave per stage
+    static_assert((NTL * IPT) % NW == 0 && (NSM < NW || NSM % NW == 0), "loads must split evenly over waves");
+    static_assert(NSTG >= 2 && NSTG <= 4 && LPS * (NSTG - 2) < 64, "ring depth and vmcnt range");
     constexpr int KS = D / 16;                    // k-steps of q.k
     constexpr int DB = D / 32;                    // 32-wide d blocks of O
-    constexpr int KBN = BN / 32;                  // 32-key blocks per tile
     constexpr int PS = BN / 16;                   // 16-key k-steps of P.V per tile
     constexpr int SM = 64;                        // bias/pos entries per tile (one dword load)
+    constexpr int STAGEB = NTL * TILEB;
 
-    __shared__ __attribute__((aligned(1024))) char tile0[SPL][2][TILEB];  // stage 0: [split][K,V]
-    __shared__ __attribute__((aligned(1024))) char tile1[SPL][2][TILEB];  // stage 1
-    // [split][bias bits, position][key] per stage
-    __shared__ __attribute__((aligned(16))) uint32_t small0[SPL][2][SM], small1[SPL][2][SM];
+    __shared__ __attribute__((aligned(1024))) char ring[NSTG][STAGEB];   // [stage][split][K,V][tile]
+    __shared__ __attribute__((aligned(16))) uint32_t smallr[NSTG][SPL][2][SM];  // [stage][split][bias, pos][key]
     // per wave: this head's bias term of the current tile, in units of q.k
     __shared__ __attribute__((aligned(16))) float sbias[NW][BN];
 
@@ -149,7 +159,8 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
     const int G = hq / hkv;
     const int ngroups = G / HW;
     const int hl = wave % HW;
-    const int split = wave / HW;
+    const int qs = (wave / HW) % QS;
+    const int split = wave / (HW * QS);
 
     // Work item: consecutive items differ in KV head first, so with 8 KV
     // heads each XCD (items are dealt round-robin to the 8 XCDs) serves one
@@ -166,15 +177,16 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
     const int64_t off = t.s[sg].kept_off;
     const int n = t.s[sg].n;
     const int h = kvh * G + hg * HW + hl;
-    const int i0 = qb * 32;
+    const int b0 = qb * 32 * QS;                  // first row of the workgroup's block
+    const int i0 = b0 + 32 * qs;                  // first row of this wave's slab
+    const bool live = i0 < n;                     // the block's last slabs may lie past the segment
     const int q_last = min(n, i0 + 32) - 1;
-    const int n_tiles = key_tile_end<BN>(pos, off, n, q_last);
-    const int n_it = (n_tiles + SPL - 1) / SPL;
+    const int n_tiles = live ? key_tile_end<BN>(pos, off, n, q_last) : 0;
+    const int n_tiles_wg = key_tile_end<BN>(pos, off, n, min(n, b0 + 32 * QS) - 1);
+    const int n_it = (n_tiles_wg + SPL - 1) / SPL;
 
     const int qi = min(i0 + l32, n - 1);
     const int32_t my_pos = pos[off + qi];
-    const int32_t wave_pos_lo = pos[off + i0];
-    const int32_t wave_pos_hi = pos[off + q_last];
     const float c = qk_scale * LOG2E;
     // The logit in the exp2 domain is c * (q.k + gb * bias): the bias term
     // seeds the S^T accumulators, the scale c is applied inside exp2.
@@ -229,9 +241,14 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
         const uint32_t flip = (uint32_t)((kind ? swz_v<CH>(rg * RPI) : swz_k<CH>(rg * RPI)) * 16);
         voff[i] = (lo ^ flip) + (uint32_t)(rg * RPI * rowb);
     }
-    // bias/position loads: SPW per wave, small load id wave*SPW + i
+    const uint32_t ring0 = LDS_ADDR(&ring[0][0]);
+    const uint32_t small0 = LDS_ADDR(&smallr[0][0][0][0]);
+    constexpr uint32_t SMALL_STAGE = SPL * 2 * SM * 4;
     const uint32_t wave_lds = (uint32_t)(wave * TPW * 1024);
-    auto issue = [&](int it, uint32_t tl, uint32_t sm) __attribute__((always_inline)) {
+    auto issue = [&](int it) __attribute__((always_inline)) {
+        const int st = it % NSTG;
+        const uint32_t tl = ring0 + (uint32_t)st * STAGEB;
+        const uint32_t sm = small0 + (uint32_t)st * SMALL_STAGE;
         if ((SPL * it + SPL) * BN <= n) {
             const int64_t adv = (int64_t)it * step_b;
             const uint32_t ldsw = tl + wave_lds;
@@ -256,7 +273,7 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
         }
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            const int sid = wave * SPW + i;  // split sid/2, bias (even) or position (odd)
+            const int sid = (wave * SPW + i) % NSM;  // split sid/2, bias (even) or position (odd)
             const int sp_ = sid >> 1;
             const int key0 = (SPL * it + sp_) * BN;
             const int r0 = min(key0, n - 1);
@@ -268,11 +285,11 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
     };
 
     // Per-lane parts of the LDS operand addresses (stage base added per tile).
-    // K: key row l32 (+32 per 32-key block), chunk (2s + hh) ^ swz_k(row),
-    // which is the s = 0 chunk with bits flipped by 2s. V^T (transpose
-    // reads): lane L of group g = L/16 addresses key 16s + 4(g/2) + (L%16)/4
-    // (+8 for the upper four slots) at d = 32b + 16(g%2) + 4(L%4); the
-    // swizzled chunk of d-block b is the b = 0 chunk with bits flipped by 4b.
+    // K: key row l32, chunk (2s + hh) ^ swz_k(row), which is the s = 0 chunk
+    // with bits flipped by 2s. V^T (transpose reads): lane L of group
+    // g = L/16 addresses key 16s + 4(g/2) + (L%16)/4 (+8 for the upper four
+    // slots) at d = 32b + 16(g%2) + 4(L%4); the swizzled chunk of d-block b is
+    // the b = 0 chunk with bits flipped by 4b.
     const uint32_t k_lane = (uint32_t)(l32 * ROWB + ((hh ^ swz_k<CH>(l32)) * 16));
     uint32_t v_lane;
     {
@@ -281,6 +298,7 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
         const int keyo = 4 * (g >> 1) + (r16 >> 2);
         v_lane = (uint32_t)(keyo * ROWB + (((dsub >> 3) ^ swz_v<CH>(keyo)) * 16) + (dsub & 7) * 2);
     }
+    const uint32_t k_split = (uint32_t)(split * 2 * TILEB), v_split = (uint32_t)((split * 2 + 1) * TILEB);
 
     f32x16 acc_o[DB];
 #pragma unroll
@@ -291,50 +309,56 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
 
     // One key tile for this wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
     // Every LDS operand is read ahead of its use so that the read latency
-    // overlaps other work: the accumulator seeds and all K operands before the
-    // first q.k MFMA, the V^T operands right after the q.k MFMAs (the softmax
-    // runs while they arrive). sched_barrier keeps the compiler from sinking
-    // the reads back next to their uses.
-    auto compute = [&](int kt, const char* kt_lds, const char* vt_lds, const uint32_t (*smv)[SM])
-                       __attribute__((always_inline)) {
-        const LDS_AS float* bsv = (const LDS_AS float*)smv[0];
-        const LDS_AS int32_t* psv = (const LDS_AS int32_t*)smv[1];
-        if (kt >= n_tiles) return;  // past the block's last visible key
-        // Positions never decrease along the kept rows, so keys before the
-        // block's first query row are visible to all of its queries: only tiles
-        // reaching row i0 (the ragged end among them) are masked element-wise.
-        const bool need_mask = (kt + 1) * BN > i0;
-        // This head's bias term for the tile's keys, computed once per wave
-        // (the wave reads it back below; its LDS accesses stay in order).
-        static_assert(BN <= 64, "one lane per key");
+    // overlaps other work: the bias seed and all K operands before the first
+    // q.k MFMA, the V^T operands right after the q.k MFMAs (the softmax runs
+    // while they arrive). sched_barrier keeps the compiler from sinking the
+    // reads back next to their uses.
+    // K operands and the bias seed of the tile in stage st (this head's bias
+    // term for the tile's keys is computed once per wave and read back in the
+    // S^T register order: register j holds key 8(j/4) + 4hh + j%4).
+    auto read_k = [&](int st, bf16x8 (&kf)[KS], f32x16& seed) __attribute__((always_inline)) {
+        const LDS_AS float* bsv = (const LDS_AS float*)(uintptr_t)(small0 + (uint32_t)st * SMALL_STAGE +
+                                                                    (uint32_t)(split * 2 * SM * 4));
         if (lane < BN) sbias[wave][lane] = bsv[lane] * gb;
         // Operand addresses: XOR-swizzled chunks are one XOR away from the
-        // per-lane base. The empty asm makes the bases opaque per tile, so the
-        // compiler keeps one address register per kind instead of hoisting one
-        // per read and ring stage out of the loop.
-        uint32_t ka = LDS_ADDR(kt_lds) + k_lane, va = LDS_ADDR(vt_lds) + v_lane;
-        asm volatile("" : "+v"(ka), "+v"(va));
-        f32x16 acc_s[KBN];
-        bf16x8 kf[KBN][KS];
+        // per-lane base. The empty asm makes the base opaque per tile, so the
+        // compiler keeps one address register instead of hoisting one per
+        // read and ring stage out of the loop.
+        uint32_t ka = ring0 + (uint32_t)st * STAGEB + k_split + k_lane;
+        asm volatile("" : "+v"(ka));
 #pragma unroll
-        for (int kb = 0; kb < KBN; ++kb) {
-            // Register j of block kb holds key kb*32 + 8(j/4) + 4hh + j%4 of this lane's query.
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 bb = *(const LDS_AS f32x4*)&sbias[wave][8 * g4 + 4 * hh];
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4 bb = *(const LDS_AS f32x4*)&sbias[wave][kb * 32 + 8 * g4 + 4 * hh];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc_s[kb][4 * g4 + e] = bb[e];
-            }
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                kf[kb][s] = *(const LDS_AS bf16x8*)(uintptr_t)((ka ^ (uint32_t)(s << 5)) + kb * 32 * ROWB);
+            for (int e = 0; e < 4; ++e) seed[4 * g4 + e] = bb[e];
         }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kf[s] = *(const LDS_AS bf16x8*)(uintptr_t)(ka ^ (uint32_t)(s << 5));
+    };
+
+    // One key tile for this wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+    // Every LDS operand is read ahead of its use so that the read latency
+    // overlaps other work: the bias seed and all K operands before the first
+    // q.k MFMA, the V^T operands right after the q.k MFMAs (the softmax runs
+    // while they arrive). sched_barrier keeps the compiler from sinking the
+    // reads back next to their uses.
+    bf16x8 kf[KS];
+    f32x16 seed;
+    auto compute = [&](int kt, int st) __attribute__((always_inline)) {
+        if (kt >= n_tiles) return;  // past the slab's last visible key
+        const LDS_AS int32_t* psv = (const LDS_AS int32_t*)(uintptr_t)(small0 + (uint32_t)st * SMALL_STAGE +
+                                                                        (uint32_t)((split * 2 + 1) * SM * 4));
+        // Positions never decrease along the kept rows, so keys before the
+        // slab's first query row are visible to all of its queries: only tiles
+        // reaching row i0 (the ragged end among them) are masked element-wise.
+        const bool need_mask = (kt + 1) * BN > i0;
+        read_k(st, kf, seed);
+        uint32_t va = ring0 + (uint32_t)st * STAGEB + v_split + v_lane;
+        asm volatile("" : "+v"(va));
+        f32x16 acc_s = seed;  // the bias seed starts the accumulation
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kb = 0; kb < KBN; ++kb)
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][s], qf[s], acc_s[kb], 0, 0, 0);
+        for (int s = 0; s < KS; ++s) acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc_s, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 vf[DB][PS];
 #pragma unroll
@@ -351,24 +375,19 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
         // acc_s now holds q.k + gb * bias; the exp2-domain logit is c times it.
         if (need_mask) {
 #pragma unroll
-            for (int kb = 0; kb < KBN; ++kb) {
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int key0 = 8 * g4 + 4 * hh;
+                const i32x4 pp = *(const LDS_AS i32x4*)&psv[key0];
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int key0 = kb * 32 + 8 * g4 + 4 * hh;
-                    const i32x4 pp = *(const LDS_AS i32x4*)&psv[key0];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const bool vis = (kt * BN + key0 + e < n) & (pp[e] <= my_pos);
-                        acc_s[kb][4 * g4 + e] = vis ? acc_s[kb][4 * g4 + e] : -INFINITY;
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const bool vis = (kt * BN + key0 + e < n) & (pp[e] <= my_pos);
+                    acc_s[4 * g4 + e] = vis ? acc_s[4 * g4 + e] : -INFINITY;
                 }
             }
         }
-        float mx = -INFINITY;
+        float mx = acc_s[0];
 #pragma unroll
-        for (int kb = 0; kb < KBN; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, acc_s[kb][j]);
+        for (int j = 1; j < 16; ++j) mx = fmaxf(mx, acc_s[j]);
         {   // lanes l and l^32 hold the two halves of one query's keys
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
             mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;  // c > 0: max of the exp2-domain logits
@@ -390,16 +409,16 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
         }
         const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
         float lsum = 0.0f;
-        // P^T as B operands: k-step s uses S^T registers 8*(s%2) .. +8 of block s/2,
-        // i.e. keys 16s + 8(e/4) + 4hh + e%4 for slot e.
+        // P^T as B operands: k-step s uses S^T registers 8*s .. +8, i.e.
+        // keys 16s + 8(e/4) + 4hh + e%4 for slot e.
         bf16x8 pf[PS];
 #pragma unroll
         for (int s = 0; s < PS; ++s) {
             u32x4 w;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(acc_s[s >> 1][8 * (s & 1) + 2 * e], c, -m_use));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(acc_s[s >> 1][8 * (s & 1) + 2 * e + 1], c, -m_use));
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(acc_s[8 * s + 2 * e], c, -m_use));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(acc_s[8 * s + 2 * e + 1], c, -m_use));
                 lsum += p0 + p1;
                 w[e] = pack_bf16x2(p0, p1);
             }
@@ -412,69 +431,71 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
             for (int s = 0; s < PS; ++s) acc_o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[b][s], pf[s], acc_o[b], 0, 0, 0);
     };
 
-    // Two-stage ring, one barrier per iteration: stage it%2 holds iteration
-    // it. After the barrier of iteration it, every wave's loads of stage it
-    // have landed and every wave has finished iteration it-1, so the loads of
-    // it+1 go into the other stage before this iteration's compute.
-    const uint32_t tl0 = LDS_ADDR(&tile0[0][0][0]), tl1 = LDS_ADDR(&tile1[0][0][0]);
-    const uint32_t sm0 = LDS_ADDR(&small0[0][0][0]), sm1 = LDS_ADDR(&small1[0][0][0]);
-    issue(0, tl0, sm0);
-    for (int it = 0; it < n_it; it += 2) {
-        // ---- stage 0 ----
-        wait_vmcnt<0>();
+    // Ring with one barrier per iteration: stage it%NSTG holds iteration it.
+    // After the barrier of iteration it, every wave's loads of stage it have
+    // landed and every wave has finished iteration it-1, so the loads of
+    // iteration it+NSTG-1 go into that iteration's stage before this
+    // iteration's compute.
+#pragma unroll
+    for (int i = 0; i < NSTG - 1; ++i)
+        if (i < n_it) issue(i);
+    for (int it = 0; it < n_it; ++it) {
+        // every load of iterations <= it has landed (this wave's); the later
+        // ones issued so far (at most NSTG-2 stages) may still be in flight
+        const int later = min(n_it - 1, it + NSTG - 2) - it;
+        if constexpr (NSTG >= 4) {
+            if (later >= 2) wait_vmcnt<LPS * 2>();
+            else if (later == 1) wait_vmcnt<LPS>();
+            else wait_vmcnt<0>();
+        } else if constexpr (NSTG == 3) {
+            if (later >= 1) wait_vmcnt<LPS>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
         ring_barrier();
-        if (it + 1 < n_it) issue(it + 1, tl1, sm1);
-        compute(SPL * it + split, tile0[split][0], tile0[split][1], small0[split]);
-        if (it + 1 >= n_it) break;
-        // ---- stage 1 ----
-        wait_vmcnt<0>();
-        ring_barrier();
-        if (it + 2 < n_it) issue(it + 2, tl0, sm0);
-        compute(SPL * (it + 1) + split, tile1[split][0], tile1[split][1], small1[split]);
+        if (it + NSTG - 1 < n_it) issue(it + NSTG - 1);
+        compute(SPL * it + split, it % NSTG);
     }
     wait_vmcnt<0>();
     ring_barrier();  // the merge below reuses the ring buffers
 
     // Merge the key splits: splits 1.. hand (m, l, O) to split 0 through LDS
-    // (the ring buffers are free now); split 0 combines them in split order.
-    constexpr int PER = HW * DB * 16 * 64;            // floats of O per handing split
-    constexpr int CAP0 = SPL * 2 * TILEB / 4;         // floats in tile0
-    static_assert(PER <= CAP0, "merge buffer");
-    float* const f0 = (float*)&tile0[0][0][0];
-    float* const f1 = (float*)&tile1[0][0][0];
-    auto xo_of = [&](int q) -> float* {              // q = split - 1
-        return (q + 1) * PER <= CAP0 ? f0 + q * PER : f1 + (q - CAP0 / PER) * PER;
-    };
-    float* const xm = f1 + ((SPL - 1) - CAP0 / PER > 0 ? ((SPL - 1) - CAP0 / PER) * PER : 0);
-    // xm: [SPL-1][HW][64] max, then [SPL-1][HW][64] sum
+    // (the ring is free now); split 0 combines them in split order.
+    constexpr int NH = HW * QS;                        // waves per split
+    constexpr int PER = NH * DB * 16 * 64;             // floats of O per handing split
+    static_assert((SPL - 1) * (PER + 2 * NH * 64) * 4 <= NSTG * STAGEB, "merge buffer");
+    float* const xo = (float*)&ring[0][0];
+    float* const xm = xo + (SPL - 1) * PER;            // [SPL-1][NH][64] max, then the same for sums
+    constexpr int XL = (SPL - 1) * NH * 64;
+    const int wl = wave % NH;                          // this wave's slot within its split
     if (split > 0) {
-        float* xo = xo_of(split - 1);
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) xo[(hl * DB * 16 + b * 16 + j) * 64 + lane] = acc_o[b][j];
-        xm[((split - 1) * HW + hl) * 64 + lane] = m_run;
-        xm[((SPL - 1 + split - 1) * HW + hl) * 64 + lane] = l_run;
+            for (int j = 0; j < 16; ++j) xo[(split - 1) * PER + ((wl * DB + b) * 16 + j) * 64 + lane] = acc_o[b][j];
+        xm[((split - 1) * NH + wl) * 64 + lane] = m_run;
+        xm[XL + ((split - 1) * NH + wl) * 64 + lane] = l_run;
     }
-    __syncthreads();
+    if constexpr (SPL > 1) __syncthreads();
     if (split == 0) {
         float ms[SPL], ls[SPL];
         ms[0] = m_run;
         ls[0] = l_run;
         float m = m_run;
 #pragma unroll
-        for (int q = 1; q < SPL; ++q) {
-            ms[q] = xm[((q - 1) * HW + hl) * 64 + lane];
-            ls[q] = xm[((SPL - 1 + q - 1) * HW + hl) * 64 + lane];
-            m = fmaxf(m, ms[q]);
+        for (int q2 = 1; q2 < SPL; ++q2) {
+            ms[q2] = xm[((q2 - 1) * NH + wl) * 64 + lane];
+            ls[q2] = xm[XL + ((q2 - 1) * NH + wl) * 64 + lane];
+            m = fmaxf(m, ms[q2]);
         }
         const float mu = (m == -INFINITY) ? 0.0f : m;
         float a[SPL];
         float lt = 0.0f;
 #pragma unroll
-        for (int q = 0; q < SPL; ++q) {
-            a[q] = __builtin_amdgcn_exp2f(ms[q] - mu);
-            lt += ls[q] * a[q];
+        for (int q2 = 0; q2 < SPL; ++q2) {
+            a[q2] = __builtin_amdgcn_exp2f(ms[q2] - mu);
+            lt += ls[q2] * a[q2];
         }
         lt += __shfl_xor(lt, 32);
         const float inv = 1.0f / lt;
@@ -491,8 +512,8 @@ __global__ __launch_bounds__(64 * HW * SPL, BN == 32 ? 2 : 1) void attn_bf16_ker
                         const int j = 4 * g4 + e;
                         float acc = acc_o[b][j] * a[0];
 #pragma unroll
-                        for (int q = 1; q < SPL; ++q)
-                            acc += xo_of(q - 1)[(hl * DB * 16 + b * 16 + j) * 64 + lane] * a[q];
+                        for (int q2 = 1; q2 < SPL; ++q2)
+                            acc += xo[(q2 - 1) * PER + ((wl * DB + b) * 16 + j) * 64 + lane] * a[q2];
                         o[e] = acc * inv;
                     }
                     uint2 w;
@@ -597,25 +618,42 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 
 int heads_per_wg(int g) { return (g % 2 == 0) ? 2 : 1; }
 
-// Keys per K/V tile of the bf16 kernel.
-#ifndef ATTN_BN
-#define ATTN_BN 32
-#endif
-// Key splits per workgroup (waves = heads per workgroup x splits).
-#ifndef ATTN_SPL
-#define ATTN_SPL 2
-#endif
+// Prompts of at least this many kept rows take the long-prompt shape.
+constexpr int64_t ATTN_LONG_ROWS = 4096;
+
+// The two kernel shapes (HW heads per item in both):
+//  0 (short prompts): 32 query rows x 2 key splits, 2-stage ring, two
+//    workgroups per CU: the splits halve the serial chain of the longest
+//    query blocks, which bounds a short causal problem;
+//  1 (long prompts): 2 slabs of 32 query rows share every K/V tile (half
+//    the loaded bytes per MFMA), one key split, 3-stage ring.
+template <int D, int HW>
+void launch_cfg(int cfg, dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                const float* bias, const int32_t* pos, const AttnTable& t, int hq, int hkv, const float* gain,
+                float qk_scale, uint16_t* out, float* lse) {
+    if (cfg == 0)
+        hipLaunchKernelGGL((attn_bf16_kernel<D, HW, 1, 2, 2, 2>), grid, dim3(64 * HW * 2), 0, st, q, k, v, bias, pos,
+                           t, hq, hkv, gain, qk_scale, out, lse);
+    else
+        hipLaunchKernelGGL((attn_bf16_kernel<D, HW, 2, 1, 3, 2>), grid, dim3(64 * HW * 2), 0, st, q, k, v, bias, pos,
+                           t, hq, hkv, gain, qk_scale, out, lse);
+}
 
 }  // namespace
 
-int attention_heads_per_item(tg_dtype dt, int hq, int hkv) {
-    return dt == TG_F32 ? 1 : heads_per_wg(hq / hkv);
-}
-
-int attention_block_rows(tg_dtype dt, int hq, int hkv) {
-    (void)hq;
-    (void)hkv;
-    return dt == TG_F32 ? 64 : 32;
+AttnConfig attention_config(tg_dtype dt, int hq, int hkv, int64_t max_rows) {
+    AttnConfig c;
+    if (dt == TG_F32) {
+        c.kind = 0;
+        c.block_rows = 64;
+        c.heads_per_item = 1;
+        return c;
+    }
+    const int cfg = max_rows >= ATTN_LONG_ROWS ? 1 : 0;
+    c.kind = cfg;
+    c.block_rows = cfg == 0 ? 32 : 64;
+    c.heads_per_item = heads_per_wg(hq / hkv);
+    return c;
 }
 
 hipError_t launch_attention(tg_dtype dt, const void* q, const void* k, const void* v,
@@ -630,13 +668,13 @@ hipError_t launch_attention(tg_dtype dt, const void* q, const void* k, const voi
         const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)k, *vv = (const uint16_t*)v;
         uint16_t* oo = (uint16_t*)out;
         if (head_dim == 128 && hw == 2)
-            hipLaunchKernelGGL((attn_bf16_kernel<128, 2, ATTN_BN, ATTN_SPL>), grid, dim3(128 * ATTN_SPL), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
+            launch_cfg<128, 2>(t.cfg, grid, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
         else if (head_dim == 128)
-            hipLaunchKernelGGL((attn_bf16_kernel<128, 1, ATTN_BN, ATTN_SPL>), grid, dim3(64 * ATTN_SPL), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
+            launch_cfg<128, 1>(t.cfg, grid, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
         else if (hw == 2)
-            hipLaunchKernelGGL((attn_bf16_kernel<64, 2, ATTN_BN, ATTN_SPL>), grid, dim3(128 * ATTN_SPL), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
+            launch_cfg<64, 2>(t.cfg, grid, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
         else
-            hipLaunchKernelGGL((attn_bf16_kernel<64, 1, ATTN_BN, ATTN_SPL>), grid, dim3(64 * ATTN_SPL), 0, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
+            launch_cfg<64, 1>(t.cfg, grid, st, qq, kk, vv, bias, pos, t, hq, hkv, gain, qk_scale, oo, lse);
     } else {
         if (head_dim == 128)
             hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, st, (const float*)q,

@@ -54,8 +54,20 @@ struct AttnTable {
     int32_t n_seg;
     int32_t n_items;
     int64_t m_total;
+    int32_t cfg;   // kernel shape (attention_config().kind)
+    int32_t pad;
     AttnSeg s[TG_MAX_SEQS];
 };
+
+// Work decomposition of the attention kernel for a call: the query rows of
+// one work item and the query heads it covers (chosen from the dtype, the
+// head ratio and the longest prompt).
+struct AttnConfig {
+    int kind;            // kernel shape
+    int block_rows;      // query rows per work item
+    int heads_per_item;  // query heads per work item
+};
+AttnConfig attention_config(tg_dtype dt, int hq, int hkv, int64_t max_rows);
 
 // Launchers (each returns hipGetLastError() after its launch).
 hipError_t launch_gate_mfma_bf16(const void* x, int64_t n, int d, const void* w1, const void* b1,
@@ -163,8 +175,6 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st);
 hipError_t launch_score_grad(const float* d_bias, const float* scores, const int32_t* kept, const SeqTable& t,
                              int64_t m, int64_t n_rows, float* d_scores, hipStream_t st);
 
-// Query-row block per attention work item for a given dtype/head ratio.
-int attention_block_rows(tg_dtype dt, int hq, int hkv);
-int attention_heads_per_item(tg_dtype dt, int hq, int hkv);
+
 
 }  // namespace tg

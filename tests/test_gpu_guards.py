@@ -98,10 +98,11 @@ def test_guard_compact():
                                         bias_kept=o["bias"]), outs)
 
 
-@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
-def test_guard_attention(dt):
-    note(f"guards: token-gated attention ({dt}), output and lse")
-    segs, hq, hkv, d = [1000, 23, 1], 16, 8, 128
+@pytest.mark.parametrize("dt,segs", [(torch.bfloat16, [1000, 23, 1]), (torch.float32, [1000, 23, 1]),
+                                     (torch.bfloat16, [4200, 23, 1])], ids=["bf16-short", "fp32", "bf16-long"])
+def test_guard_attention(dt, segs):
+    note(f"guards: token-gated attention ({dt}, prompts {segs}), output and lse")
+    hq, hkv, d = 16, 8, 128
     a = make_attention_inputs(segs, hq, hkv, d, seed=3, dtype=dt, n_query_tail=8)
     prompts, st = [], 0
     for ln in segs:
