@@ -83,8 +83,9 @@ typedef enum {
 
 typedef enum { TG_F32 = 0, TG_BF16 = 1 } tg_dtype;
 
-/* Largest number of prompts one call accepts (descriptors travel as kernel
- * arguments). */
+/* Largest number of prompts one prefill call accepts (descriptors travel as
+ * kernel arguments). Decode calls take up to 2^20 sequences, run in launches
+ * of TG_MAX_SEQS sequences each. */
 #define TG_MAX_SEQS 64
 /* Largest number of tensors one tg_compact call gathers. */
 #define TG_MAX_GATHERS 16
@@ -171,10 +172,6 @@ tg_status tg_compact(const int32_t* kept_idx, int64_t m_rows, const tg_seq* seqs
                      const int32_t* pos, int32_t* pos_kept, const float* scores,
                      float* bias_kept, hipStream_t stream);
 
-/* Device workspace tg_gated_attention needs, in bytes (0 means none). */
-size_t tg_attention_workspace_bytes(const tg_seq* seqs, int32_t n_seqs, int32_t hq,
-                                    int32_t hkv, int32_t head_dim);
-
 /* Step 4 - token-gated attention over the kept rows. q [M, hq, head_dim],
  * k and v [M, hkv, head_dim], out [M, hq, head_dim] (all contiguous, dtype
  * dt, M = tg_kept_rows(seqs)); bias_kept fp32 [M]; pos_kept int32 [M],
@@ -185,7 +182,9 @@ size_t tg_attention_workspace_bytes(const tg_seq* seqs, int32_t n_seqs, int32_t 
  *     logit_ij = q_i . k_j / (sqrt(head_dim) * tau) + gain[h] * bias_kept[j]
  * over the keys with pos_kept[j] <= pos_kept[i], softmax, times V.
  * lse (nullable) fp32 [hq, M] receives log sum_j exp(logit_ij). bf16 runs on
- * MFMA with fp32 softmax and accumulation; fp32 runs on plain FMA.
+ * MFMA with fp32 softmax and accumulation; fp32 runs on plain FMA. Needs no
+ * workspace. Positions that decrease inside a prompt break the contract and
+ * give wrong outputs with TG_OK; tg_check_positions tests a pos_kept array.
  * head_dim in {64, 128}; hq % hkv == 0. Sources: section "Was ist
  * token-gated Attention?" (kept-token score as a bias on the attention
  * logits above the gate, per-head gain, temperature) and "Wie wird TokenGate
@@ -194,8 +193,7 @@ tg_status tg_gated_attention(tg_dtype dt, const void* q, const void* k, const vo
                              const float* bias_kept, const int32_t* pos_kept,
                              const tg_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv,
                              int32_t head_dim, const float* gain, float tau, void* out,
-                             float* lse, void* workspace, size_t workspace_bytes,
-                             hipStream_t stream);
+                             float* lse, hipStream_t stream);
 
 /* Device workspace tg_gated_attention_backward needs, in bytes (0 for an
  * invalid table, which the call then reports). */
@@ -373,7 +371,8 @@ size_t tg_decode_workspace_bytes(const tg_kv_seq* seqs, int32_t n_seqs, int32_t 
  * out [R, hq, head_dim] (all contiguous, dtype dt; q_new, k, v 16-byte
  * aligned); bias fp32 and pos int32 per cache row; gain fp32 [hq] (device);
  * tau > 0; lse (nullable) fp32 [hq, R]. (hq / hkv) * n_new <= 8 per
- * sequence; head_dim in {64, 128}. Workspace: device memory of at least
+ * sequence; head_dim in {64, 128}; up to 2^20 sequences (run in launches of
+ * TG_MAX_SEQS sequences, in stream order, sharing the workspace). Workspace: device memory of at least
  * tg_decode_workspace_bytes bytes, 4-byte aligned, owned by the caller
  * (scratch; two calls in flight need two). Deterministic: the key splits
  * are fixed by the table and merged in key order. Sources: section "Wie hat
@@ -408,6 +407,18 @@ tg_status tg_decode_attention_noalloc(tg_dtype dt, const void* q_new, const void
                                       const float* bias, const int32_t* pos, const tg_kv_seq* seqs, int32_t n_seqs,
                                       int32_t hq, int32_t hkv, int32_t head_dim, const float* gain, float tau,
                                       void* out, float* lse, hipStream_t stream);
+
+/* Checks the original positions of kept rows (tg_compact's output, or a
+ * caller's own) for the order tg_gated_attention, its backward and
+ * tg_dense_layer rely on: non-decreasing within each prompt. Writes to
+ * *n_bad (device int32) the number of kept rows whose position is below the
+ * previous kept row's in the same prompt; 0 means the positions are valid.
+ * pos_kept int32 [M], M = tg_kept_rows(seqs). A check for debugging and
+ * checked modes: the attention calls themselves do not run it. Source:
+ * causality by original position (the pruned rows keep their original
+ * positions; section "Wie hat TokenGate das Pruning von Tokens verstanden?"). */
+tg_status tg_check_positions(const int32_t* pos_kept, const tg_seq* seqs, int32_t n_seqs, int32_t* n_bad,
+                             hipStream_t stream);
 
 /* Static text of a status code. */
 const char* tg_status_string(tg_status status);

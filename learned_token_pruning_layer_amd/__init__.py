@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     load,
     seq_array,
     kv_seq_array,
+    tg_check_positions,
     tg_compact,
     tg_decode_attention,
     tg_decode_attention_noalloc,

@@ -25,11 +25,11 @@ TG_MAX_GATHERS = 16
 
 EXPORTED = (
     "tg_kept_rows", "tg_gate_score", "tg_select_workspace_bytes", "tg_select_topk", "tg_compact",
-    "tg_attention_workspace_bytes", "tg_gated_attention", "tg_decode_workspace_bytes", "tg_decode_attention",
+    "tg_gated_attention", "tg_decode_workspace_bytes", "tg_decode_attention",
     "tg_attention_backward_workspace_bytes", "tg_gated_attention_backward", "tg_score_grad",
     "tg_gate_backward_workspace_bytes", "tg_gate_backward", "tg_linear", "tg_dense_layer_workspace_bytes",
     "tg_dense_layer", "tg_delta_scan_workspace_bytes", "tg_gated_delta_scan", "tg_decode_attention_noalloc",
-    "tg_status_string", "tg_last_error",
+    "tg_check_positions", "tg_status_string", "tg_last_error",
 )
 
 
@@ -85,10 +85,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tg_select_topk.restype = c_int
     lib.tg_compact.argtypes = [vp, i64, seqp, i32, ctypes.POINTER(TgGather), i32, vp, vp, vp, vp, vp]
     lib.tg_compact.restype = c_int
-    lib.tg_attention_workspace_bytes.argtypes = [seqp, i32, i32, i32, i32]
-    lib.tg_attention_workspace_bytes.restype = ctypes.c_size_t
     lib.tg_gated_attention.argtypes = [c_int, vp, vp, vp, vp, vp, seqp, i32, i32, i32, i32, vp, f32,
-                                       vp, vp, vp, ctypes.c_size_t, vp]
+                                       vp, vp, vp]
     lib.tg_gated_attention.restype = c_int
     lib.tg_attention_backward_workspace_bytes.argtypes = [seqp, i32, i32, i32, i32]
     lib.tg_attention_backward_workspace_bytes.restype = ctypes.c_size_t
@@ -123,6 +121,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tg_decode_attention_noalloc.argtypes = [c_int, vp, vp, vp, vp, vp, kvp, i32, i32, i32, i32, vp, f32, vp, vp,
                                                 vp]
     lib.tg_decode_attention_noalloc.restype = c_int
+    lib.tg_check_positions.argtypes = [vp, seqp, i32, vp, vp]
+    lib.tg_check_positions.restype = c_int
     lib.tg_status_string.argtypes = [c_int]
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_last_error.argtypes = []
@@ -263,7 +263,7 @@ def tg_compact(kept_idx: torch.Tensor, seqs: Sequence, tensors: Sequence[torch.T
 def tg_gated_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias_kept: torch.Tensor,
                        pos_kept: torch.Tensor, seqs: Sequence, gain: torch.Tensor, tau: float,
                        out: Optional[torch.Tensor] = None, want_lse: bool = False,
-                       lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None,
                        stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Token-gated causal attention over the kept rows.
 
@@ -284,13 +284,9 @@ def tg_gated_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias_k
     if want_lse and lse is None:
         lse = torch.empty((hq, m), dtype=torch.float32, device=q.device)
     sa = seq_array(seqs)
-    ws_bytes = lib.tg_attention_workspace_bytes(sa, len(seqs), hq, hkv, dh)
-    if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     _check(lib.tg_gated_attention(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), bias_kept.data_ptr(),
                                   pos_kept.data_ptr(), sa, len(seqs), hq, hkv, dh, gain.data_ptr(), float(tau),
-                                  out.data_ptr(), _ptr(lse if want_lse else None), _ptr(workspace),
-                                  ws_bytes if workspace is not None else 0, _stream(stream)))
+                                  out.data_ptr(), _ptr(lse if want_lse else None), _stream(stream)))
     return out, (lse if want_lse else None)
 
 
@@ -367,6 +363,20 @@ def tg_decode_attention_noalloc(q_new: torch.Tensor, k: torch.Tensor, v: torch.T
                                            dh, gain.data_ptr(), float(tau), out.data_ptr(),
                                            _ptr(lse if want_lse else None), _stream(stream)))
     return out, (lse if want_lse else None)
+
+
+def tg_check_positions(pos_kept: torch.Tensor, seqs: Sequence, n_bad: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Number of kept rows (int32 [1] on the device) whose position is below the
+    previous kept row's in the same prompt; 0 means the order the attention relies on holds."""
+    lib = load()
+    _dev(pos_kept, "pos_kept")
+    if pos_kept.dtype != torch.int32:
+        raise ValueError("pos_kept must be int32")
+    if n_bad is None:
+        n_bad = torch.empty(1, dtype=torch.int32, device=pos_kept.device)
+    _check(lib.tg_check_positions(pos_kept.data_ptr(), seq_array(seqs), len(seqs), n_bad.data_ptr(), _stream(stream)))
+    return n_bad
 
 
 def tg_gated_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias_kept: torch.Tensor,

@@ -89,6 +89,20 @@ const char* tg_status_string(tg_status st) {
 
 const char* tg_last_error(void) { return g_err.c_str(); }
 
+tg_status tg_check_positions(const int32_t* pos_kept, const tg_seq* seqs, int32_t n_seqs, int32_t* n_bad,
+                             hipStream_t stream) {
+    g_err.clear();
+    tg::SeqTable t;
+    int64_t m = 0;
+    tg_status st = build_seq_table(seqs, n_seqs, &t, &m);
+    if (st != TG_OK) return st;
+    if (!n_bad) return fail(TG_ERR_INVALID_ARGUMENT, "n_bad is NULL");
+    if (m > 0 && !pos_kept) return fail(TG_ERR_INVALID_ARGUMENT, "pos_kept is NULL");
+    hipError_t e = tg::launch_check_positions(pos_kept, m, t, n_bad, stream);
+    if (e != hipSuccess) return hip_fail(e, "tg_check_positions launch");
+    return TG_OK;
+}
+
 int64_t tg_kept_rows(const tg_seq* seqs, int32_t n_seqs) {
     tg::SeqTable t;
     int64_t m = 0;
@@ -194,24 +208,11 @@ tg_status tg_compact(const int32_t* kept_idx, int64_t m_rows, const tg_seq* seqs
     return TG_OK;
 }
 
-size_t tg_attention_workspace_bytes(const tg_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv,
-                                    int32_t head_dim) {
-    (void)seqs;
-    (void)n_seqs;
-    (void)hq;
-    (void)hkv;
-    (void)head_dim;
-    return 0;
-}
-
 tg_status tg_gated_attention(tg_dtype dt, const void* q, const void* k, const void* v,
                              const float* bias_kept, const int32_t* pos_kept, const tg_seq* seqs,
                              int32_t n_seqs, int32_t hq, int32_t hkv, int32_t head_dim,
-                             const float* gain, float tau, void* out, float* lse, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+                             const float* gain, float tau, void* out, float* lse, hipStream_t stream) {
     g_err.clear();
-    (void)workspace;
-    (void)workspace_bytes;
     if (dt != TG_F32 && dt != TG_BF16) return fail(TG_ERR_INVALID_ARGUMENT, "dtype %d unknown", (int)dt);
     if (hq <= 0 || hkv <= 0 || hq % hkv)
         return fail(TG_ERR_INVALID_ARGUMENT, "hq=%d must be a positive multiple of hkv=%d", hq, hkv);
@@ -259,20 +260,25 @@ tg_status tg_gated_attention(tg_dtype dt, const void* q, const void* k, const vo
 
 namespace {
 
-// Decode table: sequences with new tokens, their splits and output rows.
-tg_status build_decode_table(tg_dtype dt, const tg_kv_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv,
-                             int32_t head_dim, tg::DecTable* t, int64_t* r_total, size_t* ws_bytes) {
+// Decode tables: the sequences with new tokens, their splits and output
+// rows, in launches of up to TG_MAX_SEQS sequences. Validates every sequence
+// before returning, so a refused call enqueues nothing.
+constexpr int32_t TG_MAX_DECODE_SEQS = 1 << 20;
+
+tg_status build_decode_tables(tg_dtype dt, const tg_kv_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv,
+                              int32_t head_dim, std::vector<tg::DecTable>* tables, int64_t* r_total,
+                              size_t* ws_bytes) {
     if (dt != TG_F32 && dt != TG_BF16) return fail(TG_ERR_INVALID_ARGUMENT, "dtype %d unknown", (int)dt);
     if (hq <= 0 || hkv <= 0 || hq % hkv)
         return fail(TG_ERR_INVALID_ARGUMENT, "hq=%d must be a positive multiple of hkv=%d", hq, hkv);
     if (head_dim != 64 && head_dim != 128)
         return fail(TG_ERR_UNSUPPORTED, "head_dim=%d (built: 64, 128)", head_dim);
-    if (n_seqs < 0 || n_seqs > TG_MAX_SEQS)
-        return fail(TG_ERR_INVALID_ARGUMENT, "n_seqs=%d outside [0, %d]", n_seqs, TG_MAX_SEQS);
+    if (n_seqs < 0 || n_seqs > TG_MAX_DECODE_SEQS)
+        return fail(TG_ERR_INVALID_ARGUMENT, "n_seqs=%d outside [0, %d]", n_seqs, TG_MAX_DECODE_SEQS);
     if (n_seqs > 0 && !seqs) return fail(TG_ERR_INVALID_ARGUMENT, "seqs is NULL");
-    memset(t, 0, sizeof *t);
+    tables->clear();
     const int g = hq / hkv;
-    int64_t rows = 0, keys = 0;
+    int64_t rows = 0, keys = 0, max_len = 0;
     int nq_max = 0;
     for (int b = 0; b < n_seqs; ++b) {
         const tg_kv_seq& s = seqs[b];
@@ -284,41 +290,59 @@ tg_status build_decode_table(tg_dtype dt, const tg_kv_seq* seqs, int32_t n_seqs,
             return fail(TG_ERR_UNSUPPORTED, "sequence %d: (hq/hkv) * n_new = %d > 8", b, g * s.n_new);
         nq_max = nq_max > g * s.n_new ? nq_max : g * s.n_new;
         keys += s.len;
-        tg::DecSeq& d = t->s[t->n++];
-        d.start = s.start;
-        d.len = s.len;
-        d.n_new = s.n_new;
-        d.q_row0 = (int32_t)rows;
+        max_len = max_len > s.len ? max_len : s.len;
         rows += s.n_new;
     }
-    if (rows > (int64_t)INT32_MAX / hq) return fail(TG_ERR_UNSUPPORTED, "too many new tokens for one launch");
+    if (rows > (int64_t)INT32_MAX / hq) return fail(TG_ERR_UNSUPPORTED, "too many new tokens for one call");
     *r_total = rows;
-    t->nq_max = nq_max;
-    if (t->n == 0) {
-        *ws_bytes = 0;
-        return TG_OK;
-    }
+    *ws_bytes = 0;
+    if (rows == 0) return TG_OK;
     // Keys per split: a power of two, a multiple of the keys one wave's lane
-    // groups take per block, sized for about 4096 waves in all and for at
-    // most 256 splits per sequence (the merge walks a query's splits).
+    // groups take per block, sized for about 4096 waves over the call and for
+    // at most 256 splits per sequence (the merge walks a query's splits).
     const int esize = dt == TG_BF16 ? 2 : 4;
     const int lpk = head_dim * esize / 16;
     const int granule = (64 / lpk) * 8;
-    int64_t max_len = 0;
-    for (int b = 0; b < t->n; ++b) max_len = max_len > t->s[b].len ? max_len : t->s[b].len;
     int64_t kpw = granule;
     while (kpw < (1 << 20) && (kpw * 4096 < keys * hkv || kpw * 256 < max_len)) kpw *= 2;
-    t->kpw = (int32_t)kpw;
-    int64_t splits = 0;
-    for (int b = 0; b < t->n; ++b) {
-        t->s[b].split_base = (int32_t)splits;
-        splits += (t->s[b].len + kpw - 1) / kpw;
-    }
-    if (splits * hkv > (int64_t)INT32_MAX / 2) return fail(TG_ERR_UNSUPPORTED, "too many splits for one launch");
-    t->n_waves = (int32_t)(splits * hkv);
     const int nq = tg::decode_query_slots(nq_max);
-    *ws_bytes = (size_t)t->n_waves * nq * (head_dim + 2) * sizeof(float);
-    return TG_OK;
+    tg::DecTable t;
+    memset(&t, 0, sizeof t);
+    int64_t q_row = 0, splits = 0;
+    auto flush = [&]() -> tg_status {
+        if (t.n == 0) return TG_OK;
+        if (splits * hkv > (int64_t)INT32_MAX / 2) return fail(TG_ERR_UNSUPPORTED, "too many splits for one launch");
+        t.n_waves = (int32_t)(splits * hkv);
+        t.n_rows = (int32_t)(q_row - t.row0);
+        const size_t need = (size_t)t.n_waves * nq * (head_dim + 2) * sizeof(float);
+        *ws_bytes = need > *ws_bytes ? need : *ws_bytes;
+        tables->push_back(t);
+        memset(&t, 0, sizeof t);
+        splits = 0;
+        return TG_OK;
+    };
+    for (int b = 0; b < n_seqs; ++b) {
+        const tg_kv_seq& s = seqs[b];
+        if (s.n_new == 0) continue;
+        if (t.n == TG_MAX_SEQS) {
+            const tg_status st = flush();
+            if (st != TG_OK) return st;
+        }
+        if (t.n == 0) {
+            t.kpw = (int32_t)kpw;
+            t.nq_max = nq_max;
+            t.row0 = (int32_t)q_row;
+        }
+        tg::DecSeq& d = t.s[t.n++];
+        d.start = s.start;
+        d.len = s.len;
+        d.n_new = s.n_new;
+        d.q_row0 = (int32_t)q_row;
+        d.split_base = (int32_t)splits;
+        splits += (s.len + kpw - 1) / kpw;
+        q_row += s.n_new;
+    }
+    return flush();
 }
 
 }  // namespace
@@ -564,7 +588,7 @@ tg_status tg_dense_layer(tg_dtype dt, const void* hidden_kept, const float* bias
                                     v, stream);
     if (e != hipSuccess) return hip_fail(e, "tg_dense_layer launch");
     st = tg_gated_attention(TG_BF16, q, k, v, bias_kept, pos_kept, seqs, n_seqs, hq, hkv, dh, w->gain, w->tau, o,
-                            nullptr, nullptr, 0, stream);
+                            nullptr, stream);
     if (st != TG_OK) return st;
     e = tg::launch_linear(TG_LINEAR_RESIDUAL, o, m, hq * dh, w->wo, nullptr, d, hidden_kept, h2, stream);
     if (e == hipSuccess) e = tg::launch_rmsnorm(h2, m, d, w->ln2, w->eps, a, stream);
@@ -612,12 +636,12 @@ tg_status tg_gated_delta_scan(tg_dtype dt, const void* q, const void* k, const v
 }
 
 size_t tg_decode_workspace_bytes(const tg_kv_seq* seqs, int32_t n_seqs, int32_t hq, int32_t hkv, int32_t head_dim) {
-    tg::DecTable t;
+    std::vector<tg::DecTable> t;
     int64_t r = 0;
     size_t ws = 0;
-    if (build_decode_table(TG_BF16, seqs, n_seqs, hq, hkv, head_dim, &t, &r, &ws) != TG_OK) return 0;
+    if (build_decode_tables(TG_BF16, seqs, n_seqs, hq, hkv, head_dim, &t, &r, &ws) != TG_OK) return 0;
     size_t ws32 = 0;
-    build_decode_table(TG_F32, seqs, n_seqs, hq, hkv, head_dim, &t, &r, &ws32);
+    build_decode_tables(TG_F32, seqs, n_seqs, hq, hkv, head_dim, &t, &r, &ws32);
     g_err.clear();
     return ws > ws32 ? ws : ws32;  // enough for either dtype
 }
@@ -635,12 +659,12 @@ tg_status decode_common(tg_dtype dt, const void* q_new, const void* k, const voi
     g_err.clear();
     if (!(tau > 0.0f) || tau != tau || tau > 3.0e38f)
         return fail(TG_ERR_INVALID_ARGUMENT, "tau must be finite and > 0");
-    tg::DecTable t;
+    std::vector<tg::DecTable> tables;
     int64_t r_total = 0;
     size_t need = 0;
-    tg_status st = build_decode_table(dt, seqs, n_seqs, hq, hkv, head_dim, &t, &r_total, &need);
+    tg_status st = build_decode_tables(dt, seqs, n_seqs, hq, hkv, head_dim, &tables, &r_total, &need);
     if (st != TG_OK) return st;
-    if (t.n == 0) return TG_OK;
+    if (tables.empty()) return TG_OK;
     if (!q_new || !k || !v || !bias || !pos || !gain || !out)
         return fail(TG_ERR_INVALID_ARGUMENT, "q_new, k, v, bias, pos, gain, out must be non-NULL");
     if (!(aligned16(q_new) && aligned16(k) && aligned16(v)))
@@ -657,9 +681,13 @@ tg_status decode_common(tg_dtype dt, const void* q_new, const void* k, const voi
                         need);
         if ((uintptr_t)workspace % 4 != 0) return fail(TG_ERR_INVALID_ARGUMENT, "workspace not 4-byte aligned");
     }
-    hipError_t e = tg::launch_decode(dt, q_new, k, v, bias, pos, t, hq, hkv, head_dim, gain, tau, out, lse, r_total,
-                                     workspace, stream);
-    if (e != hipSuccess) return hip_fail(e, "tg_decode_attention launch");
+    // Launch groups of sequences in stream order; they reuse the workspace
+    // (each group's combine finishes before the next group's splits start).
+    for (const tg::DecTable& t : tables) {
+        hipError_t e = tg::launch_decode(dt, q_new, k, v, bias, pos, t, hq, hkv, head_dim, gain, tau, out, lse,
+                                         r_total, workspace, stream);
+        if (e != hipSuccess) return hip_fail(e, "tg_decode_attention launch");
+    }
     return TG_OK;
 }
 

@@ -112,7 +112,31 @@ __global__ __launch_bounds__(CT) void compact_kernel(const int32_t* __restrict__
     }
 }
 
+// Position check: counts the kept rows whose position is below the previous
+// kept row's in the same prompt (one thread per kept row; integer atomics,
+// so the count is exact and deterministic).
+__global__ __launch_bounds__(64) void pos_check_zero_kernel(int32_t* __restrict__ n_bad) {
+    if (threadIdx.x == 0) *n_bad = 0;
+}
+__global__ __launch_bounds__(256) void pos_check_kernel(const int32_t* __restrict__ pos, int64_t m, SeqTable t,
+                                                       int32_t* __restrict__ n_bad) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= m) return;
+    int b = 0;
+    for (int s = 1; s < t.n; ++s)
+        if (t.s[s].kept_off <= i) b = s;
+    if (i > t.s[b].kept_off && pos[i] < pos[i - 1]) atomicAdd(n_bad, 1);
+}
+
 }  // namespace
+
+hipError_t launch_check_positions(const int32_t* pos, int64_t m, const SeqTable& t, int32_t* n_bad,
+                                  hipStream_t st) {
+    hipLaunchKernelGGL(pos_check_zero_kernel, dim3(1), dim3(64), 0, st, n_bad);
+    if (m > 0)
+        hipLaunchKernelGGL(pos_check_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, pos, m, t, n_bad);
+    return hipGetLastError();
+}
 
 hipError_t launch_compact(const int32_t* kept, int64_t m, const SeqTable& t, const GatherTable& g,
                           const int32_t* pos, int32_t* pos_kept, const float* scores,

@@ -273,7 +273,7 @@ __global__ __launch_bounds__(CB_THREADS) void decode_combine_kernel(DecTable t, 
                                                                     int64_t r_total) {
     constexpr int P = CB_THREADS / D;
     __shared__ float sm[P], sl[P], so[P][D];
-    const int row = blockIdx.x / hq, h = blockIdx.x % hq;
+    const int row = t.row0 + (int)(blockIdx.x / hq), h = blockIdx.x % hq;
     int b = 0;
     for (int i = 1; i < t.n; ++i)
         if (t.s[i].q_row0 <= row) b = i;
@@ -330,7 +330,7 @@ hipError_t launch_decode_t(const void* q, const void* k, const void* v, const fl
     const unsigned g1 = (unsigned)((t.n_waves + DEC_WAVES - 1) / DEC_WAVES);
     hipLaunchKernelGGL((decode_partial_kernel<E, D, NQ>), dim3(g1), dim3(64 * DEC_WAVES), 0, st, (const E*)q,
                        (const E*)k, (const E*)v, bias, pos, t, hq, hkv, gain, c, (float*)ws);
-    hipLaunchKernelGGL((decode_combine_kernel<E, D, NQ>), dim3((unsigned)(r_total * hq)), dim3(CB_THREADS), 0, st, t, hq,
+    hipLaunchKernelGGL((decode_combine_kernel<E, D, NQ>), dim3((unsigned)(t.n_rows * hq)), dim3(CB_THREADS), 0, st, t, hq,
                        hkv, (const float*)ws, (E*)out, lse, r_total);
     return hipGetLastError();
 }

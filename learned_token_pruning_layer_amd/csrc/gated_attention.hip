@@ -632,7 +632,7 @@ void launch_cfg(int cfg, dim3 grid, hipStream_t st, const uint16_t* q, const uin
                 const float* bias, const int32_t* pos, const AttnTable& t, int hq, int hkv, const float* gain,
                 float qk_scale, uint16_t* out, float* lse) {
     if (cfg == 0)
-        hipLaunchKernelGGL((attn_bf16_kernel<D, HW, 1, 2, 2, 2>), grid, dim3(64 * HW * 2), 0, st, q, k, v, bias, pos,
+        hipLaunchKernelGGL((attn_bf16_kernel<D, HW, 1, 2, 2, HW == 2 ? 2 : 1>), grid, dim3(64 * HW * 2), 0, st, q, k, v, bias, pos,
                            t, hq, hkv, gain, qk_scale, out, lse);
     else
         hipLaunchKernelGGL((attn_bf16_kernel<D, HW, 2, 1, 3, 2>), grid, dim3(64 * HW * 2), 0, st, q, k, v, bias, pos,

@@ -34,40 +34,49 @@ __device__ __forceinline__ void wait_vmcnt() {
 // a ring's next-stage prefetch) stays out of the pipelines; those order
 // themselves with explicit wait_vmcnt. The compiler's own waits can only get
 // stronger from this, since it undercounts the loads in flight.
-// The compiler reserves m0 and warns that the clobber is not honoured; no
-// other code in these kernels reads or writes m0, so nothing depends on it.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
+// The compiler reserves m0 and may keep a value of its own there, so every
+// block saves m0 into a scratch SGPR, sets it for the load and restores it
+// before returning control: m0 is unchanged across each statement, which is
+// what the compiler assumes of an inline asm that does not list it.
 __device__ __forceinline__ void dma16(const void* g, const LDS_AS void* l) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "s"(m0), "v"(g) : "memory");
 }
 __device__ __forceinline__ void dma4(const void* g, const LDS_AS void* l) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "s"(m0), "v"(g) : "memory");
 }
 // The same with a wave-uniform 64-bit base (SGPR pair), a per-lane 32-bit
 // byte offset and the LDS destination as a plain LDS byte address.
 __device__ __forceinline__ void dma16_so(const void* sbase, uint32_t voff, uint32_t lds) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "s"(m0), "v"(voff), "s"(sbase) : "memory");
 }
 __device__ __forceinline__ void dma4_so(const void* sbase, uint32_t voff, uint32_t lds) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "s"(m0), "v"(voff), "s"(sbase) : "memory");
 }
 // The same with m0 = lds_base + IMM (one scalar add, no separate move).
 template <int IMM>
 __device__ __forceinline__ void dma16_so_at(const void* sbase, uint32_t voff, uint32_t lds_base) {
-    asm volatile("s_add_u32 m0, %0, %3\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase), "n"(IMM)
-                 : "memory", "m0");
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_add_u32 m0, %1, %4\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "s"(lds_base), "v"(voff), "s"(sbase), "n"(IMM) : "memory", "scc");
 }
 template <int IMM>
 __device__ __forceinline__ void dma4_so_at(const void* sbase, uint32_t voff, uint32_t lds_base) {
-    asm volatile("s_add_u32 m0, %0, %3\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase), "n"(IMM)
-                 : "memory", "m0");
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_add_u32 m0, %1, %4\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "s"(lds_base), "v"(voff), "s"(sbase), "n"(IMM) : "memory", "scc");
 }
-#pragma clang diagnostic pop
 
 // LDS byte address of a __shared__ object (the cast of a variable's address
 // needs no null check, unlike a cast of an arbitrary generic pointer).

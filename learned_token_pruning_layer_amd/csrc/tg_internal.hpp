@@ -99,6 +99,10 @@ struct LongTable {
 size_t select_plan(const SeqTable& t, LongTable* lt);
 hipError_t launch_select(const float* scores, const SeqTable& t, const LongTable& lt, void* workspace,
                          int32_t* kept, hipStream_t st);
+// *n_bad = number of kept rows whose position is below the previous kept
+// row's in the same prompt.
+hipError_t launch_check_positions(const int32_t* pos, int64_t m, const SeqTable& t, int32_t* n_bad,
+                                  hipStream_t st);
 hipError_t launch_compact(const int32_t* kept, int64_t m, const SeqTable& t, const GatherTable& g,
                           const int32_t* pos, int32_t* pos_kept, const float* scores,
                           float* bias_kept, hipStream_t st);
@@ -115,11 +119,16 @@ struct DecSeq {
     int32_t q_row0;      // first row of q_new / out for this sequence
     int32_t split_base;  // first global split id (splits of kpw keys)
 };
+// One launch's share of a decode call: up to TG_MAX_SEQS sequences with new
+// tokens (a call with more is split into several launches in stream order,
+// which reuse one workspace).
 struct DecTable {
     int32_t n;
-    int32_t kpw;      // keys per split (one wave per split and KV head)
-    int32_t n_waves;  // splits x KV heads
-    int32_t nq_max;   // largest (hq/hkv) * n_new over the sequences
+    int32_t kpw;      // keys per split (one wave per split and KV head), same in every launch of a call
+    int32_t n_waves;  // splits x KV heads of this launch
+    int32_t nq_max;   // largest (hq/hkv) * n_new over the call's sequences
+    int32_t row0;     // first query row of this launch's sequences
+    int32_t n_rows;   // query rows of this launch's sequences
     DecSeq s[TG_MAX_SEQS];
 };
 // Query slots per wave for nq queries (0: more than supported).

@@ -144,7 +144,7 @@ class GatedPrefillLayer:
             self._attn_args.append((dt, qk.data_ptr(), kk.data_ptr(), vk.data_ptr(), self.bias_kept.data_ptr(),
                                     self.pos_kept.data_ptr(), self._seqs, ns, self.hq, self.hkv, self.head_dim,
                                     lay.gain.data_ptr(), ctypes.c_float(lay.tau), self.outs[i].data_ptr(),
-                                    None if lse is None else lse.data_ptr(), None, 0))
+                                    None if lse is None else lse.data_ptr()))
 
     @staticmethod
     def _stream(stream):

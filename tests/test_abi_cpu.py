@@ -170,7 +170,7 @@ def test_attention_rejects_before_launch(lib):
 
     def call(dt=1, hq=16, hkv=8, d=128, tau=1.2, q=None):
         return lib.tg_gated_attention(dt, q, None, None, None, None, sa, 1, hq, hkv, d, None, tau,
-                                      None, None, None, 0, None)
+                                      None, None, None)
 
     assert call(hq=12, hkv=8) == INVALID
     assert call(hkv=0) == INVALID
@@ -180,7 +180,6 @@ def test_attention_rejects_before_launch(lib):
     assert call(tau=float("inf")) == INVALID
     assert call(dt=5) == INVALID
     assert call() == INVALID  # NULL tensors
-    assert lib.tg_attention_workspace_bytes(sa, 1, 16, 8, 128) == 0
 
 
 def test_gate_backward_workspace_and_rejects_before_launch(lib):
@@ -285,3 +284,22 @@ def test_noalloc_decode_refuses_beyond_its_scratch(lib):
     # an invalid table is still reported as such first
     assert lib.tg_decode_attention_noalloc(1, fake, fake, fake, fake, fake, kv_seq_array([(0, 3, 4)]), 1, 16, 8, 128,
                                            fake, 1.0, fake, None, None) == 1
+
+
+def test_check_positions_and_large_decode_tables_on_host(lib):
+    """Host-side checks of the position check and of decode calls over more than
+    64 sequences (their workspace covers the largest launch group)."""
+    from learned_token_pruning_layer_amd._lib import kv_seq_array
+    sa = seq_array([Prompt(0, 10, 0, 8, 3)])
+    assert lib.tg_check_positions(None, sa, 1, None, None) == INVALID       # n_bad NULL
+    assert lib.tg_check_positions(None, sa, 1, ctypes.c_void_p(64), None) == INVALID  # pos NULL with rows
+    # 300 sequences: five launch groups; the workspace is that of the largest group
+    segs = [(i * 1000, 1000, 1) for i in range(300)]
+    many = lib.tg_decode_workspace_bytes(kv_seq_array(segs), len(segs), 16, 8, 128)
+    one_group = lib.tg_decode_workspace_bytes(kv_seq_array(segs[:64]), 64, 16, 8, 128)
+    assert many > 0 and one_group > 0
+    # a bad sequence anywhere in the call is refused before anything is enqueued
+    bad = segs[:200] + [(0, 3, 4)] + segs[200:]
+    fake = ctypes.c_void_p(4096)
+    assert lib.tg_decode_attention(1, fake, fake, fake, fake, fake, kv_seq_array(bad), len(bad), 16, 8, 128, fake,
+                                   1.0, fake, None, fake, 1 << 30, None) == INVALID

@@ -629,6 +629,45 @@ def test_decode_position_ties_and_fp32():
     check_decode([(0, 300, 2)], 4, 4, 128, seed=7, dtype=torch.float32)
 
 
+def test_decode_many_sequences():
+    """300 sequences in one call (five launch groups of at most 64 sharing one
+    workspace): ragged caches of 1..400 rows with 1..4 new tokens each."""
+    note("decode bf16 16/8 heads D=128 over 300 sequences")
+    rng = np.random.default_rng(8)
+    segs, st = [], 0
+    for i in range(300):
+        ln = int(rng.integers(1, 401))
+        nn = int(min(ln, rng.integers(1, 5)))
+        segs.append((st, ln, nn))
+        st += ln + int(rng.integers(0, 3))  # gaps between caches are allowed
+    out = check_decode(segs, 16, 8, 128, seed=12)
+    assert not torch.isnan(out).any()
+
+
+def test_check_positions():
+    """tg_check_positions counts exactly the kept rows whose position is below the
+    previous kept row's inside a prompt; a decrease across a prompt boundary is fine."""
+    note("position check: valid positions, planted decreases, boundary between prompts")
+    prompts = [Prompt(0, 3000, 50, 2900, 400), Prompt(3000, 1000, 0, 744, 100), Prompt(4000, 64, 0, 0, 0)]
+    s = make_scores(4064, seed=31).to(DEV)
+    kept = tg.tg_select_topk(s, prompts)
+    _, pk, _ = tg.tg_compact(kept, prompts, [])
+    assert int(tg.tg_check_positions(pk, prompts)[0]) == 0  # positions restart per prompt: no violation
+    bad = pk.clone()
+    m = bad.numel()
+    idx = torch.tensor([5, 77, 500, m - 1], device=DEV)
+    bad[idx] = -7  # each planted row now sits below its predecessor
+    assert int(tg.tg_check_positions(bad, prompts)[0]) == 4
+    ties = pk.clone()
+    off = 0
+    for p in prompts:  # each prompt's positions shifted by one row: every one repeated once
+        n = p.n_kept
+        if n > 1:
+            ties[off + 1:off + n] = pk[off:off + n - 1].clone()
+        off += n
+    assert int(tg.tg_check_positions(ties, prompts)[0]) == 0  # repeated positions are allowed
+
+
 def test_decode_deterministic_and_matches_prefill_rows():
     note("decode: bitwise repeatable; equals the prefill kernel's last rows within the bf16 bar")
     segs = [(0, 2384, 1), (2384, 1500, 2)]
