@@ -39,6 +39,9 @@ def parse():
                     help="skip the extra measurements (re-measured peaks, percentiles, cold runs, large select)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (the scale reference for --pmc byte counters)")
+    ap.add_argument("--workload", default="qwen16k", choices=("qwen16k", "long128k"),
+                    help="the layer the timed steps run (qwen16k is the reported metric; long128k serves "
+                         "profiling runs of the 128k layer)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="CPU only: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
                          "--calibrate-copy run into profiles/traffic_qwen16k.json and exit")
@@ -93,6 +96,13 @@ def measured_traffic(kernel):
     return rec.get("hbm_bytes_per_launch")
 
 
+WORKLOAD_TEXT = {
+    "qwen16k": "qwen16k: one pruned-prefill layer, N=16384 (16000 doc + 384 query), keep 2000 doc rows (12.5%), "
+               "d_model 2048, gate 2048->256->1, 16 Q / 8 KV heads, head_dim 128, 16 planted rows",
+    "long128k": "long128k: one pruned-prefill layer, N=131072 (130048 doc + 1024 query), keep 8128 doc rows "
+                "(6.25%), d_model 2048, gate 2048->256->1, 16 Q / 8 KV heads, head_dim 128, planted rows 1 per 8192",
+}
+
 COPY_BYTES = 256 << 20
 KERNEL_NAMES = {"gate": "gate_mfma_kernel", "select": "select_kernel", "compact": "compact_kernel",
                 "attention": "attn_bf16_kernel"}
@@ -134,7 +144,47 @@ def traffic_summary(fetch_csv, write_csv):
     print(json.dumps(out, indent=1, sort_keys=True))
 
 
-def cpu_baseline(w, budget_s):
+def kernel_times(torch, layer, reps, cold_buf=None):
+    """Median per-kernel durations (us) of the four steps, HIP events around each
+    launch on the layer's stream. With cold_buf, a 1 GiB device write before
+    every step evicts the 256 MB Infinity Cache, so each kernel reads its
+    inputs from HBM (the writes of the step's earlier kernels stay cached)."""
+    stream = torch.cuda.current_stream()
+    names = ["gate", "select", "compact", "attention"]
+    samples = {k: [] for k in names}
+    for _ in range(reps):
+        if cold_buf is not None:
+            cold_buf.fill_(3.0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        ev[0].record(stream)
+        layer.gate()
+        ev[1].record(stream)
+        layer.select()
+        ev[2].record(stream)
+        layer.compact()
+        ev[3].record(stream)
+        layer.attention(0)
+        ev[4].record(stream)
+        torch.cuda.synchronize()
+        for i, k in enumerate(names):
+            samples[k].append(ev[i].elapsed_time(ev[i + 1]) * 1e3)
+    return {k: round(sorted(v)[len(v) // 2], 2) for k, v in samples.items()}
+
+
+def rooflines_of(work, us, cache):
+    """Roofline fractions of the kernels from their algorithmic work and times."""
+    out = {}
+    for k in ("gate", "compact", "select"):
+        ach = work[k]["bytes"] / (us[k] * 1e-6) / 1e9
+        out[k] = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                      frac=round(ach / PEAK_HBM_GBS, 4), cache=cache)
+    ach = work["attention"]["flops"] / (us["attention"] * 1e-6) / 1e12
+    out["attention"] = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                            frac=round(ach / PEAK_BF16_TFLOPS, 4), cache=cache)
+    return out
+
+
+def cpu_baseline(w, budget_s, gpu_layer=None):
     """The fp64 oracle, untuned, on the host cores: one whole layer if it
     fits the budget, else the gate + select + compaction in full and the
     attention on an evenly spaced sample of query rows, scaled by the
@@ -159,6 +209,16 @@ def cpu_baseline(w, budget_s):
     kept = oracle.select_topk(s.astype(np.float32), w.prompts)
     (qk, kk, vk), pk, bk = oracle.compact(kept, w.prompts, (q, k, v), s)
     t_front = time.perf_counter() - t0
+    parity = None
+    if gpu_layer is not None:
+        # The selection the GPU made from its own scores against the one the
+        # fp64 gate implies: rows near the threshold may change sides (the
+        # scores differ by the fp32 accumulation of the bf16 products).
+        gk = set(gpu_layer.kept.cpu().numpy().tolist())
+        gs = gpu_layer.scores.cpu().double().numpy()
+        parity = {"kept_flips_vs_fp64_gate": len(gk ^ set(kept.tolist())),
+                  "max_abs_score_diff": float(np.abs(gs - s).max()),
+                  "max_abs_score": float(np.abs(s).max())}
     m = len(kept)
     qk, kk, vk = qk.view(m, hq, dh), kk.view(m, hkv, dh), vk.view(m, hkv, dh)
     # probe the attention cost on a small sample to size the run
@@ -185,7 +245,7 @@ def cpu_baseline(w, budget_s):
     total_ms = (t_front + t_attn) * 1e3
     return dict(value=round(total_ms, 3), unit="ms", cores=int(threads), kind="oracle", sample=sample,
                 split_ms=dict(gate_select_compact=round(t_front * 1e3, 3), attention=round(t_attn * 1e3, 3)),
-                blas=blas, host_cpus=len(os.sched_getaffinity(0)))
+                blas=blas, host_cpus=len(os.sched_getaffinity(0))), parity
 
 
 def measure_extras(torch, tg, layer, w, steps, dev):
@@ -236,6 +296,11 @@ def measure_extras(torch, tg, layer, w, steps, dev):
     out["layer_us_cold"] = {"p10": round(pct(cold, 0.1), 2), "p50": round(pct(cold, 0.5), 2),
                             "p90": round(pct(cold, 0.9), 2),
                             "note": "a 1 GiB device write before each step evicts the Infinity Cache"}
+    # Per-kernel times with the Infinity Cache evicted before every step.
+    kc = kernel_times(torch, layer, 20, cold_buf=dst)
+    work = algorithmic_work(w, layer.m)
+    out["kernels_us_cold"] = kc
+    out["kernel_rooflines_cold"] = rooflines_of(work, kc, "cold")
     del src, dst
     # Decode after this prefill: one new token over the kept K/V cache.
     out["decode_qwen16k"] = measure_decode(torch, tg, layer, timed, pct)
@@ -428,6 +493,9 @@ def measure_dense_layer(torch, tg, lay, w, timed, pct, reps=10):
 
     def one(h, bias, pos, prompts):
         m = h.shape[0]
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
         sa = seq_array(prompts)
         need = lib.tg_dense_layer_workspace_bytes(sa, len(prompts), ctypes.byref(desc))
         ws = torch.empty(need, dtype=torch.uint8, device=h.device)
@@ -448,8 +516,10 @@ def measure_dense_layer(torch, tg, lay, w, timed, pct, reps=10):
                                                                         + 1) // 2 for p in prompts)
         fl = 2 * m * d * ((hq + 2 * hkv) * dh + hq * dh + 3 * d_ff) + 4 * dh * hq * pairs
         mem = need + (2 * kc.numel() + out.numel()) * 2
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
         return {"rows": m, "us": round(us, 1), "tflops": round(fl / (us * 1e-6) / 1e12, 1),
-                "row_scaled_bytes": int(mem)}
+                "row_scaled_bytes": int(mem), "peak_allocated_bytes": int(peak)}
 
     pruned = one(lay.hidden_kept if lay.hidden_kept is not None else lay.x[lay.kept.long()].contiguous(),
                  lay.bias_kept, lay.pos_kept, lay.prompts)
@@ -457,7 +527,11 @@ def measure_dense_layer(torch, tg, lay, w, timed, pct, reps=10):
     full = one(w.x, torch.zeros(n, dtype=torch.float32, device=w.x.device),
                torch.arange(n, dtype=torch.int32, device=w.x.device), [Prompt(0, n, 0, 0, 0)])
     return {"pruned": pruned, "unpruned": full, "speedup": round(full["us"] / pruned["us"], 2),
-            "memory_ratio": round(full["row_scaled_bytes"] / pruned["row_scaled_bytes"], 2), "d_ff": d_ff}
+            "memory_ratio": round(full["row_scaled_bytes"] / pruned["row_scaled_bytes"], 2),
+            "peak_memory_ratio": round(full["peak_allocated_bytes"] / max(1, pruned["peak_allocated_bytes"]), 2),
+            "d_ff": d_ff,
+            "memory_note": "peak_allocated_bytes: torch.cuda.max_memory_allocated over the call's own "
+                           "allocations (workspace, K/V cache, output), inputs excluded"}
 
 
 def measure_delta_scan(torch, tg, lay, timed, pct, reps=10):
@@ -530,6 +604,17 @@ def measure_configs(torch, tg, dev, timed, pct):
     w = make_workload("long128k", device=dev)
     p0 = w.prompts[0]
     pruned = run_one(w, w.prompts, 20, decode=True)
+    lay = tg.GatedPrefillLayer(w.x, w.w1, w.w2, w.prompts, w.layers, w.hq, w.hkv, w.head_dim)
+    lay.run()
+    work = algorithmic_work(w, lay.m)
+    kw = kernel_times(torch, lay, 20)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    kc = kernel_times(torch, lay, 10, cold_buf=flush)
+    del flush, lay
+    pruned["kernels_us_warm"] = kw
+    pruned["kernels_us_cold"] = kc
+    pruned["kernel_rooflines_warm"] = rooflines_of(work, kw, "warm")
+    pruned["kernel_rooflines_cold"] = rooflines_of(work, kc, "cold")
     full = run_one(w, [p0._replace(k_doc=p0.n_doc)], 3, attn_reps=3, decode=True)
     out["long128k"] = {"n_rows": w.n_rows, "k_doc": p0.k_doc, **pruned,
                        "unpruned": {k: full[k] for k in ("kept_rows", "attention_us", "attention_tflops",
@@ -563,7 +648,7 @@ def main():
 
     torch.cuda.set_device(0)
     dev = "cuda:0"
-    w = make_workload("qwen16k", device=dev)
+    w = make_workload(args.workload, device=dev)
     layer = tg.GatedPrefillLayer(w.x, w.w1, w.w2, w.prompts, w.layers, w.hq, w.hkv, w.head_dim)
     m = layer.m
     work = algorithmic_work(w, m)
@@ -616,15 +701,18 @@ def main():
     torch.cuda.synchronize()
     dom_us = e0.elapsed_time(e1) / args.steps * 1e3
 
+    def measured_traffic_of(kernel):
+        return measured_traffic(kernel) if args.workload == "qwen16k" else None
+
     def roofline(kernel, us):
         wk = work[kernel]
         if kernel == "attention":
             ach = wk["flops"] / (us * 1e-6) / 1e12
             return dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                        frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic(kernel))
+                        frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic_of(kernel))
         ach = wk["bytes"] / (us * 1e-6) / 1e9
         return dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=measured_traffic(kernel))
+                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=measured_traffic_of(kernel))
 
     attn_tflops = work["attention"]["flops"] / (per["attention"] * 1e-6) / 1e12
     rec = {
@@ -640,14 +728,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "qwen16k: one pruned-prefill layer, N=16384 (16000 doc + 384 query), "
-                               "keep 2000 doc rows (12.5%), d_model 2048, gate 2048->256->1, "
-                               "16 Q / 8 KV heads, head_dim 128, 16 planted rows",
+        "config": {"workload": WORKLOAD_TEXT[args.workload],
                    "n_rows": w.n_rows, "kept_rows": m, "global_batch": 1, "seq_len": w.n_rows},
         "attn_tflops": round(attn_tflops, 2),
         "attn_frac_mfma_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "kernels_us": {k: round(v, 2) for k, v in per.items()},
-        "kernel_rooflines": {k: roofline(k, per[k]) for k in names if k != "select"},
+        "kernel_rooflines": {k: dict(roofline(k, per[k]), cache="warm") for k in names if k != "select"},
         "roofline": dict(kernel=dom, launch_us=round(dom_us, 2), **roofline(dom, dom_us)),
         "wall_s_timed": round(wall, 4),
     }
@@ -665,7 +751,8 @@ def main():
             **{f"{k}_of_copy": round(work[k]["bytes"] / (per[k] * 1e-6) / 1e9 / cp, 4) for k in ("gate", "compact")}}
         rec["extras"] = ex
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
+        rec["cpu_baseline"], parity = cpu_baseline(w, args.cpu_budget_s, gpu_layer=layer)
+        rec["parity"] = parity
     print(json.dumps(rec), flush=True)
 
 
