@@ -56,7 +56,9 @@ def test_gate_fp32_tiny():
 
 @pytest.mark.parametrize("n,d,h,with_b1", [(1000, 2048, 256, False), (65, 512, 128, True),
                                            (1, 2048, 256, True), (77, 320, 256, True), (300, 1088, 128, False),
-                                           (200, 192, 64, False), (130, 100, 24, True)])
+                                           (200, 192, 64, False), (130, 100, 24, True), (70, 64, 256, True),
+                                           (32769, 192, 256, True), (40001, 2048, 256, False),
+                                           (33001, 128, 128, True)])
 def test_gate_bf16(n, d, h, with_b1):
     note(f"gate bf16 n={n} d={d} h={h} b1={with_b1}")
     g = torch.Generator(device=DEV).manual_seed(n + d + h)
