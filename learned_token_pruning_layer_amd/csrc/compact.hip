@@ -29,11 +29,18 @@ constexpr int CT = 256;
 constexpr int CU = 12;       // 16-byte units per thread (in flight at once)
 constexpr int MAX_RPB = 16;
 
-__device__ __forceinline__ int find_seq(const SeqTable& t, int64_t row) {
-    int b = 0;
+// The prompt holding row `row`: its first row and document range. Walks
+// the table with uniform indices (a per-lane index into the kernel argument
+// would put the table in scratch memory).
+struct RowSeq {
+    int64_t start, len;
+    int32_t doc_begin, doc_end;
+};
+__device__ __forceinline__ RowSeq find_seq(const SeqTable& t, int64_t row) {
+    RowSeq q{t.s[0].start, t.s[0].len, t.s[0].doc_begin, t.s[0].doc_end};
     for (int i = 1; i < t.n; ++i)
-        if (t.s[i].start <= row) b = i;
-    return b;
+        if (t.s[i].start <= row) q = RowSeq{t.s[i].start, t.s[i].len, t.s[i].doc_begin, t.s[i].doc_end};
+    return q;
 }
 
 __device__ __forceinline__ float log_sigmoid(float s) {
@@ -52,21 +59,17 @@ __global__ __launch_bounds__(CT) void compact_kernel(const int32_t* __restrict__
     const int tid = threadIdx.x;
     const int64_t m0 = (int64_t)blockIdx.x * rpb;
     const int nr = (int)((m - m0) < rpb ? (m - m0) : rpb);
+    // Only the kept index precedes the barrier: the row copies depend on it,
+    // while the position and bias loads go out after the copies' loads.
+    int64_t my_row = -1;
+    RowSeq sd{};
     if (tid < nr) {
         const int64_t r = kept[m0 + tid];
-        const SeqDesc& sd = t.s[find_seq(t, r)];
+        sd = find_seq(t, r);
         // A row id outside every prompt breaks the contract; it is never
         // dereferenced (its outputs are left untouched).
-        const bool ok = r >= sd.start && r < sd.start + sd.len;
-        src_row[tid] = ok ? r : -1;
-        if (ok) {
-            if (pos_kept) pos_kept[m0 + tid] = pos ? pos[r] : (int32_t)(r - sd.start);
-            if (bias_kept) {
-                const int64_t rel = r - sd.start;
-                const bool in_doc = rel >= sd.doc_begin && rel < sd.doc_end;
-                bias_kept[m0 + tid] = in_doc ? log_sigmoid(scores[r]) : 0.0f;
-            }
-        }
+        my_row = (r >= sd.start && r < sd.start + sd.len) ? r : -1;
+        src_row[tid] = my_row;
     }
     if (tid == 0) {
         int acc = 0;
@@ -106,9 +109,25 @@ __global__ __launch_bounds__(CT) void compact_kernel(const int32_t* __restrict__
             }
             val[q] = *src;
         }
+        if (u0 == 0 && my_row >= 0) {
+            if (pos_kept) pos_kept[m0 + tid] = pos ? pos[my_row] : (int32_t)(my_row - sd.start);
+            if (bias_kept) {
+                const int64_t rel = my_row - sd.start;
+                const bool in_doc = rel >= sd.doc_begin && rel < sd.doc_end;
+                bias_kept[m0 + tid] = in_doc ? log_sigmoid(scores[my_row]) : 0.0f;
+            }
+        }
 #pragma unroll
         for (int q = 0; q < CU; ++q)
             if (dst[q]) *dst[q] = val[q];
+    }
+    if (total == 0 && my_row >= 0) {  // no tensors to gather: positions and bias only
+        if (pos_kept) pos_kept[m0 + tid] = pos ? pos[my_row] : (int32_t)(my_row - sd.start);
+        if (bias_kept) {
+            const int64_t rel = my_row - sd.start;
+            const bool in_doc = rel >= sd.doc_begin && rel < sd.doc_end;
+            bias_kept[m0 + tid] = in_doc ? log_sigmoid(scores[my_row]) : 0.0f;
+        }
     }
 }
 
