@@ -254,33 +254,65 @@ __global__ __launch_bounds__(ST) void select_kernel(const float* __restrict__ sc
 // per chunk, in six kernels on the stream:
 //   zero   clears the per-prompt histograms;
 //   hist   (per pass) each chunk of the document builds its histogram of
-//          the pass's digit in LDS and adds it into the prompt's histogram;
-//   pick   (per pass) one workgroup per prompt finds the bin holding the
-//          rem-th largest key and records (prefix, mask, rem);
-//   count  each chunk of the prompt counts its "above" and "tied" rows;
-//   scan   one workgroup per prompt turns the chunk counts into each
-//          chunk's number of above/tied rows before it;
-//   place  each chunk ranks its rows (block scan of per-thread counts) and
-//          writes its kept row ids, staged in LDS: a chunk's kept rows take
-//          a contiguous run of output slots, written out coalesced.
-// Workspace, in 32-bit words: hist [n_long][3][NB], state [n_long][4]
-// (prefix, mask, rem), counts [n_emit][2], offsets [n_emit][2].
+//          the pass's digit in LDS and adds it into the prompt's histogram.
+//          From pass 1 on, every workgroup first finds the previous pass's
+//          bin (the one holding the rem-th largest key) from that pass's
+//          completed histogram; the prompt's first chunk records the
+//          resulting (prefix, mask, rem) for the next kernel;
+//   count  every workgroup finds the last pass's bin the same way (the
+//          threshold key T and how many keys equal to T are kept), then
+//          counts its chunk's "above" and "tied" rows;
+//   place  each chunk adds up the counts of the chunks before it, ranks
+//          its rows (block scan of per-thread counts) and writes its kept
+//          row ids, staged in LDS: a chunk's kept rows take a contiguous
+//          run of output slots, written out coalesced.
+// The bin search is repeated in every workgroup of the next kernel rather
+// than run by a kernel of its own: one launch less per pass.
+// Workspace, in 32-bit words: hist [n_long][3][NB], state [n_long][3][4]
+// ((prefix, mask, rem) after each pass), counts [n_emit][2].
 // ---------------------------------------------------------------------------
 
 struct SelWs {
     uint32_t* hist;
     uint32_t* state;
     uint32_t* counts;
-    uint32_t* offs;
 };
 
 __device__ __forceinline__ SelWs sel_ws(void* base, const LongTable& lt) {
     SelWs w;
     w.hist = (uint32_t*)base;
     w.state = w.hist + (size_t)lt.n * 3 * NB;
-    w.counts = w.state + (size_t)lt.n * 4;
-    w.offs = w.counts + (size_t)lt.n_emit * 2;
+    w.counts = w.state + (size_t)lt.n * 12;
     return w;
+}
+
+// (prefix, mask, rem) after pass `pass` of long prompt li: this workgroup
+// redoes the bin search over the pass's completed histogram, starting from
+// the state the previous pass left (pass 0 starts from (0, 0, k)). The
+// first chunk's workgroup (`store`) records the result for later kernels.
+__device__ __forceinline__ void pick_after(PickSmem& sm, const SelWs& ws, int li, int pass, uint32_t k_doc,
+                                           bool store, uint32_t& prefix, uint32_t& mask, uint32_t& rem, int tid,
+                                           int lane, int wave) {
+    if (pass == 0) {
+        prefix = 0u;
+        mask = 0u;
+        rem = k_doc;
+    } else {
+        const uint32_t* st = ws.state + (size_t)(li * 3 + pass - 1) * 4;
+        prefix = st[0];
+        mask = st[1];
+        rem = st[2];
+    }
+    const uint32_t* g = ws.hist + ((size_t)li * 3 + pass) * NB;
+    for (int b = tid; b <= (int)digit_mask(pass); b += ST) sm.hist[pass * NB + b] = g[b];
+    __syncthreads();
+    pick_bin(sm, pass, 0u, prefix, mask, rem, tid, lane, wave);
+    if (store && tid == 0) {
+        uint32_t* st = ws.state + (size_t)(li * 3 + pass) * 4;
+        st[0] = prefix;
+        st[1] = mask;
+        st[2] = rem;
+    }
 }
 
 // Long prompt and chunk of workgroup b, given each prompt's first workgroup.
@@ -297,6 +329,7 @@ __global__ __launch_bounds__(256) void sel_zero_kernel(uint32_t* __restrict__ p,
 
 __global__ __launch_bounds__(ST) void sel_hist_kernel(const float* __restrict__ scores, SeqTable t, LongTable lt,
                                                      void* ws_base, int pass) {
+    __shared__ PickSmem sm;
     __shared__ uint32_t h[NB];
     int li, chunk;
     long_item(lt, blockIdx.x, false, li, chunk);
@@ -305,17 +338,21 @@ __global__ __launch_bounds__(ST) void sel_hist_kernel(const float* __restrict__ 
     if (!(sd.k_doc > 0 && sd.k_doc < n_doc)) return;  // keep none / all: no threshold needed
     const SelWs ws = sel_ws(ws_base, lt);
     const int tid = threadIdx.x;
-    const uint32_t prefix = pass ? ws.state[li * 4 + 0] : 0u, mask = pass ? ws.state[li * 4 + 1] : 0u;
-    const int shift = digit_shift(pass);
-    const uint32_t dmask = digit_mask(pass);
-    h[tid] = 0u;
-    h[tid + ST] = 0u;
-    __syncthreads();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t dbeg = sd.start + sd.doc_begin;
     const int32_t i0 = chunk * SEL_CHUNK;
     float f[SEL_CHUNK / ST];
 #pragma unroll
     for (int u = 0; u < SEL_CHUNK / ST; ++u) f[u] = scores[dbeg + min(i0 + u * ST + tid, n_doc - 1)];
+    h[tid] = 0u;
+    h[tid + ST] = 0u;
+    uint32_t prefix = 0u, mask = 0u, rem = 0u;
+    if (pass > 0)
+        pick_after(sm, ws, li, pass - 1, (uint32_t)sd.k_doc, chunk == 0, prefix, mask, rem, tid, lane, wave);
+    const int shift = digit_shift(pass);
+    const uint32_t dmask = digit_mask(pass);
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < SEL_CHUNK / ST; ++u) {
         const uint32_t key = score_key(f[u]);
@@ -327,46 +364,19 @@ __global__ __launch_bounds__(ST) void sel_hist_kernel(const float* __restrict__ 
         if (h[b]) atomicAdd(&g[b], h[b]);
 }
 
-__global__ __launch_bounds__(ST) void sel_pick_kernel(SeqTable t, LongTable lt, void* ws_base, int pass) {
-    __shared__ PickSmem sm;
-    const int li = blockIdx.x;
-    const SeqDesc sd = t.s[lt.s[li].seq];
-    const int32_t n_doc = sd.doc_end - sd.doc_begin;
-    if (!(sd.k_doc > 0 && sd.k_doc < n_doc)) return;
-    const SelWs ws = sel_ws(ws_base, lt);
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    uint32_t prefix = pass ? ws.state[li * 4 + 0] : 0u, mask = pass ? ws.state[li * 4 + 1] : 0u;
-    uint32_t rem = pass ? ws.state[li * 4 + 2] : (uint32_t)sd.k_doc;
-    const uint32_t* g = ws.hist + ((size_t)li * 3 + pass) * NB;
-    for (int b = tid; b <= (int)digit_mask(pass); b += ST) sm.hist[pass * NB + b] = g[b];
-    __syncthreads();
-    pick_bin(sm, pass, 0u, prefix, mask, rem, tid, lane, wave);
-    if (tid == 0) {
-        ws.state[li * 4 + 0] = prefix;
-        ws.state[li * 4 + 1] = mask;
-        ws.state[li * 4 + 2] = rem;
-    }
-}
-
 // Classification of this thread's SEL_CHUNK/ST consecutive rows of chunk
 // `chunk` (rows rbase + u): bit u of *ma (above) / *mt (tied). Keys are read
 // coalesced and transposed through LDS (padded, conflict-free).
 constexpr int CU_ROWS = SEL_CHUNK / ST;  // rows per thread in a chunk
-__device__ __forceinline__ void classify_chunk(const float* __restrict__ scores, const SeqDesc& sd, const SelWs& ws,
-                                               int li, int chunk, uint32_t* stage, uint32_t& ma, uint32_t& mt,
-                                               uint32_t& rem_out) {
+__device__ __forceinline__ void classify_chunk(const float* __restrict__ scores, const SeqDesc& sd, uint32_t thr,
+                                               int chunk, uint32_t* stage, uint32_t& ma, uint32_t& mt) {
     const int tid = threadIdx.x;
     const int32_t n_doc = sd.doc_end - sd.doc_begin;
     const int mode = (sd.k_doc == 0) ? 0 : (sd.k_doc == n_doc ? 1 : 2);
     const int32_t cbase = chunk * SEL_CHUNK;  // first row of the chunk (prompt-relative)
     const int32_t rbase = cbase + tid * CU_ROWS;
-    uint32_t thr = 0, rem = 0;
     uint32_t key[CU_ROWS];
     if (mode == 2) {
-        thr = ws.state[li * 4 + 0];
-        rem = ws.state[li * 4 + 2];
         float f[CU_ROWS];
 #pragma unroll
         for (int u = 0; u < CU_ROWS; ++u)
@@ -401,7 +411,6 @@ __device__ __forceinline__ void classify_chunk(const float* __restrict__ scores,
         ma = mode == 1 ? in_len : (in_len & ~in_doc);
         mt = 0u;
     }
-    rem_out = rem;
 }
 
 // Block-wide exclusive prefix of a per-thread count (wave DPP scans + one
@@ -425,43 +434,29 @@ __device__ __forceinline__ uint32_t block_prefix(uint32_t v, uint32_t* wtot, uin
 
 __global__ __launch_bounds__(ST) void sel_count_kernel(const float* __restrict__ scores, SeqTable t, LongTable lt,
                                                       void* ws_base) {
+    __shared__ PickSmem sm;
     __shared__ uint32_t stage[SEL_CHUNK + SEL_CHUNK / 64];
     __shared__ uint32_t wtot[2][NW];
     int li, chunk;
     long_item(lt, blockIdx.x, true, li, chunk);
     const SeqDesc sd = t.s[lt.s[li].seq];
     const SelWs ws = sel_ws(ws_base, lt);
-    uint32_t ma, mt, rem;
-    classify_chunk(scores, sd, ws, li, chunk, stage, ma, mt, rem);
+    const int tid = threadIdx.x;
+    const int32_t n_doc = sd.doc_end - sd.doc_begin;
+    uint32_t thr = 0u;
+    if (sd.k_doc > 0 && sd.k_doc < n_doc) {
+        uint32_t mask, rem;
+        pick_after(sm, ws, li, 2, (uint32_t)sd.k_doc, chunk == 0, thr, mask, rem, tid, tid & 63,
+                   __builtin_amdgcn_readfirstlane(tid >> 6));
+    }
+    uint32_t ma, mt;
+    classify_chunk(scores, sd, thr, chunk, stage, ma, mt);
     uint32_t ta, tt;
     block_prefix((uint32_t)__popc(ma), wtot[0], ta);
     block_prefix((uint32_t)__popc(mt), wtot[1], tt);
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         ws.counts[(size_t)(lt.s[li].emit_base + chunk) * 2 + 0] = ta;
         ws.counts[(size_t)(lt.s[li].emit_base + chunk) * 2 + 1] = tt;
-    }
-}
-
-__global__ __launch_bounds__(ST) void sel_scan_kernel(LongTable lt, void* ws_base) {
-    __shared__ uint32_t wtot[2][NW];
-    const int li = blockIdx.x;
-    const SelWs ws = sel_ws(ws_base, lt);
-    const int n = lt.s[li].n_emit;
-    uint32_t* c = ws.counts + (size_t)lt.s[li].emit_base * 2;
-    uint32_t* o = ws.offs + (size_t)lt.s[li].emit_base * 2;
-    uint32_t carry_a = 0, carry_t = 0;
-    for (int i0 = 0; i0 < n; i0 += ST) {
-        const int i = i0 + (int)threadIdx.x;
-        const uint32_t a = i < n ? c[i * 2 + 0] : 0u, b = i < n ? c[i * 2 + 1] : 0u;
-        uint32_t ta, tb;
-        const uint32_t pa = block_prefix(a, wtot[0], ta), pb = block_prefix(b, wtot[1], tb);
-        if (i < n) {
-            o[i * 2 + 0] = carry_a + pa;
-            o[i * 2 + 1] = carry_t + pb;
-        }
-        carry_a += ta;
-        carry_t += tb;
-        __syncthreads();  // wtot is rewritten by the next block
     }
 }
 
@@ -476,11 +471,26 @@ __global__ __launch_bounds__(ST) void sel_place_kernel(const float* __restrict__
     long_item(lt, blockIdx.x, true, li, chunk);
     const SeqDesc sd = t.s[lt.s[li].seq];
     const SelWs ws = sel_ws(ws_base, lt);
-    uint32_t ma, mt, rem;
-    classify_chunk(scores, sd, ws, li, chunk, stage, ma, mt, rem);
+    const int32_t n_doc = sd.doc_end - sd.doc_begin;
+    const bool radix = sd.k_doc > 0 && sd.k_doc < n_doc;
+    const uint32_t thr = radix ? ws.state[(size_t)(li * 3 + 2) * 4 + 0] : 0u;
+    const uint32_t rem = radix ? ws.state[(size_t)(li * 3 + 2) * 4 + 2] : 0u;
+    // Above / tied rows of the chunks before this one: their counts from
+    // the count kernel, added up here.
+    const uint32_t* cnt = ws.counts + (size_t)lt.s[li].emit_base * 2;
+    uint32_t ba = 0u, bt = 0u;
+    for (int j = threadIdx.x; j < chunk; j += ST) {
+        ba += cnt[j * 2 + 0];
+        bt += cnt[j * 2 + 1];
+    }
+    uint32_t oa, ot;
+    block_prefix(ba, wtot[0], oa);
+    block_prefix(bt, wtot[1], ot);
+    __syncthreads();  // wtot is rewritten by the ranking below
+    uint32_t ma, mt;
+    classify_chunk(scores, sd, thr, chunk, stage, ma, mt);
     uint32_t* const slots = stage;
     const size_t ci = (size_t)(lt.s[li].emit_base + chunk) * 2;
-    const uint32_t oa = ws.offs[ci + 0], ot = ws.offs[ci + 1];  // above / tied rows before the chunk
     const uint32_t ca = ws.counts[ci + 0], ct = ws.counts[ci + 1];
     const uint32_t first = oa + min(ot, rem);                 // the chunk's first output slot
     const uint32_t n_out = oa + ca + min(ot + ct, rem) - first;  // and how many slots it fills
@@ -523,7 +533,7 @@ size_t select_plan(const SeqTable& t, LongTable* lt) {
         lt->n_emit += l.n_emit;
     }
     if (lt->n == 0) return 0;
-    return ((size_t)lt->n * (3 * NB + 4) + (size_t)lt->n_emit * 4) * sizeof(uint32_t);
+    return ((size_t)lt->n * (3 * NB + 12) + (size_t)lt->n_emit * 2) * sizeof(uint32_t);
 }
 
 hipError_t launch_select(const float* scores, const SeqTable& t, const LongTable& lt, void* workspace,
@@ -534,13 +544,10 @@ hipError_t launch_select(const float* scores, const SeqTable& t, const LongTable
     if (lt.n == 0) return hipGetLastError();
     hipLaunchKernelGGL(sel_zero_kernel, dim3((unsigned)lt.n * 6), dim3(256), 0, st, (uint32_t*)workspace,
                        (int64_t)lt.n * 3 * NB);
-    for (int pass = 0; pass < 3; ++pass) {
+    for (int pass = 0; pass < 3; ++pass)
         if (lt.n_hist)
             hipLaunchKernelGGL(sel_hist_kernel, dim3((unsigned)lt.n_hist), dim3(ST), 0, st, scores, t, lt, workspace, pass);
-        hipLaunchKernelGGL(sel_pick_kernel, dim3((unsigned)lt.n), dim3(ST), 0, st, t, lt, workspace, pass);
-    }
     hipLaunchKernelGGL(sel_count_kernel, dim3((unsigned)lt.n_emit), dim3(ST), 0, st, scores, t, lt, workspace);
-    hipLaunchKernelGGL(sel_scan_kernel, dim3((unsigned)lt.n), dim3(ST), 0, st, lt, workspace);
     hipLaunchKernelGGL(sel_place_kernel, dim3((unsigned)lt.n_emit), dim3(ST), 0, st, scores, t, lt, workspace, kept);
     return hipGetLastError();
 }

@@ -74,7 +74,7 @@ def test_select_rejects_before_launch(lib):
     # plus 4 words per 16384-row chunk of the prompt.
     long = [Prompt(0, 100, 0, 90, 5), Prompt(100, 40000, 0, 39000, 7), Prompt(40100, 131072, 0, 130048, 8128)]
     need = lib.tg_select_workspace_bytes(seq_array(long), 3)
-    assert need == 4 * (2 * (3 * 2048 + 4) + 4 * (3 + 8))
+    assert need == 4 * (2 * (3 * 2048 + 12) + 2 * (3 + 8))
     # Missing or short workspace is refused before anything is enqueued (the
     # pointers below are never dereferenced).
     fake = ctypes.c_void_p(4096)
