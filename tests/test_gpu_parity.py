@@ -203,8 +203,9 @@ def test_select_workspace_reuse_and_2p24():
 
 # --------------------------------------------------------------- compact ----
 
-def test_compact_bit_exact_and_bias():
-    note("compact: 5 tensors, positions, bias")
+@pytest.mark.parametrize("n_tensors", [5, 0])
+def test_compact_bit_exact_and_bias(n_tensors):
+    note(f"compact: {n_tensors} tensors, positions, bias")
     prompts = [Prompt(0, 3000, 50, 2900, 400), Prompt(3000, 1000, 0, 744, 100), Prompt(4000, 64, 0, 0, 0)]
     n = 4064
     s = make_scores(n, seed=21) * 4
@@ -214,7 +215,7 @@ def test_compact_bit_exact_and_bias():
           torch.randn(n, 16, 128, generator=g, device=DEV).to(torch.bfloat16),
           torch.randn(n, 8, 128, generator=g, device=DEV).to(torch.bfloat16),
           torch.randn(n, 4, generator=g, device=DEV),
-          torch.randint(-2**31, 2**31 - 1, (n, 12), generator=g, device=DEV, dtype=torch.int32)]
+          torch.randint(-2**31, 2**31 - 1, (n, 12), generator=g, device=DEV, dtype=torch.int32)][:n_tensors]
     pos = torch.randint(0, 10**6, (n,), generator=g, device=DEV, dtype=torch.int32)
     kd = kept.to(DEV)
     for use_pos in (False, True):
