@@ -148,8 +148,6 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
 
     __shared__ __attribute__((aligned(1024))) char ring[NSTG][STAGEB];   // [stage][split][K,V][tile]
     __shared__ __attribute__((aligned(16))) uint32_t smallr[NSTG][SPL][2][SM];  // [stage][split][bias, pos][key]
-    // per wave: this head's bias term of the current tile, in units of q.k
-    __shared__ __attribute__((aligned(16))) float sbias[NW][BN];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -313,13 +311,13 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
     // q.k MFMA, the V^T operands right after the q.k MFMAs (the softmax runs
     // while they arrive). sched_barrier keeps the compiler from sinking the
     // reads back next to their uses.
-    // K operands and the bias seed of the tile in stage st (this head's bias
-    // term for the tile's keys is computed once per wave and read back in the
-    // S^T register order: register j holds key 8(j/4) + 4hh + j%4).
+    // K operands and the bias seed of the tile in stage st: register j of
+    // the S^T layout holds key 8(j/4) + 4hh + j%4, so each lane reads its 16
+    // keys' bias as four 16-byte vectors straight from the stage and scales
+    // them by this head's gain (no round trip through a per-wave array).
     auto read_k = [&](int st, bf16x8 (&kf)[KS], f32x16& seed) __attribute__((always_inline)) {
         const LDS_AS float* bsv = (const LDS_AS float*)(uintptr_t)(small0 + (uint32_t)st * SMALL_STAGE +
                                                                     (uint32_t)(split * 2 * SM * 4));
-        if (lane < BN) sbias[wave][lane] = bsv[lane] * gb;
         // Operand addresses: XOR-swizzled chunks are one XOR away from the
         // per-lane base. The empty asm makes the base opaque per tile, so the
         // compiler keeps one address register instead of hoisting one per
@@ -328,9 +326,9 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
         asm volatile("" : "+v"(ka));
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 bb = *(const LDS_AS f32x4*)&sbias[wave][8 * g4 + 4 * hh];
+            const f32x4 bb = *(const LDS_AS f32x4*)&bsv[8 * g4 + 4 * hh];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) seed[4 * g4 + e] = bb[e];
+            for (int e = 0; e < 4; ++e) seed[4 * g4 + e] = bb[e] * gb;
         }
 #pragma unroll
         for (int s = 0; s < KS; ++s) kf[s] = *(const LDS_AS bf16x8*)(uintptr_t)(ka ^ (uint32_t)(s << 5));
