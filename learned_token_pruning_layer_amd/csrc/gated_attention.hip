@@ -148,6 +148,8 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
 
     __shared__ __attribute__((aligned(1024))) char ring[NSTG][STAGEB];   // [stage][split][K,V][tile]
     __shared__ __attribute__((aligned(16))) uint32_t smallr[NSTG][SPL][2][SM];  // [stage][split][bias, pos][key]
+    // long shape: per wave, this head's bias term of the current tile, in units of q.k
+    __shared__ __attribute__((aligned(16))) float sbias[QS == 1 ? 1 : NW][BN];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -312,9 +314,12 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
     // while they arrive). sched_barrier keeps the compiler from sinking the
     // reads back next to their uses.
     // K operands and the bias seed of the tile in stage st: register j of
-    // the S^T layout holds key 8(j/4) + 4hh + j%4, so each lane reads its 16
-    // keys' bias as four 16-byte vectors straight from the stage and scales
-    // them by this head's gain (no round trip through a per-wave array).
+    // the S^T layout holds key 8(j/4) + 4hh + j%4. The short shape, bound by
+    // the latency of its per-tile chain, reads its 16 keys' bias as four
+    // 16-byte vectors straight from the stage and scales them by this head's
+    // gain in registers. The long shape, closer to its issue rate, scales the
+    // tile's 32 bias values once per wave (one multiply per lane) and reads
+    // them back through a per-wave array.
     auto read_k = [&](int st, bf16x8 (&kf)[KS], f32x16& seed) __attribute__((always_inline)) {
         const LDS_AS float* bsv = (const LDS_AS float*)(uintptr_t)(small0 + (uint32_t)st * SMALL_STAGE +
                                                                     (uint32_t)(split * 2 * SM * 4));
@@ -324,11 +329,21 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
         // read and ring stage out of the loop.
         uint32_t ka = ring0 + (uint32_t)st * STAGEB + k_split + k_lane;
         asm volatile("" : "+v"(ka));
+        if constexpr (QS == 1) {
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 bb = *(const LDS_AS f32x4*)&bsv[8 * g4 + 4 * hh];
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 bb = *(const LDS_AS f32x4*)&bsv[8 * g4 + 4 * hh];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) seed[4 * g4 + e] = bb[e] * gb;
+                for (int e = 0; e < 4; ++e) seed[4 * g4 + e] = bb[e] * gb;
+            }
+        } else {
+            if (lane < BN) sbias[wave][lane] = bsv[lane] * gb;
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 bb = *(const LDS_AS f32x4*)&sbias[wave][8 * g4 + 4 * hh];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) seed[4 * g4 + e] = bb[e];
+            }
         }
 #pragma unroll
         for (int s = 0; s < KS; ++s) kf[s] = *(const LDS_AS bf16x8*)(uintptr_t)(ka ^ (uint32_t)(s << 5));
