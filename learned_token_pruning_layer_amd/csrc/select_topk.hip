@@ -22,7 +22,9 @@
 //  2. A 3-pass MSB radix select (11, 11 and 10-bit digits; LDS histograms
 //     with integer atomics; a DPP wave scan over the bins from the top)
 //     finds the k-th largest key T and rem = how many keys equal to T are
-//     kept.
+//     kept. Pass 0 counts the keys in row order as the coalesced loads
+//     return, before the transpose, so its atomics overlap the load
+//     latency (a histogram does not depend on the order of its keys).
 //  3. Emission: a row is "above" (outside the document, or key > T) or
 //     "tied" (document key == T); each lane classifies its rows into two bit
 //     masks. Kept rows are the above rows and the first rem tied rows; a
@@ -39,6 +41,7 @@
 // loops are kept to a few instructions per key.
 // Integer work only: the result is bit-exact and deterministic.
 #include "tg_internal.hpp"
+#include "tg_device.hpp"
 
 namespace tg {
 namespace {
@@ -145,22 +148,26 @@ __device__ __forceinline__ void select_registers(Smem& sm, const SeqDesc& sd,
             const int32_t r = wbase + u * 64 + lane;
             f[u] = scores[sd.start + min(max(r, sd.doc_begin), sd.doc_end - 1)];
         }
+        // The histograms are clear once every wave passes this barrier; it
+        // does not wait for the score loads, which are still in flight.
+        ring_barrier();
+        // Pass 0 counts every key, in row order as the loads return (a
+        // histogram does not depend on the order), while the keys are also
+        // staged for the transpose.
 #pragma unroll
         for (int u = 0; u < WU; ++u) {
             const int32_t r = wbase + u * 64 + lane;
-            sm.stage[tpad(r)] = (r >= sd.doc_begin && r < sd.doc_end) ? score_key(f[u]) : 0u;
+            const uint32_t kk = (r >= sd.doc_begin && r < sd.doc_end) ? score_key(f[u]) : 0u;
+            sm.stage[tpad(r)] = kk;
+            atomicAdd(&sm.hist[kk >> 21], 1u);
         }
-        __syncthreads();  // histograms cleared, keys staged
+        __syncthreads();  // keys staged, pass 0's histogram complete
 #pragma unroll
         for (int u = 0; u < WU; ++u) key[u] = sm.stage[tpad(rbase + u)];
         // Rows of this workgroup's range that are not document rows (key 0).
         const uint32_t npad = (uint32_t)(NW * 64 * WU - n_doc);
         uint32_t prefix = 0, mask = 0;
         rem = (uint32_t)k;
-        // Pass 0 counts every key.
-#pragma unroll
-        for (int u = 0; u < WU; ++u) atomicAdd(&sm.hist[key[u] >> 21], 1u);
-        __syncthreads();
         pick_bin(sm, 0, npad, prefix, mask, rem, tid, lane, wave);
 #pragma nounroll
         for (int pass = 1; pass < 3; ++pass) {
