@@ -9,6 +9,8 @@
 
 #include "tg_internal.hpp"
 
+#include <atomic>
+
 #include <vector>
 
 namespace {
@@ -208,6 +210,19 @@ tg_status tg_compact(const int32_t* kept_idx, int64_t m_rows, const tg_seq* seqs
     return TG_OK;
 }
 
+// Compute units of the current device, looked up once per device.
+static int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = -1;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v > 0 ? v : 0;
+}
+
 tg_status tg_gated_attention(tg_dtype dt, const void* q, const void* k, const void* v,
                              const float* bias_kept, const int32_t* pos_kept, const tg_seq* seqs,
                              int32_t n_seqs, int32_t hq, int32_t hkv, int32_t head_dim,
@@ -239,6 +254,7 @@ tg_status tg_gated_attention(tg_dtype dt, const void* q, const void* k, const vo
     t.n_seg = n_seqs;
     t.m_total = m;
     t.cfg = cfg.kind;
+    t.cus = device_cus();
     int64_t items = 0;
     for (int b = 0; b < n_seqs; ++b) {
         const tg::SeqDesc& d = st_.s[b];

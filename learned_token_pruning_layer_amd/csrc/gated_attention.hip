@@ -31,7 +31,9 @@
 //    non-decreasing positions, repeats included); key tiles past the
 //    workgroup's last visible key are skipped, and waves whose queries
 //    precede a whole tile skip its math.
-//  * Work items run longest-first (last query blocks of a prompt first).
+//  * Work items run longest-first (last query blocks of a prompt first),
+//    except that the second CU's worth of items runs in reverse, pairing the
+//    longest items with shorter neighbours on each CU.
 //
 // fp32 path: one thread per query row, K/V tiles in LDS, plain fp32 FMA.
 #include "tg_internal.hpp"
@@ -165,10 +167,23 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
     // Work item: consecutive items differ in KV head first, so with 8 KV
     // heads each XCD (items are dealt round-robin to the 8 XCDs) serves one
     // KV head and keeps its K/V in its own L2; query blocks run longest first.
+    // The first C workgroups (C = the device's CUs) take the C longest items,
+    // one per CU; the next C, which share those CUs, take the following items
+    // in reverse order (in groups of 8, so each XCD keeps its KV head), so
+    // the longest items share their CU with the shortest of that group and
+    // soon run alone, at the faster single-workgroup rate, through the tail.
+    int item = blockIdx.x;
+    {
+        const int C = t.cus, n2 = min(2 * t.cus, t.n_items);
+        if (C > 0 && item >= C && item < n2) {
+            const int g = (item - C) >> 3, r = (item - C) & 7, G2 = (n2 - C) >> 3;
+            if (g < G2) item = C + ((G2 - 1 - g) << 3) + r;
+        }
+    }
     int sg = 0;
     for (int i = 1; i < t.n_seg; ++i)
-        if (t.s[i].item_base <= (int)blockIdx.x) sg = i;
-    const int local = blockIdx.x - t.s[sg].item_base;
+        if (t.s[i].item_base <= item) sg = i;
+    const int local = item - t.s[sg].item_base;
     const int per_qb = hkv * ngroups;
     const int qb = t.s[sg].n_qblk - 1 - local / per_qb;
     const int rest = local % per_qb;

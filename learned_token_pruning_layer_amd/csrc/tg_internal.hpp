@@ -55,7 +55,7 @@ struct AttnTable {
     int32_t n_items;
     int64_t m_total;
     int32_t cfg;   // kernel shape (attention_config().kind)
-    int32_t pad;
+    int32_t cus;   // compute units of the device (0: unknown)
     AttnSeg s[TG_MAX_SEQS];
 };
 
