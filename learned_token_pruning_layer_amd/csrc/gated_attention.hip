@@ -192,33 +192,6 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
     const int64_t off = t.s[sg].kept_off;
     const int n = t.s[sg].n;
     const int h = kvh * G + hg * HW + hl;
-    const int b0 = qb * 32 * QS;                  // first row of the workgroup's block
-    const int i0 = b0 + 32 * qs;                  // first row of this wave's slab
-    const bool live = i0 < n;                     // the block's last slabs may lie past the segment
-    const int q_last = min(n, i0 + 32) - 1;
-    const int n_tiles = live ? key_tile_end<BN>(pos, off, n, q_last) : 0;
-    const int n_tiles_wg = key_tile_end<BN>(pos, off, n, min(n, b0 + 32 * QS) - 1);
-    const int n_it = (n_tiles_wg + SPL - 1) / SPL;
-
-    const int qi = min(i0 + l32, n - 1);
-    const int32_t my_pos = pos[off + qi];
-    const float c = qk_scale * LOG2E;
-    // The logit in the exp2 domain is c * (q.k + gb * bias): the bias term
-    // seeds the S^T accumulators, the scale c is applied inside exp2.
-    const float gb = gain[h] / qk_scale;
-
-    bf16x8 qf[KS];
-    {
-        const uint16_t* qrow = q + ((off + qi) * hq + h) * D + 8 * hh;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(qrow + s * 16);
-    }
-    // The ring's vmcnt bookkeeping counts only its own loads: finish every
-    // other vector-memory load first and keep the compiler from moving any
-    // past this point.
-    wait_vmcnt<0>();
-    asm volatile("" ::: "memory");
-
     const int64_t rowb = (int64_t)hkv * ROWB;  // bytes between consecutive keys of one KV head
     const char* kbase = (const char*)(k + (off * hkv + kvh) * D);
     const char* vbase = (const char*)(v + (off * hkv + kvh) * D);
@@ -298,6 +271,39 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
             dma4_so(base, vo, sm + (uint32_t)((sp_ * 2 + (sid & 1)) * SM * 4));
         }
     };
+
+    // The first stage exists for every block (it covers the block's first
+    // rows); its loads go out before the position lookups and the Q loads, so
+    // their latencies overlap. Only the wait below, for every load of the
+    // wave, separates them from the ring's own counting.
+    issue(0);
+
+    const int b0 = qb * 32 * QS;                  // first row of the workgroup's block
+    const int i0 = b0 + 32 * qs;                  // first row of this wave's slab
+    const bool live = i0 < n;                     // the block's last slabs may lie past the segment
+    const int q_last = min(n, i0 + 32) - 1;
+    const int n_tiles = live ? key_tile_end<BN>(pos, off, n, q_last) : 0;
+    const int n_tiles_wg = key_tile_end<BN>(pos, off, n, min(n, b0 + 32 * QS) - 1);
+    const int n_it = (n_tiles_wg + SPL - 1) / SPL;
+
+    const int qi = min(i0 + l32, n - 1);
+    const int32_t my_pos = pos[off + qi];
+    const float c = qk_scale * LOG2E;
+    // The logit in the exp2 domain is c * (q.k + gb * bias): the bias term
+    // seeds the S^T accumulators, the scale c is applied inside exp2.
+    const float gb = gain[h] / qk_scale;
+
+    bf16x8 qf[KS];
+    {
+        const uint16_t* qrow = q + ((off + qi) * hq + h) * D + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(qrow + s * 16);
+    }
+    // The ring's vmcnt bookkeeping counts only its own loads: finish every
+    // other vector-memory load (and the first stage) first and keep the
+    // compiler from moving any past this point.
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
 
     // Per-lane parts of the LDS operand addresses (stage base added per tile).
     // K: key row l32, chunk (2s + hh) ^ swz_k(row), which is the s = 0 chunk
@@ -465,7 +471,7 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
     // iteration it+NSTG-1 go into that iteration's stage before this
     // iteration's compute.
 #pragma unroll
-    for (int i = 0; i < NSTG - 1; ++i)
+    for (int i = 1; i < NSTG - 1; ++i)
         if (i < n_it) issue(i);
     for (int it = 0; it < n_it; ++it) {
         // every load of iterations <= it has landed (this wave's); the later
