@@ -11,9 +11,10 @@
 // bf16 path (flash-attention style, online softmax, v_mfma_f32_32x32x16_bf16):
 //  * Each wave owns 32 query rows of one query head. A workgroup holds the
 //    query heads of one KV head that share its K/V (GQA; 2 when Hq/Hkv is
-//    even), times query slabs, times key splits; two shapes (see
-//    attention_config): short prompts take 32 rows x 2 key splits, long
-//    prompts 2 slabs of 32 rows sharing every K/V tile with one split.
+//    even), times query slabs, times key splits; three shapes (see
+//    launch_cfg): short prompts take 32 rows x 2 key splits, long prompts 2
+//    slabs of 32 rows sharing every K/V tile with one split, and the longest
+//    the same at three workgroups per CU.
 //  * S^T = K Q^T: K (keys x d) is the A operand read from LDS, Q^T the B
 //    operand kept in registers for the whole key loop. The 32x32 result
 //    layout puts one query column in each lane (keys down its registers),
@@ -119,7 +120,7 @@ __device__ __forceinline__ int swz_v(int row) { return CH == 16 ? ((row & 3) << 
 // (ds_read_b128) and the V^T operand reads (ds_read_b64_tr_b16) free of
 // bank conflicts. The splits' (max, sum, O) are merged through LDS at the
 // end, in split order.
-template <int D, int HW, int QS, int SPL, int NSTG, int OCC>
+template <int D, int HW, int QS, int SPL, int NSTG, int OCC, int VA = D / 32>
 __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ bias, const int32_t* __restrict__ pos, AttnTable t, int hq, int hkv,
@@ -145,6 +146,7 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
     constexpr int KS = D / 16;                    // k-steps of q.k
     constexpr int DB = D / 32;                    // 32-wide d blocks of O
     constexpr int PS = BN / 16;                   // 16-key k-steps of P.V per tile
+    static_assert(VA >= 1 && VA <= DB, "V^T blocks read ahead");
     constexpr int SM = 64;                        // bias/pos entries per tile (one dword load)
     constexpr int STAGEB = NTL * TILEB;
 
@@ -395,8 +397,7 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
         for (int s = 0; s < KS; ++s) acc_s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc_s, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 vf[DB][PS];
-#pragma unroll
-        for (int b = 0; b < DB; ++b) {
+        auto read_v = [&](int b) __attribute__((always_inline)) {
             const uint32_t vb = va ^ (uint32_t)(b << 6);
 #pragma unroll
             for (int s = 0; s < PS; ++s) {
@@ -404,7 +405,9 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
                 const v4i16 hi = lds_read_tr16((const LDS_AS char*)(uintptr_t)(vb + (16 * s + 8) * ROWB));
                 vf[b][s] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
-        }
+        };
+#pragma unroll
+        for (int b = 0; b < VA; ++b) read_v(b);
         __builtin_amdgcn_sched_barrier(0);
         // acc_s now holds q.k + gb * bias; the exp2-domain logit is c times it.
         if (need_mask) {
@@ -459,10 +462,19 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
             pf[s] = __builtin_bit_cast(bf16x8, w);
         }
         l_run += lsum;
+        // With VA < DB only VA d blocks of V^T are read ahead of the softmax;
+        // block b + VA's reads go out before block b's MFMAs, so at most
+        // VA + 1 blocks of V^T are live (fewer registers).
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
+        for (int b = 0; b < DB; ++b) {
+            if (b + VA < DB) {
+                __builtin_amdgcn_sched_barrier(0);
+                read_v(b + VA);
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int s = 0; s < PS; ++s) acc_o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[b][s], pf[s], acc_o[b], 0, 0, 0);
+        }
     };
 
     // Ring with one barrier per iteration: stage it%NSTG holds iteration it.
@@ -652,19 +664,35 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 
 int heads_per_wg(int g) { return (g % 2 == 0) ? 2 : 1; }
 
-// Prompts of at least this many kept rows take the long-prompt shape.
+// Prompts of at least this many kept rows take the long-prompt shape, and
+// from ATTN_XL_ROWS on (head_dim 128) its three-workgroups-per-CU form.
 constexpr int64_t ATTN_LONG_ROWS = 4096;
+constexpr int64_t ATTN_XL_ROWS = 16384;
 
-// The two kernel shapes (HW heads per item in both):
+// The kernel shapes (HW heads per item in all):
 //  0 (short prompts): 32 query rows x 2 key splits, 2-stage ring, two
 //    workgroups per CU: the splits halve the serial chain of the longest
 //    query blocks, which bounds a short causal problem;
 //  1 (long prompts): 2 slabs of 32 query rows share every K/V tile (half
-//    the loaded bytes per MFMA), one key split, 3-stage ring.
+//    the loaded bytes per MFMA), one key split, 3-stage ring, two workgroups
+//    per CU;
+//  2 (the longest prompts, head_dim 128, two query heads per KV head in
+//    the workgroup; other heads take shape 1): shape 1 at three workgroups per
+//    CU, which the registers allow once only one d block of V^T is read
+//    ahead of the softmax (the rest one block ahead of its MFMAs). The third
+//    workgroup hides more latency than the later V^T reads expose once
+//    there are enough work items to keep it busy.
 template <int D, int HW>
 void launch_cfg(int cfg, dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                 const float* bias, const int32_t* pos, const AttnTable& t, int hq, int hkv, const float* gain,
                 float qk_scale, uint16_t* out, float* lse) {
+    if constexpr (D == 128 && HW == 2) {
+        if (cfg == 2) {
+            hipLaunchKernelGGL((attn_bf16_kernel<D, HW, 2, 1, 3, 3, 1>), grid, dim3(64 * HW * 2), 0, st, q, k, v, bias,
+                               pos, t, hq, hkv, gain, qk_scale, out, lse);
+            return;
+        }
+    }
     if (cfg == 0)
         hipLaunchKernelGGL((attn_bf16_kernel<D, HW, 1, 2, 2, HW == 2 ? 2 : 1>), grid, dim3(64 * HW * 2), 0, st, q, k, v, bias, pos,
                            t, hq, hkv, gain, qk_scale, out, lse);
@@ -683,7 +711,7 @@ AttnConfig attention_config(tg_dtype dt, int hq, int hkv, int64_t max_rows) {
         c.heads_per_item = 1;
         return c;
     }
-    const int cfg = max_rows >= ATTN_LONG_ROWS ? 1 : 0;
+    const int cfg = max_rows >= ATTN_XL_ROWS ? 2 : (max_rows >= ATTN_LONG_ROWS ? 1 : 0);
     c.kind = cfg;
     c.block_rows = cfg == 0 ? 32 : 64;
     c.heads_per_item = heads_per_wg(hq / hkv);

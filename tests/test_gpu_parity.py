@@ -359,9 +359,9 @@ def test_attention_reduces_to_sdpa_full_budget_zero_gain():
     assert_rowmax_close(f64(o), ref[0].permute(1, 0, 2).double().numpy())
 
 
-def test_attention_bf16_long_sampled():
-    note("attention bf16 long kept set (M=9152), 128 sampled query rows")
-    m = 9152
+@pytest.mark.parametrize("m", [9152, 17000], ids=["long-shape", "xl-shape"])
+def test_attention_bf16_long_sampled(m):
+    note(f"attention bf16 long kept set (M={m}), 128 sampled query rows")
     a = make_attention_inputs([m], 16, 8, 128, seed=31, dtype=torch.bfloat16, n_query_tail=1024)
     o, lse = run_attention(a, 16, 8)
     rows = np.unique(np.concatenate([np.random.default_rng(1).choice(m, 120, replace=False),
@@ -370,7 +370,8 @@ def test_attention_bf16_long_sampled():
     assert_rowmax_close(f64(o)[rows], ro[rows])
 
 
-@pytest.mark.parametrize("segs", [[1000, 23], [4200, 23, 1]], ids=["short-shape", "long-shape"])
+@pytest.mark.parametrize("segs", [[1000, 23], [4200, 23, 1], [16500, 23, 1]],
+                         ids=["short-shape", "long-shape", "xl-shape"])
 def test_attention_deterministic_and_fully_written(segs):
     note(f"attention determinism and poisoned-output check, prompts {segs}")
     a = make_attention_inputs(segs, 16, 8, 128, seed=3, dtype=torch.bfloat16)
