@@ -34,7 +34,9 @@
 //     16 wave totals rank every lane's first row; the lane then walks its
 //     own consecutive rows, writing each kept row id to its slot of an LDS
 //     staging array (rows not kept write a per-lane scratch word, so no lane
-//     masking is needed), and the staged slots go out in one coalesced copy.
+//     masking is needed; at 16 rows per lane, a lane without tied rows
+//     visits only the bits of its kept rows), and the staged slots go out in
+//     one coalesced copy.
 //     Streaming path: lane l of a wave step holds rows l, l+64, ...; ballots
 //     + mbcnt rank them and kept rows are stored directly.
 // The kernel is bound by its own instruction count on one CU, so the hot
@@ -225,16 +227,32 @@ __device__ __forceinline__ void select_registers(Smem& sm, const SeqDesc& sd,
         pt += (w < wave) ? sm.wtot[w][1] : 0u;
     }
     const uint32_t n_kept = (uint32_t)sd.n_kept;
-    const int trash = RMAX + RMAX / 64 + lane;
+    if (WU == 16 && mt_bits == 0u) {
+        // A lane with no tied row (all but a few): its kept rows are exactly
+        // its above rows, in consecutive slots from pa + min(pt, rem), so
+        // only their bits are visited. (At 32 rows per lane the longer
+        // per-bit loop does not pay.)
+        uint32_t m = ma_bits;
+        uint32_t slot = pa + min(pt, rem);
+        const uint32_t row0 = (uint32_t)(sd.start + rbase);
+        while (m != 0u) {
+            const int u = __builtin_ctz(m);
+            if (slot < n_kept) sm.stage[slot] = row0 + (uint32_t)u;  // always true when the counts are right
+            ++slot;
+            m &= m - 1u;
+        }
+    } else {
+        const int trash = RMAX + RMAX / 64 + lane;
 #pragma unroll
-    for (int u = 0; u < WU; ++u) {
-        const uint32_t above = (ma_bits >> u) & 1u, tied = (mt_bits >> u) & 1u;
-        const uint32_t slot = pa + min(pt, rem);
-        // slot < n_kept always holds for a kept row when the counts are right
-        const uint32_t keep = (above | (tied & (uint32_t)(pt < rem))) & (uint32_t)(slot < n_kept);
-        sm.stage[keep ? (int)slot : trash] = (uint32_t)(sd.start + rbase + u);
-        pa += above;
-        pt += tied;
+        for (int u = 0; u < WU; ++u) {
+            const uint32_t above = (ma_bits >> u) & 1u, tied = (mt_bits >> u) & 1u;
+            const uint32_t slot = pa + min(pt, rem);
+            // slot < n_kept always holds for a kept row when the counts are right
+            const uint32_t keep = (above | (tied & (uint32_t)(pt < rem))) & (uint32_t)(slot < n_kept);
+            sm.stage[keep ? (int)slot : trash] = (uint32_t)(sd.start + rbase + u);
+            pa += above;
+            pt += tied;
+        }
     }
     __syncthreads();
     for (int j = tid; j < sd.n_kept; j += ST) kept[sd.kept_off + j] = (int32_t)sm.stage[j];
