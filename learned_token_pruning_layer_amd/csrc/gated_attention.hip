@@ -33,8 +33,10 @@
 //    workgroup's last visible key are skipped, and waves whose queries
 //    precede a whole tile skip its math.
 //  * Work items run longest-first (last query blocks of a prompt first),
-//    except that the second CU's worth of items runs in reverse, pairing the
-//    longest items with shorter neighbours on each CU.
+//    except that the longest items share their CU with short ones, and when
+//    fewer than a CU's worth of items remain after two per CU, the shortest
+//    go first (their CUs then take the rest), so the longest items soon run
+//    alone.
 //
 // fp32 path: one thread per query row, K/V tiles in LDS, plain fp32 FMA.
 #include "tg_internal.hpp"
@@ -169,17 +171,31 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
     // Work item: consecutive items differ in KV head first, so with 8 KV
     // heads each XCD (items are dealt round-robin to the 8 XCDs) serves one
     // KV head and keeps its K/V in its own L2; query blocks run longest first.
-    // The first C workgroups (C = the device's CUs) take the C longest items,
-    // one per CU; the next C, which share those CUs, take the following items
-    // in reverse order (in groups of 8, so each XCD keeps its KV head), so
-    // the longest items share their CU with the shortest of that group and
-    // soon run alone, at the faster single-workgroup rate, through the tail.
+    // Workgroups b and b + C (C = the device's CUs) share a CU, and
+    // workgroups from 2C on take the first slots that free up. The mapping
+    // below pairs the longest items with short ones (reversed in groups of
+    // 8, so each XCD keeps its KV head), so that they soon run alone, at the
+    // faster single-workgroup rate, through the tail. With L = N - 2C later
+    // workgroups (0 < L < C), the L shortest items go first, to their own
+    // CUs: those slots free up first and take the later workgroups, away
+    // from the CUs of the longest items.
     int item = blockIdx.x;
     {
-        const int C = t.cus, n2 = min(2 * t.cus, t.n_items);
-        if (C > 0 && item >= C && item < n2) {
-            const int g = (item - C) >> 3, r = (item - C) & 7, G2 = (n2 - C) >> 3;
-            if (g < G2) item = C + ((G2 - 1 - g) << 3) + r;
+        const int C = t.cus, N = t.n_items, L = N - 2 * C, b = item;
+        if (C > 0 && L > 0 && L < C && (C & 7) == 0 && (L & 7) == 0) {
+            if (b < L) item = N - L + b;                      // the L shortest items
+            else if (b < C + L) item = b - L;                 // the C - L longest, then their
+                                                              // partners of the shortest
+            else if (b < 2 * C) {                             // partners of the longest, reversed
+                const int j = b - C - L, g = j >> 3, r = j & 7, G = (C - L) >> 3;
+                item = C + L + ((G - 1 - g) << 3) + r;
+            } else item = C + (b - 2 * C);                    // the later workgroups
+        } else {
+            const int n2 = min(2 * C, N);
+            if (C > 0 && item >= C && item < n2) {
+                const int g = (item - C) >> 3, r = (item - C) & 7, G2 = (n2 - C) >> 3;
+                if (g < G2) item = C + ((G2 - 1 - g) << 3) + r;
+            }
         }
     }
     int sg = 0;
