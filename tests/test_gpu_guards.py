@@ -99,7 +99,8 @@ def test_guard_compact():
 
 
 @pytest.mark.parametrize("dt,segs", [(torch.bfloat16, [1000, 23, 1]), (torch.float32, [1000, 23, 1]),
-                                     (torch.bfloat16, [4200, 23, 1])], ids=["bf16-short", "fp32", "bf16-long"])
+                                     (torch.bfloat16, [4200, 23, 1]), (torch.bfloat16, [16400, 23, 1])],
+                         ids=["bf16-short", "fp32", "bf16-long", "bf16-xl"])
 def test_guard_attention(dt, segs):
     note(f"guards: token-gated attention ({dt}, prompts {segs}), output and lse")
     hq, hkv, d = 16, 8, 128
