@@ -183,10 +183,10 @@ __global__ __launch_bounds__(64 * HW * QS * SPL, OCC) void attn_bf16_kernel(
     {
         const int C = t.cus, N = t.n_items, L = N - 2 * C, b = item;
         if (C > 0 && L > 0 && L < C && (C & 7) == 0 && (L & 7) == 0) {
-            if (b < L) item = N - L + b;                      // the L shortest items
-            else if (b < C + L) item = b - L;                 // the C - L longest, then their
-                                                              // partners of the shortest
-            else if (b < 2 * C) {                             // partners of the longest, reversed
+            if (b < L) item = N - L + b;                      // CUs 0..L-1: the L shortest items
+            else if (b < C + L) item = b - L;                 // CUs L..C-1: the C - L longest items;
+                                                              // then the partners on CUs 0..L-1
+            else if (b < 2 * C) {                             // partners on CUs L..C-1, reversed
                 const int j = b - C - L, g = j >> 3, r = j & 7, G = (C - L) >> 3;
                 item = C + L + ((G - 1 - g) << 3) + r;
             } else item = C + (b - 2 * C);                    // the later workgroups
