@@ -16,7 +16,10 @@
 // and the score of a kept document row gets db_j * sigmoid(-s_j) (the
 // derivative of logsigmoid); question and pruned rows get 0.
 //
-// Kernels (bf16 inputs, fp32 gradients):
+// Three launches (bf16 inputs, fp32 gradients): prep; one grid whose work
+// items alternate between the dkdv pass (2) and the dq pass (3), so that the
+// two passes share the chip and neither's tail runs alone; one grid for the
+// reductions (4).
 //  1. prep: Dl[h][i] = dO_i . o_i (the softmax row term).
 //  2. dkdv: one wave per (prompt, 32-key block, query head). The key block
 //     sits in LDS; the wave walks the query blocks that can see it and
@@ -40,10 +43,11 @@
 //  and 3 is split over two waves, each walking half of the blocks; their
 //  partials are summed in a fixed order below.
 //  4. reduce: sums the per-head partials of each KV head in a fixed order
-//     (so the result is deterministic) and applies the gains to db; a last
-//     kernel reduces dg_h = sum_j b_j sum_i dS_ij per head and dtau from the
-//     per-key sums of dS_ij (q_i . k_j), each in a fixed order. The score
-//     kernel applies sigmoid(-s).
+//     (so the result is deterministic) and applies the gains to db; other
+//     workgroups of the same grid reduce dg_h = sum_j b_j sum_i dS_ij per
+//     head and dtau from the per-key sums of dS_ij (q_i . k_j), each in a
+//     fixed order, and sum the dq parts of split items. The score kernel
+//     applies sigmoid(-s).
 // LDS tiles are row-major with a 16-byte pad per row (row stride D*2+16
 // bytes), which spreads both the row reads and the transpose reads over
 // the banks.
@@ -196,21 +200,19 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 // sum_i dS_ij and sum_i dS_ij (q_i . k_j). ws layout per part (fp32): dk
 // [hq][M][D], dv [hq][M][D], db [hq][M], dt [hq][M].
 template <int D>
-__global__ __launch_bounds__(64) void bwd_dkdv_kernel(
+__device__ __forceinline__ void bwd_dkdv_body(
+    int item, LDS_AS char* kt, LDS_AS char* vt, LDS_AS char* qt, LDS_AS char* dot, LDS_AS float* s_nlse,
+    LDS_AS float* s_dl, LDS_AS int32_t* s_pos,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ d_out, const float* __restrict__ lse, const float* __restrict__ dl,
     const float* __restrict__ bias, const int32_t* __restrict__ pos, BwdTable t, int hq, int hkv,
     const float* __restrict__ gain, float c, float* __restrict__ ws_dk, float* __restrict__ ws_dv,
     float* __restrict__ ws_db, float* __restrict__ ws_dt) {
     constexpr int KS = D / 16, DB = D / 32;
-    __shared__ __attribute__((aligned(16))) char kt[Tile<D>::BYTES], vt[Tile<D>::BYTES];
-    __shared__ __attribute__((aligned(16))) char qt[Tile<D>::BYTES], dot[Tile<D>::BYTES];
-    __shared__ __attribute__((aligned(16))) float s_nlse[32], s_dl[32];
-    __shared__ __attribute__((aligned(16))) int32_t s_pos[32];
     const int lane = threadIdx.x;
     const int hh = lane >> 5, l32 = lane & 31;
     int sg, jb, h, part;
-    bwd_item(t, blockIdx.x, hq, false, sg, jb, h, part);  // early key blocks see the most queries
+    bwd_item(t, item, hq, false, sg, jb, h, part);  // early key blocks see the most queries
     const int64_t off = t.s[sg].off, m = t.m_total;
     const int n = t.s[sg].n;
     const int kvh = h / (hq / hkv);
@@ -395,20 +397,19 @@ __global__ __launch_bounds__(64) void bwd_dkdv_kernel(
 
 // 3. dQ of one (prompt, query block, head).
 template <int D>
-__global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+__device__ __forceinline__ void bwd_dq_body(int item, LDS_AS char* kt, LDS_AS char* vt, LDS_AS float* s_kb,
+                                            LDS_AS int32_t* s_p, const uint16_t* __restrict__ q,
+                                            const uint16_t* __restrict__ k,
                                                    const uint16_t* __restrict__ v,
                                                    const uint16_t* __restrict__ d_out, const float* __restrict__ lse,
                                                    const float* __restrict__ dl, const float* __restrict__ bias,
                                                    const int32_t* __restrict__ pos, BwdTable t, int hq, int hkv,
                                                    const float* __restrict__ gain, float c, float* __restrict__ dq) {
     constexpr int KS = D / 16, DB = D / 32;
-    __shared__ __attribute__((aligned(16))) char kt[Tile<D>::BYTES], vt[Tile<D>::BYTES];
-    __shared__ __attribute__((aligned(16))) float s_kb[32];
-    __shared__ __attribute__((aligned(16))) int32_t s_p[32];
     const int lane = threadIdx.x;
     const int hh = lane >> 5, l32 = lane & 31;
     int sg, ib, h, part;
-    bwd_item(t, blockIdx.x, hq, true, sg, ib, h, part);  // late query blocks see the most keys
+    bwd_item(t, item, hq, true, sg, ib, h, part);  // late query blocks see the most keys
     const int64_t off = t.s[sg].off, m = t.m_total;
     const int n = t.s[sg].n;
     const int kvh = h / (hq / hkv);
@@ -554,17 +555,43 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const uint16_t* __restrict__
     }
 }
 
+// 2 + 3 in one launch: work item pairs alternate between the dkdv and dq
+// passes (both in their longest-first orders), so one grid keeps the chip
+// busy through both and neither pass's tail runs alone. The LDS of a
+// workgroup is shared by the two bodies (one runs per workgroup).
+template <int D>
+__global__ __launch_bounds__(64) void bwd_main_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ d_out, const float* __restrict__ lse, const float* __restrict__ dl,
+    const float* __restrict__ bias, const int32_t* __restrict__ pos, BwdTable t, int hq, int hkv,
+    const float* __restrict__ gain, float c, float* __restrict__ ws_dk, float* __restrict__ ws_dv,
+    float* __restrict__ ws_db, float* __restrict__ ws_dt, float* __restrict__ dq) {
+    __shared__ __attribute__((aligned(16))) char tiles[4 * Tile<D>::BYTES];
+    __shared__ __attribute__((aligned(16))) float sf[2][32];
+    __shared__ __attribute__((aligned(16))) int32_t si[32];
+    LDS_AS char* base = (LDS_AS char*)tiles;
+    LDS_AS float* f0 = (LDS_AS float*)&sf[0][0];
+    LDS_AS float* f1 = (LDS_AS float*)&sf[1][0];
+    LDS_AS int32_t* i0 = (LDS_AS int32_t*)&si[0];
+    constexpr int TB = Tile<D>::BYTES;
+    const int item = (int)(blockIdx.x >> 1);
+    if ((blockIdx.x & 1) == 0)
+        bwd_dkdv_body<D>(item, base, base + TB, base + 2 * TB, base + 3 * TB, f0, f1, i0, q, k, v, d_out, lse, dl,
+                         bias, pos, t, hq, hkv, gain, c, ws_dk, ws_dv, ws_db, ws_dt);
+    else
+        bwd_dq_body<D>(item, base, base + TB, f0, i0, q, k, v, d_out, lse, dl, bias, pos, t, hq, hkv, gain, c, dq);
+}
+
 // 4a. dK, dV = sums of the per-head partials over each KV head's query
 // heads (in head order); db = sum over heads of g_h times the head's
 // sum_i dS_ij.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ ws_dk,
+__device__ __forceinline__ void bwd_reduce_body(int64_t idx, const float* __restrict__ ws_dk,
                                                         const float* __restrict__ ws_dv,
                                                         const float* __restrict__ ws_db,
                                                         const float* __restrict__ gain, int64_t m, int hq, int hkv,
                                                         int parts, float* __restrict__ dk, float* __restrict__ dv,
                                                         float* __restrict__ db) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over m * hkv * D
     const int gsz = hq / hkv;
     if (idx < m * hkv * D) {
         const int64_t row = idx / (hkv * D);
@@ -604,9 +631,8 @@ __device__ __forceinline__ float block_sum_1024(float v, float* part) {
 }
 
 // dQ = the sum of its parts, in part order.
-__global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const float* __restrict__ ws_dq, int64_t n,
-                                                        float* __restrict__ dq) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void bwd_dq_sum_body(int64_t i, const float* __restrict__ ws_dq, int64_t n,
+                                                float* __restrict__ dq) {
     if (i < n) dq[i] = ws_dq[i] + ws_dq[n + i];
 }
 
@@ -614,12 +640,10 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const float* __restrict
 // Workgroup hq: dtau = -(c/tau) times the sum of the per-key, per-head sums
 // of dS_ij (q_i . k_j) over every part. Each thread keeps four loads in
 // flight; the summation order is fixed.
-__global__ __launch_bounds__(1024) void bwd_scalars_kernel(const float* __restrict__ ws_db,
-                                                          const float* __restrict__ bias, int64_t m, int hq, int parts,
-                                                          const float* __restrict__ ws_dt, float dtau_scale,
-                                                          float* __restrict__ dgain, float* __restrict__ dtau) {
-    __shared__ float part[16];
-    const int h = blockIdx.x;
+__device__ __forceinline__ void bwd_scalars_body(int h, float* part, const float* __restrict__ ws_db,
+                                                 const float* __restrict__ bias, int64_t m, int hq, int parts,
+                                                 const float* __restrict__ ws_dt, float dtau_scale,
+                                                 float* __restrict__ dgain, float* __restrict__ dtau) {
     const bool gain_wg = h < hq;
     const float* x = gain_wg ? ws_db + (int64_t)h * m : ws_dt;
     const int64_t len = gain_wg ? m : (int64_t)parts * hq * m;
@@ -650,6 +674,30 @@ __global__ __launch_bounds__(1024) void bwd_scalars_kernel(const float* __restri
     }
 }
 
+// 4 in one launch of 1024-thread workgroups: workgroups 0 .. hq the
+// scalars (the longest, latency-bound sums, first), then the reduction of
+// dK / dV / db, then (split items only) the dQ part sums.
+template <int D>
+__global__ __launch_bounds__(1024) void bwd_post_kernel(const float* __restrict__ ws_dk, const float* __restrict__ ws_dv,
+                                                       const float* __restrict__ ws_db, const float* __restrict__ gain,
+                                                       int64_t m, int hq, int hkv, int parts, float* __restrict__ dk,
+                                                       float* __restrict__ dv, float* __restrict__ db,
+                                                       const float* __restrict__ bias, const float* __restrict__ ws_dt,
+                                                       float dtau_scale, float* __restrict__ dgain,
+                                                       float* __restrict__ dtau, int n_red,
+                                                       const float* __restrict__ ws_dq, float* __restrict__ dq) {
+    __shared__ float part[16];
+    const int b = (int)blockIdx.x;
+    if (b <= hq) {
+        bwd_scalars_body(b, part, ws_db, bias, m, hq, parts, ws_dt, dtau_scale, dgain, dtau);
+    } else if (b <= hq + n_red) {
+        bwd_reduce_body<D>((int64_t)(b - hq - 1) * 1024 + threadIdx.x, ws_dk, ws_dv, ws_db, gain, m, hq, hkv, parts,
+                           dk, dv, db);
+    } else {
+        bwd_dq_sum_body((int64_t)(b - hq - 1 - n_red) * 1024 + threadIdx.x, ws_dq, m * hq * D, dq);
+    }
+}
+
 template <int D>
 hipError_t launch_bwd_d(const AttnBwdArgs& a, const BwdTable& t, float c, hipStream_t st) {
     const int64_t m = t.m_total;
@@ -661,22 +709,18 @@ hipError_t launch_bwd_d(const AttnBwdArgs& a, const BwdTable& t, float c, hipStr
     float* ws_db = ws_dv + (int64_t)np * a.hq * m * D;
     float* ws_dt = ws_db + (int64_t)np * a.hq * m;
     float* ws_dq = ws_dt + (int64_t)np * a.hq * m;  // split: the dq parts; else dq is written directly
-    const int64_t n_red = (m * a.hkv * D + 255) / 256;
     const uint16_t *q = (const uint16_t*)a.q, *k = (const uint16_t*)a.k, *v = (const uint16_t*)a.v;
     const uint16_t *dout = (const uint16_t*)a.d_out, *out = (const uint16_t*)a.out;
     hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((m * a.hq + 255) / 256)), dim3(256), 0, st, dout, out, m,
                        a.hq, dl);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)t.n_items), dim3(64), 0, st, q, k, v, dout, a.lse, dl,
-                       a.bias, a.pos, t, a.hq, a.hkv, a.gain, c, ws_dk, ws_dv, ws_db, ws_dt);
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)t.n_items), dim3(64), 0, st, q, k, v, dout, a.lse, dl,
-                       a.bias, a.pos, t, a.hq, a.hkv, a.gain, c, np > 1 ? ws_dq : a.d_q);
-    if (np > 1)
-        hipLaunchKernelGGL(bwd_dq_sum_kernel, dim3((unsigned)((m * a.hq * D + 255) / 256)), dim3(256), 0, st, ws_dq,
-                           m * a.hq * D, a.d_q);
-    hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3((unsigned)n_red), dim3(256), 0, st, ws_dk, ws_dv, ws_db,
-                       a.gain, m, a.hq, a.hkv, np, a.d_k, a.d_v, a.d_bias);
-    hipLaunchKernelGGL(bwd_scalars_kernel, dim3((unsigned)(a.hq + 1)), dim3(1024), 0, st, ws_db, a.bias, m, a.hq, np,
-                       ws_dt, -c / a.tau, a.d_gain, a.d_tau);
+    hipLaunchKernelGGL((bwd_main_kernel<D>), dim3((unsigned)(2 * t.n_items)), dim3(64), 0, st, q, k, v, dout, a.lse,
+                       dl, a.bias, a.pos, t, a.hq, a.hkv, a.gain, c, ws_dk, ws_dv, ws_db, ws_dt,
+                       np > 1 ? ws_dq : a.d_q);
+    const int n_red = (int)((m * a.hkv * D + 1023) / 1024);
+    const int n_sum = np > 1 ? (int)((m * a.hq * D + 1023) / 1024) : 0;
+    hipLaunchKernelGGL((bwd_post_kernel<D>), dim3((unsigned)(a.hq + 1 + n_red + n_sum)), dim3(1024), 0, st, ws_dk,
+                       ws_dv, ws_db, a.gain, m, a.hq, a.hkv, np, a.d_k, a.d_v, a.d_bias, a.bias, ws_dt, -c / a.tau,
+                       a.d_gain, a.d_tau, n_red, ws_dq, a.d_q);
     return hipGetLastError();
 }
 
