@@ -27,6 +27,9 @@
 //     list) workgroup, one wave per 32 hidden units; the chunk's gathered
 //     x columns are staged in LDS and read transposed.
 //  D. reductions of the partials in a fixed order (deterministic).
+// Launches: A; then B, C and the small reductions of D (which read only
+// what A wrote) in one grid, so none of them runs alone; then dW1's
+// reduction.
 // Inside each 16-wide k step the transpose read hands lane half hh the k
 // indices 8(e/4) + 4hh + e%4 (e = 0..7); dZ and dZ^T are stored with bits
 // 2 and 3 of the index inside each 16-group swapped, so a plain 16-byte
@@ -164,18 +167,20 @@ __global__ __launch_bounds__(256) void gbwd_dz_kernel(const uint16_t* __restrict
 // B. dx[rows[m]] += dZ[m] W1 for 128 list rows x 32 columns of d (one wave
 // per 32 rows). acc register j: list row m0 + 8(j/4) + 4hh + j%4, column
 // d0 + lane%32.
-__global__ __launch_bounds__(256) void gbwd_dx_kernel(const uint16_t* __restrict__ dz,
-                                                      const uint16_t* __restrict__ w1, int d, int hdim,
-                                                      const int32_t* __restrict__ rows, int64_t n_list,
-                                                      int64_t n_rows, float* __restrict__ d_x) {
-    __shared__ __attribute__((aligned(16))) char wt[256 * 64];  // W1[0..H)[d0..d0+32)
-    const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
-    const int d0 = 32 * blockIdx.y;
-    const int64_t m0 = 128LL * blockIdx.x + 32 * (tid >> 6);
-    for (int idx = tid; idx < hdim * 4; idx += 256)
-        *(LDS_AS u32x4*)(wt + idx * 16) = *(const u32x4*)(w1 + (int64_t)(idx >> 2) * d + d0 + (idx & 3) * 8);
+// Runs on 256 threads (tid 0..255) with a 16 KB LDS slice; `live` false:
+// only the barrier (the other half of the workgroup may need it).
+__device__ __forceinline__ void gbwd_dx_body(bool live, int bx, int by, int tid, LDS_AS char* wt,
+                                             const uint16_t* __restrict__ dz, const uint16_t* __restrict__ w1,
+                                             int d, int hdim, const int32_t* __restrict__ rows, int64_t n_list,
+                                             int64_t n_rows, float* __restrict__ d_x) {
+    const int lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+    const int d0 = 32 * by;
+    const int64_t m0 = 128LL * bx + 32 * (tid >> 6);
+    if (live)
+        for (int idx = tid; idx < hdim * 4; idx += 256)
+            *(LDS_AS u32x4*)(wt + idx * 16) = *(const u32x4*)(w1 + (int64_t)(idx >> 2) * d + d0 + (idx & 3) * 8);
     __syncthreads();
-    if (m0 >= n_list) return;
+    if (!live || m0 >= n_list) return;
     const uint16_t* arow = dz + (m0 + l32) * hdim + 8 * hh;
     f32x16 acc;
 #pragma unroll
@@ -207,25 +212,28 @@ constexpr int GKC = 256;  // list rows per dW1 chunk
 // the wave's dZ^T operands, which are loaded before any MFMA). acc
 // register j: hidden unit 32 wave + 8(j/4) + 4hh + j%4, column d0 + 32cb +
 // lane%32.
-__global__ __launch_bounds__(512) void gbwd_dw1_kernel(const uint16_t* __restrict__ x, int d,
-                                                       const uint16_t* __restrict__ dzt, int hdim,
-                                                       const int32_t* __restrict__ rows, int64_t n_list,
-                                                       int64_t n_rows, int64_t n_pad, float* __restrict__ pw1) {
-    __shared__ __attribute__((aligned(16))) char xt[2][GKC * 64];  // chunk rows x 32 columns, per block
-    const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
-    const int d0 = 64 * blockIdx.x;
-    const int64_t c0 = (int64_t)GKC * blockIdx.y;
+// Runs on all 512 threads; waves from hdim / 32 on only help stage x.
+__device__ __forceinline__ void gbwd_dw1_body(int bx, int by, int tid, LDS_AS char* xt0, LDS_AS char* xt1,
+                                              const uint16_t* __restrict__ x, int d,
+                                              const uint16_t* __restrict__ dzt, int hdim,
+                                              const int32_t* __restrict__ rows, int64_t n_list, int64_t n_rows,
+                                              int64_t n_pad, float* __restrict__ pw1) {
+    const int lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+    const bool mw = (tid >> 6) < hdim / 32;  // this wave owns 32 hidden units
+    const int d0 = 64 * bx;
+    const int64_t c0 = (int64_t)GKC * by;
     const int n_steps = (int)(min((int64_t)GKC, n_pad - c0) / 16);
     const int hrow = 32 * (tid >> 6) + l32;
     const uint16_t* arow = dzt + (int64_t)hrow * n_pad + c0 + 8 * hh;
     bf16x8 a[16];
 #pragma unroll
     for (int s = 0; s < 16; ++s)
-        if (s < n_steps) a[s] = *(const bf16x8*)(arow + 16 * s);
-    for (int idx = tid; idx < GKC * 8; idx += blockDim.x)
-        *(LDS_AS u32x4*)(xt[(idx >> 2) & 1] + (idx >> 3) * 64 + (idx & 3) * 16) =
+        if (mw && s < n_steps) a[s] = *(const bf16x8*)(arow + 16 * s);
+    for (int idx = tid; idx < GKC * 8; idx += 512)
+        *(LDS_AS u32x4*)((((idx >> 2) & 1) ? xt1 : xt0) + (idx >> 3) * 64 + (idx & 3) * 16) =
             *(const u32x4*)(x + list_row(rows, c0 + (idx >> 3), n_list, n_rows) * d + d0 + (idx & 7) * 8);
     __syncthreads();
+    if (!mw) return;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
         f32x16 acc;
@@ -235,8 +243,8 @@ __global__ __launch_bounds__(512) void gbwd_dw1_kernel(const uint16_t* __restric
         for (int s = 0; s < 16; ++s)
             if (s < n_steps)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    a[s], tr_operand64((const LDS_AS char*)xt[cb], 16 * s, lane), acc, 0, 0, 0);
-        float* out = pw1 + ((int64_t)blockIdx.y * hdim + 32 * (tid >> 6)) * d + d0 + 32 * cb + l32;
+                    a[s], tr_operand64((const LDS_AS char*)(cb ? xt1 : xt0), 16 * s, lane), acc, 0, 0, 0);
+        float* out = pw1 + ((int64_t)by * hdim + 32 * (tid >> 6)) * d + d0 + 32 * cb + l32;
 #pragma unroll
         for (int j = 0; j < 16; ++j) out[(int64_t)(8 * (j >> 2) + 4 * hh + (j & 3)) * d] = acc[j];
     }
@@ -256,22 +264,21 @@ __global__ __launch_bounds__(256) void gbwd_reduce_w1_kernel(const float* __rest
 // partials (each lane a strided share, then a butterfly). Workgroup H: db2,
 // the sum of the listed score gradients (four loads in flight per thread,
 // then a fixed-order tree). Summation orders are fixed.
-__global__ __launch_bounds__(256) void gbwd_reduce_small_kernel(const float* __restrict__ pw2,
-                                                                const float* __restrict__ pb1, int n_mt, int hdim,
-                                                                const float* __restrict__ d_scores,
-                                                                const int32_t* __restrict__ rows, int64_t n_list,
-                                                                int64_t n_rows, float* __restrict__ d_w2,
-                                                                float* __restrict__ d_b1, float* __restrict__ d_b2) {
-    __shared__ float part[2][4];
-    const int tid = threadIdx.x;
-    const int h = blockIdx.x;
+// Runs on 256 threads (tid 0..255); h > hdim: only the barrier.
+__device__ __forceinline__ void gbwd_reduce_small_body(int h, int tid, float (*part)[4],
+                                                       const float* __restrict__ pw2,
+                                                       const float* __restrict__ pb1, int n_mt, int hdim,
+                                                       const float* __restrict__ d_scores,
+                                                       const int32_t* __restrict__ rows, int64_t n_list,
+                                                       int64_t n_rows, float* __restrict__ d_w2,
+                                                       float* __restrict__ d_b1, float* __restrict__ d_b2) {
     float sw = 0.0f, sb = 0.0f;
     if (h < hdim) {
         for (int t = tid; t < n_mt; t += 256) {
             sw += pw2[(int64_t)t * hdim + h];
             sb += pb1[(int64_t)t * hdim + h];
         }
-    } else {
+    } else if (h == hdim) {
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int64_t i0 = tid; i0 < n_list; i0 += 4 * 256) {
             float v[4];
@@ -295,7 +302,7 @@ __global__ __launch_bounds__(256) void gbwd_reduce_small_kernel(const float* __r
         part[1][tid >> 6] = sb;
     }
     __syncthreads();
-    if (tid == 0) {
+    if (tid == 0 && h <= hdim) {
         const float tw = (part[0][0] + part[0][1]) + (part[0][2] + part[0][3]);
         const float tb = (part[1][0] + part[1][1]) + (part[1][2] + part[1][3]);
         if (h < hdim) {
@@ -305,6 +312,39 @@ __global__ __launch_bounds__(256) void gbwd_reduce_small_kernel(const float* __r
             *d_b2 = tw;
         }
     }
+}
+
+// B + C + D2 in one launch of 512-thread workgroups (all three read only
+// what A wrote): first the small reductions (two hidden units per
+// workgroup, one per half), then the dW1 partials, then dx (two of its
+// 128-row x 32-column tiles per workgroup, one per half).
+__global__ __launch_bounds__(512) void gbwd_mid_kernel(
+    const uint16_t* __restrict__ x, int d, const uint16_t* __restrict__ w1, int hdim,
+    const uint16_t* __restrict__ dz, const uint16_t* __restrict__ dzt, const float* __restrict__ pw2,
+    const float* __restrict__ pb1, int n_mt, const float* __restrict__ d_scores, const int32_t* __restrict__ rows,
+    int64_t n_list, int64_t n_rows, int64_t n_pad, float* __restrict__ pw1, float* __restrict__ d_x,
+    float* __restrict__ d_w2, float* __restrict__ d_b1, float* __restrict__ d_b2, int n_small, int dw1_x,
+    int n_dw1, int dx_x, int n_dx_tiles) {
+    __shared__ __attribute__((aligned(16))) char lds[2 * GKC * 64];  // 32 KB: x chunk, or two W1 slices
+    __shared__ float part[2][2][4];
+    LDS_AS char* base = (LDS_AS char*)lds;
+    const int tid = threadIdx.x, half = tid >> 8;
+    int b = (int)blockIdx.x;
+    if (b < n_small) {
+        gbwd_reduce_small_body(2 * b + half, tid & 255, part[half], pw2, pb1, n_mt, hdim, d_scores, rows, n_list,
+                               n_rows, d_w2, d_b1, d_b2);
+        return;
+    }
+    b -= n_small;
+    if (b < n_dw1) {
+        gbwd_dw1_body(b % dw1_x, b / dw1_x, tid, base, base + GKC * 64, x, d, dzt, hdim, rows, n_list, n_rows,
+                      n_pad, pw1);
+        return;
+    }
+    b -= n_dw1;
+    const int kt = 2 * b + half;
+    gbwd_dx_body(kt < n_dx_tiles, kt % dx_x, kt / dx_x, tid & 255, base + half * (256 * 64), dz, w1, d, hdim, rows,
+                 n_list, n_rows, d_x);
 }
 
 __global__ __launch_bounds__(256) void gbwd_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -362,16 +402,14 @@ hipError_t launch_gate_backward(const void* x, int64_t n_rows, int d, const void
     hipLaunchKernelGGL(gbwd_dz_kernel, dim3((unsigned)l.n_mt, (unsigned)(hdim / 32)), dim3(256), 0, st, xb, d, w1b,
                        (const uint16_t*)b1, (const uint16_t*)w2, d_scores, rows, n_list, n_rows, hdim, l.n_pad, dz,
                        dzt, pw2, pb1);
-    if (d_x)
-        hipLaunchKernelGGL(gbwd_dx_kernel, dim3((unsigned)((l.n_pad + 127) / 128), (unsigned)(d / 32)), dim3(256), 0,
-                           st, dz, w1b, d, hdim, rows, n_list, n_rows, d_x);
-    hipLaunchKernelGGL(gbwd_dw1_kernel, dim3((unsigned)(d / 64), (unsigned)l.n_kc), dim3(hdim * 2), 0, st, xb, d,
-                       dzt, hdim, rows, n_list, n_rows, l.n_pad, pw1);
+    const int dw1_x = d / 64, n_dw1 = dw1_x * (int)l.n_kc;
+    const int dx_x = (int)((l.n_pad + 127) / 128), n_dx_tiles = d_x ? dx_x * (d / 32) : 0;
+    const int n_small = (hdim + 2) / 2;  // hdim + 1 reductions, two per workgroup
+    hipLaunchKernelGGL(gbwd_mid_kernel, dim3((unsigned)(n_small + n_dw1 + (n_dx_tiles + 1) / 2)), dim3(512), 0, st, xb,
+                       d, w1b, hdim, dz, dzt, pw2, pb1, (int)l.n_mt, d_scores, rows, n_list, n_rows, l.n_pad, pw1, d_x,
+                       d_w2, d_b1, d_b2, n_small, dw1_x, n_dw1, dx_x, n_dx_tiles);
     hipLaunchKernelGGL(gbwd_reduce_w1_kernel, dim3((unsigned)((hd + 255) / 256)), dim3(256), 0, st, pw1,
                        (int)l.n_kc, hd, d_w1);
-    hipLaunchKernelGGL(gbwd_reduce_small_kernel, dim3((unsigned)(hdim + 1)), dim3(256), 0, st, pw2, pb1, (int)l.n_mt,
-                       hdim, d_scores,
-                       rows, n_list, n_rows, d_w2, d_b1, d_b2);
     return hipGetLastError();
 }
 
