@@ -370,8 +370,9 @@ def test_attention_bf16_long_sampled(m):
     assert_rowmax_close(f64(o)[rows], ro[rows])
 
 
-@pytest.mark.parametrize("segs", [[1000, 23], [2384], [4200, 23, 1], [16500, 23, 1]],
-                         ids=["short-shape", "short-shape-600-items", "long-shape", "xl-shape"])
+@pytest.mark.parametrize("segs", [[1000, 23], [2384], [1200, 1000, 300], [4200, 23, 1], [16500, 23, 1]],
+                         ids=["short-shape", "short-shape-600-items", "short-shape-640-items-ragged", "long-shape",
+                              "xl-shape"])
 def test_attention_deterministic_and_fully_written(segs):
     note(f"attention determinism and poisoned-output check, prompts {segs}")
     a = make_attention_inputs(segs, 16, 8, 128, seed=3, dtype=torch.bfloat16)
