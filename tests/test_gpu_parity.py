@@ -271,6 +271,7 @@ def test_attention_fp32(segs, hq, hkv, d):
 
 BF16_CASES = [
     ([2384], 16, 8, 128, False),          # the 16k layer's kept set
+    ([1200, 1000, 300], 16, 8, 128, False),  # 640 work items over three prompts
     ([1, 31, 64, 65, 200], 16, 8, 128, False),
     ([300, 129], 16, 8, 128, True),       # repeated positions
     ([257], 8, 8, 128, False),            # no GQA (G = 1)
