@@ -303,3 +303,52 @@ def test_check_positions_and_large_decode_tables_on_host(lib):
     fake = ctypes.c_void_p(4096)
     assert lib.tg_decode_attention(1, fake, fake, fake, fake, fake, kv_seq_array(bad), len(bad), 16, 8, 128, fake,
                                    1.0, fake, None, fake, 1 << 30, None) == INVALID
+
+
+C_CONSUMER = r"""
+#include "tokengate.h"
+#include <stdio.h>
+#include <string.h>
+
+int main(void) {
+    /* a 100-row prompt (rows 10..89 are the document, keep 20 of them) and a
+       50-row prompt that is all document, kept whole */
+    tg_seq s[2] = {{0, 100, 10, 90, 20}, {100, 50, 0, 50, 50}};
+    if (tg_kept_rows(s, 2) != 90) return 1;
+    tg_seq bad = {0, 10, 5, 4, 0};                 /* doc_end < doc_begin */
+    if (tg_kept_rows(&bad, 1) != -1) return 2;
+    if (strlen(tg_last_error()) == 0) return 3;
+    if (tg_select_workspace_bytes(s, 2) != 0) return 4;
+    tg_seq big = {0, 40000, 0, 39000, 100};        /* above 32768 rows: needs a workspace */
+    if (tg_select_workspace_bytes(&big, 1) == 0) return 5;
+    if (tg_gate_score(TG_BF16, NULL, 10, 64, NULL, NULL, 128, NULL, 0.0f, NULL, NULL) != TG_ERR_INVALID_ARGUMENT)
+        return 6;
+    if (tg_select_topk(NULL, &big, 1, NULL, NULL, 0, NULL) == TG_OK) return 7;
+    if (strlen(tg_status_string(TG_ERR_WORKSPACE)) == 0) return 8;
+    puts("ok");
+    return 0;
+}
+"""
+
+
+def test_header_compiles_as_c11_and_links(tmp_path):
+    """The header is plain C (C11, -Wall -Werror, gcc) and the host-side calls
+    behave the same from a C program as through the binding."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    from learned_token_pruning_layer_amd._lib import LIB_PATH as so
+    src = tmp_path / "consumer.c"
+    src.write_text(C_CONSUMER)
+    exe = tmp_path / "consumer"
+    libdir = os.path.dirname(so)
+    cmd = [gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", str(src), "-o", str(exe),
+           "-L", libdir, "-l:" + os.path.basename(so), "-Wl,-rpath," + libdir]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
