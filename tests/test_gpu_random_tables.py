@@ -1,6 +1,7 @@
 """GPU parity on seeded random prompt tables: the whole pruned-prefill layer
 (gate, select, compaction, attention) through the C ABI against the fp64
-oracle, over prompt tables no hand-written case covers.
+oracle, over prompt tables no hand-written case covers; then the backward of
+the attention and decode over the pruned cache on random tables of their own.
 
 Each seed draws one to five packed prompts with rows before the document
 (sometimes none), a document of 0 to ~1400 rows, a question of 1 to 160
@@ -11,6 +12,8 @@ with or without an explicit non-decreasing position array that repeats
 and skips positions. Bars as in the other parity tests: selection,
 gathers and positions bit-exact on the GPU's own scores; gate scores and
 attention within the dtype's bar of the oracle; bias within 1e-6 relative.
+The backward and decode cases use the bars of their hand-written tests
+(check_backward, check_decode).
 """
 
 import sys
@@ -22,6 +25,7 @@ import torch
 import oracle
 import learned_token_pruning_layer_amd as tg
 from synthetic import Prompt
+from tests.test_gpu_parity import check_backward, check_decode
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -133,3 +137,44 @@ def test_end_to_end_random_table(seed):
         assert np.all(err <= 2e-2 * np.abs(o).max(axis=-1))
     else:
         assert np.abs(got - o).max() <= 1e-4
+
+
+# (hq, hkv, head_dim) for the backward and decode tables
+HEADS = [(16, 8, 128), (4, 2, 64), (6, 3, 128), (8, 1, 64), (4, 4, 128)]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_backward_random_table(seed):
+    """One to four prompts of 1-899 kept rows, a question tail of 1-60 rows, random
+    temperature, with or without repeated positions."""
+    hq, hkv, d = HEADS[seed % len(HEADS)]
+    rng = np.random.default_rng(8000 + seed)
+    lens = [int(x) for x in rng.integers(1, 900, size=int(rng.integers(1, 5)))]
+    ties = bool(rng.random() < 0.5)
+    tau = float(rng.uniform(0.6, 1.6))
+    tail = int(rng.integers(1, 61))
+    note(f"backward random table seed={seed}: hq={hq} hkv={hkv} D={d} lens={lens} ties={ties} "
+         f"tau={tau:.3f} tail={tail}")
+    check_backward(lens, hq, hkv, d, seed=8000 + seed, pos_ties=ties, tau=tau, tail=tail)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_decode_random_table(seed):
+    """One to forty cached sequences of 1-2999 rows with gaps between them, 1 to
+    8/G new tokens each, random temperature, with or without repeated positions;
+    bf16, and fp32 for every fifth seed."""
+    hq, hkv, d = HEADS[seed % len(HEADS)]
+    rng = np.random.default_rng(9000 + seed)
+    g = hq // hkv
+    segs, st = [], int(rng.integers(0, 5))
+    for _ in range(int(rng.integers(1, 41))):
+        ln = int(rng.integers(1, 3000))
+        nn = int(min(ln, rng.integers(1, 8 // g + 1)))
+        segs.append((st, ln, nn))
+        st += ln + int(rng.integers(0, 3))
+    dt = torch.float32 if seed % 5 == 4 else torch.bfloat16
+    ties = bool(rng.random() < 0.5)
+    tau = float(rng.uniform(0.6, 1.6))
+    note(f"decode random table seed={seed}: {dt} hq={hq} hkv={hkv} D={d} {len(segs)} sequences, "
+         f"{sum(s[1] for s in segs)} cached rows, {sum(s[2] for s in segs)} new, ties={ties} tau={tau:.3f}")
+    check_decode(segs, hq, hkv, d, seed=9000 + seed, dtype=dt, pos_ties=ties, tau=tau)
