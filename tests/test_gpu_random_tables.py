@@ -1,7 +1,8 @@
 """GPU parity on seeded random prompt tables: the whole pruned-prefill layer
 (gate, select, compaction, attention) through the C ABI against the fp64
 oracle, over prompt tables no hand-written case covers; then the backward of
-the attention and decode over the pruned cache on random tables of their own.
+the attention, decode over the pruned cache, the above-gate decoder layer and
+the gated delta rule on random tables of their own.
 
 Each seed draws one to five packed prompts with rows before the document
 (sometimes none), a document of 0 to ~1400 rows, a question of 1 to 160
@@ -12,8 +13,8 @@ with or without an explicit non-decreasing position array that repeats
 and skips positions. Bars as in the other parity tests: selection,
 gathers and positions bit-exact on the GPU's own scores; gate scores and
 attention within the dtype's bar of the oracle; bias within 1e-6 relative.
-The backward and decode cases use the bars of their hand-written tests
-(check_backward, check_decode).
+The other calls use the bars of their hand-written tests (check_backward,
+check_decode, check_dense_layer, check_delta_scan).
 """
 
 import sys
@@ -25,7 +26,7 @@ import torch
 import oracle
 import learned_token_pruning_layer_amd as tg
 from synthetic import Prompt
-from tests.test_gpu_parity import check_backward, check_decode
+from tests.test_gpu_parity import check_backward, check_decode, check_delta_scan, check_dense_layer
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -178,3 +179,32 @@ def test_decode_random_table(seed):
     note(f"decode random table seed={seed}: {dt} hq={hq} hkv={hkv} D={d} {len(segs)} sequences, "
          f"{sum(s[1] for s in segs)} cached rows, {sum(s[2] for s in segs)} new, ties={ties} tau={tau:.3f}")
     check_decode(segs, hq, hkv, d, seed=9000 + seed, dtype=dt, pos_ties=ties, tau=tau)
+
+
+# (d_model, hq, hkv, head_dim, d_ff) of the above-gate decoder layer
+DENSE = [(256, 4, 2, 64, 384), (512, 8, 4, 128, 1024), (384, 6, 3, 64, 448), (256, 2, 2, 128, 192),
+         (640, 10, 2, 64, 704)]
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_dense_layer_random_table(seed):
+    """One to four prompts of 1-699 kept rows, positions starting at 0 or far out."""
+    d, hq, hkv, dh, d_ff = DENSE[seed]
+    rng = np.random.default_rng(9500 + seed)
+    segs = [int(x) for x in rng.integers(1, 700, size=int(rng.integers(1, 5)))]
+    pos_offset = 0 if rng.random() < 0.5 else int(rng.integers(1, 100000))
+    note(f"dense layer random table seed={seed}: d={d} hq={hq} hkv={hkv} D={dh} d_ff={d_ff} "
+         f"segs={segs} pos_offset={pos_offset}")
+    check_dense_layer(segs, d, hq, hkv, dh, d_ff, seed=9500 + seed, pos_offset=pos_offset)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_delta_scan_random_table(seed):
+    """One to five prompts of 1-499 kept rows, 1-8 heads, with or without initial
+    states (prompts without rows have a test of their own)."""
+    rng = np.random.default_rng(9700 + seed)
+    segs = [int(x) for x in rng.integers(1, 500, size=int(rng.integers(1, 6)))]
+    nh = int(rng.choice([1, 2, 4, 8]))
+    with_state = bool(rng.random() < 0.5)
+    note(f"delta scan random table seed={seed}: segs={segs} heads={nh} state={with_state}")
+    check_delta_scan(segs, nh, seed=9700 + seed, with_state=with_state)
