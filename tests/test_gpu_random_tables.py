@@ -1,8 +1,9 @@
 """GPU parity on seeded random prompt tables: the whole pruned-prefill layer
 (gate, select, compaction, attention) through the C ABI against the fp64
 oracle, over prompt tables no hand-written case covers; then the backward of
-the attention, decode over the pruned cache, the above-gate decoder layer and
-the gated delta rule on random tables of their own.
+the attention, the gate MLP's backward, decode over the pruned cache, the
+above-gate decoder layer and the gated delta rule on random tables of their
+own.
 
 Each seed draws one to five packed prompts with rows before the document
 (sometimes none), a document of 0 to ~1400 rows, a question of 1 to 160
@@ -14,7 +15,7 @@ and skips positions. Bars as in the other parity tests: selection,
 gathers and positions bit-exact on the GPU's own scores; gate scores and
 attention within the dtype's bar of the oracle; bias within 1e-6 relative.
 The other calls use the bars of their hand-written tests (check_backward,
-check_decode, check_dense_layer, check_delta_scan).
+check_gate_backward, check_decode, check_dense_layer, check_delta_scan).
 """
 
 import sys
@@ -26,7 +27,8 @@ import torch
 import oracle
 import learned_token_pruning_layer_amd as tg
 from synthetic import Prompt
-from tests.test_gpu_parity import check_backward, check_decode, check_delta_scan, check_dense_layer
+from tests.test_gpu_parity import (check_backward, check_decode, check_delta_scan, check_dense_layer,
+                                   check_gate_backward)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -208,3 +210,19 @@ def test_delta_scan_random_table(seed):
     with_state = bool(rng.random() < 0.5)
     note(f"delta scan random table seed={seed}: segs={segs} heads={nh} state={with_state}")
     check_delta_scan(segs, nh, seed=9700 + seed, with_state=with_state)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_gate_backward_random_table(seed):
+    """1-3000 rows, d a multiple of 64 up to 1024, every built d_hidden, a random
+    row list (sometimes empty or every row), with or without b1 and dx."""
+    rng = np.random.default_rng(9900 + seed)
+    n = int(rng.integers(1, 3001))
+    d = 64 * int(rng.integers(1, 17))
+    h = int(rng.choice([64, 128, 192, 256]))
+    r = rng.random()
+    n_list = 0 if r < 0.15 else (n if r < 0.3 else int(rng.integers(1, n + 1)))
+    with_b1 = bool(rng.random() < 0.5)
+    with_dx = bool(rng.random() < 0.7)
+    note(f"gate backward random table seed={seed}: n={n} d={d} H={h} listed={n_list} b1={with_b1} dx={with_dx}")
+    check_gate_backward(n, d, h, n_list, seed=9900 + seed, with_b1=with_b1, with_dx=with_dx)
