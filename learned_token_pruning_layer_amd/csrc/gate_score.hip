@@ -16,8 +16,11 @@
 // it: at 64-row tiles W1 is 4x the X bytes a CU receives. Hence
 //  * both operands move global -> LDS with direct loads
 //    (global_load_lds_dwordx4, no staging registers), the fastest path into
-//    LDS on this part: X through a 6-stage (3 at 128 rows) ring of 64-wide
-//    k chunks, W1 through a 3-stage ring. Every load instruction covers 8
+//    LDS on this part, through rings of 64-wide k chunks: 4 stages each for
+//    X and W1 at 64-row tiles (all 160 KB of LDS; the epilogue's partial
+//    sums reuse the X ring once the k loop is done), 3 each at 128 rows.
+//    The W1 ring's depth sets how many chunks ahead its loads are issued,
+//    which matters more than the X ring's. Every load instruction covers 8
 //    whole 128-byte row segments, so each fetched cache line is used in
 //    full;
 //  * one barrier per chunk: after it every wave refills the slots of the
@@ -82,7 +85,9 @@ __global__ __launch_bounds__(64 * WH * WR) void gate_mfma_kernel(const uint16_t*
     constexpr int U = (NX % NW1 == 0) ? NX : NX * NW1;  // unroll: every ring slot a constant
     __shared__ __attribute__((aligned(1024))) char xs[NX][GBM * GBK * 2];
     __shared__ __attribute__((aligned(1024))) char ws[NW1][H * GBK * 2];
-    __shared__ float part[H / 32][GBM];
+    // Partial sums of the epilogue, in the X ring's memory (free after the k loop).
+    static_assert((H / 32) * GBM * 4 <= NX * GBM * GBK * 2, "partial sums fit in the X ring");
+    float (*part)[GBM] = (float (*)[GBM])(&xs[0][0]);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -185,6 +190,7 @@ __global__ __launch_bounds__(64 * WH * WR) void gate_mfma_kernel(const uint16_t*
         }
     }
     wait_vmcnt<0>();
+    __syncthreads();  // every wave's loads have landed and its LDS reads are done
 
     // Epilogue. acc[th][tr] register j holds hidden unit 32*(wh*TH + th) +
     // 8*(j/4) + 4*hh + j%4 of token 32*(wr*TR + tr) + l32. Each 32-unit
@@ -259,7 +265,7 @@ hipError_t launch_gate_mfma_bf16(const void* x, int64_t n, int d, const void* w1
     // CU busy); longer prompts take 128-row tiles, which halve the W1 bytes
     // each row costs (W1 streams from L2 once per tile).
     if (h == 256) {
-        if (n <= 2 * 256 * 64) go(gate_mfma_kernel<8, 1, 1, 2, 6, 3, false, 2>, 64, 512);
+        if (n <= 2 * 256 * 64) go(gate_mfma_kernel<8, 1, 1, 2, 4, 4, false, 2>, 64, 512);
         else go(gate_mfma_kernel<4, 2, 2, 2, 3, 3, false, 2>, 128, 512);
     } else {
         go(gate_mfma_kernel<4, 1, 2, 1, 6, 3, false, 2>, 64, 512);
