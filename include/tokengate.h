@@ -125,10 +125,10 @@ int64_t tg_kept_rows(const tg_seq* seqs, int32_t n_seqs);
  * with W1 row-major [d_hidden, d_model] (nn.Linear layout), b1 [d_hidden]
  * (nullable: zero), w2 [d_hidden], all of dtype dt; scores is fp32 [n_rows].
  * Accumulation is fp32. bf16 inputs with d_model % 64 == 0, d_hidden in
- * {128, 256} and 16-byte-aligned x and w1 take the MFMA path; every other
- * shape takes a plain fp32-FMA path. Source: section "Wie hat TokenGate das
- * Pruning von Tokens verstanden?" (the MLP gate scores every token from its
- * post-attention residual at gate layer L). */
+ * {64, 128, 192, 256} and 16-byte-aligned x and w1 take the MFMA path;
+ * every other shape takes a plain fp32-FMA path. Source: section "Wie hat
+ * TokenGate das Pruning von Tokens verstanden?" (the MLP gate scores every
+ * token from its post-attention residual at gate layer L). */
 tg_status tg_gate_score(tg_dtype dt, const void* x, int64_t n_rows, int32_t d_model,
                         const void* w1, const void* b1, int32_t d_hidden, const void* w2,
                         float b2, float* scores, hipStream_t stream);

@@ -124,7 +124,7 @@ tg_status tg_gate_score(tg_dtype dt, const void* x, int64_t n_rows, int32_t d_mo
     if (!x || !w1 || !w2 || !scores) return fail(TG_ERR_INVALID_ARGUMENT, "x, w1, w2, scores must be non-NULL");
     if ((n_rows + 3) / 4 > (int64_t)INT32_MAX)
         return fail(TG_ERR_UNSUPPORTED, "n_rows=%lld too large for one launch", (long long)n_rows);
-    const bool mfma = dt == TG_BF16 && d_model % 64 == 0 && (d_hidden == 128 || d_hidden == 256) &&
+    const bool mfma = dt == TG_BF16 && d_model % 64 == 0 && (d_hidden == 64 || d_hidden == 128 || d_hidden == 192 || d_hidden == 256) &&
                       aligned16(x) && aligned16(w1);
     hipError_t e = mfma ? tg::launch_gate_mfma_bf16(x, n_rows, d_model, w1, b1, d_hidden, w2, b2, scores, stream)
                         : tg::launch_gate_simple(dt, x, n_rows, d_model, w1, b1, d_hidden, w2, b2, scores, stream);

@@ -267,8 +267,14 @@ hipError_t launch_gate_mfma_bf16(const void* x, int64_t n, int d, const void* w1
     if (h == 256) {
         if (n <= 2 * 256 * 64) go(gate_mfma_kernel<8, 1, 1, 2, 4, 4, false, 2>, 64, 512);
         else go(gate_mfma_kernel<4, 2, 2, 2, 3, 3, false, 2>, 128, 512);
-    } else {
+    } else if (h == 128) {
         go(gate_mfma_kernel<4, 1, 2, 1, 6, 3, false, 2>, 64, 512);
+    } else if (h == 192) {
+        // 8 waves of 3 hidden tiles x 1 row tile: 192 units x 128 rows
+        go(gate_mfma_kernel<2, 3, 4, 1, 3, 3, false, 2>, 128, 512);
+    } else {
+        // h == 64: 8 waves of 1 hidden tile x 1 row tile: 64 units x 128 rows
+        go(gate_mfma_kernel<2, 1, 4, 1, 4, 4, false, 2>, 128, 512);
     }
     return hipGetLastError();
 }

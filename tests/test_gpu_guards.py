@@ -63,9 +63,11 @@ def run_guarded(call, outs):
 
 
 def test_guard_gate_score():
-    note("guards: gate scores (bf16 MFMA path and fp32 path)")
+    note("guards: gate scores (bf16 MFMA path at every built hidden size, ragged tails; fp32 path)")
     g = torch.Generator(device=DEV).manual_seed(1)
-    for n, d, h, dt in ((1000, 2048, 256, torch.bfloat16), (77, 256, 64, torch.float32)):
+    for n, d, h, dt in ((1000, 2048, 256, torch.bfloat16), (33000, 256, 256, torch.bfloat16),
+                        (1001, 512, 192, torch.bfloat16), (129, 512, 128, torch.bfloat16),
+                        (300, 256, 64, torch.bfloat16), (77, 256, 64, torch.float32)):
         x = torch.randn(n, d, generator=g, device=DEV).to(dt)
         w1 = (torch.randn(h, d, generator=g, device=DEV) / math.sqrt(d)).to(dt)
         w2 = (torch.randn(h, generator=g, device=DEV) / math.sqrt(h)).to(dt)

@@ -58,7 +58,8 @@ def test_gate_fp32_tiny():
                                            (1, 2048, 256, True), (77, 320, 256, True), (300, 1088, 128, False),
                                            (200, 192, 64, False), (130, 100, 24, True), (70, 64, 256, True),
                                            (32769, 192, 256, True), (40001, 2048, 256, False),
-                                           (33001, 128, 128, True)])
+                                           (33001, 128, 128, True), (1000, 2048, 192, True), (129, 1024, 192, False),
+                                           (300, 512, 64, False), (40000, 256, 64, True)])
 def test_gate_bf16(n, d, h, with_b1):
     note(f"gate bf16 n={n} d={d} h={h} b1={with_b1}")
     g = torch.Generator(device=DEV).manual_seed(n + d + h)

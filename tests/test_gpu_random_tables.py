@@ -36,8 +36,8 @@ DEV = "cuda"
 # (dtype, d_model, d_hidden, hq, hkv, head_dim)
 SHAPES = [
     (torch.bfloat16, 256, 128, 4, 2, 64),
-    (torch.bfloat16, 512, 256, 8, 1, 128),
-    (torch.bfloat16, 320, 64, 6, 3, 128),    # d_hidden 64: the plain gate path
+    (torch.bfloat16, 512, 192, 8, 1, 128),
+    (torch.bfloat16, 320, 48, 6, 3, 128),    # d_hidden 48: the plain gate path
     (torch.float32, 192, 64, 4, 4, 64),
     (torch.bfloat16, 2048, 256, 16, 8, 128),
     (torch.bfloat16, 256, 256, 2, 2, 64),
