@@ -135,10 +135,12 @@ tg_status tg_gate_score(tg_dtype dt, const void* x, int64_t n_rows, int32_t d_mo
 
 /* Device workspace tg_select_topk needs, in bytes: 0 (pass NULL) when every
  * prompt has at most 32768 rows, else about 24.6 KB per longer prompt plus
- * 8 bytes per 16384 of its rows (histograms, per-pass bin state and
- * per-chunk counts of the multi-workgroup select). Also 0 for an invalid table (tg_select_topk then
- * reports the error). The caller owns the buffer; its contents need no
- * initialisation and are scratch after the call. */
+ * 65552 bytes per 16384 of its rows, rounded up to whole chunks (about 4
+ * bytes per row: histograms, per-pass bin state, per-chunk counts and the
+ * per-chunk lists of candidate keys of the multi-workgroup select). Also 0
+ * for an invalid table (tg_select_topk then reports the error). The caller
+ * owns the buffer; its contents need no initialisation and are scratch
+ * after the call. */
 size_t tg_select_workspace_bytes(const tg_seq* seqs, int32_t n_seqs);
 
 /* Step 2 - top-K select. For each prompt, ranks its document rows by

@@ -276,31 +276,43 @@ __global__ __launch_bounds__(ST) void select_kernel(const float* __restrict__ sc
 // ---------------------------------------------------------------------------
 // Long prompts (more than SEL_REG_MAX rows): the same radix select and
 // emission spread over chunks of SEL_CHUNK rows, one 1024-thread workgroup
-// per chunk, in six kernels on the stream:
+// per chunk, in six kernels on the stream, three of which read the scores:
 //   zero   clears the per-prompt histograms;
-//   hist   (per pass) each chunk of the document builds its histogram of
-//          the pass's digit in LDS and adds it into the prompt's histogram.
-//          From pass 1 on, every workgroup first finds the previous pass's
-//          bin (the one holding the rem-th largest key) from that pass's
-//          completed histogram; the prompt's first chunk records the
-//          resulting (prefix, mask, rem) for the next kernel;
-//   count  every workgroup finds the last pass's bin the same way (the
-//          threshold key T and how many keys equal to T are kept), then
-//          counts its chunk's "above" and "tied" rows;
+//   hist   each chunk of the document builds its histogram of the first
+//          (top 11-bit) digit in LDS and adds it into the prompt's
+//          histogram (read 1);
+//   cand   each chunk of the prompt finds the first digit's bin (the one
+//          holding the k-th largest key) from the finished histogram, counts
+//          its rows that are kept whatever the rest of the threshold is
+//          (rows outside the document, keys in higher bins), copies the keys
+//          inside the bin to its own candidate list in the workspace, and
+//          adds their second digits into the prompt's second histogram
+//          (read 2);
+//   cand_hist  each chunk finds the second digit's bin and adds the third
+//          digits of its matching candidates into the third histogram;
+//   count  each chunk finds the threshold key T and how many keys equal to
+//          T are kept, and counts its "above" rows (the rows counted by cand
+//          plus its candidates above T) and "tied" rows (candidates equal
+//          to T) from its candidate list;
 //   place  each chunk adds up the counts of the chunks before it, ranks
 //          its rows (block scan of per-thread counts) and writes its kept
 //          row ids, staged in LDS: a chunk's kept rows take a contiguous
-//          run of output slots, written out coalesced.
-// The bin search is repeated in every workgroup of the next kernel rather
-// than run by a kernel of its own: one launch less per pass.
+//          run of output slots, written out coalesced (read 3).
+// Each bin search is repeated in every workgroup of the kernel that needs
+// it rather than run by a kernel of its own (one launch less per pass); the
+// prompt's first chunk records (prefix, mask, rem) for the later kernels.
 // Workspace, in 32-bit words: hist [n_long][3][NB], state [n_long][3][4]
-// ((prefix, mask, rem) after each pass), counts [n_emit][2].
+// ((prefix, mask, rem) after each pass), counts [n_emit][2] (above, tied),
+// ccnt [n_emit][2] (candidates, rows kept by the first digit alone),
+// cand [n_emit][SEL_CHUNK] (candidate keys, in no particular order).
 // ---------------------------------------------------------------------------
 
 struct SelWs {
     uint32_t* hist;
     uint32_t* state;
     uint32_t* counts;
+    uint32_t* ccnt;
+    uint32_t* cand;
 };
 
 __device__ __forceinline__ SelWs sel_ws(void* base, const LongTable& lt) {
@@ -308,6 +320,8 @@ __device__ __forceinline__ SelWs sel_ws(void* base, const LongTable& lt) {
     w.hist = (uint32_t*)base;
     w.state = w.hist + (size_t)lt.n * 3 * NB;
     w.counts = w.state + (size_t)lt.n * 12;
+    w.ccnt = w.counts + (size_t)lt.n_emit * 2;
+    w.cand = w.ccnt + (size_t)lt.n_emit * 2;
     return w;
 }
 
@@ -353,8 +367,8 @@ __global__ __launch_bounds__(256) void sel_zero_kernel(uint32_t* __restrict__ p,
 }
 
 __global__ __launch_bounds__(ST) void sel_hist_kernel(const float* __restrict__ scores, SeqTable t, LongTable lt,
-                                                     void* ws_base, int pass) {
-    __shared__ PickSmem sm;
+                                                     void* ws_base) {
+    constexpr int pass = 0;
     __shared__ uint32_t h[NB];
     int li, chunk;
     long_item(lt, blockIdx.x, false, li, chunk);
@@ -372,16 +386,15 @@ __global__ __launch_bounds__(ST) void sel_hist_kernel(const float* __restrict__ 
     for (int u = 0; u < SEL_CHUNK / ST; ++u) f[u] = scores[dbeg + min(i0 + u * ST + tid, n_doc - 1)];
     h[tid] = 0u;
     h[tid + ST] = 0u;
-    uint32_t prefix = 0u, mask = 0u, rem = 0u;
-    if (pass > 0)
-        pick_after(sm, ws, li, pass - 1, (uint32_t)sd.k_doc, chunk == 0, prefix, mask, rem, tid, lane, wave);
+    (void)lane;
+    (void)wave;
     const int shift = digit_shift(pass);
     const uint32_t dmask = digit_mask(pass);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < SEL_CHUNK / ST; ++u) {
         const uint32_t key = score_key(f[u]);
-        if (i0 + u * ST + tid < n_doc && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & dmask], 1u);
+        if (i0 + u * ST + tid < n_doc) atomicAdd(&h[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
     uint32_t* g = ws.hist + ((size_t)li * 3 + pass) * NB;
@@ -457,6 +470,92 @@ __device__ __forceinline__ uint32_t block_prefix(uint32_t v, uint32_t* wtot, uin
     return before;
 }
 
+// Rows of the chunk kept whatever the threshold's lower digits are, and the
+// keys of the first digit's bin, copied to the chunk's candidate list; their
+// second digits go into the prompt's second histogram.
+__global__ __launch_bounds__(ST) void sel_cand_kernel(const float* __restrict__ scores, SeqTable t, LongTable lt,
+                                                     void* ws_base) {
+    __shared__ PickSmem sm;
+    __shared__ uint32_t h[NB];
+    __shared__ uint32_t wtot[NW];
+    __shared__ uint32_t n_cand;
+    int li, chunk;
+    long_item(lt, blockIdx.x, true, li, chunk);
+    const SeqDesc sd = t.s[lt.s[li].seq];
+    const int32_t n_doc = sd.doc_end - sd.doc_begin;
+    if (!(sd.k_doc > 0 && sd.k_doc < n_doc)) return;  // keep none / all: counted from the ranges alone
+    const SelWs ws = sel_ws(ws_base, lt);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int32_t cbase = chunk * SEL_CHUNK;  // first row of the chunk (prompt-relative)
+    float f[CU_ROWS];
+#pragma unroll
+    for (int u = 0; u < CU_ROWS; ++u)  // clamped into the document: every load is valid
+        f[u] = scores[sd.start + min(max(cbase + u * ST + tid, sd.doc_begin), sd.doc_end - 1)];
+    h[tid] = 0u;
+    h[tid + ST] = 0u;
+    if (tid == 0) n_cand = 0u;
+    uint32_t prefix, mask, rem;
+    pick_after(sm, ws, li, 0, (uint32_t)sd.k_doc, chunk == 0, prefix, mask, rem, tid, lane, wave);
+    (void)rem;
+    const uint32_t top = prefix | ~mask;  // largest key of the chosen bin
+    uint32_t* const cand = ws.cand + (size_t)(lt.s[li].emit_base + chunk) * SEL_CHUNK;
+    uint32_t above = 0u;
+#pragma unroll
+    for (int u = 0; u < CU_ROWS; ++u) {
+        const int32_t r = cbase + u * ST + tid;
+        const bool in_doc = r >= sd.doc_begin && r < sd.doc_end;
+        const uint32_t key = score_key(f[u]);
+        if (r < sd.len && (!in_doc || key > top)) {
+            ++above;
+        } else if (in_doc && (key & mask) == prefix) {
+            atomicAdd(&h[(key >> digit_shift(1)) & digit_mask(1)], 1u);
+            cand[atomicAdd(&n_cand, 1u)] = key;
+        }
+    }
+    uint32_t total_above;
+    block_prefix(above, wtot, total_above);  // its barrier also completes h and n_cand
+    uint32_t* g = ws.hist + ((size_t)li * 3 + 1) * NB;
+    for (int b = tid; b < NB; b += ST)
+        if (h[b]) atomicAdd(&g[b], h[b]);
+    if (tid == 0) {
+        ws.ccnt[(size_t)(lt.s[li].emit_base + chunk) * 2 + 0] = n_cand;
+        ws.ccnt[(size_t)(lt.s[li].emit_base + chunk) * 2 + 1] = total_above;
+    }
+}
+
+// The third digits of the candidates that match the second digit's bin.
+__global__ __launch_bounds__(ST) void sel_cand_hist_kernel(SeqTable t, LongTable lt, void* ws_base) {
+    __shared__ PickSmem sm;
+    __shared__ uint32_t h[NB];
+    int li, chunk;
+    long_item(lt, blockIdx.x, true, li, chunk);
+    const SeqDesc sd = t.s[lt.s[li].seq];
+    const int32_t n_doc = sd.doc_end - sd.doc_begin;
+    if (!(sd.k_doc > 0 && sd.k_doc < n_doc)) return;
+    const SelWs ws = sel_ws(ws_base, lt);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    h[tid] = 0u;
+    h[tid + ST] = 0u;
+    uint32_t prefix, mask, rem;
+    pick_after(sm, ws, li, 1, (uint32_t)sd.k_doc, chunk == 0, prefix, mask, rem, tid, lane, wave);
+    (void)rem;
+    const size_t ci = (size_t)(lt.s[li].emit_base + chunk);
+    const uint32_t n = ws.ccnt[ci * 2];
+    const uint32_t* const cand = ws.cand + ci * SEL_CHUNK;
+    for (uint32_t i = tid; i < n; i += ST) {
+        const uint32_t key = cand[i];
+        if ((key & mask) == prefix) atomicAdd(&h[(key >> digit_shift(2)) & digit_mask(2)], 1u);
+    }
+    __syncthreads();
+    uint32_t* g = ws.hist + ((size_t)li * 3 + 2) * NB;
+    for (int b = tid; b <= (int)digit_mask(2); b += ST)
+        if (h[b]) atomicAdd(&g[b], h[b]);
+}
+
 __global__ __launch_bounds__(ST) void sel_count_kernel(const float* __restrict__ scores, SeqTable t, LongTable lt,
                                                       void* ws_base) {
     __shared__ PickSmem sm;
@@ -468,17 +567,31 @@ __global__ __launch_bounds__(ST) void sel_count_kernel(const float* __restrict__
     const SelWs ws = sel_ws(ws_base, lt);
     const int tid = threadIdx.x;
     const int32_t n_doc = sd.doc_end - sd.doc_begin;
-    uint32_t thr = 0u;
+    uint32_t ta, tt;
     if (sd.k_doc > 0 && sd.k_doc < n_doc) {
-        uint32_t mask, rem;
+        // Above: the rows the first digit already keeps plus the candidates
+        // above T; tied: the candidates equal to T.
+        uint32_t thr, mask, rem;
         pick_after(sm, ws, li, 2, (uint32_t)sd.k_doc, chunk == 0, thr, mask, rem, tid, tid & 63,
                    __builtin_amdgcn_readfirstlane(tid >> 6));
+        const size_t ci = (size_t)(lt.s[li].emit_base + chunk);
+        const uint32_t n = ws.ccnt[ci * 2];
+        const uint32_t* const cand = ws.cand + ci * SEL_CHUNK;
+        uint32_t gt = 0u, eq = 0u;
+        for (uint32_t i = tid; i < n; i += ST) {
+            const uint32_t key = cand[i];
+            gt += key > thr ? 1u : 0u;
+            eq += key == thr ? 1u : 0u;
+        }
+        block_prefix(gt, wtot[0], ta);
+        block_prefix(eq, wtot[1], tt);
+        ta += ws.ccnt[ci * 2 + 1];
+    } else {
+        uint32_t ma, mt;
+        classify_chunk(scores, sd, 0u, chunk, stage, ma, mt);  // no keys read: the ranges decide
+        block_prefix((uint32_t)__popc(ma), wtot[0], ta);
+        block_prefix((uint32_t)__popc(mt), wtot[1], tt);
     }
-    uint32_t ma, mt;
-    classify_chunk(scores, sd, thr, chunk, stage, ma, mt);
-    uint32_t ta, tt;
-    block_prefix((uint32_t)__popc(ma), wtot[0], ta);
-    block_prefix((uint32_t)__popc(mt), wtot[1], tt);
     if (tid == 0) {
         ws.counts[(size_t)(lt.s[li].emit_base + chunk) * 2 + 0] = ta;
         ws.counts[(size_t)(lt.s[li].emit_base + chunk) * 2 + 1] = tt;
@@ -558,7 +671,7 @@ size_t select_plan(const SeqTable& t, LongTable* lt) {
         lt->n_emit += l.n_emit;
     }
     if (lt->n == 0) return 0;
-    return ((size_t)lt->n * (3 * NB + 12) + (size_t)lt->n_emit * 2) * sizeof(uint32_t);
+    return ((size_t)lt->n * (3 * NB + 12) + (size_t)lt->n_emit * (4 + SEL_CHUNK)) * sizeof(uint32_t);
 }
 
 hipError_t launch_select(const float* scores, const SeqTable& t, const LongTable& lt, void* workspace,
@@ -569,9 +682,10 @@ hipError_t launch_select(const float* scores, const SeqTable& t, const LongTable
     if (lt.n == 0) return hipGetLastError();
     hipLaunchKernelGGL(sel_zero_kernel, dim3((unsigned)lt.n * 6), dim3(256), 0, st, (uint32_t*)workspace,
                        (int64_t)lt.n * 3 * NB);
-    for (int pass = 0; pass < 3; ++pass)
-        if (lt.n_hist)
-            hipLaunchKernelGGL(sel_hist_kernel, dim3((unsigned)lt.n_hist), dim3(ST), 0, st, scores, t, lt, workspace, pass);
+    if (lt.n_hist)
+        hipLaunchKernelGGL(sel_hist_kernel, dim3((unsigned)lt.n_hist), dim3(ST), 0, st, scores, t, lt, workspace);
+    hipLaunchKernelGGL(sel_cand_kernel, dim3((unsigned)lt.n_emit), dim3(ST), 0, st, scores, t, lt, workspace);
+    hipLaunchKernelGGL(sel_cand_hist_kernel, dim3((unsigned)lt.n_emit), dim3(ST), 0, st, t, lt, workspace);
     hipLaunchKernelGGL(sel_count_kernel, dim3((unsigned)lt.n_emit), dim3(ST), 0, st, scores, t, lt, workspace);
     hipLaunchKernelGGL(sel_place_kernel, dim3((unsigned)lt.n_emit), dim3(ST), 0, st, scores, t, lt, workspace, kept);
     return hipGetLastError();

@@ -70,11 +70,12 @@ def test_select_rejects_before_launch(lib):
     assert lib.tg_select_topk(None, seq_array(ok), 1, None, None, 0, None) == INVALID  # NULL scores
     assert lib.tg_select_workspace_bytes(seq_array(ok), 1) == 0
     # Prompts above 32768 rows take the multi-workgroup select, which needs a
-    # workspace: per long prompt 3 histograms of 2048 words and 4 state words,
-    # plus 4 words per 16384-row chunk of the prompt.
+    # workspace: per long prompt 3 histograms of 2048 words and 3 x 4 state
+    # words, plus per 16384-row chunk of the prompt 4 count words and a
+    # candidate list of 16384 words.
     long = [Prompt(0, 100, 0, 90, 5), Prompt(100, 40000, 0, 39000, 7), Prompt(40100, 131072, 0, 130048, 8128)]
     need = lib.tg_select_workspace_bytes(seq_array(long), 3)
-    assert need == 4 * (2 * (3 * 2048 + 12) + 2 * (3 + 8))
+    assert need == 4 * (2 * (3 * 2048 + 12) + (3 + 8) * (4 + 16384))
     # Missing or short workspace is refused before anything is enqueued (the
     # pointers below are never dereferenced).
     fake = ctypes.c_void_p(4096)
