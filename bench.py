@@ -337,8 +337,9 @@ def measure_extras(torch, tg, layer, w, steps, dev):
     out["select_2p24_keys"] = {"us": round(pct(t, 0.5), 1),
                                "algorithmic_gb_s": round(sel_bytes / (pct(t, 0.5) * 1e-6) / 1e9, 1),
                                "note": "one prompt of 2^24 document rows, keep 1/8; chunks of 16384 rows, "
-                                       "one workgroup each, reading the scores in 3 histogram passes, "
-                                       "a count pass and a placement pass"}
+                                       "one workgroup each, reading the scores three times (first-digit "
+                                       "histogram, candidate lists, placement); the other two digits and "
+                                       "the counts run over the candidate lists"}
     del sc, kept, ws
     out["configs"] = measure_configs(torch, tg, dev, timed, pct)
     return out
