@@ -17,8 +17,9 @@
 //     all zero they fall into bin 0, whose count is corrected by their known
 //     number, so the inner loops carry no bounds or document tests. Longer
 //     prompts are split into chunks of 16384 rows, one workgroup each, and
-//     the per-prompt histograms and chunk counts meet in a workspace (the
-//     multi-workgroup kernels at the end of this file).
+//     the per-prompt histograms, the chunks' candidate keys and their counts
+//     meet in a workspace (the multi-workgroup kernels at the end of this
+//     file).
 //  2. A 3-pass MSB radix select (11, 11 and 10-bit digits; LDS histograms
 //     with integer atomics; a DPP wave scan over the bins from the top)
 //     finds the k-th largest key T and rem = how many keys equal to T are
@@ -377,8 +378,6 @@ __global__ __launch_bounds__(ST) void sel_hist_kernel(const float* __restrict__ 
     if (!(sd.k_doc > 0 && sd.k_doc < n_doc)) return;  // keep none / all: no threshold needed
     const SelWs ws = sel_ws(ws_base, lt);
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t dbeg = sd.start + sd.doc_begin;
     const int32_t i0 = chunk * SEL_CHUNK;
     float f[SEL_CHUNK / ST];
@@ -386,8 +385,6 @@ __global__ __launch_bounds__(ST) void sel_hist_kernel(const float* __restrict__ 
     for (int u = 0; u < SEL_CHUNK / ST; ++u) f[u] = scores[dbeg + min(i0 + u * ST + tid, n_doc - 1)];
     h[tid] = 0u;
     h[tid + ST] = 0u;
-    (void)lane;
-    (void)wave;
     const int shift = digit_shift(pass);
     const uint32_t dmask = digit_mask(pass);
     __syncthreads();
