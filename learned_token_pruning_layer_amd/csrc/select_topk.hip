@@ -7,41 +7,39 @@
 // works (same rule). The pages do not say how ties break: here the lower row
 // id wins, -0 equals +0 and NaN ranks below every number.
 //
-// One 1024-thread workgroup per prompt of up to 32768 rows.
+// Prompts of up to 32768 rows: 16 workgroups of 1024 threads per prompt,
+// each of which finds the threshold on its own and writes one sixteenth of
+// the rows.
 //  1. Scores map to order-preserving u32 keys (larger key = better rank).
-//     Prompts of up to 32768 rows keep every key in registers (WU = 16 or
-//     32 per lane) for the whole kernel: HBM is read once (coalesced, then
-//     transposed through LDS so that lane l of wave w holds the WU
-//     consecutive rows starting at (64w + l) * WU). Rows outside the
-//     document hold key 0 and are not counted: while the chosen digits are
-//     all zero they fall into bin 0, whose count is corrected by their known
-//     number, so the inner loops carry no bounds or document tests. Longer
-//     prompts are split into chunks of 16384 rows, one workgroup each, and
-//     the per-prompt histograms, the chunks' candidate keys and their counts
-//     meet in a workspace (the multi-workgroup kernels at the end of this
-//     file).
+//     Every workgroup of the prompt keeps every key in registers (WU = 16
+//     or 32 per lane, read coalesced: wave w, register u, lane l holds row
+//     64*WU*w + 64u + l). Rows outside the document hold key 0 and are not
+//     counted: while the chosen digits are all zero they fall into bin 0,
+//     whose count is corrected by their known number, so the inner loops
+//     carry no bounds or document tests. Longer prompts are split into
+//     chunks of 16384 rows, one workgroup each, and the per-prompt
+//     histograms, the chunks' candidate keys and their counts meet in a
+//     workspace (the multi-workgroup kernels at the end of this file).
 //  2. A 3-pass MSB radix select (11, 11 and 10-bit digits; LDS histograms
 //     with integer atomics; a DPP wave scan over the bins from the top)
 //     finds the k-th largest key T and rem = how many keys equal to T are
-//     kept. Pass 0 counts the keys in row order as the coalesced loads
-//     return, before the transpose, so its atomics overlap the load
-//     latency (a histogram does not depend on the order of its keys).
+//     kept. Pass 0 counts each key as its load returns. The steps are
+//     integer and see the same keys in every workgroup of the prompt, so
+//     all of them reach the same T and rem; none reads another's results.
 //  3. Emission: a row is "above" (outside the document, or key > T) or
-//     "tied" (document key == T); each lane classifies its rows into two bit
-//     masks. Kept rows are the above rows and the first rem tied rows; a
-//     kept row's output slot is (#above before it) + min(#tied before it,
-//     rem), so rows land in ascending order without a sort. Register path:
-//     popcounts of the masks, a DPP scan over the wave and one pass over the
-//     16 wave totals rank every lane's first row; the lane then walks its
-//     own consecutive rows, writing each kept row id to its slot of an LDS
-//     staging array (rows not kept write a per-lane scratch word, so no lane
-//     masking is needed; at 16 rows per lane, a lane without tied rows
-//     visits only the bits of its kept rows), and the staged slots go out in
-//     one coalesced copy.
-//     Streaming path: lane l of a wave step holds rows l, l+64, ...; ballots
-//     + mbcnt rank them and kept rows are stored directly.
-// The kernel is bound by its own instruction count on one CU, so the hot
-// loops are kept to a few instructions per key.
+//     "tied" (document key == T). Kept rows are the above rows and the
+//     first rem tied rows; a kept row's output slot is (#above before it) +
+//     min(#tied before it, rem), so rows land in ascending order without a
+//     sort. Workgroup g writes slice g, the 64*WU consecutive rows held by
+//     its wave g: every wave's above / tied totals (DPP scans) and wave
+//     g's per-lane row masks meet in LDS, and each wave ranks 64 (or 2 x
+//     64) of the slice's rows with ballots + mbcnt, from the totals of the
+//     slices before g and of the slice's earlier rows.
+//     Chunked path: the same ranking per chunk, kept row ids staged in LDS
+//     by slot and written out coalesced.
+// Replicating the threshold search costs 16 reads of the prompt's scores
+// (from L2) instead of the one-workgroup emission's many dependent steps,
+// whose instruction count on a single CU set that kernel's time.
 // Integer work only: the result is bit-exact and deterministic.
 #include "tg_internal.hpp"
 #include "tg_device.hpp"
@@ -54,22 +52,19 @@ constexpr int NW = ST / 64;
 constexpr int NB = 2048;               // histogram bins (11-bit digits)
 constexpr int HTOT = 2 * NB + NB / 2;  // the three passes' histograms (11, 11 and 10 bits)
 
-constexpr int RMAX = ST * 32;                // rows of the largest register path
-constexpr int STAGE = RMAX + RMAX / 64 + 64;  // padded transpose / staging words + scratch words
-
 struct PickSmem {
     uint32_t hist[HTOT];  // one histogram per pass, cleared once
-    uint32_t wtot[NW][2];
-    uint32_t pick[3][2];  // per pass: chosen bin, rank inside it
+    uint32_t wtot[NW][1];  // per-wave bin totals of the current bin search
 };
 
-struct Smem : PickSmem {
-    uint32_t stage[STAGE];  // key transpose, then kept-slot staging
+struct RegSmem : PickSmem {
+    uint32_t ctot[NW][2];  // per-wave above / tied totals
+    uint32_t em[64][2];    // the written slice's per-lane above / tied masks
 };
 
-// Padded LDS index of row r in the key transpose: one spare word per 64
-// rows spreads both the row-order writes and the lane-contiguous reads
-// (stride 16 or 32 words) over all 64 banks.
+// Padded LDS index of row r in a chunk's key transpose: one spare word per
+// 64 rows spreads both the row-order writes and the lane-contiguous reads
+// (stride 16 words) over all 64 banks.
 __device__ __forceinline__ int tpad(int r) { return r + (r >> 6); }
 
 __device__ __forceinline__ uint32_t score_key(float f) {
@@ -101,73 +96,88 @@ __device__ __forceinline__ uint32_t digit_mask(int pass) { return pass == 2 ? 10
 // After pass `pass`'s histogram is complete: find the bin that holds the
 // rem-th largest counted key (bins scanned from the top; bin 0 is first
 // reduced by `excess` uncounted keys) and narrow prefix/mask/rem to it.
+// Lane slot i (thread i, or lane l of the chosen wave range) covers bins
+// dmask - 2i and dmask - 2i - 1. One barrier: each wave publishes its
+// range's total, then every wave finds the range holding the rem-th key
+// from the totals, re-reads that range's bins and finds the bin itself, so
+// all waves reach the same result with no broadcast. sm.wtot is free again
+// once every wave has passed the caller's next barrier.
 __device__ __forceinline__ void pick_bin(PickSmem& sm, int pass, uint32_t excess, uint32_t& prefix,
                                          uint32_t& mask, uint32_t& rem, int tid, int lane, int wave) {
     const int shift = digit_shift(pass);
     const uint32_t dmask = digit_mask(pass);
     const uint32_t* h = sm.hist + pass * NB;
-    const int b0 = (int)dmask - 2 * tid, b1 = b0 - 1;  // two bins per thread, from the top
-    uint32_t c0 = b0 >= 0 ? h[b0] : 0u, c1 = b1 >= 0 ? h[b1] : 0u;
-    if (b0 == 0) c0 -= excess;
-    if (b1 == 0) c1 -= excess;
+    auto bins = [&](int i, uint32_t& c0, uint32_t& c1) {
+        const int b0 = (int)dmask - 2 * i, b1 = b0 - 1;
+        c0 = b0 >= 0 ? h[b0] : 0u;
+        c1 = b1 >= 0 ? h[b1] : 0u;
+        if (b0 == 0) c0 -= excess;
+        if (b1 == 0) c1 -= excess;
+    };
+    uint32_t c0, c1;
+    bins(tid, c0, c1);
     const uint32_t inc = wave_scan(c0 + c1);
     if (lane == 63) sm.wtot[wave][0] = inc;
     __syncthreads();
-    uint32_t before = inc - (c0 + c1);
-#pragma unroll
-    for (int w = 0; w < NW; ++w) before += (w < wave) ? sm.wtot[w][0] : 0u;
-    if (before < rem && rem <= before + c0) {
-        sm.pick[pass][0] = (uint32_t)b0;
-        sm.pick[pass][1] = rem - before;
-    } else if (before + c0 < rem && rem <= before + c0 + c1) {
-        sm.pick[pass][0] = (uint32_t)b1;
-        sm.pick[pass][1] = rem - before - c0;
-    }
-    __syncthreads();
-    prefix |= sm.pick[pass][0] << shift;
+    // The wave range W holding the rem-th key (rem >= 1 keys are counted).
+    const uint32_t wt = lane < NW ? sm.wtot[lane][0] : 0u;
+    const uint32_t winc = wave_scan(wt);
+    const uint64_t wb = __ballot(lane < NW && winc >= rem);
+    const int W = wb ? (int)__builtin_ctzll(wb) : NW - 1;
+    const uint32_t wbefore = (uint32_t)__builtin_amdgcn_readlane((int)(winc - wt), W);
+    // ... and the lane slot inside it.
+    uint32_t d0, d1;
+    bins(64 * W + lane, d0, d1);
+    const uint32_t dinc = wave_scan(d0 + d1);
+    const uint64_t lb = __ballot(wbefore + dinc >= rem);
+    const int L = lb ? (int)__builtin_ctzll(lb) : 63;
+    const uint32_t before = wbefore + (uint32_t)__builtin_amdgcn_readlane((int)(dinc - d0 - d1), L);
+    const uint32_t d0l = (uint32_t)__builtin_amdgcn_readlane((int)d0, L);
+    const uint32_t top = dmask - 2u * (uint32_t)(64 * W + L);
+    const bool first = rem <= before + d0l;
+    prefix |= (first ? top : top - 1u) << shift;
     mask |= dmask << shift;
-    rem = sm.pick[pass][1];
+    rem = first ? rem - before : rem - before - d0l;
 }
 
-// Prompts of at most NW*64*WU rows: every key in registers.
-template <int WU>  // WU <= 32: a lane's rows fit one 32-bit mask
-__device__ __forceinline__ void select_registers(Smem& sm, const SeqDesc& sd,
+// Prompts of at most NW*64*WU rows: every key in registers. Wave w holds
+// rows 64*WU*w + 64u + lane (register u), so the rows split into NW slices
+// of 64*WU consecutive rows, slice w being exactly wave w's rows. Each of
+// the prompt's NW workgroups finds the threshold from every key on its own
+// (the same integer steps on the same keys, so every workgroup reaches the
+// same T and rem) and writes the kept rows of slice g = its index within
+// the prompt; no workgroup waits for or reads from another.
+template <int WU>  // WU <= 32
+__device__ __forceinline__ void select_registers(RegSmem& sm, const SeqDesc& sd, int g,
                                                  const float* __restrict__ scores,
                                                  int32_t* __restrict__ kept, int tid, int lane,
                                                  int wave) {
-    static_assert(WU <= 32, "a lane's rows must fit one 32-bit mask");
     const int32_t n_doc = sd.doc_end - sd.doc_begin;
     const int32_t k = sd.k_doc;
     const int mode = (k == 0) ? 0 : (k == n_doc ? 1 : 2);  // keep no / all / top-k document rows
     const int32_t wbase = wave * 64 * WU;
-    const int32_t rbase = (wave * 64 + lane) * WU;  // this lane's WU consecutive rows
     uint32_t key[WU];
     uint32_t thr = 0, rem = 0;
     if (mode == 2) {
         for (int i = tid; i < HTOT; i += ST) sm.hist[i] = 0u;
         float f[WU];
 #pragma unroll
-        for (int u = 0; u < WU; ++u) {  // row order, clamped into the document: every load is valid
+        for (int u = 0; u < WU; ++u) {  // clamped into the document: every load is valid
             const int32_t r = wbase + u * 64 + lane;
             f[u] = scores[sd.start + min(max(r, sd.doc_begin), sd.doc_end - 1)];
         }
         // The histograms are clear once every wave passes this barrier; it
         // does not wait for the score loads, which are still in flight.
         ring_barrier();
-        // Pass 0 counts every key, in row order as the loads return (a
-        // histogram does not depend on the order), while the keys are also
-        // staged for the transpose.
+        // Pass 0 counts every key as its load returns.
 #pragma unroll
         for (int u = 0; u < WU; ++u) {
             const int32_t r = wbase + u * 64 + lane;
-            const uint32_t kk = (r >= sd.doc_begin && r < sd.doc_end) ? score_key(f[u]) : 0u;
-            sm.stage[tpad(r)] = kk;
-            atomicAdd(&sm.hist[kk >> 21], 1u);
+            key[u] = (r >= sd.doc_begin && r < sd.doc_end) ? score_key(f[u]) : 0u;
+            atomicAdd(&sm.hist[key[u] >> 21], 1u);
         }
-        __syncthreads();  // keys staged, pass 0's histogram complete
-#pragma unroll
-        for (int u = 0; u < WU; ++u) key[u] = sm.stage[tpad(rbase + u)];
-        // Rows of this workgroup's range that are not document rows (key 0).
+        __syncthreads();  // pass 0's histogram complete
+        // Rows of the register range that are not document rows (key 0).
         const uint32_t npad = (uint32_t)(NW * 64 * WU - n_doc);
         uint32_t prefix = 0, mask = 0;
         rem = (uint32_t)k;
@@ -189,20 +199,23 @@ __device__ __forceinline__ void select_registers(Smem& sm, const SeqDesc& sd,
         for (int u = 0; u < WU; ++u) key[u] = 0u;
     }
 
-    // Bit u of each mask describes row rbase + u. A lane's rows are
-    // consecutive, so "inside the prompt" and "inside the document" are bit
-    // ranges; only the key comparisons are per row.
-    auto range_bits = [&](int32_t lo, int32_t hi) -> uint32_t {  // rows [lo, hi) of this lane
-        const int32_t a = min(max(lo - rbase, 0), WU), b = min(max(hi - rbase, 0), WU);
-        const uint32_t upto_b = b >= 32 ? 0xffffffffu : ((1u << b) - 1u);
-        const uint32_t upto_a = a >= 32 ? 0xffffffffu : ((1u << a) - 1u);
-        return upto_b & ~upto_a;
+    // A row is "above" (inside the prompt and outside the document, or a
+    // document key > T; every document row when all are kept) or "tied" (a
+    // document key == T). Kept: the above rows and the first rem tied rows
+    // in row order; a kept row's slot is (#above before it) + min(#tied
+    // before it, rem).
+    // Bit u of the lane's masks describes its row wbase + 64u + lane. The
+    // prompt and the document are row ranges, so for each lane they are
+    // ranges of u; only the key comparisons are per row.
+    auto u_bound = [&](int32_t row) -> int {  // first u whose row is >= row
+        return min(max((row - wbase - lane + 63) >> 6, 0), WU);
     };
-    const uint32_t in_len = range_bits(0, sd.len);
-    const uint32_t in_doc = range_bits(sd.doc_begin, sd.doc_end);
+    auto bits_below = [](int b) -> uint32_t { return b >= 32 ? 0xffffffffu : ((1u << b) - 1u); };
+    const uint32_t in_len = bits_below(u_bound(sd.len));
+    const uint32_t in_doc = bits_below(u_bound(sd.doc_end)) & ~bits_below(u_bound(sd.doc_begin));
     uint32_t ma_bits, mt_bits;  // above / tied
     if (mode == 2) {
-        uint32_t gt_bits = 0, eq_bits = 0;
+        uint32_t gt_bits = 0u, eq_bits = 0u;
 #pragma unroll
         for (int u = 0; u < WU; ++u) {
             gt_bits |= (key[u] > thr ? 1u : 0u) << u;
@@ -214,64 +227,63 @@ __device__ __forceinline__ void select_registers(Smem& sm, const SeqDesc& sd,
         ma_bits = mode == 1 ? in_len : (in_len & ~in_doc);
         mt_bits = 0u;
     }
-    const uint32_t ca = (uint32_t)__popc(ma_bits), ct = (uint32_t)__popc(mt_bits);
-    const uint32_t ia = wave_scan(ca), it = wave_scan(ct);
+    // Every wave's above / tied totals; wave g also leaves its masks for the
+    // workgroup, which ranks slice g's rows 64 per wave.
+    const uint32_t ia = wave_scan((uint32_t)__popc(ma_bits)), it = wave_scan((uint32_t)__popc(mt_bits));
     if (lane == 63) {
-        sm.wtot[wave][0] = ia;
-        sm.wtot[wave][1] = it;
+        sm.ctot[wave][0] = ia;
+        sm.ctot[wave][1] = it;
     }
-    __syncthreads();  // also: every lane has read its keys from the stage
-    uint32_t pa = ia - ca, pt = it - ct;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        pa += (w < wave) ? sm.wtot[w][0] : 0u;
-        pt += (w < wave) ? sm.wtot[w][1] : 0u;
-    }
-    const uint32_t n_kept = (uint32_t)sd.n_kept;
-    if (WU == 16 && mt_bits == 0u) {
-        // A lane with no tied row (all but a few): its kept rows are exactly
-        // its above rows, in consecutive slots from pa + min(pt, rem), so
-        // only their bits are visited. (At 32 rows per lane the longer
-        // per-bit loop does not pay.)
-        uint32_t m = ma_bits;
-        uint32_t slot = pa + min(pt, rem);
-        const uint32_t row0 = (uint32_t)(sd.start + rbase);
-        while (m != 0u) {
-            const int u = __builtin_ctz(m);
-            if (slot < n_kept) sm.stage[slot] = row0 + (uint32_t)u;  // always true when the counts are right
-            ++slot;
-            m &= m - 1u;
-        }
-    } else {
-        const int trash = RMAX + RMAX / 64 + lane;
-#pragma unroll
-        for (int u = 0; u < WU; ++u) {
-            const uint32_t above = (ma_bits >> u) & 1u, tied = (mt_bits >> u) & 1u;
-            const uint32_t slot = pa + min(pt, rem);
-            // slot < n_kept always holds for a kept row when the counts are right
-            const uint32_t keep = (above | (tied & (uint32_t)(pt < rem))) & (uint32_t)(slot < n_kept);
-            sm.stage[keep ? (int)slot : trash] = (uint32_t)(sd.start + rbase + u);
-            pa += above;
-            pt += tied;
-        }
+    if (wave == g) {
+        sm.em[lane][0] = ma_bits;
+        sm.em[lane][1] = mt_bits;
     }
     __syncthreads();
-    for (int j = tid; j < sd.n_kept; j += ST) kept[sd.kept_off + j] = (int32_t)sm.stage[j];
+    uint32_t pa = 0, pt = 0;  // above / tied rows of the slices before g
+    for (int w = 0; w < g; ++w) {
+        pa += sm.ctot[w][0];
+        pt += sm.ctot[w][1];
+    }
+    const uint32_t ea = sm.em[lane][0], et = sm.em[lane][1];
+    const uint32_t n_kept = (uint32_t)sd.n_kept;
+    const int32_t sbase = g * 64 * WU;  // slice g's first row
+#pragma unroll
+    for (int j = 0; j < WU / NW; ++j) {
+        const int u = wave + NW * j;  // this wave ranks the slice's rows 64u .. 64u + 63
+        // rows of the slice before row 64u: the bits below u, over all lanes
+        const uint32_t lo = bits_below(u);
+        const uint32_t sa = wave_scan((uint32_t)__popc(ea & lo)), sti = wave_scan((uint32_t)__popc(et & lo));
+        const uint32_t ua = pa + (uint32_t)__builtin_amdgcn_readlane((int)sa, 63);
+        const uint32_t ut = pt + (uint32_t)__builtin_amdgcn_readlane((int)sti, 63);
+        const bool above = (ea >> u) & 1u, tied = (et >> u) & 1u;
+        const uint64_t ba = __ballot(above), bt = __ballot(tied);
+        const uint32_t la = __builtin_amdgcn_mbcnt_hi((uint32_t)(ba >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ba, 0u));
+        const uint32_t lt = __builtin_amdgcn_mbcnt_hi((uint32_t)(bt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bt, 0u));
+        const uint32_t tr = ut + lt;  // tied rows before this one
+        const uint32_t slot = ua + la + min(tr, rem);
+        // slot < n_kept always holds for a kept row when the counts are right
+        if ((above || (tied && tr < rem)) && slot < n_kept)
+            kept[sd.kept_off + slot] = (int32_t)(sd.start + sbase + u * 64 + lane);
+    }
 }
 
+// Grid: NW workgroups per prompt (prompt b = blockIdx / NW, slice g =
+// blockIdx % NW). Slices past the prompt's end have nothing to write and
+// exit at once; prompts above SEL_REG_MAX rows take the kernels below.
 __global__ __launch_bounds__(ST) void select_kernel(const float* __restrict__ scores, SeqTable t,
                                                     int32_t* __restrict__ kept) {
-    __shared__ Smem sm;
-    const SeqDesc sd = t.s[blockIdx.x];
+    __shared__ RegSmem sm;
+    const SeqDesc sd = t.s[blockIdx.x / NW];
+    const int g = (int)(blockIdx.x % NW);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave tests stay scalar
     static_assert(ST * 32 == SEL_REG_MAX, "register path bound");
-    if (sd.len <= ST * 16)
-        select_registers<16>(sm, sd, scores, kept, tid, lane, wave);
-    else if (sd.len <= ST * 32)
-        select_registers<32>(sm, sd, scores, kept, tid, lane, wave);
-    // longer prompts: the multi-workgroup kernels below
+    if (sd.len <= ST * 16) {
+        if (g * 64 * 16 < sd.len) select_registers<16>(sm, sd, g, scores, kept, tid, lane, wave);
+    } else if (sd.len <= ST * 32) {
+        if (g * 64 * 32 < sd.len) select_registers<32>(sm, sd, g, scores, kept, tid, lane, wave);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -675,7 +687,7 @@ hipError_t launch_select(const float* scores, const SeqTable& t, const LongTable
                          int32_t* kept, hipStream_t st) {
     bool any_short = false;
     for (int b = 0; b < t.n; ++b) any_short |= t.s[b].len > 0 && t.s[b].len <= SEL_REG_MAX;
-    if (any_short) hipLaunchKernelGGL(select_kernel, dim3((unsigned)t.n), dim3(ST), 0, st, scores, t, kept);
+    if (any_short) hipLaunchKernelGGL(select_kernel, dim3((unsigned)t.n * NW), dim3(ST), 0, st, scores, t, kept);
     if (lt.n == 0) return hipGetLastError();
     hipLaunchKernelGGL(sel_zero_kernel, dim3((unsigned)lt.n * 6), dim3(256), 0, st, (uint32_t*)workspace,
                        (int64_t)lt.n * 3 * NB);
