@@ -144,17 +144,36 @@ def traffic_summary(fetch_csv, write_csv):
     print(json.dumps(out, indent=1, sort_keys=True))
 
 
-def kernel_times(torch, layer, reps, cold_buf=None):
+class Evictor:
+    """Evicts the caches before a cold step: a 1 GiB device write (the 256 MB
+    Infinity Cache and the L2s then hold none of the layer's inputs), and, with
+    read=True, a 1 GiB read after it, which replaces the write's dirty lines
+    with clean ones, so the timed kernels do not also pay for writing back
+    the eviction buffer."""
+
+    def __init__(self, torch, dev, read=True):
+        self.torch = torch
+        self.wbuf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        self.rbuf = torch.ones(1 << 28, dtype=torch.float32, device=dev) if read else None
+        self.acc = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.wbuf.fill_(3.0)
+        if self.rbuf is not None:
+            self.acc.add_(self.rbuf.sum())
+
+
+def kernel_times(torch, layer, reps, evict=None):
     """Median per-kernel durations (us) of the four steps, HIP events around each
-    launch on the layer's stream. With cold_buf, a 1 GiB device write before
-    every step evicts the 256 MB Infinity Cache, so each kernel reads its
-    inputs from HBM (the writes of the step's earlier kernels stay cached)."""
+    launch on the layer's stream. With evict (an Evictor), the caches are
+    evicted before every step, so each kernel reads its inputs from HBM (the
+    writes of the step's earlier kernels stay cached)."""
     stream = torch.cuda.current_stream()
     names = ["gate", "select", "compact", "attention"]
     samples = {k: [] for k in names}
     for _ in range(reps):
-        if cold_buf is not None:
-            cold_buf.fill_(3.0)
+        if evict is not None:
+            evict()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
         ev[0].record(stream)
         layer.gate()
@@ -288,20 +307,27 @@ def measure_extras(torch, tg, layer, w, steps, dev):
     # Per-step percentiles (warm) and the layer with the Infinity Cache evicted first.
     t = timed(layer.run, steps)
     out["layer_us_warm"] = {"p10": round(pct(t, 0.1), 2), "p50": round(pct(t, 0.5), 2), "p90": round(pct(t, 0.9), 2)}
-    cold = []
-    for _ in range(20):
-        dst.fill_(2.0)  # 1 GiB written: the 256 MB Infinity Cache holds none of the layer's inputs
-        cold += timed(layer.run, 1)
-    cold.sort()
-    out["layer_us_cold"] = {"p10": round(pct(cold, 0.1), 2), "p50": round(pct(cold, 0.5), 2),
-                            "p90": round(pct(cold, 0.9), 2),
-                            "note": "a 1 GiB device write before each step evicts the Infinity Cache"}
-    # Per-kernel times with the Infinity Cache evicted before every step.
-    kc = kernel_times(torch, layer, 20, cold_buf=dst)
-    work = algorithmic_work(w, layer.m)
-    out["kernels_us_cold"] = kc
-    out["kernel_rooflines_cold"] = rooflines_of(work, kc, "cold")
     del src, dst
+    torch.cuda.empty_cache()
+    work = algorithmic_work(w, layer.m)
+    ev_read, ev_write = Evictor(torch, dev, read=True), Evictor(torch, dev, read=False)
+    for name, evict, note in (
+            ("cold", ev_read, "a 1 GiB device write, then a 1 GiB read, before each step: no cache holds the "
+                              "layer's inputs, and the eviction leaves no dirty lines to write back"),
+            ("cold_write_evicted", ev_write, "a 1 GiB device write before each step; its dirty lines are "
+                                             "written back while the step runs")):
+        cold = []
+        for _ in range(20):
+            evict()
+            cold += timed(layer.run, 1)
+        cold.sort()
+        out[f"layer_us_{name}"] = {"p10": round(pct(cold, 0.1), 2), "p50": round(pct(cold, 0.5), 2),
+                                   "p90": round(pct(cold, 0.9), 2), "note": note}
+        # Per-kernel times with the caches evicted before every step.
+        kc = kernel_times(torch, layer, 20, evict=evict)
+        out[f"kernels_us_{name}"] = kc
+        out[f"kernel_rooflines_{name}"] = rooflines_of(work, kc, name)
+    del ev_read, ev_write
     # Decode after this prefill: one new token over the kept K/V cache.
     out["decode_qwen16k"] = measure_decode(torch, tg, layer, timed, pct)
     # Backward of this layer's token-gated attention (the gradient path to the gate).
@@ -609,13 +635,17 @@ def measure_configs(torch, tg, dev, timed, pct):
     lay.run()
     work = algorithmic_work(w, lay.m)
     kw = kernel_times(torch, lay, 20)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    kc = kernel_times(torch, lay, 10, cold_buf=flush)
-    del flush, lay
+    evict = Evictor(torch, dev, read=True)
+    kc = kernel_times(torch, lay, 10, evict=evict)
+    evict.rbuf = None
+    kcw = kernel_times(torch, lay, 10, evict=evict)
+    del evict, lay
     pruned["kernels_us_warm"] = kw
     pruned["kernels_us_cold"] = kc
+    pruned["kernels_us_cold_write_evicted"] = kcw
     pruned["kernel_rooflines_warm"] = rooflines_of(work, kw, "warm")
     pruned["kernel_rooflines_cold"] = rooflines_of(work, kc, "cold")
+    pruned["kernel_rooflines_cold_write_evicted"] = rooflines_of(work, kcw, "cold_write_evicted")
     full = run_one(w, [p0._replace(k_doc=p0.n_doc)], 3, attn_reps=3, decode=True)
     out["long128k"] = {"n_rows": w.n_rows, "k_doc": p0.k_doc, **pruned,
                        "unpruned": {k: full[k] for k in ("kept_rows", "attention_us", "attention_tflops",
