@@ -104,6 +104,28 @@ def test_select_single_prompt(kind):
         check_select(s, [Prompt(0, 16384, 0, 16000, k)])
 
 
+def test_select_slice_edges():
+    # A prompt of up to 32768 rows is ranked in 16 slices (1024 or 2048 rows,
+    # one per workgroup): document edges on slice boundaries, runs of tied
+    # keys crossing many slices, last slices of one row, and prompts at
+    # unaligned offsets in one batch.
+    note("select slices: document edges on slice boundaries, ties across slices, one-row last slices")
+    s = make_scores(16384, seed=70, kind="few")
+    doc = s[1024:15360]
+    n1, n0 = int((doc == 1.0).sum()), int((doc == 0.0).sum())
+    for k in (1, n1 - 1, n1, n1 + 1, n1 + n0 // 2, n1 + n0, 14335):
+        check_select(s, [Prompt(0, 16384, 1024, 15360, k)])
+    s = make_scores(4097, seed=71, kind="ties")
+    for k in (1, 2048, 4096):
+        check_select(s, [Prompt(0, 4097, 0, 4097, k)])
+    s = make_scores(32768, seed=72, kind="few")
+    for k in (3, 12000, 28671):
+        check_select(s, [Prompt(0, 32768, 2048, 30720, k)])
+    s = make_scores(60000, seed=73, kind="ties")
+    check_select(s, [Prompt(7, 2049, 1, 2048, 1000), Prompt(2056, 1025, 1024, 1025, 1),
+                     Prompt(3081, 20000, 3000, 19000, 4321), Prompt(23081, 32767, 0, 32767, 32766)])
+
+
 def test_select_nan_inf_and_spans():
     note("select NaN/inf, inner document span")
     s = make_scores(5000, seed=5)
