@@ -101,9 +101,10 @@ __device__ __forceinline__ uint32_t digit_mask(int pass) { return pass == 2 ? 10
 // range's total, then every wave finds the range holding the rem-th key
 // from the totals, re-reads that range's bins and finds the bin itself, so
 // all waves reach the same result with no broadcast. sm.wtot is free again
-// once every wave has passed the caller's next barrier.
-__device__ __forceinline__ void pick_bin(PickSmem& sm, int pass, uint32_t excess, uint32_t& prefix,
-                                         uint32_t& mask, uint32_t& rem, int tid, int lane, int wave) {
+// once every wave has passed the caller's next barrier. Returns the chosen
+// bin's count.
+__device__ __forceinline__ uint32_t pick_bin(PickSmem& sm, int pass, uint32_t excess, uint32_t& prefix,
+                                             uint32_t& mask, uint32_t& rem, int tid, int lane, int wave) {
     const int shift = digit_shift(pass);
     const uint32_t dmask = digit_mask(pass);
     const uint32_t* h = sm.hist + pass * NB;
@@ -133,11 +134,13 @@ __device__ __forceinline__ void pick_bin(PickSmem& sm, int pass, uint32_t excess
     const int L = lb ? (int)__builtin_ctzll(lb) : 63;
     const uint32_t before = wbefore + (uint32_t)__builtin_amdgcn_readlane((int)(dinc - d0 - d1), L);
     const uint32_t d0l = (uint32_t)__builtin_amdgcn_readlane((int)d0, L);
+    const uint32_t d1l = (uint32_t)__builtin_amdgcn_readlane((int)d1, L);
     const uint32_t top = dmask - 2u * (uint32_t)(64 * W + L);
     const bool first = rem <= before + d0l;
     prefix |= (first ? top : top - 1u) << shift;
     mask |= dmask << shift;
     rem = first ? rem - before : rem - before - d0l;
+    return first ? d0l : d1l;
 }
 
 // Prompts of at most NW*64*WU rows: every key in registers. Wave w holds
@@ -181,9 +184,15 @@ __device__ __forceinline__ void select_registers(RegSmem& sm, const SeqDesc& sd,
         const uint32_t npad = (uint32_t)(NW * 64 * WU - n_doc);
         uint32_t prefix = 0, mask = 0;
         rem = (uint32_t)k;
-        pick_bin(sm, 0, npad, prefix, mask, rem, tid, lane, wave);
+        uint32_t cnt = pick_bin(sm, 0, npad, prefix, mask, rem, tid, lane, wave);
+        // When the chosen bin holds exactly rem keys, all of them are kept:
+        // the threshold is then the key just below the bin (prefix - 1, the
+        // lower digits zero), with no tied row kept, and the later passes
+        // are skipped. (A bin with prefix 0 would need T = -1, so it always
+        // takes the full passes.) The test is uniform over the workgroup.
+        int pass = 1;
 #pragma nounroll
-        for (int pass = 1; pass < 3; ++pass) {
+        for (; pass < 3 && !(cnt == rem && prefix != 0u); ++pass) {
             const int shift = digit_shift(pass);
             const uint32_t dmask = digit_mask(pass);
             uint32_t* const h = sm.hist + pass * NB;
@@ -191,9 +200,14 @@ __device__ __forceinline__ void select_registers(RegSmem& sm, const SeqDesc& sd,
             for (int u = 0; u < WU; ++u)
                 if ((key[u] & mask) == prefix) atomicAdd(&h[(key[u] >> shift) & dmask], 1u);
             __syncthreads();
-            pick_bin(sm, pass, prefix == 0 ? npad : 0u, prefix, mask, rem, tid, lane, wave);
+            cnt = pick_bin(sm, pass, prefix == 0 ? npad : 0u, prefix, mask, rem, tid, lane, wave);
         }
-        thr = prefix;
+        if (pass < 3) {
+            thr = prefix - 1u;
+            rem = 0u;
+        } else {
+            thr = prefix;
+        }
     } else {
 #pragma unroll
         for (int u = 0; u < WU; ++u) key[u] = 0u;
