@@ -26,6 +26,8 @@
 //     kept. Pass 0 counts each key as its load returns. The steps are
 //     integer and see the same keys in every workgroup of the prompt, so
 //     all of them reach the same T and rem; none reads another's results.
+//     A pass whose chosen bin is kept whole ends the search early (T is
+//     then the key just below the bin and rem is 0).
 //  3. Emission: a row is "above" (outside the document, or key > T) or
 //     "tied" (document key == T). Kept rows are the above rows and the
 //     first rem tied rows; a kept row's output slot is (#above before it) +
